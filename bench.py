@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Throughput of one tensor-parallel rank's MLP shard on one MI355X.
+
+Workload: the t = 8 shard of a Megatron MLP at hidden 8192 (ffn 32768, f =
+4096 per rank) over 16384 tokens.  One step runs ALL 8 rank shards back to
+back on the one GPU (Z_r = GeLU(X A_r) B_r, fp32 partials), each through the
+C-ABI entry point tp_mlp_shard_fwd; inputs are resident in HBM before the
+timed region.  The headline value is TFLOP/s over the step (the per-shard
+rate: 8 shards of 4*M*h*f FLOP in the step's time).
+
+Also reported:
+  roofline      the dominant kernel (column GEMM + GeLU, or row GEMM), timed
+                live with HIP events on the launch stream, against the bf16
+                dense MFMA peak; ``traffic`` from committed rocprofv3 counter
+                summaries when they match the current kernel source
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of rows of the same
+                shard, on this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s + % bf16 MFMA peak, t=8 MLP shard (h=8192, 16384 tok), 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/gemm_bf16.hip",
+                  "megatron_tensor_transformer_tp_amd/csrc/device_common.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary, or
+    None if there is none or it was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_sha") != kernel_source_sha():
+        return None
+    entry = data.get("kernels", {}).get(kernel)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s: float):
+    """Time the fp64 oracle on rows of rank 0's shard (the MLP is row-independent,
+    so rows/s is a true rate).  Returns the JSON object."""
+    import oracle
+    from megatron_tensor_transformer_tp_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    a0 = inputs.bf16_bits_to_f32(inputs.mlp_a_block(wl, 0)).astype(np.float64)
+    b0 = inputs.bf16_bits_to_f32(inputs.mlp_b_block(wl, 0)).astype(np.float64)
+
+    def run(rows: int) -> float:
+        x = inputs.bf16_bits_to_f32(inputs.mlp_x_rows(wl, 0, rows)).astype(np.float64)
+        t0 = time.perf_counter()
+        h = oracle.column_linear(x, a0, apply_gelu=True)
+        oracle.row_linear(h, b0, rank=0)
+        return time.perf_counter() - t0
+
+    probe_rows = 128
+    t_probe = run(probe_rows)
+    rows = int(np.clip(probe_rows * target_s / max(t_probe, 1e-6), probe_rows, wl.tokens))
+    rows = max(probe_rows, rows // probe_rows * probe_rows)
+    elapsed = run(rows)
+    flops = 4.0 * rows * wl.hidden * wl.f
+    return {
+        "value": round(flops / elapsed / 1e12, 4),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"rows 0..{rows - 1} of rank 0's shard ({rows} of {wl.tokens} tokens, "
+                   f"hidden {wl.hidden}, f {wl.f}), fp64 NumPy/OpenBLAS + SciPy erfc; "
+                   f"{elapsed:.2f} s wall, {rows / elapsed:.1f} tokens/s"),
+        "seconds": round(elapsed, 3),
+        "tokens_per_s": round(rows / elapsed, 2),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="t8_h8192_m16384")
+    ap.add_argument("--kernel-reps", type=int, default=10,
+                    help="launches per kernel for the live per-kernel timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the bounded oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's shard only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path: the exchange step (a SUM All-Reduce of the "
+              "partials) is not implemented.", file=sys.stderr)
+        return 2
+
+    import torch
+    from megatron_tensor_transformer_tp_amd import binding, inputs
+
+    if not os.path.exists(binding.LIB_PATH):
+        from megatron_tensor_transformer_tp_amd.build import build
+        build()
+    binding.lib()
+    wl = inputs.MLP_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    log(f"workload {wl.name}: tokens {wl.tokens}, hidden {wl.hidden}, ffn {wl.ffn}, t {wl.t}")
+    t_gen = time.perf_counter()
+    x = up(inputs.mlp_x_rows(wl))
+    a = [up(inputs.mlp_a_block(wl, r)) for r in range(wl.t)]
+    b = [up(inputs.mlp_b_block(wl, r)) for r in range(wl.t)]
+    out_dt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    z = [torch.empty((wl.tokens, wl.hidden), dtype=out_dt, device=dev) for _ in range(wl.t)]
+    ws = torch.empty(binding.tp_mlp_shard_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t,
+                                                          torch.bfloat16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs generated and resident in HBM ({time.perf_counter() - t_gen:.1f} s)")
+
+    def step():
+        for r in range(wl.t):
+            binding.tp_mlp_shard_fwd(x, a[r], b[r], z[r], ws, ffn=wl.ffn, t=wl.t, rank=r, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    flops_step = wl.flops_per_shard() * wl.t
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (events), wall {wall * 1e3 / args.steps:.3f} ms/step")
+
+    # ---- per-kernel live timing (same launches as inside the step, rank 0 operands)
+    h_view = ws[: wl.tokens * wl.f * 2].view(torch.bfloat16).view(wl.tokens, wl.f)
+    kernels = {
+        "column_gemm_gelu": (lambda: binding.tp_column_linear(x, a[0], h_view, ffn=wl.ffn, t=wl.t, rank=0,
+                                                              apply_gelu=True, stream=stream),
+                             2.0 * wl.tokens * wl.hidden * wl.f,
+                             # algorithmic bytes: X + A_i read, H written (bf16)
+                             2.0 * (wl.tokens * wl.hidden + wl.hidden * wl.f + wl.tokens * wl.f)),
+        "row_gemm": (lambda: binding.tp_row_linear(h_view, b[0], z[0], ffn=wl.ffn, t=wl.t, rank=0,
+                                                   stream=stream),
+                     2.0 * wl.tokens * wl.f * wl.hidden,
+                     # H + B_i read (bf16), Z written (fp32)
+                     2.0 * (wl.tokens * wl.f + wl.f * wl.hidden) + 4.0 * wl.tokens * wl.hidden),
+    }
+    per_kernel = {}
+    for name, (fn, flops, nbytes) in kernels.items():
+        fn()
+        torch.cuda.synchronize()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k0.record(stream)
+        for _ in range(args.kernel_reps):
+            fn()
+        k1.record(stream)
+        torch.cuda.synchronize()
+        us = k0.elapsed_time(k1) * 1e3 / args.kernel_reps
+        per_kernel[name] = {"avg_us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+                            "algorithmic_bytes": int(nbytes), "flops": int(flops)}
+        log(f"kernel {name}: {us:.1f} us/launch, {flops / (us * 1e-6) / 1e12:.1f} TFLOP/s")
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["avg_us"])
+    achieved = per_kernel[dom]["tflops"]
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy of 1 GiB x3 done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"cpu baseline: {cpu['sample']}")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, rounded to bf16)",
+        "config": {
+            "workload": (f"{wl.name}: all {wl.t} rank shards of a t={wl.t} Megatron MLP "
+                         f"(hidden {wl.hidden}, ffn {wl.ffn}, f {wl.f}) over {wl.tokens} tokens, "
+                         "back to back per step; fp32 partial sums"),
+            "tokens": wl.tokens, "hidden": wl.hidden, "ffn": wl.ffn, "t": wl.t,
+            "shards_per_step": wl.t, "parallelism": "one rank's shard per launch, 1 GPU",
+        },
+        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "ms_per_shard": round(ms_step / wl.t, 4),
+        "tokens_per_s_per_shard": round(wl.tokens / (ms_step / wl.t * 1e-3), 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": dom,
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(dom),
+            "algorithmic_bytes": per_kernel[dom]["algorithmic_bytes"],
+            "avg_us": per_kernel[dom]["avg_us"],
+        },
+        "kernels": per_kernel,
+        "kernel_source_sha": kernel_source_sha(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

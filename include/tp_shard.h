@@ -1,0 +1,183 @@
+/*
+ * tp_shard.h -- C ABI of the tensor-parallel MLP / attention shard library
+ * (one rank's share of a Megatron-style Transformer block, gfx950 / MI355X).
+ *
+ * Notation.  X [M, h] is the input (M = tokens = seq x batch, h = hidden),
+ * A [h, F] and B [F, h] are the two MLP weights (F = ffn width, 4h in the
+ * standard block), t is the tensor-parallel degree and f = F / t the shard
+ * width.  Rank r owns the contiguous index block S_r = [r*f, (r+1)*f): columns
+ * S_r of A (A_r, [h, f]) and rows S_r of B (B_r, [f, h]).
+ *
+ * Passages defining the operations (page titles as printed on the pages):
+ *   - Column-parallel linear: W split by output columns, X replicated, each
+ *     rank produces its column block of the output with no communication.
+ *     Tencent Hunyuan AI-Infra interview write-up, 参考解析 (first paragraph);
+ *     列并行 tutorial (aiqz.cc), 切分原理 and 数学基础; Megatron expert
+ *     interview Level 2 (blog.cptz.space), M025.
+ *   - GeLU(z) = z * Phi(z), elementwise, valid on each column block:
+ *     列并行 tutorial, MLP 应用.
+ *   - Row-parallel linear: W split by input rows, the input split on its last
+ *     dimension, each rank produces a full-hidden partial that the ranks sum:
+ *     Megatron Level 2, M026; distributed-parallelism overview
+ *     (talentme.airsota.com), 考点 2.
+ *   - MLP shard = column layer -> GeLU -> row layer with no exchange between
+ *     them: Tencent write-up, FFN paragraph; 列并行 tutorial, MLP 应用;
+ *     Megatron Level 2, M027.
+ *   - Attention shard: heads split over ranks, packed QKV interleaved per
+ *     head, local softmax(Q K^T / sqrt(d)) V, row-parallel output projection:
+ *     Tencent write-up, attention paragraph; Megatron Level 2, M028.
+ *   - Shapes that do not divide are rejected, never padded: 列并行 tutorial,
+ *     切分原理; Megatron Level 2, M031.
+ *
+ * Conventions shared by every entry point.
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; it enqueues kernels on
+ *     `stream` (a hipStream_t passed as void*, NULL = the default stream) and
+ *     returns.  Outputs are valid once the caller synchronises that stream.
+ *   - Matrices are row-major with an explicit leading dimension in ELEMENTS
+ *     (ld >= row width).  bf16 data is the 16-bit bfloat16 bit pattern.
+ *   - The caller passes the LOGICAL (unsharded) ffn / heads plus t and rank;
+ *     the library derives the shard width itself, so the divisibility check
+ *     is always live.  Weight pointers point AT the rank's shard (the library
+ *     never offsets by rank); rank decides who adds the output bias and the
+ *     residual (rank 0 only, so that the sum of the partials is the layer).
+ *   - Alignment: every pointer 16-byte aligned; row widths and leading
+ *     dimensions a multiple of 8 elements (bf16) or 4 elements (fp32).
+ *     Any tokens >= 0 is accepted (tokens == 0 enqueues nothing).
+ *   - Errors: every argument is checked before anything is enqueued; on an
+ *     error nothing is enqueued and a tp_status code is returned.  A failed
+ *     launch returns TP_ERR_HIP.  Nothing is printed, no exception crosses
+ *     the ABI.  Calls are stateless and thread-safe; calls that write the
+ *     same output buffer concurrently race, as with any kernel.
+ *   - Numerics: bf16 inputs are multiplied with fp32 accumulation (MFMA);
+ *     fp32 inputs with fp32 FMA.  GeLU is applied to the fp32 accumulator;
+ *     a bf16 output is rounded to nearest-even.  Inputs must be finite.
+ */
+#ifndef TP_SHARD_H_
+#define TP_SHARD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_INVALID_ARG = 1,   /* null pointer, negative size, ld < width, bad flag */
+  TP_ERR_NOT_DIVISIBLE = 2, /* ffn (or heads) not divisible by t                  */
+  TP_ERR_BAD_RANK = 3,      /* rank outside [0, t) or t < 1                       */
+  TP_ERR_DTYPE = 4,         /* unsupported dtype or dtype combination             */
+  TP_ERR_MISALIGNED = 5,    /* pointer / width / leading dimension misaligned     */
+  TP_ERR_WORKSPACE = 6,     /* workspace missing or smaller than required         */
+  TP_ERR_UNSUPPORTED = 7,   /* valid request outside what the kernels implement   */
+  TP_ERR_HIP = 8            /* a HIP launch failed                                */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* tp_status_string(tp_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int tp_version(void);
+
+/*
+ * Column-parallel linear: Y_i = X A_i (+ a_i), then GeLU if apply_gelu.
+ *   x      [tokens, hidden], ld ldx          (in_dt)
+ *   a_i    [hidden, f], ld lda, f = ffn / t  (in_dt) -- the rank's column block
+ *   bias_i [f] or NULL                       (in_dt) -- the rank's block of a
+ *   y_i    [tokens, f], ld ldy               (out_dt)
+ * dtype pairs (in -> out): bf16 -> bf16, bf16 -> f32, f32 -> f32.
+ */
+tp_status tp_column_linear(const void* x, int64_t ldx, const void* a_i, int64_t lda,
+                           const void* bias_i, void* y_i, int64_t ldy,
+                           int64_t tokens, int64_t hidden, int64_t ffn, int t, int rank,
+                           tp_dtype in_dt, tp_dtype out_dt, int apply_gelu, void* stream);
+
+/*
+ * Elementwise exact GeLU, out[k] = in[k] * Phi(in[k]), k < n.  in and out may
+ * alias exactly (in place) when in_dt == out_dt; partial overlap is not
+ * allowed.  dtype pairs: any of f32/bf16 -> f32/bf16.  n >= 0; pointers
+ * 16-byte aligned.
+ */
+tp_status tp_gelu(const void* in, void* out, int64_t n, tp_dtype in_dt, tp_dtype out_dt,
+                  void* stream);
+
+/*
+ * Row-parallel linear: Z_i = H_i B_i, plus (rank 0 only) bias and residual.
+ *   h_i      [tokens, f], ld ldh, f = ffn / t (in_dt) -- the rank's input block
+ *   b_i      [f, hidden], ld ldb              (in_dt) -- the rank's row block
+ *   bias     [hidden] or NULL                 (in_dt) -- added by rank 0 only
+ *   residual [tokens, hidden], ld ldr, or NULL (in_dt) -- added by rank 0 only
+ *   z_i      [tokens, hidden], ld ldz         (out_dt) -- full-hidden partial
+ * dtype pairs: bf16 -> f32 (partial for t > 1), bf16 -> bf16, f32 -> f32.
+ * On ranks != 0 bias and residual are ignored (they may be NULL).
+ */
+tp_status tp_row_linear(const void* h_i, int64_t ldh, const void* b_i, int64_t ldb,
+                        const void* bias, const void* residual, int64_t ldr,
+                        void* z_i, int64_t ldz,
+                        int64_t tokens, int64_t ffn, int64_t hidden, int t, int rank,
+                        tp_dtype in_dt, tp_dtype out_dt, void* stream);
+
+/*
+ * Bytes of workspace tp_mlp_shard_fwd needs: the GeLU intermediate
+ * H_i [tokens, f] in in_dt (bf16 for bf16 inputs, f32 for f32), rounded up to
+ * 256 bytes.  Returns 0 for invalid arguments (and for tokens == 0).
+ */
+size_t tp_mlp_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int t,
+                                    tp_dtype in_dt);
+
+/*
+ * One rank's MLP shard: Z_i = GeLU(X A_i + a_i) B_i (+ b + R on rank 0).
+ *   x         [tokens, hidden] contiguous (ld = hidden)  (in_dt)
+ *   a_i       [hidden, f], ld lda                          (in_dt)
+ *   b_i       [f, hidden] contiguous (ld = hidden)         (in_dt)
+ *   bias_a_i  [f] or NULL (the rank's block of a)          (in_dt)
+ *   bias_b    [hidden] or NULL (rank 0 only)               (in_dt)
+ *   residual  [tokens, hidden] contiguous or NULL (rank 0) (in_dt)
+ *   z_i       [tokens, hidden] contiguous                  (out_dt)
+ *   workspace >= tp_mlp_shard_workspace_bytes(...), 256-byte aligned; it
+ *             holds H_i between the two GEMMs (one HBM round trip) and is
+ *             scratch: its contents after the call are unspecified.
+ * dtype pairs: bf16 -> f32, bf16 -> bf16, f32 -> f32.
+ */
+tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const void* b_i,
+                           const void* bias_a_i, const void* bias_b, const void* residual,
+                           void* z_i, void* workspace, size_t workspace_bytes,
+                           int64_t tokens, int64_t hidden, int64_t ffn, int t, int rank,
+                           tp_dtype in_dt, tp_dtype out_dt, void* stream);
+
+/*
+ * Bytes of workspace tp_attn_shard_fwd needs (Q, K, V of the local heads and
+ * the local attention output), rounded up to 256 bytes; 0 if invalid.
+ */
+size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int64_t heads,
+                                     int64_t head_dim, int t, tp_dtype in_dt);
+
+/*
+ * One rank's head-local attention shard.
+ *   x       [batch, seq, hidden] contiguous                     (in_dt)
+ *   wqkv_i  [hidden, 3 * hl * head_dim] contiguous, hl = heads / t: the
+ *           rank's column block of the packed QKV weight, laid out per local
+ *           head as [q | k | v] blocks of head_dim columns each  (in_dt)
+ *   wo_i    [hl * head_dim, hidden] contiguous: the rank's row block of the
+ *           output projection                                   (in_dt)
+ *   out_i   [batch, seq, hidden] contiguous full-hidden partial (out_dt)
+ *   causal  0: every query sees every key; 1: key j <= query i only.
+ * Per local head j: O_j = softmax(Q_j K_j^T / sqrt(head_dim)) V_j;
+ * out_i = [O_0 | ... | O_{hl-1}] wo_i.  hidden == heads * head_dim.
+ * dtype pairs: bf16 -> f32, bf16 -> bf16.  head_dim must be 128.
+ */
+tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i, void* out_i,
+                            void* workspace, size_t workspace_bytes,
+                            int64_t batch, int64_t seq, int64_t hidden, int64_t heads,
+                            int64_t head_dim, int causal, int t, int rank,
+                            tp_dtype in_dt, tp_dtype out_dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H_ */

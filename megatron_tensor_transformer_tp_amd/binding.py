@@ -1,0 +1,180 @@
+"""Thin ctypes binding of ``libtp_shard.so`` (C ABI in ``include/tp_shard.h``).
+
+Argument marshalling only: shapes, leading dimensions, dtypes and the current
+HIP stream are read off torch tensors and handed to the C entry points of the
+same names; every step of the computation runs in the library's kernels.
+torch is used for device memory and streams, nothing else.  There is no
+fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtp_shard.so")
+
+TP_F32, TP_BF16 = 0, 1
+
+STATUS_NAMES = {
+    0: "TP_OK", 1: "TP_ERR_INVALID_ARG", 2: "TP_ERR_NOT_DIVISIBLE", 3: "TP_ERR_BAD_RANK",
+    4: "TP_ERR_DTYPE", 5: "TP_ERR_MISALIGNED", 6: "TP_ERR_WORKSPACE", 7: "TP_ERR_UNSUPPORTED",
+    8: "TP_ERR_HIP",
+}
+
+_I64, _INT, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/tp_shard.h
+SIGNATURES = {
+    "tp_status_string": (ctypes.c_char_p, [_INT]),
+    "tp_version": (_INT, []),
+    "tp_column_linear": (_INT, [_VP, _I64, _VP, _I64, _VP, _VP, _I64, _I64, _I64, _I64, _INT,
+                                _INT, _INT, _INT, _INT, _VP]),
+    "tp_gelu": (_INT, [_VP, _VP, _I64, _INT, _INT, _VP]),
+    "tp_row_linear": (_INT, [_VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _I64, _I64, _I64, _I64,
+                             _INT, _INT, _INT, _INT, _VP]),
+    "tp_mlp_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
+    "tp_mlp_shard_fwd": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I64, _I64,
+                                _I64, _INT, _INT, _INT, _INT, _VP]),
+    "tp_attn_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _INT, _INT]),
+    "tp_attn_shard_fwd": (_INT, [_VP, _VP, _VP, _VP, _VP, _SZ, _I64, _I64, _I64, _I64, _I64,
+                                 _INT, _INT, _INT, _INT, _INT, _VP]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built: run `python -m megatron_tensor_transformer_tp_amd.build` "
+                "(or __graft_entry__.build()); there is no CPU fallback")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a 2-D row-major view (rows may be strided, columns not)."""
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise TpError(status, where)
+
+
+def tp_column_linear(x: torch.Tensor, a_i: torch.Tensor, y_i: torch.Tensor, *, ffn: int, t: int,
+                     rank: int, bias_i: Optional[torch.Tensor] = None, apply_gelu: bool = False,
+                     stream=None) -> torch.Tensor:
+    """y_i <- X A_i (+ a_i) [then GeLU]; x [tokens, hidden], a_i [hidden, ffn/t]."""
+    tokens, hidden = x.shape
+    _check(lib().tp_column_linear(_ptr(x), _rows(x, "x"), _ptr(a_i), _rows(a_i, "a_i"),
+                                  _ptr(bias_i), _ptr(y_i), _rows(y_i, "y_i"), tokens, hidden, ffn,
+                                  t, rank, _dt(x), _dt(y_i), int(apply_gelu), _stream(stream)),
+           "tp_column_linear")
+    return y_i
+
+
+def tp_gelu(inp: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """out <- GeLU(inp), elementwise over contiguous tensors of equal numel."""
+    if not (inp.is_contiguous() and out.is_contiguous()) or inp.numel() != out.numel():
+        raise ValueError("tp_gelu needs contiguous tensors of equal size")
+    _check(lib().tp_gelu(_ptr(inp), _ptr(out), inp.numel(), _dt(inp), _dt(out), _stream(stream)),
+           "tp_gelu")
+    return out
+
+
+def tp_row_linear(h_i: torch.Tensor, b_i: torch.Tensor, z_i: torch.Tensor, *, ffn: int, t: int,
+                  rank: int, bias: Optional[torch.Tensor] = None,
+                  residual: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """z_i <- H_i B_i (+ bias + residual on rank 0); h_i [tokens, ffn/t], b_i [ffn/t, hidden]."""
+    tokens = h_i.shape[0]
+    hidden = b_i.shape[1]
+    ldr = _rows(residual, "residual") if residual is not None else 0
+    _check(lib().tp_row_linear(_ptr(h_i), _rows(h_i, "h_i"), _ptr(b_i), _rows(b_i, "b_i"),
+                               _ptr(bias), _ptr(residual), ldr, _ptr(z_i), _rows(z_i, "z_i"),
+                               tokens, ffn, hidden, t, rank, _dt(h_i), _dt(z_i), _stream(stream)),
+           "tp_row_linear")
+    return z_i
+
+
+def tp_mlp_shard_workspace_bytes(tokens: int, hidden: int, ffn: int, t: int, dtype) -> int:
+    dt = TP_BF16 if dtype == torch.bfloat16 else TP_F32
+    return int(lib().tp_mlp_shard_workspace_bytes(tokens, hidden, ffn, t, dt))
+
+
+def tp_mlp_shard_fwd(x: torch.Tensor, a_i: torch.Tensor, b_i: torch.Tensor, z_i: torch.Tensor,
+                     workspace: torch.Tensor, *, ffn: int, t: int, rank: int,
+                     bias_a_i: Optional[torch.Tensor] = None, bias_b: Optional[torch.Tensor] = None,
+                     residual: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """z_i <- GeLU(X A_i + a_i) B_i (+ b + R on rank 0), H_i kept in ``workspace``."""
+    tokens, hidden = x.shape
+    for name, ten in (("x", x), ("b_i", b_i), ("z_i", z_i)):
+        if not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if residual is not None and not residual.is_contiguous():
+        raise ValueError("residual must be contiguous")
+    _check(lib().tp_mlp_shard_fwd(_ptr(x), _ptr(a_i), _rows(a_i, "a_i"), _ptr(b_i), _ptr(bias_a_i),
+                                  _ptr(bias_b), _ptr(residual), _ptr(z_i), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), tokens, hidden, ffn,
+                                  t, rank, _dt(x), _dt(z_i), _stream(stream)),
+           "tp_mlp_shard_fwd")
+    return z_i
+
+
+def tp_attn_shard_workspace_bytes(batch: int, seq: int, hidden: int, heads: int, head_dim: int,
+                                  t: int, dtype) -> int:
+    dt = TP_BF16 if dtype == torch.bfloat16 else TP_F32
+    return int(lib().tp_attn_shard_workspace_bytes(batch, seq, hidden, heads, head_dim, t, dt))
+
+
+def tp_attn_shard_fwd(x: torch.Tensor, wqkv_i: torch.Tensor, wo_i: torch.Tensor, out_i: torch.Tensor,
+                      workspace: Optional[torch.Tensor], *, heads: int, head_dim: int, t: int,
+                      rank: int, causal: bool = False, stream=None) -> torch.Tensor:
+    """out_i <- head-local attention of the rank's heads, projected by wo_i (fp32 partial)."""
+    batch, seq, hidden = x.shape
+    for name, ten in (("x", x), ("wqkv_i", wqkv_i), ("wo_i", wo_i), ("out_i", out_i)):
+        if not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().tp_attn_shard_fwd(_ptr(x), _ptr(wqkv_i), _ptr(wo_i), _ptr(out_i), _ptr(workspace),
+                                   ws_bytes, batch, seq, hidden, heads, head_dim, int(causal), t,
+                                   rank, _dt(x), _dt(out_i), _stream(stream)),
+           "tp_attn_shard_fwd")
+    return out_i

@@ -1,0 +1,269 @@
+// bf16 GEMM with fp32 accumulation on gfx950 matrix cores, with the
+// column-/row-parallel epilogues fused in.
+//
+//   C[M, N] = A[M, K] . B[K, N]      A, B row-major bf16, C fp32 accumulators
+//
+// The column-parallel linear of a tensor-parallel MLP calls it with
+// A = X [tokens, hidden], B = A_i [hidden, f] and the GeLU epilogue; the
+// row-parallel linear with A = H_i [tokens, f], B = B_i [f, hidden] and the
+// bias/residual epilogue (列并行 tutorial, 数学基础 and MLP 应用; Megatron
+// expert interview Level 2, M025/M026).
+//
+// Design (gfx950, 256 CUs in 8 XCDs, 160 KiB LDS per CU, wave64):
+//   * Workgroup = 4 waves (256 threads) computing a BM x BN tile, BK = 64.
+//     The 4 waves form a 2 x 2 grid; each owns a (BM/2) x (BN/2) sub-tile as
+//     a grid of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16).
+//   * Operand roles inside the MFMA are swapped (the weight fragment is the
+//     MFMA's first operand, the activation fragment the second), so each lane
+//     ends up owning 4 CONSECUTIVE output columns of one row: the epilogue
+//     stores 16-byte fp32 or 8-byte bf16 vectors.
+//   * Both operands are staged in LDS as [row][k] with k contiguous and a
+//     row pitch of 72 elements (144 B = 9 x 16 B).  An MFMA fragment is one
+//     16-byte ds_read per lane; 16 lanes reading 16 consecutive rows at the
+//     same k hit 16 distinct 16-byte bank groups.
+//   * The row-major weight tile [BK, BN] has n contiguous in memory but the
+//     MFMA wants k contiguous per lane: each loader thread fetches an 8x8
+//     block (8 rows of 16 B) and transposes it in registers with v_perm_b32
+//     before the 16-byte LDS stores.
+//   * Two LDS stages (2 x (BM + BN) x 144 B; 144 KiB for 256 x 256) and a
+//     register prefetch of the next k-tile: global loads for k-tile t+1 are
+//     in flight while the MFMAs consume k-tile t; one barrier per k-tile.
+//   * Workgroup -> tile mapping is XCD-aware: consecutive workgroup ids are
+//     dealt round-robin to the 8 XCDs, so ids are first regrouped so that
+//     each XCD owns a contiguous range of logical tiles, then tiles are
+//     ordered in groups of 8 tile-rows so that concurrently running tiles
+//     on one XCD share A row-panels and B column-panels in its L2.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tpk {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;
+constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 elements (144 B)
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int tiles_n,
+                                            int& tm, int& tn) {
+  int pid = bid;
+  if (nblk % kXcds == 0) pid = (bid % kXcds) * (nblk / kXcds) + bid / kXcds;
+  const int width = kGroupM * tiles_n;
+  const int group = pid / width;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_group = pid - group * width;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+template <int BM, int BN, bool MASKED, bool GELU, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
+    int64_t ldr, void* __restrict__ out, int64_t ldo) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_CHUNKS = BM * kBK / 8 / kThreads;  // 16-byte chunks per thread
+  static_assert(A_CHUNKS >= 1 && BN <= kThreads, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = (K + kBK - 1) / kBK;
+
+  // A loader: chunk i of thread t covers row i*32 + t/8, k-chunk t%8.
+  const int a_row = tid >> 3, a_kc = tid & 7;
+  // B loader: thread t (< BN) covers the 8x8 block k-rows (t%8)*8.., n-cols (t/8)*8..
+  const bool b_loader = (BN == kThreads) || tid < BN;
+  const int b_kb = tid & 7, b_nb = tid >> 3;
+
+  u32x4_t ra[A_CHUNKS];
+  u32x4_t rb[8];
+
+  auto load_tiles = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kBK;
+    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
+      const int gm = m0 + I * 32 + a_row, gk = k0 + a_kc * 8;
+      if (!MASKED || (gm < M && gk < K))
+        ra[I] = *reinterpret_cast<const u32x4_t*>(A + static_cast<int64_t>(gm) * lda + gk);
+      else
+        ra[I] = zero4();
+    });
+    if (b_loader) {
+      static_for<8>([&](auto J) __attribute__((always_inline)) {
+        const int gk = k0 + b_kb * 8 + J, gn = n0 + b_nb * 8;
+        if (!MASKED || (gk < K && gn < N))
+          rb[J] = *reinterpret_cast<const u32x4_t*>(B + static_cast<int64_t>(gk) * ldb + gn);
+        else
+          rb[J] = zero4();
+      });
+    }
+  };
+
+  auto store_tiles = [&](int buf) __attribute__((always_inline)) {
+    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
+      *reinterpret_cast<u32x4_t*>(&sA[buf][(I * 32 + a_row) * kPitch + a_kc * 8]) = ra[I];
+    });
+    if (b_loader) {
+      // rb[j] holds B[k0 + kb*8 + j][n0 + nb*8 .. +7]; write column e of the
+      // 8x8 block as 8 consecutive k values of row n = nb*8 + e.
+      static_for<8>([&](auto E) __attribute__((always_inline)) {
+        constexpr int q = E >> 1;
+        constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t t;
+        t[0] = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
+        t[1] = __builtin_amdgcn_perm(rb[3][q], rb[2][q], sel);
+        t[2] = __builtin_amdgcn_perm(rb[5][q], rb[4][q], sel);
+        t[3] = __builtin_amdgcn_perm(rb[7][q], rb[6][q], sel);
+        *reinterpret_cast<u32x4_t*>(&sB[buf][(b_nb * 8 + E) * kPitch + b_kb * 8]) = t;
+      });
+    }
+  };
+
+  f32x16_t acc[TN][TM];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
+
+  load_tiles(0);
+  store_tiles(0);
+  __syncthreads();
+
+  const int frag_row = lane & 31;
+  const int frag_k = (lane >> 5) * 8;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tiles(kt + 1);
+    const uint16_t* a_s = sA[cur] + (wm * WM + frag_row) * kPitch + frag_k;
+    const uint16_t* b_s = sB[cur] + (wn * WN + frag_row) * kPitch + frag_k;
+#pragma unroll
+    for (int s = 0; s < kBK / 16; ++s) {
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * kPitch + s * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_s + j * 32 * kPitch + s * 16);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tiles(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.  acc[j][i][4g + r] is C[m][n] with
+  //   m = m0 + wm*WM + i*32 + lane%32,  n = n0 + wn*WN + j*32 + 8g + 4*(lane/32) + r.
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + wm * WM + i * 32 + (lane & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN + j * 32 + g * 8 + (lane >> 5) * 4;
+        if (MASKED && (m >= M || n >= N)) continue;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[j][i][4 * g + r];
+        if (bias != nullptr) {
+          const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(bias + n);
+          v[0] += __uint_as_float(bb[0] << 16);
+          v[1] += __uint_as_float(bb[0] & 0xFFFF0000u);
+          v[2] += __uint_as_float(bb[1] << 16);
+          v[3] += __uint_as_float(bb[1] & 0xFFFF0000u);
+        }
+        if (GELU) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = gelu_f32(v[r]);
+        }
+        if (residual != nullptr) {
+          const u32x2_t rr =
+              *reinterpret_cast<const u32x2_t*>(residual + static_cast<int64_t>(m) * ldr + n);
+          v[0] += __uint_as_float(rr[0] << 16);
+          v[1] += __uint_as_float(rr[0] & 0xFFFF0000u);
+          v[2] += __uint_as_float(rr[1] << 16);
+          v[3] += __uint_as_float(rr[1] & 0xFFFF0000u);
+        }
+        if (OUT_F32) {
+          float* o = static_cast<float*>(out) + static_cast<int64_t>(m) * ldo + n;
+          typedef float f32x4_t __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
+        } else {
+          uint16_t* o = static_cast<uint16_t*>(out) + static_cast<int64_t>(m) * ldo + n;
+          *reinterpret_cast<u32x2_t*>(o) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, bool GELU, bool OUT_F32>
+hipError_t launch_tile(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
+                       int N, int K, const Epilogue& ep, hipStream_t stream) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const bool masked = (M % BM) || (N % BN) || (K % kBK);
+  const uint16_t* bias = static_cast<const uint16_t*>(ep.bias);
+  const uint16_t* res = static_cast<const uint16_t*>(ep.residual);
+  if (masked)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, GELU, OUT_F32>), dim3(tiles), dim3(kThreads),
+                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, GELU, OUT_F32>), dim3(tiles), dim3(kThreads),
+                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_epi(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N,
+                      int K, const Epilogue& ep, hipStream_t stream) {
+  if (ep.gelu)
+    return ep.out_f32 ? launch_tile<BM, BN, true, true>(A, lda, B, ldb, M, N, K, ep, stream)
+                      : launch_tile<BM, BN, true, false>(A, lda, B, ldb, M, N, K, ep, stream);
+  return ep.out_f32 ? launch_tile<BM, BN, false, true>(A, lda, B, ldb, M, N, K, ep, stream)
+                    : launch_tile<BM, BN, false, false>(A, lda, B, ldb, M, N, K, ep, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                            int64_t M, int64_t N, int64_t K, const Epilogue& ep,
+                            hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+  // Large problems: 256x256 tiles (one workgroup per CU, 144 KiB LDS).
+  // Smaller ones: 128x128 tiles so that the 256 CUs still get work.
+  if (tiles256 >= 256)
+    return launch_epi<256, 256>(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
+                                static_cast<int>(K), ep, stream);
+  return launch_epi<128, 128>(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
+                              static_cast<int>(K), ep, stream);
+}
+
+}  // namespace tpk

@@ -1,0 +1,224 @@
+// C-ABI front end: argument validation and kernel dispatch for the
+// tensor-parallel shard entry points declared in include/tp_shard.h.
+//
+// Every check runs before anything is enqueued, and no check touches the HIP
+// runtime, so the error paths work (and are tested) on a machine with no GPU.
+// The shard width is derived here from the logical ffn (or heads) and t,
+// rejecting splits that do not divide (列并行 tutorial, 切分原理; Megatron
+// expert interview Level 2, M031).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <climits>
+
+#include "../../include/tp_shard.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_known(int dt) { return dt == TP_F32 || dt == TP_BF16; }
+
+int64_t elem_bytes(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
+
+// Row widths / leading dimensions must be a multiple of this many elements so
+// that every 16-byte vector access stays inside one row and aligned.
+int64_t elem_align(tp_dtype dt) { return dt == TP_BF16 ? 8 : 4; }
+
+// bf16 -> bf16, bf16 -> f32 and f32 -> f32 are the GEMM pairs.
+bool gemm_pair_ok(int in_dt, int out_dt) {
+  return (in_dt == TP_BF16 && (out_dt == TP_BF16 || out_dt == TP_F32)) ||
+         (in_dt == TP_F32 && out_dt == TP_F32);
+}
+
+tp_status check_split(int64_t split, int t, int rank, int64_t* width) {
+  if (t < 1 || rank < 0 || rank >= t) return TP_ERR_BAD_RANK;
+  if (split < 1) return TP_ERR_INVALID_ARG;
+  if (split % t != 0) return TP_ERR_NOT_DIVISIBLE;
+  *width = split / t;
+  return TP_OK;
+}
+
+// A required row-major operand of `width` elements per row.
+tp_status check_matrix(const void* p, int64_t ld, int64_t width, tp_dtype dt) {
+  if (p == nullptr) return TP_ERR_INVALID_ARG;
+  if (ld < width) return TP_ERR_INVALID_ARG;
+  if (!aligned16(p) || ld % elem_align(dt) != 0 || width % elem_align(dt) != 0)
+    return TP_ERR_MISALIGNED;
+  return TP_OK;
+}
+
+tp_status check_optional_vec(const void* p) {
+  if (p != nullptr && !aligned16(p)) return TP_ERR_MISALIGNED;
+  return TP_OK;
+}
+
+bool fits_int32(int64_t v) { return v <= static_cast<int64_t>(INT_MAX); }
+
+tp_status from_hip(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
+
+#define TP_TRY(expr)                  \
+  do {                                \
+    const tp_status s_ = (expr);      \
+    if (s_ != TP_OK) return s_;       \
+  } while (0)
+
+// Launch C[M, N] = A[M, K] B[K, N] with the given epilogue in dtype `in_dt`.
+tp_status run_gemm(tp_dtype in_dt, const void* a, int64_t lda, const void* b, int64_t ldb,
+                   int64_t M, int64_t N, int64_t K, const tpk::Epilogue& ep, hipStream_t stream) {
+  if (in_dt == TP_BF16)
+    return from_hip(tpk::launch_gemm_bf16(static_cast<const uint16_t*>(a), lda,
+                                          static_cast<const uint16_t*>(b), ldb, M, N, K, ep,
+                                          stream));
+  return from_hip(tpk::launch_gemm_f32(static_cast<const float*>(a), lda,
+                                       static_cast<const float*>(b), ldb, M, N, K, ep, stream));
+}
+
+size_t round256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_string(tp_status s) {
+  switch (s) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_INVALID_ARG: return "TP_ERR_INVALID_ARG: null pointer, negative size or ld < width";
+    case TP_ERR_NOT_DIVISIBLE: return "TP_ERR_NOT_DIVISIBLE: split dimension not divisible by t";
+    case TP_ERR_BAD_RANK: return "TP_ERR_BAD_RANK: t < 1 or rank outside [0, t)";
+    case TP_ERR_DTYPE: return "TP_ERR_DTYPE: unsupported dtype combination";
+    case TP_ERR_MISALIGNED: return "TP_ERR_MISALIGNED: pointer, width or leading dimension misaligned";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace missing or too small";
+    case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED: request outside what the kernels implement";
+    case TP_ERR_HIP: return "TP_ERR_HIP: a HIP launch failed";
+  }
+  return "TP_ERR_UNKNOWN";
+}
+
+int tp_version(void) { return kVersion; }
+
+tp_status tp_column_linear(const void* x, int64_t ldx, const void* a_i, int64_t lda,
+                           const void* bias_i, void* y_i, int64_t ldy, int64_t tokens,
+                           int64_t hidden, int64_t ffn, int t, int rank, tp_dtype in_dt,
+                           tp_dtype out_dt, int apply_gelu, void* stream) {
+  if (!dtype_known(in_dt) || !dtype_known(out_dt) || !gemm_pair_ok(in_dt, out_dt))
+    return TP_ERR_DTYPE;
+  if (tokens < 0 || hidden < 1 || (apply_gelu != 0 && apply_gelu != 1)) return TP_ERR_INVALID_ARG;
+  int64_t f = 0;
+  TP_TRY(check_split(ffn, t, rank, &f));
+  if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(f)) return TP_ERR_UNSUPPORTED;
+  if (tokens == 0) return TP_OK;
+  TP_TRY(check_matrix(x, ldx, hidden, in_dt));
+  TP_TRY(check_matrix(a_i, lda, f, in_dt));
+  TP_TRY(check_matrix(y_i, ldy, f, out_dt));
+  TP_TRY(check_optional_vec(bias_i));
+  tpk::Epilogue ep{bias_i, nullptr, 0, y_i, ldy, out_dt == TP_F32, apply_gelu == 1};
+  return run_gemm(in_dt, x, ldx, a_i, lda, tokens, f, hidden, ep,
+                  static_cast<hipStream_t>(stream));
+}
+
+tp_status tp_gelu(const void* in, void* out, int64_t n, tp_dtype in_dt, tp_dtype out_dt,
+                  void* stream) {
+  if (!dtype_known(in_dt) || !dtype_known(out_dt)) return TP_ERR_DTYPE;
+  if (n < 0) return TP_ERR_INVALID_ARG;
+  if (n == 0) return TP_OK;
+  if (in == nullptr || out == nullptr) return TP_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(out)) return TP_ERR_MISALIGNED;
+  // exact aliasing is allowed when the element sizes match; partial overlap is not
+  const uintptr_t ib = reinterpret_cast<uintptr_t>(in), ob = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t ie = ib + static_cast<uintptr_t>(n) * elem_bytes(in_dt);
+  const uintptr_t oe = ob + static_cast<uintptr_t>(n) * elem_bytes(out_dt);
+  const bool overlap = ib < oe && ob < ie;
+  if (overlap && !(ib == ob && in_dt == out_dt)) return TP_ERR_INVALID_ARG;
+  return from_hip(tpk::launch_gelu(in, out, n, in_dt, out_dt, static_cast<hipStream_t>(stream)));
+}
+
+tp_status tp_row_linear(const void* h_i, int64_t ldh, const void* b_i, int64_t ldb,
+                        const void* bias, const void* residual, int64_t ldr, void* z_i,
+                        int64_t ldz, int64_t tokens, int64_t ffn, int64_t hidden, int t,
+                        int rank, tp_dtype in_dt, tp_dtype out_dt, void* stream) {
+  if (!dtype_known(in_dt) || !dtype_known(out_dt) || !gemm_pair_ok(in_dt, out_dt))
+    return TP_ERR_DTYPE;
+  if (tokens < 0 || hidden < 1) return TP_ERR_INVALID_ARG;
+  int64_t f = 0;
+  TP_TRY(check_split(ffn, t, rank, &f));
+  if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(f)) return TP_ERR_UNSUPPORTED;
+  if (tokens == 0) return TP_OK;
+  TP_TRY(check_matrix(h_i, ldh, f, in_dt));
+  TP_TRY(check_matrix(b_i, ldb, hidden, in_dt));
+  TP_TRY(check_matrix(z_i, ldz, hidden, out_dt));
+  const bool owner = rank == 0;  // bias and residual belong to the summed output
+  const void* bias_use = owner ? bias : nullptr;
+  const void* res_use = owner ? residual : nullptr;
+  TP_TRY(check_optional_vec(bias_use));
+  if (res_use != nullptr) TP_TRY(check_matrix(res_use, ldr, hidden, in_dt));
+  tpk::Epilogue ep{bias_use, res_use, ldr, z_i, ldz, out_dt == TP_F32, false};
+  return run_gemm(in_dt, h_i, ldh, b_i, ldb, tokens, hidden, f, ep,
+                  static_cast<hipStream_t>(stream));
+}
+
+size_t tp_mlp_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int t,
+                                    tp_dtype in_dt) {
+  if (!dtype_known(in_dt) || tokens < 0 || hidden < 1) return 0;
+  int64_t f = 0;
+  if (check_split(ffn, t, 0, &f) != TP_OK) return 0;
+  return round256(static_cast<size_t>(tokens) * static_cast<size_t>(f) *
+                  static_cast<size_t>(elem_bytes(in_dt)));
+}
+
+tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const void* b_i,
+                           const void* bias_a_i, const void* bias_b, const void* residual,
+                           void* z_i, void* workspace, size_t workspace_bytes, int64_t tokens,
+                           int64_t hidden, int64_t ffn, int t, int rank, tp_dtype in_dt,
+                           tp_dtype out_dt, void* stream) {
+  if (!dtype_known(in_dt) || !dtype_known(out_dt) || !gemm_pair_ok(in_dt, out_dt))
+    return TP_ERR_DTYPE;
+  if (tokens < 0 || hidden < 1) return TP_ERR_INVALID_ARG;
+  int64_t f = 0;
+  TP_TRY(check_split(ffn, t, rank, &f));
+  if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(f)) return TP_ERR_UNSUPPORTED;
+  if (tokens == 0) return TP_OK;
+  TP_TRY(check_matrix(x, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(a_i, lda, f, in_dt));
+  TP_TRY(check_matrix(b_i, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(z_i, hidden, hidden, out_dt));
+  TP_TRY(check_optional_vec(bias_a_i));
+  const bool owner = rank == 0;
+  const void* bias_use = owner ? bias_b : nullptr;
+  const void* res_use = owner ? residual : nullptr;
+  TP_TRY(check_optional_vec(bias_use));
+  TP_TRY(check_optional_vec(res_use));
+  const size_t need = tp_mlp_shard_workspace_bytes(tokens, hidden, ffn, t, in_dt);
+  if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Column-parallel GEMM with GeLU fused into its epilogue: H_i = GeLU(X A_i + a_i)
+  // stored once in the workspace (bf16 for bf16 inputs, fp32 for fp32).
+  tpk::Epilogue ep1{bias_a_i, nullptr, 0, workspace, f, in_dt == TP_F32, true};
+  TP_TRY(run_gemm(in_dt, x, hidden, a_i, lda, tokens, f, hidden, ep1, s));
+  // Row-parallel GEMM: Z_i = H_i B_i (+ b + R on rank 0).
+  tpk::Epilogue ep2{bias_use, res_use, hidden, z_i, hidden, out_dt == TP_F32, false};
+  return run_gemm(in_dt, workspace, f, b_i, hidden, tokens, hidden, f, ep2, s);
+}
+
+size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int64_t heads,
+                                     int64_t head_dim, int t, tp_dtype in_dt) {
+  (void)batch; (void)seq; (void)hidden; (void)heads; (void)head_dim; (void)t; (void)in_dt;
+  return 0;
+}
+
+tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i, void* out_i,
+                            void* workspace, size_t workspace_bytes, int64_t batch, int64_t seq,
+                            int64_t hidden, int64_t heads, int64_t head_dim, int causal, int t,
+                            int rank, tp_dtype in_dt, tp_dtype out_dt, void* stream) {
+  (void)x; (void)wqkv_i; (void)wo_i; (void)out_i; (void)workspace; (void)workspace_bytes;
+  (void)batch; (void)seq; (void)hidden; (void)heads; (void)head_dim; (void)causal; (void)t;
+  (void)rank; (void)in_dt; (void)out_dt; (void)stream;
+  return TP_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments before anything reaches the GPU.
+
+Every call here fails validation (or has tokens == 0), so no HIP call is
+made; the pointers are fake integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+
+OK, INVALID, NOT_DIV, BAD_RANK, DTYPE, MISALIGNED, WORKSPACE, UNSUPPORTED, HIP = range(9)
+F32, BF16 = 0, 1
+P = 0x10000  # a fake, 16-byte aligned "device pointer"; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from megatron_tensor_transformer_tp_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from megatron_tensor_transformer_tp_amd.build import build
+        build()
+    return binding.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from megatron_tensor_transformer_tp_amd import binding
+    names = header_functions()
+    assert {"tp_column_linear", "tp_gelu", "tp_row_linear", "tp_mlp_shard_fwd",
+            "tp_attn_shard_fwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in binding.SIGNATURES, f"binding lacks {n}"
+    assert set(binding.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version(lib):
+    for s in range(9):
+        assert lib.tp_status_string(s).decode().startswith(
+            ["TP_OK", "TP_ERR_INVALID_ARG", "TP_ERR_NOT_DIVISIBLE", "TP_ERR_BAD_RANK", "TP_ERR_DTYPE",
+             "TP_ERR_MISALIGNED", "TP_ERR_WORKSPACE", "TP_ERR_UNSUPPORTED", "TP_ERR_HIP"][s])
+    assert lib.tp_version() >= 100
+
+
+def col(lib, **kw):
+    a = dict(x=P, ldx=1024, a=P, lda=512, bias=None, y=P, ldy=512, tokens=16, hidden=1024,
+             ffn=4096, t=8, rank=0, in_dt=BF16, out_dt=BF16, gelu=1)
+    a.update(kw)
+    return lib.tp_column_linear(a["x"], a["ldx"], a["a"], a["lda"], a["bias"], a["y"], a["ldy"],
+                                a["tokens"], a["hidden"], a["ffn"], a["t"], a["rank"], a["in_dt"],
+                                a["out_dt"], a["gelu"], None)
+
+
+def test_column_linear_validation(lib):
+    assert col(lib, ffn=4100) == NOT_DIV          # F mod t != 0
+    assert col(lib, t=0) == BAD_RANK
+    assert col(lib, rank=8) == BAD_RANK
+    assert col(lib, rank=-1) == BAD_RANK
+    assert col(lib, x=None) == INVALID
+    assert col(lib, ldy=256) == INVALID           # ld < width
+    assert col(lib, tokens=-1) == INVALID
+    assert col(lib, gelu=2) == INVALID
+    assert col(lib, x=P + 8) == MISALIGNED        # not 16-byte aligned
+    assert col(lib, hidden=1020, ldx=1020) == MISALIGNED  # row width not a multiple of 8
+    assert col(lib, lda=516) == MISALIGNED
+    assert col(lib, bias=P + 2) == MISALIGNED
+    assert col(lib, in_dt=F32, out_dt=BF16) == DTYPE
+    assert col(lib, in_dt=7) == DTYPE
+    assert col(lib, tokens=0) == OK               # empty input: nothing enqueued
+    assert col(lib, tokens=0, ffn=4100) == NOT_DIV  # config still validated when empty
+    # fp32 rows need 4-element alignment only
+    assert col(lib, tokens=0, in_dt=F32, out_dt=F32, hidden=1020, ldx=1020) == OK
+
+
+def row(lib, **kw):
+    a = dict(h=P, ldh=512, b=P, ldb=1024, bias=None, res=None, ldr=0, z=P, ldz=1024, tokens=16,
+             ffn=4096, hidden=1024, t=8, rank=0, in_dt=BF16, out_dt=F32)
+    a.update(kw)
+    return lib.tp_row_linear(a["h"], a["ldh"], a["b"], a["ldb"], a["bias"], a["res"], a["ldr"],
+                             a["z"], a["ldz"], a["tokens"], a["ffn"], a["hidden"], a["t"], a["rank"],
+                             a["in_dt"], a["out_dt"], None)
+
+
+def test_row_linear_validation(lib):
+    assert row(lib, ffn=30, t=4) == NOT_DIV
+    assert row(lib, rank=8) == BAD_RANK
+    assert row(lib, b=None) == INVALID
+    assert row(lib, res=P, ldr=100) == INVALID    # residual ld < hidden
+    assert row(lib, res=P + 4, ldr=1024) == MISALIGNED
+    # ranks != 0 ignore bias / residual entirely (even malformed ones)
+    assert row(lib, rank=3, res=P + 4, ldr=100, bias=P + 2, tokens=0) == OK
+    assert row(lib, z=P + 8) == MISALIGNED
+    assert row(lib, in_dt=F32, out_dt=BF16) == DTYPE
+    assert row(lib, tokens=0) == OK
+
+
+def test_gelu_validation(lib):
+    assert lib.tp_gelu(P, P + 4096, -1, BF16, BF16, None) == INVALID
+    assert lib.tp_gelu(None, P, 10, BF16, BF16, None) == INVALID
+    assert lib.tp_gelu(P + 2, P + 4096, 10, BF16, BF16, None) == MISALIGNED
+    assert lib.tp_gelu(P, P + 16, 100, BF16, BF16, None) == INVALID  # partial overlap
+    assert lib.tp_gelu(P, P, 100, F32, BF16, None) == INVALID        # in place, sizes differ
+    assert lib.tp_gelu(P, P + 4096, 10, 3, BF16, None) == DTYPE
+    assert lib.tp_gelu(P, P, 0, BF16, BF16, None) == OK
+
+
+def mlp(lib, **kw):
+    a = dict(x=P, a=P, lda=512, b=P, bias_a=None, bias_b=None, res=None, z=P, ws=P, ws_bytes=1 << 30,
+             tokens=16, hidden=1024, ffn=4096, t=8, rank=0, in_dt=BF16, out_dt=F32)
+    a.update(kw)
+    return lib.tp_mlp_shard_fwd(a["x"], a["a"], a["lda"], a["b"], a["bias_a"], a["bias_b"], a["res"],
+                                a["z"], a["ws"], a["ws_bytes"], a["tokens"], a["hidden"], a["ffn"],
+                                a["t"], a["rank"], a["in_dt"], a["out_dt"], None)
+
+
+def test_mlp_shard_validation(lib):
+    need = lib.tp_mlp_shard_workspace_bytes(16, 1024, 4096, 8, BF16)
+    assert need == 16 * 512 * 2
+    assert lib.tp_mlp_shard_workspace_bytes(3, 1024, 4096, 8, F32) == 3 * 512 * 4
+    assert lib.tp_mlp_shard_workspace_bytes(3, 1024, 40, 8, F32) == 256  # 60 B rounded up
+    assert lib.tp_mlp_shard_workspace_bytes(16, 1024, 4100, 8, BF16) == 0
+    assert mlp(lib, ws_bytes=need - 1) == WORKSPACE
+    assert mlp(lib, ws=None) == WORKSPACE
+    assert mlp(lib, ws=P + 16) == MISALIGNED      # workspace must be 256-byte aligned
+    assert mlp(lib, ffn=4097) == NOT_DIV
+    assert mlp(lib, t=3, ffn=4096, rank=0) == NOT_DIV
+    assert mlp(lib, t=3, ffn=4095, rank=0, lda=1368) == MISALIGNED  # f = 1365, not a multiple of 8
+    assert mlp(lib, rank=9) == BAD_RANK
+    assert mlp(lib, x=None) == INVALID
+    assert mlp(lib, lda=500) == INVALID
+    assert mlp(lib, bias_a=P + 2) == MISALIGNED
+    assert mlp(lib, in_dt=F32, out_dt=BF16) == DTYPE
+    assert mlp(lib, tokens=0, ws=None) == OK
+
+
+def test_attn_shard_is_validated(lib):
+    rc = lib.tp_attn_shard_fwd(P, P, P, P, P, 1 << 30, 1, 64, 1024, 8, 128, 0, 3, 0, BF16, F32, None)
+    assert rc in (NOT_DIV, UNSUPPORTED)
+
+
+def test_product_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "megatron_tensor_transformer_tp_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), fn
+                assert "oracle." not in text.replace("the oracle.", ""), fn
