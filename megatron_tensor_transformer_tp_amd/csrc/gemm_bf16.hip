@@ -67,6 +67,25 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
 
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
+// Scheduling fence between the k-substeps of the main loop: nothing moves
+// across it, so the LDS reads issued in substep s for substep s+1 stay ahead
+// of the MFMAs of substep s (the default scheduler would sink them next to
+// their uses and expose the LDS latency to the matrix pipe).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Within a substep, an explicit interleave: each MFMA is followed by one of
+// the substep's memory operations, LDS reads for the next substep first.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
+
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+  __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+
 template <int BM, int BN, bool MASKED, bool GELU, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
@@ -99,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   u32x4_t ra[A_CHUNKS];
   u32x4_t rb[8];
 
-  auto load_tiles = [&](int kt) __attribute__((always_inline)) {
+  auto load_a = [&](int kt) __attribute__((always_inline)) {
     const int k0 = kt * kBK;
     static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
       const int gm = m0 + I * 32 + a_row, gk = k0 + a_kc * 8;
@@ -108,6 +127,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       else
         ra[I] = zero4();
     });
+  };
+  auto load_b = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kBK;
     if (b_loader) {
       static_for<8>([&](auto J) __attribute__((always_inline)) {
         const int gk = k0 + b_kb * 8 + J, gn = n0 + b_nb * 8;
@@ -118,11 +140,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
       });
     }
   };
-
-  auto store_tiles = [&](int buf) __attribute__((always_inline)) {
+  auto store_a = [&](int buf) __attribute__((always_inline)) {
     static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
       *reinterpret_cast<u32x4_t*>(&sA[buf][(I * 32 + a_row) * kPitch + a_kc * 8]) = ra[I];
     });
+  };
+  auto store_b = [&](int buf) __attribute__((always_inline)) {
     if (b_loader) {
       // rb[j] holds B[k0 + kb*8 + j][n0 + nb*8 .. +7]; write column e of the
       // 8x8 block as 8 consecutive k values of row n = nb*8 + e.
@@ -139,43 +162,114 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     }
   };
 
-  f32x16_t acc[TN][TM];
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.0f;
-
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-
+  // MFMA operand fragments, double-buffered by k-substep parity.
   const int frag_row = lane & 31;
   const int frag_k = (lane >> 5) * 8;
+  const int a_frag = (wm * WM + frag_row) * kPitch + frag_k;
+  const int b_frag = (wn * WN + frag_row) * kPitch + frag_k;
+  bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
+  auto read_frags = [&](int buf, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
+      __attribute__((always_inline)) {
+    const uint16_t* a_s = sA[buf] + a_frag + s * 16;
+    const uint16_t* b_s = sB[buf] + b_frag + s * 16;
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      af[I] = *reinterpret_cast<const bf16x8_t*>(a_s + I * 32 * kPitch);
+    });
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      bf[J] = *reinterpret_cast<const bf16x8_t*>(b_s + J * 32 * kPitch);
+    });
+  };
+
+  f32x16_t acc[TN][TM];
+  static_for<TN>([&](auto J) __attribute__((always_inline)) {
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      acc[J][I] = (f32x16_t)(0.0f);
+    });
+  });
+  auto mfmas = [&](const bf16x8_t(&af)[TM], const bf16x8_t(&bf)[TN]) __attribute__((always_inline)) {
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      static_for<TM>([&](auto I) __attribute__((always_inline)) {
+        acc[J][I] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[J], af[I], acc[J][I], 0, 0, 0);
+      });
+    });
+  };
+
+  // Software pipeline over k-tiles (4 k-substeps of 16 each).  In iteration kt
+  // the registers ra/rb hold k-tile kt+1 (loaded one iteration earlier):
+  //   s0: LDS-store A of tile kt+1 into the other stage, issue global loads of
+  //       A for tile kt+2, read fragments of s1, MFMAs of s0
+  //   s1: same for B (with the 8x8 transposes), fragments of s2, MFMAs of s1
+  //   s2: fragments of s3, MFMAs of s2
+  //   s3: barrier (tile kt+1 complete in the other stage, all reads of this
+  //       stage done), fragments of tile kt+1 s0, MFMAs of s3
+  // The prefetch index is clamped to the last tile, so the loop body has no
+  // branches; the clamped loads re-read a tile that is never consumed.
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  store_b(0);
+  const int k_second = nk > 1 ? 1 : 0;
+  load_a(k_second);
+  load_b(k_second);
+  __syncthreads();
+  read_frags(0, 0, af0, bf0);
+
+  constexpr int kFrags = TM + TN;        // LDS fragment reads per substep
+  constexpr int kMfma = TM * TN;         // MFMAs per substep
+  static_assert(kMfma >= 2 * kFrags || BM != 256, "interleave pattern");
+  auto interleave_reads = [&]() __attribute__((always_inline)) {
+    static_for<kFrags>([&](auto) __attribute__((always_inline)) {
+      sched_group<kSchedMfma, 1>();
+      sched_group<kSchedDsRead, 1>();
+    });
+    sched_group<kSchedMfma, kMfma - kFrags>();
+  };
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tiles(kt + 1);
-    const uint16_t* a_s = sA[cur] + (wm * WM + frag_row) * kPitch + frag_k;
-    const uint16_t* b_s = sB[cur] + (wn * WN + frag_row) * kPitch + frag_k;
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + i * 32 * kPitch + s * 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_s + j * 32 * kPitch + s * 16);
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[j][i], 0, 0, 0);
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const int kpre = min(kt + 2, nk - 1);
+    // s0: A of tile kt+1 to LDS, global loads of A for tile kt+2
+    read_frags(cur, 1, af1, bf1);
+    store_a(nxt);
+    load_a(kpre);
+    mfmas(af0, bf0);
+    if constexpr (BM == 256 && BN == 256) {
+      static_for<8>([&](auto) __attribute__((always_inline)) {
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsRead, 1>();
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsWrite, 1>();
+        sched_group<kSchedVmemRead, 1>();
+      });
     }
-    if (kt + 1 < nk) store_tiles(cur ^ 1);
+    sched_fence();
+    // s1: B of tile kt+1 (transposed) to LDS, global loads of B for tile kt+2
+    read_frags(cur, 2, af0, bf0);
+    store_b(nxt);
+    load_b(kpre);
+    mfmas(af1, bf1);
+    if constexpr (BM == 256 && BN == 256) {
+      static_for<8>([&](auto) __attribute__((always_inline)) {
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsRead, 1>();
+        sched_group<kSchedValu, 4>();
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsWrite, 1>();
+        sched_group<kSchedVmemRead, 1>();
+      });
+    }
+    sched_fence();
+    // s2
+    read_frags(cur, 3, af1, bf1);
+    mfmas(af0, bf0);
+    if constexpr (BM == 256 && BN == 256) interleave_reads();
+    sched_fence();
+    // s3: tile kt+1 is complete in the other stage after the barrier
     __syncthreads();
+    read_frags(nxt, 0, af0, bf0);
+    mfmas(af1, bf1);
+    if constexpr (BM == 256 && BN == 256) interleave_reads();
+    sched_fence();
   }
 
   // Epilogue.  acc[j][i][4g + r] is C[m][n] with
