@@ -35,7 +35,8 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s + % bf16 MFMA peak, t=8 MLP shard (h=8192, 16384 tok), 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/gemm_bf16.hip",
+KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/gemm_bf16_impl.h",
+                  "megatron_tensor_transformer_tp_amd/csrc/gemm_bf16.hip",
                   "megatron_tensor_transformer_tp_amd/csrc/device_common.h"]
 
 

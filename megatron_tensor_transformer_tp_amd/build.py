@@ -23,6 +23,10 @@ ARCH = "gfx950"
 SOURCES = [
     "tp_shard_abi.cpp",
     "gemm_bf16.hip",
+    "gemm_bf16_256_gelu.hip",
+    "gemm_bf16_256_plain.hip",
+    "gemm_bf16_128_gelu.hip",
+    "gemm_bf16_128_plain.hip",
     "gemm_f32.hip",
     "gelu.hip",
 ]

@@ -1,0 +1,19 @@
+// bf16 GEMM instantiations: 256x256 tiles, GeLU epilogue (column-parallel layer).
+#include "gemm_bf16_impl.h"
+
+namespace tpk {
+
+template <int BM, int BN, bool GELU, bool OUT_F32>
+hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                int M, int N, int K, const Epilogue& ep, hipStream_t stream) {
+  return gemm_detail::launch_tile<BM, BN, GELU, OUT_F32>(A, lda, B, ldb, M, N, K, ep, stream);
+}
+
+template hipError_t launch_gemm_bf16_cfg<256, 256, true, true>(const uint16_t*, int64_t,
+                                                                const uint16_t*, int64_t, int, int,
+                                                                int, const Epilogue&, hipStream_t);
+template hipError_t launch_gemm_bf16_cfg<256, 256, true, false>(const uint16_t*, int64_t,
+                                                                 const uint16_t*, int64_t, int, int,
+                                                                 int, const Epilogue&, hipStream_t);
+
+}  // namespace tpk

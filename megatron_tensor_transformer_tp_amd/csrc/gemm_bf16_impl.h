@@ -1,0 +1,368 @@
+// bf16 GEMM with fp32 accumulation on gfx950 matrix cores, with the
+// column-/row-parallel epilogues fused in (kernel template; the launch
+// configurations are instantiated in gemm_bf16_*.hip, one translation unit
+// per tile shape and output type, so that they compile in parallel).
+//
+//   C[M, N] = A[M, K] . B[K, N]      A, B row-major bf16, C fp32 accumulators
+//
+// The column-parallel linear of a tensor-parallel MLP calls it with
+// A = X [tokens, hidden], B = A_i [hidden, f] and the GeLU epilogue; the
+// row-parallel linear with A = H_i [tokens, f], B = B_i [f, hidden] and the
+// bias/residual epilogue (列并行 tutorial, 数学基础 and MLP 应用; Megatron
+// expert interview Level 2, M025/M026).
+//
+// Design (gfx950, 256 CUs in 8 XCDs, 160 KiB LDS per CU, wave64):
+//   * Workgroup = 4 waves (256 threads) computing a BM x BN tile, BK = 64.
+//     The 4 waves form a 2 x 2 grid; each owns a (BM/2) x (BN/2) sub-tile as
+//     a grid of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16).
+//   * Operand roles inside the MFMA are swapped (the weight fragment is the
+//     MFMA's first operand, the activation fragment the second), so each lane
+//     ends up owning 4 CONSECUTIVE output columns of one row: the epilogue
+//     stores 16-byte fp32 or 8-byte bf16 vectors.
+//   * Both operands are staged in LDS as [row][k] with k contiguous and a
+//     row pitch of 72 elements (144 B = 9 x 16 B).  An MFMA fragment is one
+//     16-byte ds_read per lane; 16 lanes reading 16 consecutive rows at the
+//     same k hit 16 distinct 16-byte bank groups.
+//   * The row-major weight tile [BK, BN] has n contiguous in memory but the
+//     MFMA wants k contiguous per lane: each loader thread fetches an 8x8
+//     block (8 rows of 16 B) and transposes it in registers with v_perm_b32
+//     before the 16-byte LDS stores.
+//   * Two LDS stages (2 x (BM + BN) x 144 B; 144 KiB for 256 x 256) and a
+//     register prefetch of the next k-tile: global loads for k-tile t+1 are
+//     in flight while the MFMAs consume k-tile t; one barrier per k-tile.
+//   * Workgroup -> tile mapping is XCD-aware: consecutive workgroup ids are
+//     dealt round-robin to the 8 XCDs, so ids are first regrouped so that
+//     each XCD owns a contiguous range of logical tiles, then tiles are
+//     ordered in groups of 8 tile-rows so that concurrently running tiles
+//     on one XCD share A row-panels and B column-panels in its L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tpk {
+namespace gemm_detail {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;
+constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 elements (144 B)
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int tiles_n,
+                                            int& tm, int& tn) {
+  int pid = bid;
+  if (nblk % kXcds == 0) pid = (bid % kXcds) * (nblk / kXcds) + bid / kXcds;
+  const int width = kGroupM * tiles_n;
+  const int group = pid / width;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_group = pid - group * width;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+// Scheduling fence between the k-substeps of the main loop: nothing moves
+// across it, so the LDS reads issued in substep s for substep s+1 stay ahead
+// of the MFMAs of substep s (the default scheduler would sink them next to
+// their uses and expose the LDS latency to the matrix pipe).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Within a substep, an explicit interleave: each MFMA is followed by one of
+// the substep's memory operations, LDS reads for the next substep first.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+constexpr int kSchedDsWrite = 0x200;
+
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+  __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+
+template <int BM, int BN, bool MASKED, bool GELU, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
+    int64_t ldr, void* __restrict__ out, int64_t ldo) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_CHUNKS = BM * kBK / 8 / kThreads;  // 16-byte chunks per thread
+  static_assert(A_CHUNKS >= 1 && BN <= kThreads, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = (K + kBK - 1) / kBK;
+
+  // A loader: chunk i of thread t covers row i*32 + t/8, k-chunk t%8.
+  const int a_row = tid >> 3, a_kc = tid & 7;
+  // B loader: thread t (< BN) covers the 8x8 block k-rows (t%8)*8.., n-cols (t/8)*8..
+  const bool b_loader = (BN == kThreads) || tid < BN;
+  const int b_kb = tid & 7, b_nb = tid >> 3;
+
+  u32x4_t ra[A_CHUNKS];
+  u32x4_t rb[8];
+
+  auto load_a = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kBK;
+    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
+      const int gm = m0 + I * 32 + a_row, gk = k0 + a_kc * 8;
+      if (!MASKED || (gm < M && gk < K))
+        ra[I] = *reinterpret_cast<const u32x4_t*>(A + static_cast<int64_t>(gm) * lda + gk);
+      else
+        ra[I] = zero4();
+    });
+  };
+  auto load_b = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kBK;
+    if (b_loader) {
+      static_for<8>([&](auto J) __attribute__((always_inline)) {
+        const int gk = k0 + b_kb * 8 + J, gn = n0 + b_nb * 8;
+        if (!MASKED || (gk < K && gn < N))
+          rb[J] = *reinterpret_cast<const u32x4_t*>(B + static_cast<int64_t>(gk) * ldb + gn);
+        else
+          rb[J] = zero4();
+      });
+    }
+  };
+  auto store_a = [&](int buf) __attribute__((always_inline)) {
+    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
+      *reinterpret_cast<u32x4_t*>(&sA[buf][(I * 32 + a_row) * kPitch + a_kc * 8]) = ra[I];
+    });
+  };
+  auto store_b = [&](int buf) __attribute__((always_inline)) {
+    if (b_loader) {
+      // rb[j] holds B[k0 + kb*8 + j][n0 + nb*8 .. +7]; write column e of the
+      // 8x8 block as 8 consecutive k values of row n = nb*8 + e.
+      static_for<8>([&](auto E) __attribute__((always_inline)) {
+        constexpr int q = E >> 1;
+        constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t t;
+        t[0] = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
+        t[1] = __builtin_amdgcn_perm(rb[3][q], rb[2][q], sel);
+        t[2] = __builtin_amdgcn_perm(rb[5][q], rb[4][q], sel);
+        t[3] = __builtin_amdgcn_perm(rb[7][q], rb[6][q], sel);
+        *reinterpret_cast<u32x4_t*>(&sB[buf][(b_nb * 8 + E) * kPitch + b_kb * 8]) = t;
+      });
+    }
+  };
+
+  // MFMA operand fragments, double-buffered by k-substep parity.
+  const int frag_row = lane & 31;
+  const int frag_k = (lane >> 5) * 8;
+  const int a_frag = (wm * WM + frag_row) * kPitch + frag_k;
+  const int b_frag = (wn * WN + frag_row) * kPitch + frag_k;
+  bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
+  auto read_frags = [&](int buf, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
+      __attribute__((always_inline)) {
+    const uint16_t* a_s = sA[buf] + a_frag + s * 16;
+    const uint16_t* b_s = sB[buf] + b_frag + s * 16;
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      af[I] = *reinterpret_cast<const bf16x8_t*>(a_s + I * 32 * kPitch);
+    });
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      bf[J] = *reinterpret_cast<const bf16x8_t*>(b_s + J * 32 * kPitch);
+    });
+  };
+
+  f32x16_t acc[TN][TM];
+  static_for<TN>([&](auto J) __attribute__((always_inline)) {
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      acc[J][I] = (f32x16_t)(0.0f);
+    });
+  });
+  auto mfmas = [&](const bf16x8_t(&af)[TM], const bf16x8_t(&bf)[TN]) __attribute__((always_inline)) {
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      static_for<TM>([&](auto I) __attribute__((always_inline)) {
+        acc[J][I] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[J], af[I], acc[J][I], 0, 0, 0);
+      });
+    });
+  };
+
+  // Software pipeline over k-tiles (4 k-substeps of 16 each).  In iteration kt
+  // the registers ra/rb hold k-tile kt+1 (loaded one iteration earlier):
+  //   s0: LDS-store A of tile kt+1 into the other stage, issue global loads of
+  //       A for tile kt+2, read fragments of s1, MFMAs of s0
+  //   s1: same for B (with the 8x8 transposes), fragments of s2, MFMAs of s1
+  //   s2: fragments of s3, MFMAs of s2
+  //   s3: barrier (tile kt+1 complete in the other stage, all reads of this
+  //       stage done), fragments of tile kt+1 s0, MFMAs of s3
+  // The prefetch index is clamped to the last tile, so the loop body has no
+  // branches; the clamped loads re-read a tile that is never consumed.
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  store_b(0);
+  const int k_second = nk > 1 ? 1 : 0;
+  load_a(k_second);
+  load_b(k_second);
+  __syncthreads();
+  read_frags(0, 0, af0, bf0);
+
+  constexpr int kFrags = TM + TN;        // LDS fragment reads per substep
+  constexpr int kMfma = TM * TN;         // MFMAs per substep
+  static_assert(kMfma >= 2 * kFrags || BM != 256, "interleave pattern");
+  auto interleave_reads = [&]() __attribute__((always_inline)) {
+    static_for<kFrags>([&](auto) __attribute__((always_inline)) {
+      sched_group<kSchedMfma, 1>();
+      sched_group<kSchedDsRead, 1>();
+    });
+    sched_group<kSchedMfma, kMfma - kFrags>();
+  };
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const int kpre = min(kt + 2, nk - 1);
+    // s0: A of tile kt+1 to LDS, global loads of A for tile kt+2
+    read_frags(cur, 1, af1, bf1);
+    store_a(nxt);
+    load_a(kpre);
+    mfmas(af0, bf0);
+    if constexpr (BM == 256 && BN == 256) {
+      static_for<8>([&](auto) __attribute__((always_inline)) {
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsRead, 1>();
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsWrite, 1>();
+        sched_group<kSchedVmemRead, 1>();
+      });
+    }
+    sched_fence();
+    // s1: B of tile kt+1 (transposed) to LDS, global loads of B for tile kt+2
+    read_frags(cur, 2, af0, bf0);
+    store_b(nxt);
+    load_b(kpre);
+    mfmas(af1, bf1);
+    if constexpr (BM == 256 && BN == 256) {
+      static_for<8>([&](auto) __attribute__((always_inline)) {
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsRead, 1>();
+        sched_group<kSchedValu, 4>();
+        sched_group<kSchedMfma, 1>();
+        sched_group<kSchedDsWrite, 1>();
+        sched_group<kSchedVmemRead, 1>();
+      });
+    }
+    sched_fence();
+    // s2
+    read_frags(cur, 3, af1, bf1);
+    mfmas(af0, bf0);
+    if constexpr (BM == 256 && BN == 256) interleave_reads();
+    sched_fence();
+    // s3: tile kt+1 is complete in the other stage after the barrier
+    __syncthreads();
+    read_frags(nxt, 0, af0, bf0);
+    mfmas(af1, bf1);
+    if constexpr (BM == 256 && BN == 256) interleave_reads();
+    sched_fence();
+  }
+
+  // Epilogue.  acc[j][i][4g + r] is C[m][n] with
+  //   m = m0 + wm*WM + i*32 + lane%32,  n = n0 + wn*WN + j*32 + 8g + 4*(lane/32) + r,
+  // i.e. each lane owns 4 consecutive columns per (i, j, g): one 16-byte fp32
+  // or 8-byte bf16 store.  The bias/residual flags are uniform, so the body is
+  // instantiated once per combination and selected with one branch.
+  const int m_lane = m0 + wm * WM + (lane & 31);
+  const int n_lane = n0 + wn * WN + (lane >> 5) * 4;
+  auto epilogue = [&](auto has_bias, auto has_res) __attribute__((always_inline)) {
+    constexpr bool kBias = decltype(has_bias)::value;
+    constexpr bool kRes = decltype(has_res)::value;
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      const int m = m_lane + I * 32;
+      if (MASKED && m >= M) return;
+      const int64_t row_out = static_cast<int64_t>(m) * ldo + n_lane;
+      const int64_t row_res = kRes ? static_cast<int64_t>(m) * ldr + n_lane : 0;
+      static_for<TN>([&](auto J) __attribute__((always_inline)) {
+        static_for<4>([&](auto G) __attribute__((always_inline)) {
+          constexpr int col = J * 32 + G * 8;
+          if (MASKED && n_lane + col >= N) return;
+          float v[4];
+          static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] = acc[J][I][4 * G + R]; });
+          if constexpr (kBias) {
+            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(bias + n_lane + col);
+            v[0] += __uint_as_float(bb[0] << 16);
+            v[1] += __uint_as_float(bb[0] & 0xFFFF0000u);
+            v[2] += __uint_as_float(bb[1] << 16);
+            v[3] += __uint_as_float(bb[1] & 0xFFFF0000u);
+          }
+          if constexpr (GELU) {
+            static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] = gelu_f32(v[R]); });
+          }
+          if constexpr (kRes) {
+            const u32x2_t rr = *reinterpret_cast<const u32x2_t*>(residual + row_res + col);
+            v[0] += __uint_as_float(rr[0] << 16);
+            v[1] += __uint_as_float(rr[0] & 0xFFFF0000u);
+            v[2] += __uint_as_float(rr[1] << 16);
+            v[3] += __uint_as_float(rr[1] & 0xFFFF0000u);
+          }
+          if constexpr (OUT_F32) {
+            typedef float f32x4_t __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + row_out + col) =
+                f32x4_t{v[0], v[1], v[2], v[3]};
+          } else {
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + row_out + col) =
+                u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+        });
+      });
+    });
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  // The column (GeLU) layer never takes a residual: that combination is not
+  // instantiated, and the front end never passes one with GeLU.
+  if constexpr (GELU) {
+    if (bias != nullptr) epilogue(T{}, F{}); else epilogue(F{}, F{});
+  } else if (bias != nullptr) {
+    if (residual != nullptr) epilogue(T{}, T{}); else epilogue(T{}, F{});
+  } else {
+    if (residual != nullptr) epilogue(F{}, T{}); else epilogue(F{}, F{});
+  }
+}
+
+template <int BM, int BN, bool GELU, bool OUT_F32>
+hipError_t launch_tile(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
+                       int N, int K, const Epilogue& ep, hipStream_t stream) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const bool masked = (M % BM) || (N % BN) || (K % kBK);
+  const uint16_t* bias = static_cast<const uint16_t*>(ep.bias);
+  const uint16_t* res = static_cast<const uint16_t*>(ep.residual);
+  if (masked)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, GELU, OUT_F32>), dim3(tiles), dim3(kThreads),
+                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, GELU, OUT_F32>), dim3(tiles), dim3(kThreads),
+                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo);
+  return hipGetLastError();
+}
+
+}  // namespace gemm_detail
+
+// One explicit instantiation set per (tile shape, GeLU, output type); defined in
+// the gemm_bf16_*.hip translation units.
+template <int BM, int BN, bool GELU, bool OUT_F32>
+hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                int M, int N, int K, const Epilogue& ep, hipStream_t stream);
+
+}  // namespace tpk
