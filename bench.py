@@ -67,8 +67,11 @@ def load_traffic(kernel: str):
 
 
 def cpu_baseline(wl, target_s: float):
-    """Time the fp64 oracle on rows of rank 0's shard (the MLP is row-independent,
-    so rows/s is a true rate).  Returns the JSON object."""
+    """Time the fp64 oracle on a bounded sample of the same workload: rows of
+    rank 0's shard if a whole shard would exceed the target time, else whole
+    rank shards 0, 1, ... until the target time is reached (the MLP is
+    row-independent, so tokens/s and FLOP/s are true rates).  Input
+    preparation (drawing, widening to fp64) is outside the timed calls."""
     import oracle
     from megatron_tensor_transformer_tp_amd import inputs
     try:
@@ -77,33 +80,111 @@ def cpu_baseline(wl, target_s: float):
                        if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    a0 = inputs.bf16_bits_to_f32(inputs.mlp_a_block(wl, 0)).astype(np.float64)
-    b0 = inputs.bf16_bits_to_f32(inputs.mlp_b_block(wl, 0)).astype(np.float64)
 
-    def run(rows: int) -> float:
-        x = inputs.bf16_bits_to_f32(inputs.mlp_x_rows(wl, 0, rows)).astype(np.float64)
+    def weights(r):
+        return (inputs.bf16_bits_to_f32(inputs.mlp_a_block(wl, r)).astype(np.float64),
+                inputs.bf16_bits_to_f32(inputs.mlp_b_block(wl, r)).astype(np.float64))
+
+    def run(x, a, b, r) -> float:
         t0 = time.perf_counter()
-        h = oracle.column_linear(x, a0, apply_gelu=True)
-        oracle.row_linear(h, b0, rank=0)
+        h = oracle.column_linear(x, a, apply_gelu=True)
+        oracle.row_linear(h, b, rank=r)
         return time.perf_counter() - t0
 
+    a0, b0 = weights(0)
     probe_rows = 128
-    t_probe = run(probe_rows)
+    t_probe = run(inputs.bf16_bits_to_f32(inputs.mlp_x_rows(wl, 0, probe_rows)).astype(np.float64), a0, b0, 0)
     rows = int(np.clip(probe_rows * target_s / max(t_probe, 1e-6), probe_rows, wl.tokens))
     rows = max(probe_rows, rows // probe_rows * probe_rows)
-    elapsed = run(rows)
-    flops = 4.0 * rows * wl.hidden * wl.f
+    x = inputs.bf16_bits_to_f32(inputs.mlp_x_rows(wl, 0, rows)).astype(np.float64)
+    elapsed, shards = run(x, a0, b0, 0), 1
+    while rows == wl.tokens and elapsed < target_s and shards < wl.t:
+        a, b = weights(shards)
+        elapsed += run(x, a, b, shards)
+        shards += 1
+    tokens_done = rows * shards
+    flops = 4.0 * tokens_done * wl.hidden * wl.f
+    what = (f"rows 0..{rows - 1} of rank 0's shard" if shards == 1 else
+            f"rank shards 0..{shards - 1}, all {rows} tokens each")
     return {
         "value": round(flops / elapsed / 1e12, 4),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"rows 0..{rows - 1} of rank 0's shard ({rows} of {wl.tokens} tokens, "
-                   f"hidden {wl.hidden}, f {wl.f}), fp64 NumPy/OpenBLAS + SciPy erfc; "
-                   f"{elapsed:.2f} s wall, {rows / elapsed:.1f} tokens/s"),
+        "sample": (f"{what} (hidden {wl.hidden}, f {wl.f}); fp64 NumPy/OpenBLAS matmul + SciPy erfc; "
+                   f"{elapsed:.2f} s wall, {tokens_done / elapsed:.1f} shard-tokens/s"),
         "seconds": round(elapsed, 3),
-        "tokens_per_s": round(rows / elapsed, 2),
+        "tokens_per_s": round(tokens_done / elapsed, 2),
     }
+
+
+PROFILE_CMDS = {
+    "trace": ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace -o kt -- "
+              "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline"),
+    "fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- "
+              "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
+    "write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- "
+              "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
+}
+KERNEL_KEYS = {"column_gemm_gelu": "gemm_bf16_kernel<256, 256, false, true, false>",
+               "row_gemm": "gemm_bf16_kernel<256, 256, false, false, true>",
+               "copy_1GiB": "copyBuffer"}
+
+
+def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str) -> None:
+    """Turn the rocprofv3 CSVs of the three PROFILE_CMDS runs into the committed
+    summaries: profiles/<kernel>_t8_h8192_m16384.md and profiles/traffic_counters.json.
+    HBM bytes = FETCH_SIZE x (1 GiB / FETCH_SIZE of the 1 GiB copy) + the same for
+    WRITE_SIZE (both counters report KiB per dispatch)."""
+    import csv
+    import statistics
+
+    def per_kernel_counter(path):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            for key, pat in KERNEL_KEYS.items():
+                if pat in row["Kernel_Name"]:
+                    vals.setdefault(key, []).append(float(row["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    fetch, write = per_kernel_counter(fetch_csv), per_kernel_counter(write_csv)
+    gib_kib = float(1 << 20)
+    f_scale, w_scale = gib_kib / fetch["copy_1GiB"], gib_kib / write["copy_1GiB"]
+    stats = {}
+    for row in csv.DictReader(open(trace_csv)):
+        for key, pat in KERNEL_KEYS.items():
+            if pat in row["Name"]:
+                stats[key] = row
+    wl_bytes = {"column_gemm_gelu": 469762048, "row_gemm": 738197504}
+    wl_flops = 2.0 * 16384 * 8192 * 4096
+    out = {"source_sha": kernel_source_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "commands": PROFILE_CMDS, "kernels": {}}
+    for key in ("column_gemm_gelu", "row_gemm"):
+        fb = fetch[key] * 1024 * f_scale
+        wb = write[key] * 1024 * w_scale
+        st = stats[key]
+        avg_us = float(st["AverageNs"]) / 1e3
+        out["kernels"][key] = {"hbm_bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb),
+                               "write_bytes": int(wb), "algorithmic_bytes": wl_bytes[key],
+                               "avg_us": round(avg_us, 2), "calls": int(st["Calls"])}
+        md = [f"# {key} — t8_h8192_m16384 (one rank shard, M=16384, h=8192, f=4096)", "",
+              f"kernel: `{st['Name'][:120]}`", f"kernel source sha: {out['source_sha']}", "",
+              "Commands (run from the repository root on the GPU box):", "",
+              *[f"    {c}" for c in PROFILE_CMDS.values()], "",
+              "| figure | value |", "|---|---|",
+              f"| calls in the trace run | {st['Calls']} |",
+              f"| average duration | {avg_us:.1f} us |",
+              f"| min / max duration | {float(st['MinNs'])/1e3:.1f} / {float(st['MaxNs'])/1e3:.1f} us |",
+              f"| achieved (algorithmic FLOP / avg duration) | {wl_flops / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s |",
+              f"| FETCH_SIZE per dispatch (median) | {fetch[key]:.0f} KiB (x{f_scale:.3f} from the 1 GiB copy) |",
+              f"| WRITE_SIZE per dispatch (median) | {write[key]:.0f} KiB (x{w_scale:.3f}) |",
+              f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.1f} MB (fetch {fb / 1e6:.1f}, write {wb / 1e6:.1f}) |",
+              f"| algorithmic bytes per launch | {wl_bytes[key] / 1e6:.1f} MB |", ""]
+        with open(os.path.join(ROOT, "profiles", f"{key}_t8_h8192_m16384.md"), "w") as fh:
+            fh.write("\n".join(md))
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def main() -> int:
@@ -119,7 +200,12 @@ def main() -> int:
                     help="target wall time of the bounded oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/ summaries from the rocprofv3 CSVs of PROFILE_CMDS and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
