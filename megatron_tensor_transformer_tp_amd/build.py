@@ -43,6 +43,8 @@ COMMON_FLAGS = [
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    if os.path.exists(obj):
+        os.remove(obj)  # a failed compile must never leave a stale object to link
     cmd = [HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -55,6 +57,8 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False, jobs: int = 0) -> str:
     """Compile every source for gfx950 and link ``libtp_shard.so``; return its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    if os.path.exists(LIB_PATH):
+        os.remove(LIB_PATH)  # a failed build leaves no library: loading then fails loudly
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))

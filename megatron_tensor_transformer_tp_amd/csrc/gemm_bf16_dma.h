@@ -1,0 +1,222 @@
+// bf16 GEMM, C[M,N] = A[M,K] . B[K,N] (both row-major), fp32 accumulation on
+// the gfx950 matrix cores, with both operand tiles brought into LDS by the
+// asynchronous global->LDS copy (global_load_lds_dwordx4) instead of through
+// registers.  Used for tile-aligned shapes (M % BM == 0, N % BN == 0,
+// K % 32 == 0): the copy cannot zero-fill a K tail.
+//
+//   * k-tiles of 32, four LDS stages of (BM + BN) x 64 B (128 KiB for
+//     256 x 256): tile kt+3 is in flight while tile kt is multiplied.
+//   * Each copy instruction moves 1 KiB: lane t's 16 bytes land at
+//     LDS base + 16 t.  The lane -> global address map applies the LDS swizzle,
+//     so the bytes of a 16-byte chunk are never split.
+//   * A stage (activations, k contiguous): rows of 64 B = 4 chunks; logical
+//     chunk c of row r sits at chunk c ^ ((r >> 2) & 3).  An MFMA fragment
+//     (16 consecutive rows, one chunk each) is one ds_read_b128 per lane and
+//     touches 16 distinct 16-byte bank groups.
+//   * B stage (weights, n contiguous as in memory): rows of BN*2 bytes;
+//     logical chunk c of k-row r sits at chunk c ^ ((r & 3) << 2).  The MFMA
+//     wants 8 consecutive k per lane for one n: ds_read_b64_tr_b16 gives it
+//     directly (within each 16-lane group, lane 4r+c points at 4 consecutive
+//     n of k-row r, and lane i receives column i of the resulting 4 x 16
+//     block), two reads per fragment; the four k-rows of one read fall in
+//     four different 64-byte bank windows.
+//   * Synchronisation is explicit: before the barrier that publishes tile
+//     kt+1 each wave waits (s_waitcnt vmcnt) only for its own copies of that
+//     tile, never for the younger tiles in flight; the barrier is a bare
+//     s_barrier with a compiler memory clobber (a workgroup fence would make
+//     the compiler drain every outstanding copy).
+#pragma once
+
+#include "gemm_bf16_impl.h"
+
+namespace tpk {
+namespace gemm_detail {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+#define TPK_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int kBKd = 32;     // k-tile of the copy kernel
+constexpr int kStagesD = 4;  // LDS stages
+
+// Workgroup barrier with no memory fence: the compiler may not move memory
+// operations across it, and inserts no waits for it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 1 KiB global->LDS copy: lane t's 16 bytes from `src` land at LDS byte
+// address lds_addr + 16 t (lds_addr uniform, loaded into M0).  Issued as
+// inline assembly so that the compiler does not treat it as an LDS store:
+// left to itself it would make later LDS reads of *other* stages wait for
+// every copy in flight (s_waitcnt vmcnt(0)), which defeats the pipeline.
+// Ordering against LDS reads is explicit instead: wait_vmcnt + lds_barrier.
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(p)));
+}
+
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt fields at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int WGM, int WGN, bool GELU, bool OUT_F32>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
+    int64_t ldr, void* __restrict__ out, int64_t ldo) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_BYTES = BM * kBKd * 2;
+  constexpr int B_BYTES = kBKd * BN * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int QA = A_BYTES / 1024 / NW;  // copy instructions per wave per k-tile (A)
+  constexpr int QB = B_BYTES / 1024 / NW;  // (B)
+  constexpr int L = QA + QB;
+  constexpr int CB = BN / 8;               // 16-byte chunks per B row
+  static_assert(QA * NW * 1024 == A_BYTES && QB * NW * 1024 == B_BYTES && CB >= 16, "shape");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStagesD * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lives in an SGPR
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, M / BM, N / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = K / kBKd;
+
+  // Per-lane copy sources for k-tile 0 (advanced by kBKd columns of A and
+  // kBKd rows of B per k-tile).
+  const uint16_t* a_src[QA];
+  const uint16_t* b_src[QB];
+  static_for<QA>([&](auto Q) __attribute__((always_inline)) {
+    const int slot = (wave * QA + Q) * 64 + lane;
+    const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+    a_src[Q] = A + static_cast<int64_t>(m0 + row) * lda + 8 * c;
+  });
+  static_for<QB>([&](auto Q) __attribute__((always_inline)) {
+    const int slot = (wave * QB + Q) * 64 + lane;
+    const int krow = slot / CB, c = (slot % CB) ^ ((krow & 3) << 2);
+    b_src[Q] = B + static_cast<int64_t>(krow) * ldb + n0 + 8 * c;
+  });
+  const int64_t b_step = static_cast<int64_t>(kBKd) * ldb;
+
+  // Copies of k-tile kt (clamped to the last tile) into stage kt % 4.
+  const uint32_t smem_base = lds_address(smem);
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const int kc = min(kt, nk - 1);
+    const uint32_t sbase = smem_base + (kt & (kStagesD - 1)) * STAGE;
+    static_for<QA>([&](auto Q) __attribute__((always_inline)) {
+      copy_to_lds(a_src[Q] + kc * kBKd, sbase + (wave * QA + Q) * 1024);
+    });
+    static_for<QB>([&](auto Q) __attribute__((always_inline)) {
+      copy_to_lds(b_src[Q] + kc * b_step, sbase + A_BYTES + (wave * QB + Q) * 1024);
+    });
+  };
+
+  // Fragment addressing (byte offsets within a stage).
+  const int sw_a = (lane >> 2) & 3;
+  const int a_row_off = (wm * WM + (lane & 31)) * 64;
+  const int gi = lane & 15;
+  const int b_row_lane = (lane >> 5) * 8 + (gi >> 2);   // + s*16 + h*4
+  const int b_sw = (gi >> 2) << 2;                       // (krow & 3) << 2
+  const int b_chunk_lane = ((lane >> 4) & 1) * 2 + ((gi & 3) >> 1);
+  const int b_within = (gi & 1) * 8;
+
+  bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
+  auto read_frags = [&](int kt, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
+      __attribute__((always_inline)) {
+    const uint8_t* st = smem + (kt & (kStagesD - 1)) * STAGE;
+    const int a_chunk = (2 * s + (lane >> 5)) ^ sw_a;
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      af[I] = *TPK_LDS(const bf16x8_t, st + a_row_off + I * 32 * 64 + a_chunk * 16);
+    });
+    const uint8_t* bs = st + A_BYTES;
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      const int chunk = (((wn * WN + J * 32) >> 3) + b_chunk_lane) ^ b_sw;
+      i16x4_t h[2];
+      static_for<2>([&](auto H) __attribute__((always_inline)) {
+        const int krow = s * 16 + H * 4 + b_row_lane;
+        h[H] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TPK_LDS(i16x4_t, bs + krow * (BN * 2) + chunk * 16 + b_within));
+      });
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+      bf[J] = __builtin_bit_cast(bf16x8_t, v);
+    });
+  };
+
+  f32x16_t acc[TN][TM];
+  static_for<TN>([&](auto J) __attribute__((always_inline)) {
+    static_for<TM>([&](auto I) __attribute__((always_inline)) { acc[J][I] = (f32x16_t)(0.0f); });
+  });
+  auto mfmas = [&](const bf16x8_t(&af)[TM], const bf16x8_t(&bf)[TN]) __attribute__((always_inline)) {
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      static_for<TM>([&](auto I) __attribute__((always_inline)) {
+        acc[J][I] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[J], af[I], acc[J][I], 0, 0, 0);
+      });
+    });
+  };
+
+  constexpr int kFrags = TM + 2 * TN;
+  constexpr int kMfma = TM * TN;
+
+  // Every iteration issues exactly L copies per wave (the copies of tiles past
+  // the end re-read the last tile into a stage that is never read again), so
+  // "tile kt+1 has landed" is always vmcnt <= L: only tile kt+2 may still be
+  // in flight when tile kt+1 is published.
+  issue(0);
+  issue(1);
+  issue(2);
+  wait_vmcnt<2 * L>();
+  lds_barrier();
+  read_frags(0, 0, af0, bf0);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // substep 0 of tile kt: fragments of substep 1 load under its MFMAs
+    read_frags(kt, 1, af1, bf1);
+    mfmas(af0, bf0);
+    interleave_substep<kMfma, kFrags, 0, 0, 0>();
+    sched_fence();
+    // substep 1: publish tile kt+1, start tile kt+3, fragments of tile kt+1
+    wait_vmcnt<L>();
+    lds_barrier();
+    issue(kt + 3);
+    read_frags(kt + 1, 0, af0, bf0);
+    mfmas(af1, bf1);
+    interleave_substep<kMfma, kFrags, 0, 0, 0>();
+    sched_fence();
+  }
+  wait_vmcnt<0>();
+
+  store_tile<TM, TN, false, GELU, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
+                                            n0 + wn * WN + (lane >> 5) * 4, M, N, bias, residual,
+                                            ldr, out, ldo);
+}
+
+template <int BM, int BN, int WGM, int WGN, bool GELU, bool OUT_F32>
+hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
+                           int N, int K, const Epilogue& ep, hipStream_t stream) {
+  const int tiles = (M / BM) * (N / BN);
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WGM, WGN, GELU, OUT_F32>), dim3(tiles),
+                     dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K,
+                     static_cast<const uint16_t*>(ep.bias),
+                     static_cast<const uint16_t*>(ep.residual), ep.ldr, ep.out, ep.ldo);
+  return hipGetLastError();
+}
+
+#undef TPK_LDS
+
+}  // namespace gemm_detail
+}  // namespace tpk

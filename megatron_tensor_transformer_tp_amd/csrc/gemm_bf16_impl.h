@@ -52,7 +52,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
 constexpr int kBK = 64;
 constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 elements (144 B)
 constexpr int kXcds = 8;
@@ -92,199 +91,17 @@ __device__ __forceinline__ void sched_group() {
   __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
 }
 
-template <int BM, int BN, bool MASKED, bool GELU, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
-    int64_t ldr, void* __restrict__ out, int64_t ldo) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_CHUNKS = BM * kBK / 8 / kThreads;  // 16-byte chunks per thread
-  static_assert(A_CHUNKS >= 1 && BN <= kThreads, "tile shape");
-
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kPitch];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = (K + kBK - 1) / kBK;
-
-  // A loader: chunk i of thread t covers row i*32 + t/8, k-chunk t%8.
-  const int a_row = tid >> 3, a_kc = tid & 7;
-  // B loader: thread t (< BN) covers the 8x8 block k-rows (t%8)*8.., n-cols (t/8)*8..
-  const bool b_loader = (BN == kThreads) || tid < BN;
-  const int b_kb = tid & 7, b_nb = tid >> 3;
-
-  u32x4_t ra[A_CHUNKS];
-  u32x4_t rb[8];
-
-  auto load_a = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * kBK;
-    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
-      const int gm = m0 + I * 32 + a_row, gk = k0 + a_kc * 8;
-      if (!MASKED || (gm < M && gk < K))
-        ra[I] = *reinterpret_cast<const u32x4_t*>(A + static_cast<int64_t>(gm) * lda + gk);
-      else
-        ra[I] = zero4();
-    });
-  };
-  auto load_b = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * kBK;
-    if (b_loader) {
-      static_for<8>([&](auto J) __attribute__((always_inline)) {
-        const int gk = k0 + b_kb * 8 + J, gn = n0 + b_nb * 8;
-        if (!MASKED || (gk < K && gn < N))
-          rb[J] = *reinterpret_cast<const u32x4_t*>(B + static_cast<int64_t>(gk) * ldb + gn);
-        else
-          rb[J] = zero4();
-      });
-    }
-  };
-  auto store_a = [&](int buf) __attribute__((always_inline)) {
-    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
-      *reinterpret_cast<u32x4_t*>(&sA[buf][(I * 32 + a_row) * kPitch + a_kc * 8]) = ra[I];
-    });
-  };
-  auto store_b = [&](int buf) __attribute__((always_inline)) {
-    if (b_loader) {
-      // rb[j] holds B[k0 + kb*8 + j][n0 + nb*8 .. +7]; write column e of the
-      // 8x8 block as 8 consecutive k values of row n = nb*8 + e.
-      static_for<8>([&](auto E) __attribute__((always_inline)) {
-        constexpr int q = E >> 1;
-        constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t t;
-        t[0] = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
-        t[1] = __builtin_amdgcn_perm(rb[3][q], rb[2][q], sel);
-        t[2] = __builtin_amdgcn_perm(rb[5][q], rb[4][q], sel);
-        t[3] = __builtin_amdgcn_perm(rb[7][q], rb[6][q], sel);
-        *reinterpret_cast<u32x4_t*>(&sB[buf][(b_nb * 8 + E) * kPitch + b_kb * 8]) = t;
-      });
-    }
-  };
-
-  // MFMA operand fragments, double-buffered by k-substep parity.
-  const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
-  const int a_frag = (wm * WM + frag_row) * kPitch + frag_k;
-  const int b_frag = (wn * WN + frag_row) * kPitch + frag_k;
-  bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
-  auto read_frags = [&](int buf, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
-      __attribute__((always_inline)) {
-    const uint16_t* a_s = sA[buf] + a_frag + s * 16;
-    const uint16_t* b_s = sB[buf] + b_frag + s * 16;
-    static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      af[I] = *reinterpret_cast<const bf16x8_t*>(a_s + I * 32 * kPitch);
-    });
-    static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      bf[J] = *reinterpret_cast<const bf16x8_t*>(b_s + J * 32 * kPitch);
-    });
-  };
-
-  f32x16_t acc[TN][TM];
-  static_for<TN>([&](auto J) __attribute__((always_inline)) {
-    static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      acc[J][I] = (f32x16_t)(0.0f);
-    });
-  });
-  auto mfmas = [&](const bf16x8_t(&af)[TM], const bf16x8_t(&bf)[TN]) __attribute__((always_inline)) {
-    static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      static_for<TM>([&](auto I) __attribute__((always_inline)) {
-        acc[J][I] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[J], af[I], acc[J][I], 0, 0, 0);
-      });
-    });
-  };
-
-  // Software pipeline over k-tiles (4 k-substeps of 16 each).  In iteration kt
-  // the registers ra/rb hold k-tile kt+1 (loaded one iteration earlier):
-  //   s0: LDS-store A of tile kt+1 into the other stage, issue global loads of
-  //       A for tile kt+2, read fragments of s1, MFMAs of s0
-  //   s1: same for B (with the 8x8 transposes), fragments of s2, MFMAs of s1
-  //   s2: fragments of s3, MFMAs of s2
-  //   s3: barrier (tile kt+1 complete in the other stage, all reads of this
-  //       stage done), fragments of tile kt+1 s0, MFMAs of s3
-  // The prefetch index is clamped to the last tile, so the loop body has no
-  // branches; the clamped loads re-read a tile that is never consumed.
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  store_b(0);
-  const int k_second = nk > 1 ? 1 : 0;
-  load_a(k_second);
-  load_b(k_second);
-  __syncthreads();
-  read_frags(0, 0, af0, bf0);
-
-  constexpr int kFrags = TM + TN;        // LDS fragment reads per substep
-  constexpr int kMfma = TM * TN;         // MFMAs per substep
-  static_assert(kMfma >= 2 * kFrags || BM != 256, "interleave pattern");
-  auto interleave_reads = [&]() __attribute__((always_inline)) {
-    static_for<kFrags>([&](auto) __attribute__((always_inline)) {
-      sched_group<kSchedMfma, 1>();
-      sched_group<kSchedDsRead, 1>();
-    });
-    sched_group<kSchedMfma, kMfma - kFrags>();
-  };
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
-    const int kpre = min(kt + 2, nk - 1);
-    // s0: A of tile kt+1 to LDS, global loads of A for tile kt+2
-    read_frags(cur, 1, af1, bf1);
-    store_a(nxt);
-    load_a(kpre);
-    mfmas(af0, bf0);
-    if constexpr (BM == 256 && BN == 256) {
-      static_for<8>([&](auto) __attribute__((always_inline)) {
-        sched_group<kSchedMfma, 1>();
-        sched_group<kSchedDsRead, 1>();
-        sched_group<kSchedMfma, 1>();
-        sched_group<kSchedDsWrite, 1>();
-        sched_group<kSchedVmemRead, 1>();
-      });
-    }
-    sched_fence();
-    // s1: B of tile kt+1 (transposed) to LDS, global loads of B for tile kt+2
-    read_frags(cur, 2, af0, bf0);
-    store_b(nxt);
-    load_b(kpre);
-    mfmas(af1, bf1);
-    if constexpr (BM == 256 && BN == 256) {
-      static_for<8>([&](auto) __attribute__((always_inline)) {
-        sched_group<kSchedMfma, 1>();
-        sched_group<kSchedDsRead, 1>();
-        sched_group<kSchedValu, 4>();
-        sched_group<kSchedMfma, 1>();
-        sched_group<kSchedDsWrite, 1>();
-        sched_group<kSchedVmemRead, 1>();
-      });
-    }
-    sched_fence();
-    // s2
-    read_frags(cur, 3, af1, bf1);
-    mfmas(af0, bf0);
-    if constexpr (BM == 256 && BN == 256) interleave_reads();
-    sched_fence();
-    // s3: tile kt+1 is complete in the other stage after the barrier
-    __syncthreads();
-    read_frags(nxt, 0, af0, bf0);
-    mfmas(af1, bf1);
-    if constexpr (BM == 256 && BN == 256) interleave_reads();
-    sched_fence();
-  }
-
-  // Epilogue.  acc[j][i][4g + r] is C[m][n] with
-  //   m = m0 + wm*WM + i*32 + lane%32,  n = n0 + wn*WN + j*32 + 8g + 4*(lane/32) + r,
-  // i.e. each lane owns 4 consecutive columns per (i, j, g): one 16-byte fp32
-  // or 8-byte bf16 store.  The bias/residual flags are uniform, so the body is
-  // instantiated once per combination and selected with one branch.
-  const int m_lane = m0 + wm * WM + (lane & 31);
-  const int n_lane = n0 + wn * WN + (lane >> 5) * 4;
+// Epilogue shared by the GEMM kernels.  acc[j][i][4g + r] is C[m][n] with
+//   m = m_lane + i*32,  n = n_lane + j*32 + 8g + r,
+// i.e. each lane owns 4 consecutive columns per (i, j, g): one 16-byte fp32
+// or 8-byte bf16 store.  The bias/residual flags are uniform, so the body is
+// instantiated once per combination and selected with one branch; the column
+// (GeLU) layer never takes a residual, so that combination is not built.
+template <int TM, int TN, bool MASKED, bool GELU, bool OUT_F32>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_lane, int n_lane,
+                                           int M, int N, const uint16_t* __restrict__ bias,
+                                           const uint16_t* __restrict__ residual, int64_t ldr,
+                                           void* __restrict__ out, int64_t ldo) {
   auto epilogue = [&](auto has_bias, auto has_res) __attribute__((always_inline)) {
     constexpr bool kBias = decltype(has_bias)::value;
     constexpr bool kRes = decltype(has_res)::value;
@@ -325,13 +142,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
                 u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           }
         });
+        // keep the accumulator reads of one 32x32 block next to its stores
+        // (hoisting all 256 of them ahead of the stores would spill)
+        sched_fence();
       });
     });
   };
   using T = std::true_type;
   using F = std::false_type;
-  // The column (GeLU) layer never takes a residual: that combination is not
-  // instantiated, and the front end never passes one with GeLU.
   if constexpr (GELU) {
     if (bias != nullptr) epilogue(T{}, F{}); else epilogue(F{}, F{});
   } else if (bias != nullptr) {
@@ -341,18 +159,214 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   }
 }
 
-template <int BM, int BN, bool GELU, bool OUT_F32>
+// Interleave for one k-substep: kM MFMAs; before MFMA i the scheduler is asked
+// for the substep's next LDS fragment reads (front-loaded, kR in total), and a
+// proportional share of its VALU ops (kP), LDS stores (kW) and global loads (kV).
+template <int kM, int kR, int kP, int kW, int kV>
+__device__ __forceinline__ void interleave_substep() {
+  static_for<kM>([&](auto I) __attribute__((always_inline)) {
+    constexpr int i = I;
+    sched_group<kSchedMfma, 1>();
+    constexpr int r = (i == kM - 1) ? (kR > i ? kR - i : 0) : (i < kR ? 1 : 0);
+    if constexpr (r > 0) sched_group<kSchedDsRead, r>();
+    constexpr int p = (i + 1) * kP / kM - i * kP / kM;
+    if constexpr (p > 0) sched_group<kSchedValu, p>();
+    constexpr int w = (i + 1) * kW / kM - i * kW / kM;
+    if constexpr (w > 0) sched_group<kSchedDsWrite, w>();
+    constexpr int v = (i + 1) * kV / kM - i * kV / kM;
+    if constexpr (v > 0) sched_group<kSchedVmemRead, v>();
+  });
+}
+
+// BM x BN tile per workgroup of WGM x WGN waves; each wave owns a
+// (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA blocks.
+template <int BM, int BN, int WGM, int WGN, bool MASKED, bool GELU, bool OUT_F32>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
+    int64_t ldr, void* __restrict__ out, int64_t ldo) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int A_CHUNKS = BM * kBK / 8 / NT;  // 16-byte chunks of the A tile per thread
+  constexpr int RB = kBK * BN / 8 / NT;        // k-rows of the B tile per thread (x 8 columns)
+  constexpr int KG = kBK / RB;                 // k-groups of RB rows
+  static_assert(A_CHUNKS >= 1 && (RB == 2 || RB == 4 || RB == 8) && KG * (BN / 8) == NT,
+                "tile / thread shape");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kPitch];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lives in an SGPR
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = (K + kBK - 1) / kBK;
+
+  // A loader: chunk i of thread t is row i*(NT/8) + t/8, k-chunk t%8.
+  const int a_row = tid >> 3, a_kc = tid & 7;
+  // B loader: thread t covers k-rows (t%KG)*RB .. +RB-1 of columns (t/KG)*8 .. +7.
+  const int b_kb = tid % KG, b_nb = tid / KG;
+
+  u32x4_t ra[A_CHUNKS];
+  u32x4_t rb[RB];
+
+  auto load_a = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kBK;
+    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
+      const int gm = m0 + I * (NT / 8) + a_row, gk = k0 + a_kc * 8;
+      if (!MASKED || (gm < M && gk < K))
+        ra[I] = *reinterpret_cast<const u32x4_t*>(A + static_cast<int64_t>(gm) * lda + gk);
+      else
+        ra[I] = zero4();
+    });
+  };
+  auto load_b = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kBK;
+    static_for<RB>([&](auto J) __attribute__((always_inline)) {
+      const int gk = k0 + b_kb * RB + J, gn = n0 + b_nb * 8;
+      if (!MASKED || (gk < K && gn < N))
+        rb[J] = *reinterpret_cast<const u32x4_t*>(B + static_cast<int64_t>(gk) * ldb + gn);
+      else
+        rb[J] = zero4();
+    });
+  };
+  auto store_a = [&](int buf) __attribute__((always_inline)) {
+    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
+      *reinterpret_cast<u32x4_t*>(&sA[buf][(I * (NT / 8) + a_row) * kPitch + a_kc * 8]) = ra[I];
+    });
+  };
+  auto store_b = [&](int buf) __attribute__((always_inline)) {
+    // rb[j] holds B[k0 + kb*RB + j][n0 + nb*8 .. +7]; column e of this RB x 8
+    // block becomes RB consecutive k values of LDS row n = nb*8 + e.
+    static_for<8>([&](auto E) __attribute__((always_inline)) {
+      constexpr int q = E >> 1;
+      constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
+      uint16_t* dst = &sB[buf][(b_nb * 8 + E) * kPitch + b_kb * RB];
+      if constexpr (RB == 8) {
+        u32x4_t t;
+        t[0] = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
+        t[1] = __builtin_amdgcn_perm(rb[3][q], rb[2][q], sel);
+        t[2] = __builtin_amdgcn_perm(rb[5][q], rb[4][q], sel);
+        t[3] = __builtin_amdgcn_perm(rb[7][q], rb[6][q], sel);
+        *reinterpret_cast<u32x4_t*>(dst) = t;
+      } else if constexpr (RB == 4) {
+        u32x2_t t;
+        t[0] = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
+        t[1] = __builtin_amdgcn_perm(rb[3][q], rb[2][q], sel);
+        *reinterpret_cast<u32x2_t*>(dst) = t;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
+      }
+    });
+  };
+
+  // MFMA operand fragments, double-buffered by k-substep parity.
+  const int frag_row = lane & 31;
+  const int frag_k = (lane >> 5) * 8;
+  const int a_frag = (wm * WM + frag_row) * kPitch + frag_k;
+  const int b_frag = (wn * WN + frag_row) * kPitch + frag_k;
+  bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
+  auto read_frags = [&](int buf, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
+      __attribute__((always_inline)) {
+    const uint16_t* a_s = sA[buf] + a_frag + s * 16;
+    const uint16_t* b_s = sB[buf] + b_frag + s * 16;
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      af[I] = *reinterpret_cast<const bf16x8_t*>(a_s + I * 32 * kPitch);
+    });
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      bf[J] = *reinterpret_cast<const bf16x8_t*>(b_s + J * 32 * kPitch);
+    });
+  };
+
+  f32x16_t acc[TN][TM];
+  static_for<TN>([&](auto J) __attribute__((always_inline)) {
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      acc[J][I] = (f32x16_t)(0.0f);
+    });
+  });
+  auto mfmas = [&](const bf16x8_t(&af)[TM], const bf16x8_t(&bf)[TN]) __attribute__((always_inline)) {
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      static_for<TM>([&](auto I) __attribute__((always_inline)) {
+        acc[J][I] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[J], af[I], acc[J][I], 0, 0, 0);
+      });
+    });
+  };
+
+  // Software pipeline over k-tiles (4 k-substeps of 16 each).  In iteration kt
+  // the registers ra/rb hold k-tile kt+1 (loaded one iteration earlier):
+  //   s0: LDS-store A of tile kt+1 into the other stage, issue global loads of
+  //       A for tile kt+2, read fragments of s1, MFMAs of s0
+  //   s1: same for B (with the in-register transposes), fragments of s2, MFMAs of s1
+  //   s2: fragments of s3, MFMAs of s2
+  //   s3: barrier (tile kt+1 complete in the other stage, all reads of this
+  //       stage done), fragments of tile kt+1 s0, MFMAs of s3
+  // The prefetch index is clamped to the last tile, so the loop body has no
+  // branches; the clamped loads re-read a tile that is never consumed.
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  store_b(0);
+  const int k_second = nk > 1 ? 1 : 0;
+  load_a(k_second);
+  load_b(k_second);
+  __syncthreads();
+  read_frags(0, 0, af0, bf0);
+
+  constexpr int kFrags = TM + TN;
+  constexpr int kMfma = TM * TN;
+  constexpr int kPermsB = 8 * (RB / 2);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const int kpre = min(kt + 2, nk - 1);
+    // s0
+    read_frags(cur, 1, af1, bf1);
+    store_a(nxt);
+    load_a(kpre);
+    mfmas(af0, bf0);
+    interleave_substep<kMfma, kFrags, 0, A_CHUNKS, A_CHUNKS>();
+    sched_fence();
+    // s1
+    read_frags(cur, 2, af0, bf0);
+    store_b(nxt);
+    load_b(kpre);
+    mfmas(af1, bf1);
+    interleave_substep<kMfma, kFrags, kPermsB, 8, RB>();
+    sched_fence();
+    // s2
+    read_frags(cur, 3, af1, bf1);
+    mfmas(af0, bf0);
+    interleave_substep<kMfma, kFrags, 0, 0, 0>();
+    sched_fence();
+    // s3: tile kt+1 is complete in the other stage after the barrier
+    __syncthreads();
+    read_frags(nxt, 0, af0, bf0);
+    mfmas(af1, bf1);
+    interleave_substep<kMfma, kFrags, 0, 0, 0>();
+    sched_fence();
+  }
+
+  store_tile<TM, TN, MASKED, GELU, OUT_F32>(acc, m0 + wm * WM + (lane & 31), n0 + wn * WN + (lane >> 5) * 4,
+                                           M, N, bias, residual, ldr, out, ldo);
+}
+
+template <int BM, int BN, int WGM, int WGN, bool GELU, bool OUT_F32>
 hipError_t launch_tile(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
                        int N, int K, const Epilogue& ep, hipStream_t stream) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const bool masked = (M % BM) || (N % BN) || (K % kBK);
   const uint16_t* bias = static_cast<const uint16_t*>(ep.bias);
   const uint16_t* res = static_cast<const uint16_t*>(ep.residual);
+  const dim3 block(64 * WGM * WGN);
   if (masked)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, true, GELU, OUT_F32>), dim3(tiles), dim3(kThreads),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, GELU, OUT_F32>), dim3(tiles), block,
                        0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, false, GELU, OUT_F32>), dim3(tiles), dim3(kThreads),
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, GELU, OUT_F32>), dim3(tiles), block,
                        0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo);
   return hipGetLastError();
 }
