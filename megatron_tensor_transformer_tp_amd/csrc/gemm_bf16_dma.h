@@ -4,8 +4,9 @@
 // registers.  Used for tile-aligned shapes (M % BM == 0, N % BN == 0,
 // K % 32 == 0): the copy cannot zero-fill a K tail.
 //
-//   * k-tiles of 32, four LDS stages of (BM + BN) x 64 B (128 KiB for
-//     256 x 256): tile kt+3 is in flight while tile kt is multiplied.
+//   * k-tiles of 32, STAGES LDS stages of (BM + BN) x 64 B (32 KiB each for
+//     256 x 256): tiles kt+1 .. kt+STAGES-1 are in flight while tile kt is
+//     multiplied (4 stages measured faster than 5 at the headline shapes).
 //   * Each copy instruction moves 1 KiB: lane t's 16 bytes land at
 //     LDS base + 16 t.  The lane -> global address map applies the LDS swizzle,
 //     so the bytes of a 16-byte chunk are never split.
@@ -36,7 +37,6 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 #define TPK_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr int kBKd = 32;     // k-tile of the copy kernel
-constexpr int kStagesD = 4;  // LDS stages
 
 // Workgroup barrier with no memory fence: the compiler may not move memory
 // operations across it, and inserts no waits for it.
@@ -67,7 +67,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int BM, int BN, int WGM, int WGN, bool GELU, bool OUT_F32>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool GELU, bool OUT_F32>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
@@ -83,8 +83,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   constexpr int L = QA + QB;
   constexpr int CB = BN / 8;               // 16-byte chunks per B row
   static_assert(QA * NW * 1024 == A_BYTES && QB * NW * 1024 == B_BYTES && CB >= 16, "shape");
+  static_assert(STAGES >= 3 && STAGES * STAGE <= 160 * 1024, "LDS stages");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStagesD * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,11 +113,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   });
   const int64_t b_step = static_cast<int64_t>(kBKd) * ldb;
 
-  // Copies of k-tile kt (clamped to the last tile) into stage kt % 4.
+  // Copies of k-tile kt (clamped to the last tile) into stage kt % STAGES.
   const uint32_t smem_base = lds_address(smem);
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const int kc = min(kt, nk - 1);
-    const uint32_t sbase = smem_base + (kt & (kStagesD - 1)) * STAGE;
+    const uint32_t sbase = smem_base + (kt % STAGES) * STAGE;
     static_for<QA>([&](auto Q) __attribute__((always_inline)) {
       copy_to_lds(a_src[Q] + kc * kBKd, sbase + (wave * QA + Q) * 1024);
     });
@@ -137,7 +138,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
   auto read_frags = [&](int kt, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
       __attribute__((always_inline)) {
-    const uint8_t* st = smem + (kt & (kStagesD - 1)) * STAGE;
+    const uint8_t* st = smem + (kt % STAGES) * STAGE;
     const int a_chunk = (2 * s + (lane >> 5)) ^ sw_a;
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
       af[I] = *TPK_LDS(const bf16x8_t, st + a_row_off + I * 32 * 64 + a_chunk * 16);
@@ -174,12 +175,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
 
   // Every iteration issues exactly L copies per wave (the copies of tiles past
   // the end re-read the last tile into a stage that is never read again), so
-  // "tile kt+1 has landed" is always vmcnt <= L: only tile kt+2 may still be
-  // in flight when tile kt+1 is published.
-  issue(0);
-  issue(1);
-  issue(2);
-  wait_vmcnt<2 * L>();
+  // "tile kt+1 has landed" is always vmcnt <= (STAGES-3)*L: only the tiles
+  // kt+2 .. kt+STAGES-2 may still be in flight when tile kt+1 is published.
+  static_for<STAGES - 1>([&](auto T) __attribute__((always_inline)) { issue(T); });
+  wait_vmcnt<(STAGES - 2) * L>();
   lds_barrier();
   read_frags(0, 0, af0, bf0);
 
@@ -189,10 +188,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     mfmas(af0, bf0);
     interleave_substep<kMfma, kFrags, 0, 0, 0>();
     sched_fence();
-    // substep 1: publish tile kt+1, start tile kt+3, fragments of tile kt+1
-    wait_vmcnt<L>();
+    // substep 1: publish tile kt+1, start tile kt+STAGES-1 (into the stage
+    // tile kt-1 occupied: every wave finished reading it before this
+    // barrier), fragments of tile kt+1
+    wait_vmcnt<(STAGES - 3) * L>();
     lds_barrier();
-    issue(kt + 3);
+    issue(kt + STAGES - 1);
     read_frags(kt + 1, 0, af0, bf0);
     mfmas(af1, bf1);
     interleave_substep<kMfma, kFrags, 0, 0, 0>();
@@ -205,11 +206,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
                                             ldr, out, ldo);
 }
 
-template <int BM, int BN, int WGM, int WGN, bool GELU, bool OUT_F32>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool GELU, bool OUT_F32>
 hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
                            int N, int K, const Epilogue& ep, hipStream_t stream) {
   const int tiles = (M / BM) * (N / BN);
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WGM, WGN, GELU, OUT_F32>), dim3(tiles),
+  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, GELU, OUT_F32>), dim3(tiles),
                      dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K,
                      static_cast<const uint16_t*>(ep.bias),
                      static_cast<const uint16_t*>(ep.residual), ep.ldr, ep.out, ep.ldo);
