@@ -29,6 +29,7 @@ SOURCES = [
     "gemm_bf16_128_plain.hip",
     "gemm_f32.hip",
     "gelu.hip",
+    "attention.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -57,4 +57,35 @@ __device__ __forceinline__ float gelu_f32(float v) {
   return v * (v >= 0.0f ? 1.0f - tail : tail);
 }
 
+// ---- global->LDS copies and explicit LDS synchronisation (gfx950) --------
+
+// Workgroup barrier with no memory fence: the compiler may not move memory
+// operations across it, and inserts no waits for it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 1 KiB global->LDS copy: lane t's 16 bytes from `src` land at LDS byte
+// address lds_addr + 16 t (lds_addr uniform, loaded into M0).  Issued as
+// inline assembly so that the compiler does not treat it as an LDS store:
+// left to itself it would make later LDS reads of *other* stages wait for
+// every copy in flight (s_waitcnt vmcnt(0)), which defeats the pipeline.
+// Ordering against LDS reads is explicit instead: wait_vmcnt + lds_barrier.
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(p)));
+}
+
+// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt fields at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 }  // namespace tpk

@@ -38,40 +38,11 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBKd = 32;     // k-tile of the copy kernel
 
-// Workgroup barrier with no memory fence: the compiler may not move memory
-// operations across it, and inserts no waits for it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// One 1 KiB global->LDS copy: lane t's 16 bytes from `src` land at LDS byte
-// address lds_addr + 16 t (lds_addr uniform, loaded into M0).  Issued as
-// inline assembly so that the compiler does not treat it as an LDS store:
-// left to itself it would make later LDS reads of *other* stages wait for
-// every copy in flight (s_waitcnt vmcnt(0)), which defeats the pipeline.
-// Ordering against LDS reads is explicit instead: wait_vmcnt + lds_barrier.
-__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_addr)
-               : "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const void*)(p)));
-}
-
-// s_waitcnt vmcnt(N) only (expcnt and lgkmcnt fields at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool GELU, bool OUT_F32>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
-    int64_t ldr, void* __restrict__ out, int64_t ldo) {
+    int64_t ldr, void* __restrict__ out, int64_t ldo, uint16_t* __restrict__ out_lo) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -203,7 +174,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
 
   store_tile<TM, TN, false, GELU, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
                                             n0 + wn * WN + (lane >> 5) * 4, M, N, bias, residual,
-                                            ldr, out, ldo);
+                                            ldr, out, ldo, out_lo);
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool GELU, bool OUT_F32>
@@ -213,7 +184,8 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
   hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, GELU, OUT_F32>), dim3(tiles),
                      dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K,
                      static_cast<const uint16_t*>(ep.bias),
-                     static_cast<const uint16_t*>(ep.residual), ep.ldr, ep.out, ep.ldo);
+                     static_cast<const uint16_t*>(ep.residual), ep.ldr, ep.out, ep.ldo,
+                     static_cast<uint16_t*>(ep.out_lo));
   return hipGetLastError();
 }
 

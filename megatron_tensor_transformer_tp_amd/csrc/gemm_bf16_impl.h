@@ -101,7 +101,8 @@ template <int TM, int TN, bool MASKED, bool GELU, bool OUT_F32>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_lane, int n_lane,
                                            int M, int N, const uint16_t* __restrict__ bias,
                                            const uint16_t* __restrict__ residual, int64_t ldr,
-                                           void* __restrict__ out, int64_t ldo) {
+                                           void* __restrict__ out, int64_t ldo,
+                                           uint16_t* __restrict__ out_lo) {
   auto epilogue = [&](auto has_bias, auto has_res) __attribute__((always_inline)) {
     constexpr bool kBias = decltype(has_bias)::value;
     constexpr bool kRes = decltype(has_res)::value;
@@ -138,8 +139,14 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
             *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + row_out + col) =
                 f32x4_t{v[0], v[1], v[2], v[3]};
           } else {
-            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + row_out + col) =
-                u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            const u32x2_t hi = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + row_out + col) = hi;
+            if (out_lo != nullptr) {
+              const u32x2_t lo = u32x2_t{
+                  pack_bf16x2(v[0] - __uint_as_float(hi[0] << 16), v[1] - __uint_as_float(hi[0] & 0xFFFF0000u)),
+                  pack_bf16x2(v[2] - __uint_as_float(hi[1] << 16), v[3] - __uint_as_float(hi[1] & 0xFFFF0000u))};
+              *reinterpret_cast<u32x2_t*>(out_lo + row_out + col) = lo;
+            }
           }
         });
         // keep the accumulator reads of one 32x32 block next to its stores
@@ -184,7 +191,7 @@ template <int BM, int BN, int WGM, int WGN, bool MASKED, bool GELU, bool OUT_F32
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
-    int64_t ldr, void* __restrict__ out, int64_t ldo) {
+    int64_t ldr, void* __restrict__ out, int64_t ldo, uint16_t* __restrict__ out_lo) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -351,7 +358,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
   }
 
   store_tile<TM, TN, MASKED, GELU, OUT_F32>(acc, m0 + wm * WM + (lane & 31), n0 + wn * WN + (lane >> 5) * 4,
-                                           M, N, bias, residual, ldr, out, ldo);
+                                           M, N, bias, residual, ldr, out, ldo, out_lo);
 }
 
 template <int BM, int BN, int WGM, int WGN, bool GELU, bool OUT_F32>
@@ -364,10 +371,12 @@ hipError_t launch_tile(const uint16_t* A, int64_t lda, const uint16_t* B, int64_
   const dim3 block(64 * WGM * WGN);
   if (masked)
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, GELU, OUT_F32>), dim3(tiles), block,
-                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo);
+                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo,
+                       static_cast<uint16_t*>(ep.out_lo));
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, GELU, OUT_F32>), dim3(tiles), block,
-                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo);
+                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo,
+                       static_cast<uint16_t*>(ep.out_lo));
   return hipGetLastError();
 }
 

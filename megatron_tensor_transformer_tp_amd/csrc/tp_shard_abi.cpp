@@ -205,20 +205,68 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
   return run_gemm(in_dt, workspace, f, b_i, hidden, tokens, hidden, f, ep2, s);
 }
 
+namespace {
+// Workspace of tp_attn_shard_fwd: the rank's packed QKV projection as a bf16
+// (hi, lo) pair [tokens, 3*hl*d] each, then the attention output [tokens, hl*d].
+struct AttnWorkspace {
+  size_t qkv_bytes, o_bytes, total;
+};
+AttnWorkspace attn_workspace(int64_t tokens, int64_t hl, int64_t head_dim) {
+  const size_t qkv = round256(static_cast<size_t>(tokens) * 3 * hl * head_dim * 2);
+  const size_t o = round256(static_cast<size_t>(tokens) * hl * head_dim * 2);
+  return {qkv, o, 2 * qkv + o};
+}
+}  // namespace
+
 size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int64_t heads,
                                      int64_t head_dim, int t, tp_dtype in_dt) {
-  (void)batch; (void)seq; (void)hidden; (void)heads; (void)head_dim; (void)t; (void)in_dt;
-  return 0;
+  if (in_dt != TP_BF16 || batch < 0 || seq < 0 || hidden < 1 || head_dim < 1) return 0;
+  int64_t hl = 0;
+  if (check_split(heads, t, 0, &hl) != TP_OK || hidden != heads * head_dim) return 0;
+  return attn_workspace(batch * seq, hl, head_dim).total;
 }
 
 tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i, void* out_i,
                             void* workspace, size_t workspace_bytes, int64_t batch, int64_t seq,
                             int64_t hidden, int64_t heads, int64_t head_dim, int causal, int t,
                             int rank, tp_dtype in_dt, tp_dtype out_dt, void* stream) {
-  (void)x; (void)wqkv_i; (void)wo_i; (void)out_i; (void)workspace; (void)workspace_bytes;
-  (void)batch; (void)seq; (void)hidden; (void)heads; (void)head_dim; (void)causal; (void)t;
-  (void)rank; (void)in_dt; (void)out_dt; (void)stream;
-  return TP_ERR_UNSUPPORTED;
+  if (!dtype_known(in_dt) || !dtype_known(out_dt) || in_dt != TP_BF16) return TP_ERR_DTYPE;
+  if (batch < 0 || seq < 0 || hidden < 1 || head_dim < 1 || (causal != 0 && causal != 1))
+    return TP_ERR_INVALID_ARG;
+  int64_t hl = 0;  // heads per rank
+  TP_TRY(check_split(heads, t, rank, &hl));
+  if (hidden != heads * head_dim) return TP_ERR_INVALID_ARG;
+  if (hidden % 8 != 0) return TP_ERR_MISALIGNED;
+  if (head_dim != 128 || seq % 128 != 0) return TP_ERR_UNSUPPORTED;
+  const int64_t tokens = batch * seq;
+  if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(3 * hl * head_dim))
+    return TP_ERR_UNSUPPORTED;
+  if (tokens == 0) return TP_OK;
+  const int64_t dl = hl * head_dim;  // local attention width
+  TP_TRY(check_matrix(x, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(wqkv_i, 3 * dl, 3 * dl, in_dt));
+  TP_TRY(check_matrix(wo_i, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(out_i, hidden, hidden, out_dt));
+  const AttnWorkspace ws = attn_workspace(tokens, hl, head_dim);
+  if (workspace == nullptr || workspace_bytes < ws.total) return TP_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  uint16_t* qkv_hi = reinterpret_cast<uint16_t*>(w);
+  uint16_t* qkv_lo = reinterpret_cast<uint16_t*>(w + ws.qkv_bytes);
+  uint16_t* o = reinterpret_cast<uint16_t*>(w + 2 * ws.qkv_bytes);
+  // 1. Column-parallel packed QKV projection of the rank's heads, kept as a
+  //    bf16 (hi, lo) pair so that Q K^T keeps ~16 significant bits.
+  tpk::Epilogue ep1{nullptr, nullptr, 0, qkv_hi, 3 * dl, false, false, qkv_lo};
+  TP_TRY(run_gemm(in_dt, x, hidden, wqkv_i, 3 * dl, tokens, 3 * dl, hidden, ep1, s));
+  // 2. softmax(Q K^T / sqrt(d)) V per local head.
+  TP_TRY(from_hip(tpk::launch_attention(qkv_hi, qkv_lo, 3 * dl, o, dl, static_cast<int>(batch),
+                                        static_cast<int>(seq), static_cast<int>(hl),
+                                        static_cast<int>(head_dim), causal == 1, s)));
+  // 3. Row-parallel output projection: the rank's full-hidden partial.
+  tpk::Epilogue ep3{nullptr, nullptr, 0, out_i, hidden, out_dt == TP_F32, false};
+  return run_gemm(in_dt, o, dl, wo_i, hidden, tokens, hidden, dl, ep3, s);
 }
 
 }  // extern "C"

@@ -90,6 +90,7 @@ class AttnWorkload:
     x_std: float
     w_std: float
     out_dtype: str
+    wo_std: Optional[float] = None   # output projection std (default w_std)
 
 
 MLP_WORKLOADS = {
@@ -109,6 +110,17 @@ MLP_WORKLOADS = {
 }
 
 ATTN_WORKLOADS = {
+    # Small shards the oracle finishes in seconds: hidden 1024, 8 heads of
+    # 128, t=2 (4 local heads).  QKV weight std chosen so the logits have std
+    # ~3 like the large case (q std = sqrt(1024) * 0.057 ~ 1.8); output
+    # projection std 0.02 * sqrt(1024 / 512) so the partial's scale (std of
+    # O times sqrt(rows of W_o)) also matches the large case.
+    # batch 2 x seq 384: 3 query blocks, 6 key blocks, tile-aligned projections.
+    "attn_t2_h1024_b2_s384": AttnWorkload("attn_t2_h1024_b2_s384", 2, 384, 1024, 8, 128, 2,
+                                          "bf16", 1.0, 0.057, "f32", 0.028),
+    # batch 3 x seq 128: one query block, 384 tokens (not a multiple of 256).
+    "attn_t2_h1024_b3_s128": AttnWorkload("attn_t2_h1024_b3_s128", 3, 128, 1024, 8, 128, 2,
+                                          "bf16", 1.0, 0.057, "f32", 0.028),
     # Head-local attention shard: hidden 8192, 64 heads of 128, t=8 (8 local
     # heads), batch 1, seq 4096, non-causal.
     "attn_t8_h8192_s4096": AttnWorkload("attn_t8_h8192_s4096", 1, 4096, 8192, 64, 128, 8,
@@ -219,4 +231,5 @@ def attn_wqkv_block(wl: AttnWorkload, r: int) -> np.ndarray:
 
 def attn_wo_block(wl: AttnWorkload, r: int) -> np.ndarray:
     """Row block r (height hidden/t) of the output projection [hidden, hidden]."""
-    return draw(wl.name, "wo", r, (wl.hidden // wl.t, wl.hidden), wl.w_std, wl.dtype)
+    std = wl.w_std if wl.wo_std is None else wl.wo_std
+    return draw(wl.name, "wo", r, (wl.hidden // wl.t, wl.hidden), std, wl.dtype)

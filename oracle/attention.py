@@ -72,13 +72,14 @@ def split_packed_qkv(wqkv: np.ndarray, heads: int, head_dim: int):
     return tuple(np.ascontiguousarray(w3[:, :, c, :].reshape(hid, heads * head_dim)) for c in range(3))
 
 
-def _attend(q, k, v, causal: bool) -> np.ndarray:
-    """softmax(q k^T / sqrt(d)) v for one head; q,k,v [s, d]."""
+def _attend(q, k, v, causal: bool, qpos=None) -> np.ndarray:
+    """softmax(q k^T / sqrt(d)) v for one head; q [n, d] at sequence positions
+    ``qpos`` (default 0..n-1), k, v [s, d].  Causal: query i sees keys j <= i."""
     d = q.shape[-1]
     s = (q @ k.T) / math.sqrt(d)
     if causal:
-        n = s.shape[0]
-        s = np.where(np.tril(np.ones((n, n), dtype=bool)), s, -np.inf)
+        qpos = np.arange(q.shape[0]) if qpos is None else np.asarray(qpos)
+        s = np.where(np.arange(k.shape[0])[None, :] <= qpos[:, None], s, -np.inf)
     return softmax_rows(s) @ v
 
 
@@ -98,11 +99,13 @@ def mha_full(x, wq, wk, wv, wo, heads: int, causal: bool = False) -> np.ndarray:
 
 
 def attn_shard(x, wqkv_i, wo_i, heads: int, head_dim: int, t: int, rank: int,
-               causal: bool = False) -> np.ndarray:
+               causal: bool = False, rows=None) -> np.ndarray:
     """Rank ``rank``'s fp64 partial: its heads/t local heads from the packed
     QKV column block ``wqkv_i`` [h, 3*h_loc], local attention per head, and
     the row block ``wo_i`` [h_loc, h] of the output projection.  Returns the
-    full-hidden [batch, seq, h] contribution that the ranks sum."""
+    full-hidden [batch, seq, h] contribution that the ranks sum, or only the
+    query positions ``rows`` ([batch, len(rows), h]; every key is still used:
+    each output row is defined by its own query alone)."""
     nl = local_heads(heads, t)
     if not (0 <= rank < t):
         raise ShardError(f"rank {rank} outside [0, {t})")
@@ -112,14 +115,15 @@ def attn_shard(x, wqkv_i, wo_i, heads: int, head_dim: int, t: int, rank: int,
     d = head_dim
     if w.shape[1] != 3 * nl * d or wo_i.shape[0] != nl * d:
         raise ShardError("shard weight shapes do not match heads/t x head_dim")
-    out = np.empty((x.shape[0], x.shape[1], wo_i.shape[1]))
+    qrows = np.arange(x.shape[1]) if rows is None else np.asarray(rows)
+    out = np.empty((x.shape[0], len(qrows), wo_i.shape[1]))
     for bi in range(x.shape[0]):
         qkv = x[bi] @ w
         heads_out = []
         for j in range(nl):
             base = j * 3 * d
-            q, k, v = qkv[:, base:base + d], qkv[:, base + d:base + 2 * d], qkv[:, base + 2 * d:base + 3 * d]
-            heads_out.append(_attend(q, k, v, causal))
+            q, k, v = qkv[qrows, base:base + d], qkv[:, base + d:base + 2 * d], qkv[:, base + 2 * d:base + 3 * d]
+            heads_out.append(_attend(q, k, v, causal, qrows))
         out[bi] = np.concatenate(heads_out, axis=1) @ wo_i
     return out
 

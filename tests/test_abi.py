@@ -143,9 +143,32 @@ def test_mlp_shard_validation(lib):
     assert mlp(lib, tokens=0, ws=None) == OK
 
 
-def test_attn_shard_is_validated(lib):
-    rc = lib.tp_attn_shard_fwd(P, P, P, P, P, 1 << 30, 1, 64, 1024, 8, 128, 0, 3, 0, BF16, F32, None)
-    assert rc in (NOT_DIV, UNSUPPORTED)
+def attn(lib, **kw):
+    a = dict(x=P, wqkv=P, wo=P, out=P, ws=P, ws_bytes=1 << 30, batch=1, seq=256, hidden=1024, heads=8,
+             head_dim=128, causal=0, t=2, rank=0, in_dt=BF16, out_dt=F32)
+    a.update(kw)
+    return lib.tp_attn_shard_fwd(a["x"], a["wqkv"], a["wo"], a["out"], a["ws"], a["ws_bytes"], a["batch"],
+                                 a["seq"], a["hidden"], a["heads"], a["head_dim"], a["causal"], a["t"],
+                                 a["rank"], a["in_dt"], a["out_dt"], None)
+
+
+def test_attn_shard_validation(lib):
+    assert attn(lib, t=3) == NOT_DIV                      # heads mod t != 0
+    assert attn(lib, rank=2) == BAD_RANK
+    assert attn(lib, hidden=1000) == INVALID               # hidden != heads * head_dim
+    assert attn(lib, head_dim=64, hidden=512) == UNSUPPORTED
+    assert attn(lib, seq=200) == UNSUPPORTED               # seq not a multiple of 128
+    assert attn(lib, in_dt=F32) == DTYPE
+    assert attn(lib, causal=2) == INVALID
+    assert attn(lib, x=None) == INVALID
+    assert attn(lib, out=P + 8) == MISALIGNED
+    need = lib.tp_attn_shard_workspace_bytes(1, 256, 1024, 8, 128, 2, BF16)
+    # (hi, lo) projection pair [256, 3*4*128] bf16 + output [256, 4*128] bf16
+    assert need == 2 * 256 * 1536 * 2 + 256 * 512 * 2
+    assert attn(lib, ws_bytes=need - 1) == WORKSPACE
+    assert attn(lib, ws=P + 16) == MISALIGNED
+    assert attn(lib, batch=0, ws=None) == OK
+    assert lib.tp_attn_shard_workspace_bytes(1, 256, 1024, 8, 128, 3, BF16) == 0
 
 
 def test_product_never_imports_the_oracle():

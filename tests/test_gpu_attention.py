@@ -1,0 +1,112 @@
+"""GPU parity of the head-local attention shard (tp_attn_shard_fwd) against
+the fp64 oracle.
+
+Every call goes through the C ABI.  Outputs and workspace are NaN-filled
+first, so an unwritten tile cannot pass.  Tolerance as for the bf16 MLP path:
+max |err| / (1 + |ref|) <= 2e-2 and relative Frobenius <= 5e-3 per shard; the
+sum over ranks is held to the relative Frobenius bound, and its normalised
+max error is reported (the shards' bf16 rounding errors add over the ranks,
+the "1 +" floor does not grow with them).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_tp_amd import binding, inputs
+from tests.gpu_helpers import BF16_FRO, assert_close, dev, errors, host64, nan_tensor, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def x_all(wl):
+    return np.stack([inputs.attn_x(wl, b) for b in range(wl.batch)])
+
+
+def run(wl, r, xd, wqkv_d, wo_d, causal, out_dtype="f32"):
+    nbytes = binding.tp_attn_shard_workspace_bytes(wl.batch, wl.seq, wl.hidden, wl.heads,
+                                                   wl.head_dim, wl.t, torch.bfloat16)
+    assert nbytes > 0
+    ws = nan_tensor((nbytes // 2,), torch.bfloat16)
+    out = nan_tensor((wl.batch, wl.seq, wl.hidden), TORCH_DT[out_dtype])
+    binding.tp_attn_shard_fwd(xd, wqkv_d, wo_d, out, ws, heads=wl.heads, head_dim=wl.head_dim,
+                              t=wl.t, rank=r, causal=causal)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", ["attn_t2_h1024_b2_s384", "attn_t2_h1024_b3_s128"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_all_ranks_and_reconstruction(name, causal):
+    wl = inputs.ATTN_WORKLOADS[name]
+    x = x_all(wl)
+    xd = dev(x, "bf16")
+    wqkv = [inputs.attn_wqkv_block(wl, r) for r in range(wl.t)]
+    wo = [inputs.attn_wo_block(wl, r) for r in range(wl.t)]
+    x64 = host64(x, "bf16")
+    total = None
+    for r in range(wl.t):
+        say(f"{name} rank {r} causal={causal}")
+        out = to_np(run(wl, r, xd, dev(wqkv[r], "bf16"), dev(wo[r], "bf16"), causal))
+        ref = oracle.attn_shard(x64, host64(wqkv[r], "bf16"), host64(wo[r], "bf16"), wl.heads,
+                                wl.head_dim, wl.t, r, causal)
+        assert_close(out, ref, "bf16", f"{name} rank {r} causal={causal}")
+        total = out if total is None else total + out
+    # The ranks' partials sum to unsharded multi-head attention with the full
+    # Q, K, V, O weights (the packed per-head layout undone).
+    wq, wk, wv = oracle.split_packed_qkv(host64(np.concatenate(wqkv, axis=1), "bf16"), wl.heads,
+                                         wl.head_dim)
+    full = oracle.mha_full(x64, wq, wk, wv, host64(np.concatenate(wo, axis=0), "bf16"), wl.heads,
+                           causal)
+    mx, fro = errors(total, full)
+    say(f"{name} sum over ranks vs unsharded attention: rel-fro = {fro:.3e} (<= {BF16_FRO}), "
+        f"max|e|/(1+|r|) = {mx:.3e} (reported)")
+    assert np.isfinite(total).all() and fro <= BF16_FRO
+
+
+def test_small_bf16_output():
+    wl = inputs.ATTN_WORKLOADS["attn_t2_h1024_b2_s384"]
+    x = x_all(wl)
+    r = 1
+    wqkv, wo = inputs.attn_wqkv_block(wl, r), inputs.attn_wo_block(wl, r)
+    say("attn_t2_h1024_b2_s384 rank 1 bf16 out")
+    out = to_np(run(wl, r, dev(x, "bf16"), dev(wqkv, "bf16"), dev(wo, "bf16"), False, "bf16"))
+    ref = oracle.attn_shard(host64(x, "bf16"), host64(wqkv, "bf16"), host64(wo, "bf16"), wl.heads,
+                            wl.head_dim, wl.t, r)
+    assert_close(out, ref, "bf16", "bf16 output")
+
+
+@pytest.mark.parametrize("rank,causal", [(0, False), (7, True)])
+def test_large_sampled_rows(rank, causal):
+    """hidden 8192, 64 heads, t=8, seq 4096: the whole shard runs on the GPU;
+    the oracle computes sampled query rows (each depends on all keys)."""
+    wl = inputs.ATTN_WORKLOADS["attn_t8_h8192_s4096"]
+    x = x_all(wl)
+    wqkv, wo = inputs.attn_wqkv_block(wl, rank), inputs.attn_wo_block(wl, rank)
+    say(f"attn_t8_h8192_s4096 rank {rank} causal={causal}")
+    out = to_np(run(wl, rank, dev(x, "bf16"), dev(wqkv, "bf16"), dev(wo, "bf16"), causal))
+    assert np.isfinite(out).all()
+    rows = np.r_[0:64, 1000:1064, 4032:4096]
+    ref = oracle.attn_shard(host64(x, "bf16"), host64(wqkv, "bf16"), host64(wo, "bf16"), wl.heads,
+                            wl.head_dim, wl.t, rank, causal, rows=rows)
+    assert_close(out[:, rows, :], ref, "bf16", f"large rank {rank} causal={causal} sampled rows")
+
+
+def test_errors_and_empty():
+    wl = inputs.ATTN_WORKLOADS["attn_t2_h1024_b3_s128"]
+    x = dev(x_all(wl), "bf16")
+    wqkv = dev(inputs.attn_wqkv_block(wl, 0), "bf16")
+    wo = dev(inputs.attn_wo_block(wl, 0), "bf16")
+    out = nan_tensor((wl.batch, wl.seq, wl.hidden), torch.float32)
+    with pytest.raises(binding.TpError):          # no workspace
+        binding.tp_attn_shard_fwd(x, wqkv, wo, out, None, heads=8, head_dim=128, t=2, rank=0)
+    with pytest.raises(binding.TpError):          # heads not divisible by t
+        binding.tp_attn_shard_fwd(x, wqkv, wo, out, None, heads=8, head_dim=128, t=3, rank=0)
+    assert torch.isnan(out).all()
+    # batch 0: nothing to do, nothing written
+    x0 = torch.empty((0, 128, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    out0 = torch.empty((0, 128, wl.hidden), dtype=torch.float32, device="cuda")
+    binding.tp_attn_shard_fwd(x0, wqkv, wo, out0, None, heads=8, head_dim=128, t=2, rank=0)
+    torch.cuda.synchronize()

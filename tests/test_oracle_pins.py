@@ -308,3 +308,16 @@ def test_packed_qkv_split_layout():
         for c, wc in enumerate((wq, wk, wv)):
             for e in range(d):
                 np.testing.assert_array_equal(wc[:, j * d + e], w[:, j * 3 * d + c * d + e])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attn_shard_row_subset_equals_full(causal):
+    """Computing only some query rows gives exactly those rows of the full
+    shard (every output row depends on its own query and all keys only)."""
+    x, wqkv, wo, heads, d, t = _tiny_attn(seed=21, batch=2, seq=9, t=2)
+    nl = heads // t
+    wq_i, wo_i = wqkv[:, :3 * nl * d], wo[:nl * d, :]
+    full = oracle.attn_shard(x, wq_i, wo_i, heads, d, t, 0, causal)
+    rows = [0, 4, 8]
+    np.testing.assert_array_equal(oracle.attn_shard(x, wq_i, wo_i, heads, d, t, 0, causal, rows=rows),
+                                  full[:, rows, :])
