@@ -15,6 +15,11 @@ Also reported:
                 summaries when they match the current kernel source
   cpu_baseline  the fp64 CPU oracle on a bounded sample of rows of the same
                 shard, on this host's cores
+  attention     the head-local attention shard (hidden 8192, 64 heads of 128,
+                t = 8, one sequence of 4096 tokens, rank 0, non-causal): whole
+                shard through tp_attn_shard_fwd, its two projection GEMMs
+                through tp_column_linear / tp_row_linear at the same shapes,
+                and the attention kernel's share as the difference
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
 """
@@ -35,9 +40,9 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s + % bf16 MFMA peak, t=8 MLP shard (h=8192, 16384 tok), 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/gemm_bf16_impl.h",
-                  "megatron_tensor_transformer_tp_amd/csrc/gemm_bf16.hip",
-                  "megatron_tensor_transformer_tp_amd/csrc/device_common.h"]
+KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/" + f for f in (
+    "device_common.h", "gemm_bf16_impl.h", "gemm_bf16_dma.h", "gemm_bf16.hip",
+    "gemm_bf16_256_gelu.hip", "gemm_bf16_256_plain.hip", "attention.hip")]
 
 
 def kernel_source_sha() -> str:
@@ -126,65 +131,173 @@ PROFILE_CMDS = {
     "write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- "
               "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
 }
-KERNEL_KEYS = {"column_gemm_gelu": "gemm_bf16_kernel<256, 256, false, true, false>",
-               "row_gemm": "gemm_bf16_kernel<256, 256, false, false, true>",
-               "copy_1GiB": "copyBuffer"}
+# Profiled kernels: name pattern in the rocprofv3 output and grid size in
+# work-items (one kernel serves several GEMM shapes), with the per-launch
+# algorithmic work (FLOP, bytes), the workload, and the summary's file stem.
+# GEMM template arguments: tile BM, BN, wave grid, LDS stages, GeLU epilogue,
+# fp32 output.
+_M, _H, _F = 16384, 8192, 4096          # MLP shard: tokens, hidden, f = ffn / t
+_S, _DL = 4096, 1024                    # attention shard: tokens, local width (8 heads x 128)
+_GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "
+PROFILED = {
+    "column_gemm_gelu": (_GEMM + "true, false>", (_M // 256) * (_F // 256) * 512,
+                         2.0 * _M * _H * _F, 2 * (_M * _H + _H * _F + _M * _F),
+                         "MLP rank shard, M=16384, h=8192, f=4096: X, A_i read, H_i written (bf16)",
+                         "column_gemm_gelu_t8_h8192_m16384"),
+    "row_gemm": (_GEMM + "false, true>", (_M // 256) * (_H // 256) * 512,
+                 2.0 * _M * _F * _H, 2 * (_M * _F + _F * _H) + 4 * _M * _H,
+                 "MLP rank shard, M=16384, h=8192, f=4096: H_i, B_i read (bf16), Z_i written (fp32)",
+                 "row_gemm_t8_h8192_m16384"),
+    "attention_core": ("attn_fwd_kernel<false>", None,
+                       4.0 * _S * _S * _DL, 2 * (5 * _S * _DL + _S * _DL),
+                       "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K as "
+                       "bf16 (hi, lo) pairs and V read once, O written (bf16)",
+                       "attention_core_t8_h8192_s4096"),
+    "attn_out_gemm": (_GEMM + "false, true>", (_S // 256) * (_H // 256) * 512,
+                      2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
+                      "attention rank shard output projection, M=4096, K=1024, N=8192 (fp32 out)",
+                      "attn_out_gemm_t8_h8192_s4096"),
+}
+COPY_KEY = ("copyBuffer", 1 << 30)    # the 1 GiB calibration copy
 
 
 def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str) -> None:
-    """Turn the rocprofv3 CSVs of the three PROFILE_CMDS runs into the committed
-    summaries: profiles/<kernel>_t8_h8192_m16384.md and profiles/traffic_counters.json.
-    HBM bytes = FETCH_SIZE x (1 GiB / FETCH_SIZE of the 1 GiB copy) + the same for
-    WRITE_SIZE (both counters report KiB per dispatch)."""
+    """Turn the rocprofv3 CSVs of the three PROFILE_CMDS runs (the per-dispatch
+    kernel trace and the two counter collections) into the committed
+    summaries: profiles/<file stem>.md per profiled kernel and
+    profiles/traffic_counters.json.  HBM bytes = FETCH_SIZE x (1 GiB / FETCH_SIZE
+    of the 1 GiB copy) + the same for WRITE_SIZE (both counters report KiB per
+    dispatch)."""
     import csv
     import statistics
+
+    def key_of(name, grid):
+        for key, (pat, g, *_rest) in PROFILED.items():
+            if pat in name and (g is None or g == grid):
+                return key
+        return "copy_1GiB" if COPY_KEY[0] in name else None
 
     def per_kernel_counter(path):
         vals = {}
         for row in csv.DictReader(open(path)):
-            for key, pat in KERNEL_KEYS.items():
-                if pat in row["Kernel_Name"]:
-                    vals.setdefault(key, []).append(float(row["Counter_Value"]))
+            key = key_of(row["Kernel_Name"], int(row["Grid_Size"]))
+            if key is not None:
+                vals.setdefault(key, []).append(float(row["Counter_Value"]))
         return {k: statistics.median(v) for k, v in vals.items()}
 
     fetch, write = per_kernel_counter(fetch_csv), per_kernel_counter(write_csv)
     gib_kib = float(1 << 20)
     f_scale, w_scale = gib_kib / fetch["copy_1GiB"], gib_kib / write["copy_1GiB"]
-    stats = {}
+    durs = {}
     for row in csv.DictReader(open(trace_csv)):
-        for key, pat in KERNEL_KEYS.items():
-            if pat in row["Name"]:
-                stats[key] = row
-    wl_bytes = {"column_gemm_gelu": 469762048, "row_gemm": 738197504}
-    wl_flops = 2.0 * 16384 * 8192 * 4096
+        grid = int(row["Grid_Size_X"]) * int(row["Grid_Size_Y"]) * int(row["Grid_Size_Z"])
+        key = key_of(row["Kernel_Name"], grid)
+        if key is not None:
+            durs.setdefault(key, []).append(
+                ((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3, row["Kernel_Name"]))
     out = {"source_sha": kernel_source_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
            "commands": PROFILE_CMDS, "kernels": {}}
-    for key in ("column_gemm_gelu", "row_gemm"):
+    for key, (_pat, _grid, flops, alg_bytes, what, stem) in PROFILED.items():
         fb = fetch[key] * 1024 * f_scale
         wb = write[key] * 1024 * w_scale
-        st = stats[key]
-        avg_us = float(st["AverageNs"]) / 1e3
+        us = [d for d, _ in durs[key]]
+        avg_us = statistics.mean(us)
         out["kernels"][key] = {"hbm_bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb),
-                               "write_bytes": int(wb), "algorithmic_bytes": wl_bytes[key],
-                               "avg_us": round(avg_us, 2), "calls": int(st["Calls"])}
-        md = [f"# {key} — t8_h8192_m16384 (one rank shard, M=16384, h=8192, f=4096)", "",
-              f"kernel: `{st['Name'][:120]}`", f"kernel source sha: {out['source_sha']}", "",
+                               "write_bytes": int(wb), "algorithmic_bytes": int(alg_bytes),
+                               "avg_us": round(avg_us, 2), "calls": len(us)}
+        md = [f"# {key} — {stem}", "",
+              f"Workload: {what}.", "",
+              f"kernel: `{durs[key][0][1][:120]}`", f"kernel source sha: {out['source_sha']}", "",
               "Commands (run from the repository root on the GPU box):", "",
               *[f"    {c}" for c in PROFILE_CMDS.values()], "",
               "| figure | value |", "|---|---|",
-              f"| calls in the trace run | {st['Calls']} |",
+              f"| dispatches in the trace run | {len(us)} |",
               f"| average duration | {avg_us:.1f} us |",
-              f"| min / max duration | {float(st['MinNs'])/1e3:.1f} / {float(st['MaxNs'])/1e3:.1f} us |",
-              f"| achieved (algorithmic FLOP / avg duration) | {wl_flops / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s |",
+              f"| median / min / max duration | {statistics.median(us):.1f} / {min(us):.1f} / {max(us):.1f} us |",
+              f"| algorithmic FLOP per launch | {flops / 1e9:.1f} G |",
+              f"| achieved (algorithmic FLOP / avg duration) | {flops / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s "
+              f"({100 * flops / (avg_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS}) |",
               f"| FETCH_SIZE per dispatch (median) | {fetch[key]:.0f} KiB (x{f_scale:.3f} from the 1 GiB copy) |",
               f"| WRITE_SIZE per dispatch (median) | {write[key]:.0f} KiB (x{w_scale:.3f}) |",
               f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.1f} MB (fetch {fb / 1e6:.1f}, write {wb / 1e6:.1f}) |",
-              f"| algorithmic bytes per launch | {wl_bytes[key] / 1e6:.1f} MB |", ""]
-        with open(os.path.join(ROOT, "profiles", f"{key}_t8_h8192_m16384.md"), "w") as fh:
+              f"| algorithmic bytes per launch | {alg_bytes / 1e6:.1f} MB |", ""]
+        with open(os.path.join(ROOT, "profiles", f"{stem}.md"), "w") as fh:
             fh.write("\n".join(md))
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def bench_attention(stream, reps: int, name: str = "attn_t8_h8192_s4096"):
+    """Time one head-local attention shard (rank 0, non-causal) and its two
+    projection GEMMs; the attention kernel's time is the difference."""
+    import torch
+    from megatron_tensor_transformer_tp_amd import binding, inputs
+
+    wl = inputs.ATTN_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    nl = wl.heads // wl.t
+    dl = nl * wl.head_dim
+    tokens = wl.batch * wl.seq
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = up(np.stack([inputs.attn_x(wl, b) for b in range(wl.batch)]))
+    wqkv, wo = up(inputs.attn_wqkv_block(wl, 0)), up(inputs.attn_wo_block(wl, 0))
+    out = torch.empty((wl.batch, wl.seq, wl.hidden), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.tp_attn_shard_workspace_bytes(wl.batch, wl.seq, wl.hidden, wl.heads,
+                                                           wl.head_dim, wl.t, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+    qkv = torch.empty((tokens, 3 * dl), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((tokens, dl), dtype=torch.bfloat16, device=dev).normal_()
+    x2 = x.view(tokens, wl.hidden)
+    out2 = out.view(tokens, wl.hidden)
+    calls = {
+        "shard": lambda: binding.tp_attn_shard_fwd(x, wqkv, wo, out, ws, heads=wl.heads,
+                                                   head_dim=wl.head_dim, t=wl.t, rank=0,
+                                                   stream=stream),
+        "qkv_gemm": lambda: binding.tp_column_linear(x2, wqkv, qkv, ffn=3 * wl.hidden, t=wl.t,
+                                                     rank=0, stream=stream),
+        "out_gemm": lambda: binding.tp_row_linear(o, wo, out2, ffn=wl.hidden, t=wl.t, rank=0,
+                                                  stream=stream),
+    }
+    us = {}
+    for key, fn in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us[key] = e0.elapsed_time(e1) * 1e3 / reps
+    f_qkv = 2.0 * tokens * wl.hidden * 3 * dl
+    f_att = 4.0 * wl.batch * wl.seq * wl.seq * wl.head_dim * nl   # Q K^T and P V, non-causal
+    f_out = 2.0 * tokens * dl * wl.hidden
+    core_us = us["shard"] - us["qkv_gemm"] - us["out_gemm"]
+
+    def tf(flops, t_us):
+        return round(flops / (t_us * 1e-6) / 1e12, 2)
+
+    res = {
+        "workload": (f"{wl.name}: rank 0 of t={wl.t}, hidden {wl.hidden}, {wl.heads} heads of "
+                     f"{wl.head_dim} ({nl} local), batch {wl.batch} x seq {wl.seq}, non-causal, "
+                     "fp32 partial"),
+        "flops": int(f_qkv + f_att + f_out),
+        "shard_us": round(us["shard"], 2),
+        "shard_tflops": tf(f_qkv + f_att + f_out, us["shard"]),
+        "pct_peak": round(100.0 * (f_qkv + f_att + f_out) / (us["shard"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "qkv_gemm": {"avg_us": round(us["qkv_gemm"], 2), "tflops": tf(f_qkv, us["qkv_gemm"])},
+        "attention_core": {"avg_us": round(core_us, 2), "tflops": tf(f_att, core_us),
+                           "note": "shard time minus the two projection GEMMs timed alone"},
+        "out_gemm": {"avg_us": round(us["out_gemm"], 2), "tflops": tf(f_out, us["out_gemm"])},
+    }
+    log(f"attention shard {us['shard']:.1f} us ({res['shard_tflops']} TFLOP/s): qkv {us['qkv_gemm']:.1f}, "
+        f"core ~{core_us:.1f} ({res['attention_core']['tflops']} TFLOP/s), out {us['out_gemm']:.1f}")
+    return res
 
 
 def main() -> int:
@@ -196,6 +309,8 @@ def main() -> int:
     ap.add_argument("--kernel-reps", type=int, default=10,
                     help="launches per kernel for the live per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the attention-shard measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the bounded oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -303,6 +418,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log("calibration copy of 1 GiB x3 done")
 
+    attention = None if args.no_attention else bench_attention(stream, args.kernel_reps)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample")
@@ -346,6 +463,7 @@ def main() -> int:
         "kernels": per_kernel,
         "kernel_source_sha": kernel_source_sha(),
         "cpu_baseline": cpu,
+        "attention": attention,
     }
     print(json.dumps(result), flush=True)
     return 0
