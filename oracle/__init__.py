@@ -11,14 +11,15 @@ except the per-head packing convention of the QKV weight, which no page fixes
 equality of the sharded form with full multi-head attention).
 """
 from .mlp import (ShardError, shard_width, shard_slice, gelu, column_linear, row_linear,
-                  mlp_full, mlp_shard, mlp_partial_sum)
+                  mlp_full, mlp_shard, mlp_partial_sum, normal_pdf, gelu_grad, mlp_shard_bwd)
 from .attention import (softmax_rows, split_packed_qkv, mha_full, attn_shard, attn_partial_sum,
                         local_heads)
 from .brute import mlp_shard_loops, attention_head_loops
 
 __all__ = [
     "ShardError", "shard_width", "shard_slice", "gelu", "column_linear", "row_linear",
-    "mlp_full", "mlp_shard", "mlp_partial_sum", "softmax_rows", "split_packed_qkv",
+    "mlp_full", "mlp_shard", "mlp_partial_sum", "normal_pdf", "gelu_grad", "mlp_shard_bwd",
+    "softmax_rows", "split_packed_qkv",
     "mha_full", "attn_shard", "attn_partial_sum", "local_heads", "mlp_shard_loops",
     "attention_head_loops",
 ]

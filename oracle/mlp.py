@@ -32,6 +32,12 @@ Passages followed (page titles as printed on each page):
     on column shards, Z = Z_1 + Z_2 with one All-Reduce) and 第三章 (contiguous
     column slices of W1, row slices of W2 with the same indices, summed over
     ranks).
+  * Backward (Megatron Level 2, M025 and M026): for Y = X W with W split by
+    columns, dW_i = X^T dY_i is local and the input-gradient contributions
+    dY_i W_i^T are SUM-reduced over the ranks; for the row-split layer the
+    input gradient dY W_i^T is already the rank's input-block gradient and
+    dW_i is local.  Chained through the elementwise GeLU with the product
+    rule, d/dz [z Phi(z)] = Phi(z) + z phi(z).
 """
 from __future__ import annotations
 
@@ -51,6 +57,9 @@ __all__ = [
     "mlp_full",
     "mlp_shard",
     "mlp_partial_sum",
+    "normal_pdf",
+    "gelu_grad",
+    "mlp_shard_bwd",
 ]
 
 
@@ -164,3 +173,57 @@ def mlp_partial_sum(x, a, b, t: int, bias_a=None, bias_b=None, residual=None,
             raise ValueError(activation)
         total = z if total is None else total + z
     return total
+
+
+def normal_pdf(z):
+    """Standard normal density phi(z) = exp(-z^2 / 2) / sqrt(2 pi)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def gelu_grad(z):
+    """d/dz GeLU(z) = Phi(z) + z phi(z): the product rule on z * Phi(z), with
+    Phi' = phi (GeLU as defined in the 列并行 tutorial, MLP 应用)."""
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * erfc(-z / math.sqrt(2.0)) + z * normal_pdf(z)
+
+
+def mlp_shard_bwd(x, a, b, dz, t: int, rank: int, bias_a=None) -> dict:
+    """Backward of rank ``rank``'s MLP shard, given dz = dL/dZ of the summed
+    output Z = sum_r Z_r (the same on every rank), with FULL weights ``a``
+    [h, F] and ``b`` [F, h] (the rank's blocks are cut here).
+
+    Forward values recomputed from the definition:
+      Y_r = X A_r + a_r,  H_r = GeLU(Y_r).
+    Row-parallel layer Z_r = H_r B_r (M026): its input gradient
+      dH_r = dz B_r^T is the rank's own block, dB_r = H_r^T dz is local.
+    GeLU, elementwise: dY_r = dH_r * GeLU'(Y_r).
+    Column-parallel layer Y_r = X A_r (M025): dA_r = X^T dY_r is local;
+      dX_r = dY_r A_r^T is the rank's contribution to dX (summed over ranks).
+    Biases: a_r is added to every token row, so its gradient is the sum of
+      dY_r over tokens; the output bias b (added once, on rank 0) gets the
+      sum of dz over tokens, the same on every rank.
+
+    Returns dict(y, dx, da, db, dbias_a, dbias_b) in fp64, with da [h, f] and
+    db [f, h] the rank's blocks of dA and dB."""
+    x, a, b, dz = _f64(x), _f64(a), _f64(b), _f64(dz)
+    ffn = a.shape[1]
+    if b.shape[0] != ffn:
+        raise ShardError(f"A is [h, {ffn}] but B has {b.shape[0]} rows")
+    if dz.shape != (x.shape[0], b.shape[1]):
+        raise ShardError(f"dz is {dz.shape}, expected {(x.shape[0], b.shape[1])}")
+    s = shard_slice(ffn, t, rank)
+    a_r, b_r = a[:, s], b[s, :]
+    bias_r = None if bias_a is None else _f64(bias_a)[s]
+    y = column_linear(x, a_r, bias_r)
+    h = gelu(y)
+    dh = dz @ b_r.T
+    dy = dh * gelu_grad(y)
+    return {
+        "y": y,
+        "dx": dy @ a_r.T,
+        "da": x.T @ dy,
+        "db": h.T @ dz,
+        "dbias_a": dy.sum(axis=0),
+        "dbias_b": dz.sum(axis=0),
+    }

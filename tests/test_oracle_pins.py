@@ -321,3 +321,98 @@ def test_attn_shard_row_subset_equals_full(causal):
     rows = [0, 4, 8]
     np.testing.assert_array_equal(oracle.attn_shard(x, wq_i, wo_i, heads, d, t, 0, causal, rows=rows),
                                   full[:, rows, :])
+
+
+# ---- backward (Megatron Level 2, M025 / M026; GeLU' by the product rule) ----
+
+def test_gelu_grad_matches_central_differences():
+    z = np.linspace(-8.0, 8.0, 161)
+    h = 1e-5
+    fd = (oracle.gelu(z + h) - oracle.gelu(z - h)) / (2 * h)
+    np.testing.assert_allclose(oracle.gelu_grad(z), fd, rtol=0, atol=1e-9)
+
+
+def test_gelu_grad_special_values(golden_dir):
+    assert oracle.gelu_grad(0.0) == 0.5                      # Phi(0) + 0
+    assert abs(oracle.gelu_grad(10.0) - 1.0) < 1e-15         # Phi -> 1, z phi -> 0
+    assert abs(oracle.gelu_grad(-10.0)) < 1e-20
+    # Phi(1) from the printed normal table, phi(1) = exp(-1/2) / sqrt(2 pi)
+    table = {float(z): float(p) for z, p in read_golden_table(os.path.join(golden_dir, "normal_cdf.txt"))}
+    expect = table[1.0] + math.exp(-0.5) / math.sqrt(2 * math.pi)
+    assert abs(oracle.gelu_grad(1.0) - expect) < 1e-9
+
+
+def _tiny_mlp_problem(seed, tokens=3, hidden=4, ffn=8):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((tokens, hidden)), rng.standard_normal((hidden, ffn)) * 0.7,
+            rng.standard_normal((ffn, hidden)) * 0.5, rng.standard_normal(ffn) * 0.3,
+            rng.standard_normal(hidden) * 0.3, rng.standard_normal((tokens, hidden)))
+
+
+def _assembled_grads(x, a, b, ba, dz, t):
+    """Rank gradients put back together: dX summed over ranks, dA / dB / da
+    concatenated along the split dimension."""
+    parts = [oracle.mlp_shard_bwd(x, a, b, dz, t, r, bias_a=ba) for r in range(t)]
+    return {
+        "x": sum(p["dx"] for p in parts),
+        "a": np.concatenate([p["da"] for p in parts], axis=1),
+        "b": np.concatenate([p["db"] for p in parts], axis=0),
+        "ba": np.concatenate([p["dbias_a"] for p in parts]),
+        "bb": parts[0]["dbias_b"],
+    }
+
+
+def _fd_grads(x, a, b, ba, bb, dz, eps=1e-6):
+    """Central differences of L = sum(dz * (GeLU(X A + a) B + b))."""
+    params = {"x": x, "a": a, "b": b, "ba": ba, "bb": bb}
+
+    def loss():
+        return float(np.sum(dz * oracle.mlp_full(params["x"], params["a"], params["b"],
+                                                   params["ba"], params["bb"])))
+
+    out = {}
+    for name, arr in params.items():
+        g = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + eps
+            up = loss()
+            arr[idx] = keep - eps
+            down = loss()
+            arr[idx] = keep
+            g[idx] = (up - down) / (2 * eps)
+        out[name] = g
+    return out
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_mlp_backward_matches_finite_differences(t):
+    x, a, b, ba, bb, dz = _tiny_mlp_problem(seed=30 + t)
+    got = _assembled_grads(x, a, b, ba, dz, t)
+    fd = _fd_grads(x.copy(), a.copy(), b.copy(), ba.copy(), bb.copy(), dz)
+    for name in fd:
+        np.testing.assert_allclose(got[name], fd[name], rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_mlp_backward_fd_check_catches_a_dropped_term(monkeypatch):
+    """Negative control: GeLU' without its z * phi(z) term must fail the
+    finite-difference comparison."""
+    import oracle.mlp as om
+    x, a, b, ba, bb, dz = _tiny_mlp_problem(seed=41)
+    fd = _fd_grads(x.copy(), a.copy(), b.copy(), ba.copy(), bb.copy(), dz)
+    monkeypatch.setattr(om, "gelu_grad", lambda z: 0.5 * om.erfc(-np.asarray(z) / math.sqrt(2.0)))
+    bad = _assembled_grads(x, a, b, ba, dz, 2)
+    assert not np.allclose(bad["x"], fd["x"], rtol=1e-6, atol=1e-7)
+    assert not np.allclose(bad["a"], fd["a"], rtol=1e-6, atol=1e-7)
+    assert np.allclose(bad["b"], fd["b"], rtol=1e-6, atol=1e-7)   # dB does not use GeLU'
+
+
+def test_mlp_backward_partition_identity():
+    """The ranks' dX contributions sum to the unsharded dX, and their weight
+    gradients are the blocks of the unsharded ones (M025 / M026)."""
+    x, a, b, ba, _bb, dz = _tiny_mlp_problem(seed=43, tokens=5, hidden=8, ffn=32)
+    full = _assembled_grads(x, a, b, ba, dz, 1)
+    for t in (2, 4, 8):
+        parts = _assembled_grads(x, a, b, ba, dz, t)
+        for name in full:
+            np.testing.assert_allclose(parts[name], full[name], rtol=1e-12, atol=1e-12)
