@@ -26,6 +26,11 @@
  *   - Attention shard: heads split over ranks, packed QKV interleaved per
  *     head, local softmax(Q K^T / sqrt(d)) V, row-parallel output projection:
  *     Tencent write-up, attention paragraph; Megatron Level 2, M028.
+ *   - Backward: for the column layer the weight gradient X^T dY_i is local
+ *     and the input-gradient contributions dY_i A_i^T are summed over the
+ *     ranks (Megatron Level 2, M025); for the row layer the input gradient
+ *     dZ B_i^T is already the rank's input-block gradient and the weight
+ *     gradient is local (Megatron Level 2, M026).
  *   - Shapes that do not divide are rejected, never padded: 列并行 tutorial,
  *     切分原理; Megatron Level 2, M031.
  *
@@ -138,6 +143,9 @@ size_t tp_mlp_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
  *   bias_b    [hidden] or NULL (rank 0 only)               (in_dt)
  *   residual  [tokens, hidden] contiguous or NULL (rank 0) (in_dt)
  *   z_i       [tokens, hidden] contiguous                  (out_dt)
+ *   y_save    [tokens, f] contiguous, or NULL: if given, also receives the
+ *             pre-activation Y_i = X A_i + a_i (in_dt), which
+ *             tp_mlp_shard_bwd takes as its saved activation
  *   workspace >= tp_mlp_shard_workspace_bytes(...), 256-byte aligned; it
  *             holds H_i between the two GEMMs (one HBM round trip) and is
  *             scratch: its contents after the call are unspecified.
@@ -145,9 +153,48 @@ size_t tp_mlp_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
  */
 tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const void* b_i,
                            const void* bias_a_i, const void* bias_b, const void* residual,
-                           void* z_i, void* workspace, size_t workspace_bytes,
+                           void* z_i, void* y_save, void* workspace, size_t workspace_bytes,
                            int64_t tokens, int64_t hidden, int64_t ffn, int t, int rank,
                            tp_dtype in_dt, tp_dtype out_dt, void* stream);
+
+/*
+ * Bytes of workspace tp_mlp_shard_bwd needs: dY_i and H_i [tokens, f] in
+ * in_dt plus the column-sum partials of the bias gradients, each part
+ * rounded up to 256 bytes.  Returns 0 for invalid arguments.
+ */
+size_t tp_mlp_shard_bwd_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int t,
+                                        tp_dtype in_dt);
+
+/*
+ * Backward of one rank's MLP shard (the adjoint of tp_mlp_shard_fwd).  dz is
+ * dL/dZ of the summed output Z = sum over ranks of Z_r (the same tensor on
+ * every rank); y_i is the rank's saved pre-activation Y_i = X A_i + a_i.
+ *   dY_i      = (dz B_i^T) * GeLU'(Y_i), GeLU'(y) = Phi(y) + y phi(y)
+ *   db_i      = GeLU(Y_i)^T dz   [f, hidden]      the rank's row block of dB
+ *   da_i      = X^T dY_i         [hidden, f]      the rank's column block of dA
+ *   dx_i      = dY_i A_i^T       [tokens, hidden] the rank's contribution:
+ *                                the sum over ranks is dX (the All-Reduce)
+ *   dbias_a_i = sum over tokens of dY_i  [f]      (f32; skipped if NULL)
+ *   dbias_b   = sum over tokens of dz    [hidden] (f32; skipped if NULL; the
+ *                                same on every rank)
+ * The residual's gradient is dz itself.
+ *   x [tokens, hidden], b_i [f, hidden], y_i [tokens, f], dz [tokens, hidden]
+ *   contiguous, a_i [hidden, f] ld lda: in_dt.
+ *   dx_i [tokens, hidden] and db_i [f, hidden] contiguous, da_i [hidden, f]
+ *   with the same ld lda as a_i: grad_dt.
+ *   workspace >= tp_mlp_shard_bwd_workspace_bytes(...), 256-byte aligned,
+ *   scratch.
+ * dtype pairs (in_dt -> grad_dt): bf16 -> f32, bf16 -> bf16, f32 -> f32.
+ * bf16 inputs: tokens, hidden and f must be multiples of 256, else
+ * TP_ERR_UNSUPPORTED (fp32: any shape).  tokens == 0 gives zero weight and
+ * bias gradients.  dY_i and H_i are rounded to in_dt (bf16: nearest-even)
+ * before the weight- and input-gradient products.
+ */
+tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const void* b_i,
+                           const void* y_i, const void* dz, void* dx_i, void* da_i, void* db_i,
+                           void* dbias_a_i, void* dbias_b, void* workspace,
+                           size_t workspace_bytes, int64_t tokens, int64_t hidden, int64_t ffn,
+                           int t, int rank, tp_dtype in_dt, tp_dtype grad_dt, void* stream);
 
 /*
  * Bytes of workspace tp_attn_shard_fwd needs (Q, K, V of the local heads and
@@ -168,7 +215,10 @@ size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden,
  *   causal  0: every query sees every key; 1: key j <= query i only.
  * Per local head j: O_j = softmax(Q_j K_j^T / sqrt(head_dim)) V_j;
  * out_i = [O_0 | ... | O_{hl-1}] wo_i.  hidden == heads * head_dim.
- * dtype pairs: bf16 -> f32, bf16 -> bf16.  head_dim must be 128.
+ * dtype pairs: bf16 -> f32, bf16 -> bf16.  head_dim must be 128 and seq a
+ * multiple of 128 (TP_ERR_UNSUPPORTED otherwise).  Q and K enter Q K^T as
+ * bf16 (hi, lo) pairs of the fp32 projection (~16 significant bits); V,
+ * the softmax weights and O are bf16 operands with fp32 accumulation.
  */
 tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i, void* out_i,
                             void* workspace, size_t workspace_bytes,

@@ -36,8 +36,11 @@ SIGNATURES = {
     "tp_row_linear": (_INT, [_VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP, _I64, _I64, _I64, _I64,
                              _INT, _INT, _INT, _INT, _VP]),
     "tp_mlp_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
-    "tp_mlp_shard_fwd": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I64, _I64,
-                                _I64, _INT, _INT, _INT, _INT, _VP]),
+    "tp_mlp_shard_fwd": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I64,
+                                _I64, _I64, _INT, _INT, _INT, _INT, _VP]),
+    "tp_mlp_shard_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
+    "tp_mlp_shard_bwd": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                                _I64, _I64, _I64, _INT, _INT, _INT, _INT, _VP]),
     "tp_attn_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _INT, _INT]),
     "tp_attn_shard_fwd": (_INT, [_VP, _VP, _VP, _VP, _VP, _SZ, _I64, _I64, _I64, _I64, _I64,
                                  _INT, _INT, _INT, _INT, _INT, _VP]),
@@ -86,6 +89,10 @@ def _rows(t: torch.Tensor, name: str) -> int:
     if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
         raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
     return t.stride(0)
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream) -> Optional[int]:
@@ -142,20 +149,48 @@ def tp_mlp_shard_workspace_bytes(tokens: int, hidden: int, ffn: int, t: int, dty
 def tp_mlp_shard_fwd(x: torch.Tensor, a_i: torch.Tensor, b_i: torch.Tensor, z_i: torch.Tensor,
                      workspace: torch.Tensor, *, ffn: int, t: int, rank: int,
                      bias_a_i: Optional[torch.Tensor] = None, bias_b: Optional[torch.Tensor] = None,
-                     residual: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """z_i <- GeLU(X A_i + a_i) B_i (+ b + R on rank 0), H_i kept in ``workspace``."""
+                     residual: Optional[torch.Tensor] = None, y_save: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """z_i <- GeLU(X A_i + a_i) B_i (+ b + R on rank 0), H_i kept in ``workspace``;
+    the pre-activation X A_i + a_i also goes to ``y_save`` if given."""
     tokens, hidden = x.shape
-    for name, ten in (("x", x), ("b_i", b_i), ("z_i", z_i)):
-        if not ten.is_contiguous():
+    for name, ten in (("x", x), ("b_i", b_i), ("z_i", z_i), ("residual", residual),
+                      ("y_save", y_save)):
+        if ten is not None and not ten.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if residual is not None and not residual.is_contiguous():
-        raise ValueError("residual must be contiguous")
     _check(lib().tp_mlp_shard_fwd(_ptr(x), _ptr(a_i), _rows(a_i, "a_i"), _ptr(b_i), _ptr(bias_a_i),
-                                  _ptr(bias_b), _ptr(residual), _ptr(z_i), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), tokens, hidden, ffn,
+                                  _ptr(bias_b), _ptr(residual), _ptr(z_i), _ptr(y_save),
+                                  _ptr(workspace), _nbytes(workspace), tokens, hidden, ffn,
                                   t, rank, _dt(x), _dt(z_i), _stream(stream)),
            "tp_mlp_shard_fwd")
     return z_i
+
+
+def tp_mlp_shard_bwd_workspace_bytes(tokens: int, hidden: int, ffn: int, t: int, dtype) -> int:
+    dt = TP_BF16 if dtype == torch.bfloat16 else TP_F32
+    return int(lib().tp_mlp_shard_bwd_workspace_bytes(tokens, hidden, ffn, t, dt))
+
+
+def tp_mlp_shard_bwd(x: torch.Tensor, a_i: torch.Tensor, b_i: torch.Tensor, y_i: torch.Tensor,
+                     dz: torch.Tensor, dx_i: torch.Tensor, da_i: torch.Tensor, db_i: torch.Tensor,
+                     workspace: Optional[torch.Tensor], *, ffn: int, t: int, rank: int,
+                     dbias_a_i: Optional[torch.Tensor] = None,
+                     dbias_b: Optional[torch.Tensor] = None, stream=None):
+    """Backward of the MLP shard: dx_i (the rank's contribution to dX), da_i,
+    db_i and optionally the fp32 bias gradients, from dz and the saved y_i."""
+    tokens, hidden = x.shape
+    for name, ten in (("x", x), ("b_i", b_i), ("y_i", y_i), ("dz", dz), ("dx_i", dx_i),
+                      ("db_i", db_i)):
+        if not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if _rows(da_i, "da_i") != _rows(a_i, "a_i"):
+        raise ValueError("da_i must have a_i's row stride")
+    _check(lib().tp_mlp_shard_bwd(_ptr(x), _ptr(a_i), _rows(a_i, "a_i"), _ptr(b_i), _ptr(y_i),
+                                  _ptr(dz), _ptr(dx_i), _ptr(da_i), _ptr(db_i), _ptr(dbias_a_i),
+                                  _ptr(dbias_b), _ptr(workspace), _nbytes(workspace), tokens,
+                                  hidden, ffn, t, rank, _dt(x), _dt(dx_i), _stream(stream)),
+           "tp_mlp_shard_bwd")
+    return dx_i, da_i, db_i
 
 
 def tp_attn_shard_workspace_bytes(batch: int, seq: int, hidden: int, heads: int, head_dim: int,

@@ -27,7 +27,10 @@ SOURCES = [
     "gemm_bf16_256_plain.hip",
     "gemm_bf16_128_gelu.hip",
     "gemm_bf16_128_plain.hip",
+    "gemm_bf16_256_nt.hip",
+    "gemm_bf16_256_tn.hip",
     "gemm_f32.hip",
+    "colsum.hip",
     "gelu.hip",
     "attention.hip",
 ]

@@ -45,7 +45,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // cancellation for v << 0.  Max |GeLU error| over fp32 inputs ~4e-7 (the
 // same class as v/2 (1 + erff(v/sqrt2)) in fp32) at about a quarter of its
 // instruction count: one v_rcp_f32, one v_exp_f32 and a few FMAs.
-__device__ __forceinline__ float gelu_f32(float v) {
+struct NormalTail {
+  float tail;  // Phi(-|v|)
+  float e;     // exp(-v^2 / 2)
+};
+__device__ __forceinline__ NormalTail normal_tail(float v) {
   const float z = __builtin_fabsf(v) * 0.70710678118654752f;
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
   float p = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
@@ -53,8 +57,21 @@ __device__ __forceinline__ float gelu_f32(float v) {
   p = __builtin_fmaf(t, p, -0.284496736f);
   p = __builtin_fmaf(t, p, 0.254829592f);
   const float e = __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
-  const float tail = 0.5f * (p * t) * e;  // Phi(-|v|)
+  return {0.5f * (p * t) * e, e};
+}
+
+__device__ __forceinline__ float gelu_f32(float v) {
+  const float tail = normal_tail(v).tail;
   return v * (v >= 0.0f ? 1.0f - tail : tail);
+}
+
+// d/dv GeLU(v) = Phi(v) + v phi(v), phi(v) = exp(-v^2/2) / sqrt(2 pi) the
+// standard normal density (the product rule on v Phi(v)); Phi as above, the
+// density from the same exponential.
+__device__ __forceinline__ float gelu_grad_f32(float v) {
+  const NormalTail n = normal_tail(v);
+  const float cdf = v >= 0.0f ? 1.0f - n.tail : n.tail;
+  return __builtin_fmaf(v * 0.39894228040143268f, n.e, cdf);
 }
 
 // ---- global->LDS copies and explicit LDS synchronisation (gfx950) --------

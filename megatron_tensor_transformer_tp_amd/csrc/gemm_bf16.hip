@@ -7,11 +7,12 @@ namespace {
 template <int BM, int BN>
 hipError_t launch_epi(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M, int N,
                       int K, const Epilogue& ep, hipStream_t stream) {
-  if (ep.gelu)
-    return ep.out_f32 ? launch_gemm_bf16_cfg<BM, BN, true, true>(A, lda, B, ldb, M, N, K, ep, stream)
-                      : launch_gemm_bf16_cfg<BM, BN, true, false>(A, lda, B, ldb, M, N, K, ep, stream);
-  return ep.out_f32 ? launch_gemm_bf16_cfg<BM, BN, false, true>(A, lda, B, ldb, M, N, K, ep, stream)
-                    : launch_gemm_bf16_cfg<BM, BN, false, false>(A, lda, B, ldb, M, N, K, ep, stream);
+  if (ep.kind == EPI_GELU)
+    return ep.out_f32 ? launch_gemm_bf16_cfg<BM, BN, EPI_GELU, true>(A, lda, B, ldb, M, N, K, ep, stream)
+                      : launch_gemm_bf16_cfg<BM, BN, EPI_GELU, false>(A, lda, B, ldb, M, N, K, ep, stream);
+  if (ep.kind != EPI_LINEAR) return hipErrorInvalidValue;
+  return ep.out_f32 ? launch_gemm_bf16_cfg<BM, BN, EPI_LINEAR, true>(A, lda, B, ldb, M, N, K, ep, stream)
+                    : launch_gemm_bf16_cfg<BM, BN, EPI_LINEAR, false>(A, lda, B, ldb, M, N, K, ep, stream);
 }
 }  // namespace
 
@@ -20,13 +21,38 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, i
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
-  // Large problems: 256x256 tiles (one workgroup per CU, 144 KiB LDS).
-  // Smaller ones: 128x128 tiles so that the 256 CUs still get work.
+  // Large problems: 256x256 tiles (one workgroup per CU).  Smaller ones:
+  // 128x128 tiles so that the 256 CUs still get work.
   if (tiles256 >= 256)
     return launch_epi<256, 256>(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
                                 static_cast<int>(K), ep, stream);
   return launch_epi<128, 128>(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
                               static_cast<int>(K), ep, stream);
+}
+
+hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B,
+                              int64_t ldb, bool b_kmajor, int64_t M, int64_t N, int64_t K,
+                              const Epilogue& ep, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K <= 0 || M % 256 != 0 || N % 256 != 0 || K % gemm_detail::kBKd != 0)
+    return hipErrorInvalidValue;
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  if (!a_kmajor && b_kmajor) {
+    if (ep.kind == EPI_GELU_BWD) return hipErrorInvalidValue;
+    return launch_gemm_bf16(A, lda, B, ldb, M, N, K, ep, stream);
+  }
+  if (!a_kmajor && !b_kmajor) {
+    if (ep.kind == EPI_GELU_BWD && !ep.out_f32)
+      return launch_gemm_bf16_t_cfg<false, false, EPI_GELU_BWD, false>(A, lda, B, ldb, m, n, k, ep, stream);
+    if (ep.kind == EPI_LINEAR)
+      return ep.out_f32 ? launch_gemm_bf16_t_cfg<false, false, EPI_LINEAR, true>(A, lda, B, ldb, m, n, k, ep, stream)
+                        : launch_gemm_bf16_t_cfg<false, false, EPI_LINEAR, false>(A, lda, B, ldb, m, n, k, ep, stream);
+    return hipErrorInvalidValue;
+  }
+  if (a_kmajor && b_kmajor && ep.kind == EPI_LINEAR)
+    return ep.out_f32 ? launch_gemm_bf16_t_cfg<true, true, EPI_LINEAR, true>(A, lda, B, ldb, m, n, k, ep, stream)
+                      : launch_gemm_bf16_t_cfg<true, true, EPI_LINEAR, false>(A, lda, B, ldb, m, n, k, ep, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tpk

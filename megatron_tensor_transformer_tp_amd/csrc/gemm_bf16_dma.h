@@ -1,8 +1,10 @@
-// bf16 GEMM, C[M,N] = A[M,K] . B[K,N] (both row-major), fp32 accumulation on
-// the gfx950 matrix cores, with both operand tiles brought into LDS by the
-// asynchronous global->LDS copy (global_load_lds_dwordx4) instead of through
-// registers.  Used for tile-aligned shapes (M % BM == 0, N % BN == 0,
-// K % 32 == 0): the copy cannot zero-fill a K tail.
+// bf16 GEMM, C[M,N] = A[M,K] . B[K,N], fp32 accumulation on the gfx950 matrix
+// cores, with both operand tiles brought into LDS by the asynchronous
+// global->LDS copy (global_load_lds_dwordx4) instead of through registers.
+// Used for tile-aligned shapes (M % BM == 0, N % BN == 0, K % 32 == 0): the
+// copy cannot zero-fill a K tail.  Each operand is stored either with k
+// contiguous ("row-major in k": A as [M, K], B as [N, K]) or k-major (A as
+// [K, M], B as [K, N]); the two LDS layouts below serve either operand.
 //
 //   * k-tiles of 32, STAGES LDS stages of (BM + BN) x 64 B (32 KiB each for
 //     256 x 256): tiles kt+1 .. kt+STAGES-1 are in flight while tile kt is
@@ -10,17 +12,18 @@
 //   * Each copy instruction moves 1 KiB: lane t's 16 bytes land at
 //     LDS base + 16 t.  The lane -> global address map applies the LDS swizzle,
 //     so the bytes of a 16-byte chunk are never split.
-//   * A stage (activations, k contiguous): rows of 64 B = 4 chunks; logical
-//     chunk c of row r sits at chunk c ^ ((r >> 2) & 3).  An MFMA fragment
-//     (16 consecutive rows, one chunk each) is one ds_read_b128 per lane and
-//     touches 16 distinct 16-byte bank groups.
-//   * B stage (weights, n contiguous as in memory): rows of BN*2 bytes;
-//     logical chunk c of k-row r sits at chunk c ^ ((r & 3) << 2).  The MFMA
-//     wants 8 consecutive k per lane for one n: ds_read_b64_tr_b16 gives it
-//     directly (within each 16-lane group, lane 4r+c points at 4 consecutive
-//     n of k-row r, and lane i receives column i of the resulting 4 x 16
-//     block), two reads per fragment; the four k-rows of one read fall in
-//     four different 64-byte bank windows.
+//   * k-contiguous operand (activations in the forward): rows of 64 B = 4
+//     chunks; logical chunk c of row r sits at chunk c ^ ((r >> 2) & 3).  An
+//     MFMA fragment (16 consecutive rows, one chunk each) is one ds_read_b128
+//     per lane and touches 16 distinct 16-byte bank groups.
+//   * k-major operand (weights [in, out] in the forward): k-rows of R*2
+//     bytes as in memory; logical chunk c of k-row r sits at chunk
+//     c ^ ((r & 3) << 2).  The MFMA wants 8 consecutive k per lane for one
+//     row: ds_read_b64_tr_b16 gives it directly (within each 16-lane group,
+//     lane 4r+c points at 4 consecutive elements of k-row r, and lane i
+//     receives column i of the resulting 4 x 16 block), two reads per
+//     fragment; the four k-rows of one read fall in four different 64-byte
+//     bank windows.
 //   * Synchronisation is explicit: before the barrier that publishes tile
 //     kt+1 each wave waits (s_waitcnt vmcnt) only for its own copies of that
 //     tile, never for the younger tiles in flight; the barrier is a bare
@@ -34,26 +37,79 @@ namespace tpk {
 namespace gemm_detail {
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 #define TPK_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kBKd = 32;     // k-tile of the copy kernel
+// One operand's share of a k-tile: R rows (M or N) x kBKd k, copied by NW
+// waves (Q copies of 1 KiB each per wave).
+template <int R, int NW, bool KMAJOR>
+struct OperandTile {
+  static constexpr int kBytes = R * kBKd * 2;
+  static constexpr int Q = kBytes / 1024 / NW;
+  static constexpr int CB = R / 8;     // 16-byte chunks per k-row (k-major)
+  static_assert(Q * NW * 1024 == kBytes && (!KMAJOR || CB >= 16), "operand tile shape");
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool GELU, bool OUT_F32>
+  const uint16_t* src[Q];
+  int64_t step;   // elements per k-tile
+
+  // Per-lane copy sources for k-tile 0 of the rows [r0, r0 + R).
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int r0, int wave, int lane) {
+    static_for<Q>([&](auto I) __attribute__((always_inline)) {
+      const int slot = (wave * Q + I) * 64 + lane;
+      if constexpr (!KMAJOR) {
+        const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+        src[I] = base + static_cast<int64_t>(r0 + row) * ld + 8 * c;
+      } else {
+        const int krow = slot / CB, c = (slot % CB) ^ ((krow & 3) << 2);
+        src[I] = base + static_cast<int64_t>(krow) * ld + r0 + 8 * c;
+      }
+    });
+    step = KMAJOR ? static_cast<int64_t>(kBKd) * ld : kBKd;
+  }
+
+  // Copies of k-tile kc into the LDS region at byte address `lds`.
+  __device__ __forceinline__ void issue(int kc, uint32_t lds, int wave) const {
+    static_for<Q>([&](auto I) __attribute__((always_inline)) {
+      copy_to_lds(src[I] + kc * step, lds + (wave * Q + I) * 1024);
+    });
+  }
+
+  // MFMA fragment of 32 rows starting at row0 (a multiple of 32), k-substep
+  // s (k = 16 s .. 16 s + 15): lane l gets row row0 + l % 32, k 16 s + 8 (l / 32) .. +7.
+  __device__ __forceinline__ bf16x8_t frag(const uint8_t* st, int row0, int s, int lane) const {
+    if constexpr (!KMAJOR) {
+      const int chunk = (2 * s + (lane >> 5)) ^ ((lane >> 2) & 3);
+      return *TPK_LDS(const bf16x8_t, st + (row0 + (lane & 31)) * 64 + chunk * 16);
+    } else {
+      const int gi = lane & 15;
+      const int row_lane = (lane >> 5) * 8 + (gi >> 2);
+      const int chunk = ((row0 >> 3) + ((lane >> 4) & 1) * 2 + ((gi & 3) >> 1)) ^ ((gi >> 2) << 2);
+      const int within = (gi & 1) * 8;
+      i16x4_t h[2];
+      static_for<2>([&](auto H) __attribute__((always_inline)) {
+        const int krow = s * 16 + H * 4 + row_lane;
+        h[H] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TPK_LDS(i16x4_t, st + krow * (R * 2) + chunk * 16 + within));
+      });
+      const i16x8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+      return __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+};
+
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,
+          bool OUT_F32>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
-    int64_t ldr, void* __restrict__ out, int64_t ldo, uint16_t* __restrict__ out_lo) {
+    int M, int N, int K, const Epilogue ep) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_BYTES = BM * kBKd * 2;
-  constexpr int B_BYTES = kBKd * BN * 2;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int QA = A_BYTES / 1024 / NW;  // copy instructions per wave per k-tile (A)
-  constexpr int QB = B_BYTES / 1024 / NW;  // (B)
-  constexpr int L = QA + QB;
-  constexpr int CB = BN / 8;               // 16-byte chunks per B row
-  static_assert(QA * NW * 1024 == A_BYTES && QB * NW * 1024 == B_BYTES && CB >= 16, "shape");
+  using TileA = OperandTile<BM, NW, A_KMAJOR>;
+  using TileB = OperandTile<BN, NW, B_KMAJOR>;
+  constexpr int A_BYTES = TileA::kBytes;
+  constexpr int STAGE = A_BYTES + TileB::kBytes;
+  constexpr int L = TileA::Q + TileB::Q;   // copies per wave per k-tile
   static_assert(STAGES >= 3 && STAGES * STAGE <= 160 * 1024, "LDS stages");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
@@ -68,64 +124,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = K / kBKd;
 
-  // Per-lane copy sources for k-tile 0 (advanced by kBKd columns of A and
-  // kBKd rows of B per k-tile).
-  const uint16_t* a_src[QA];
-  const uint16_t* b_src[QB];
-  static_for<QA>([&](auto Q) __attribute__((always_inline)) {
-    const int slot = (wave * QA + Q) * 64 + lane;
-    const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
-    a_src[Q] = A + static_cast<int64_t>(m0 + row) * lda + 8 * c;
-  });
-  static_for<QB>([&](auto Q) __attribute__((always_inline)) {
-    const int slot = (wave * QB + Q) * 64 + lane;
-    const int krow = slot / CB, c = (slot % CB) ^ ((krow & 3) << 2);
-    b_src[Q] = B + static_cast<int64_t>(krow) * ldb + n0 + 8 * c;
-  });
-  const int64_t b_step = static_cast<int64_t>(kBKd) * ldb;
+  TileA ta;
+  TileB tb;
+  ta.init(A, lda, m0, wave, lane);
+  tb.init(B, ldb, n0, wave, lane);
 
   // Copies of k-tile kt (clamped to the last tile) into stage kt % STAGES.
   const uint32_t smem_base = lds_address(smem);
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const int kc = min(kt, nk - 1);
     const uint32_t sbase = smem_base + (kt % STAGES) * STAGE;
-    static_for<QA>([&](auto Q) __attribute__((always_inline)) {
-      copy_to_lds(a_src[Q] + kc * kBKd, sbase + (wave * QA + Q) * 1024);
-    });
-    static_for<QB>([&](auto Q) __attribute__((always_inline)) {
-      copy_to_lds(b_src[Q] + kc * b_step, sbase + A_BYTES + (wave * QB + Q) * 1024);
-    });
+    ta.issue(kc, sbase, wave);
+    tb.issue(kc, sbase + A_BYTES, wave);
   };
-
-  // Fragment addressing (byte offsets within a stage).
-  const int sw_a = (lane >> 2) & 3;
-  const int a_row_off = (wm * WM + (lane & 31)) * 64;
-  const int gi = lane & 15;
-  const int b_row_lane = (lane >> 5) * 8 + (gi >> 2);   // + s*16 + h*4
-  const int b_sw = (gi >> 2) << 2;                       // (krow & 3) << 2
-  const int b_chunk_lane = ((lane >> 4) & 1) * 2 + ((gi & 3) >> 1);
-  const int b_within = (gi & 1) * 8;
 
   bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
   auto read_frags = [&](int kt, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
       __attribute__((always_inline)) {
     const uint8_t* st = smem + (kt % STAGES) * STAGE;
-    const int a_chunk = (2 * s + (lane >> 5)) ^ sw_a;
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      af[I] = *TPK_LDS(const bf16x8_t, st + a_row_off + I * 32 * 64 + a_chunk * 16);
+      af[I] = ta.frag(st, wm * WM + I * 32, s, lane);
     });
-    const uint8_t* bs = st + A_BYTES;
     static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      const int chunk = (((wn * WN + J * 32) >> 3) + b_chunk_lane) ^ b_sw;
-      i16x4_t h[2];
-      static_for<2>([&](auto H) __attribute__((always_inline)) {
-        const int krow = s * 16 + H * 4 + b_row_lane;
-        h[H] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TPK_LDS(i16x4_t, bs + krow * (BN * 2) + chunk * 16 + b_within));
-      });
-      typedef short i16x8_t __attribute__((ext_vector_type(8)));
-      const i16x8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-      bf[J] = __builtin_bit_cast(bf16x8_t, v);
+      bf[J] = tb.frag(st + A_BYTES, wn * WN + J * 32, s, lane);
     });
   };
 
@@ -172,20 +193,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   }
   wait_vmcnt<0>();
 
-  store_tile<TM, TN, false, GELU, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
-                                            n0 + wn * WN + (lane >> 5) * 4, M, N, bias, residual,
-                                            ldr, out, ldo, out_lo);
+  store_tile<TM, TN, false, EPI, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
+                                           n0 + wn * WN + (lane >> 5) * 4, M, N, ep);
 }
 
-template <int BM, int BN, int WGM, int WGN, int STAGES, bool GELU, bool OUT_F32>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,
+          bool OUT_F32>
 hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
                            int N, int K, const Epilogue& ep, hipStream_t stream) {
   const int tiles = (M / BM) * (N / BN);
-  hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, GELU, OUT_F32>), dim3(tiles),
-                     dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K,
-                     static_cast<const uint16_t*>(ep.bias),
-                     static_cast<const uint16_t*>(ep.residual), ep.ldr, ep.out, ep.ldo,
-                     static_cast<uint16_t*>(ep.out_lo));
+  hipLaunchKernelGGL(
+      (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32>),
+      dim3(tiles), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
   return hipGetLastError();
 }
 

@@ -54,6 +54,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;
 constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 elements (144 B)
+constexpr int kBKd = 32;         // k-tile of the global->LDS copy kernel
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
@@ -94,75 +95,109 @@ __device__ __forceinline__ void sched_group() {
 // Epilogue shared by the GEMM kernels.  acc[j][i][4g + r] is C[m][n] with
 //   m = m_lane + i*32,  n = n_lane + j*32 + 8g + r,
 // i.e. each lane owns 4 consecutive columns per (i, j, g): one 16-byte fp32
-// or 8-byte bf16 store.  The bias/residual flags are uniform, so the body is
-// instantiated once per combination and selected with one branch; the column
-// (GeLU) layer never takes a residual, so that combination is not built.
-template <int TM, int TN, bool MASKED, bool GELU, bool OUT_F32>
+// or 8-byte bf16 store.  EPI selects the epilogue kind at compile time; the
+// optional inputs (bias, residual) are uniform, so each combination's body is
+// instantiated once and selected with one branch (the GeLU kinds never take
+// a residual).
+__device__ __forceinline__ void load_bf16x4(const uint16_t* p, float (&v)[4]) {
+  const u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
+  v[0] = __uint_as_float(w[0] << 16);
+  v[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+  v[2] = __uint_as_float(w[1] << 16);
+  v[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+}
+
+template <bool OUT_F32>
+__device__ __forceinline__ void store_x4(void* base, int64_t off, const float (&v)[4]) {
+  if constexpr (OUT_F32) {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(base) + off) = f32x4_t{v[0], v[1], v[2], v[3]};
+  } else {
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(base) + off) =
+        u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+}
+
+template <int TM, int TN, bool MASKED, int EPI, bool OUT_F32>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_lane, int n_lane,
-                                           int M, int N, const uint16_t* __restrict__ bias,
-                                           const uint16_t* __restrict__ residual, int64_t ldr,
-                                           void* __restrict__ out, int64_t ldo,
-                                           uint16_t* __restrict__ out_lo) {
-  auto epilogue = [&](auto has_bias, auto has_res) __attribute__((always_inline)) {
+                                           int M, int N, const Epilogue& ep) {
+  const uint16_t* __restrict__ bias = static_cast<const uint16_t*>(ep.bias);
+  const uint16_t* __restrict__ residual = static_cast<const uint16_t*>(ep.residual);
+  const uint16_t* __restrict__ aux = static_cast<const uint16_t*>(ep.aux);
+  uint16_t* __restrict__ out_lo = static_cast<uint16_t*>(ep.out_lo);
+  auto epilogue = [&](auto has_bias, auto has_res, auto has_extra) __attribute__((always_inline)) {
     constexpr bool kBias = decltype(has_bias)::value;
     constexpr bool kRes = decltype(has_res)::value;
+    constexpr bool kExtra = decltype(has_extra)::value;   // pre (GeLU) or out_lo (linear)
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
       const int m = m_lane + I * 32;
       if (MASKED && m >= M) return;
-      const int64_t row_out = static_cast<int64_t>(m) * ldo + n_lane;
-      const int64_t row_res = kRes ? static_cast<int64_t>(m) * ldr + n_lane : 0;
+      const int64_t row_out = static_cast<int64_t>(m) * ep.ldo + n_lane;
+      const int64_t row_res = kRes ? static_cast<int64_t>(m) * ep.ldr + n_lane : 0;
+      const int64_t row_aux = EPI == EPI_GELU_BWD ? static_cast<int64_t>(m) * ep.ldaux + n_lane : 0;
       static_for<TN>([&](auto J) __attribute__((always_inline)) {
         static_for<4>([&](auto G) __attribute__((always_inline)) {
           constexpr int col = J * 32 + G * 8;
           if (MASKED && n_lane + col >= N) return;
           float v[4];
           static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] = acc[J][I][4 * G + R]; });
-          if constexpr (kBias) {
-            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(bias + n_lane + col);
-            v[0] += __uint_as_float(bb[0] << 16);
-            v[1] += __uint_as_float(bb[0] & 0xFFFF0000u);
-            v[2] += __uint_as_float(bb[1] << 16);
-            v[3] += __uint_as_float(bb[1] & 0xFFFF0000u);
-          }
-          if constexpr (GELU) {
-            static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] = gelu_f32(v[R]); });
-          }
-          if constexpr (kRes) {
-            const u32x2_t rr = *reinterpret_cast<const u32x2_t*>(residual + row_res + col);
-            v[0] += __uint_as_float(rr[0] << 16);
-            v[1] += __uint_as_float(rr[0] & 0xFFFF0000u);
-            v[2] += __uint_as_float(rr[1] << 16);
-            v[3] += __uint_as_float(rr[1] & 0xFFFF0000u);
-          }
-          if constexpr (OUT_F32) {
-            typedef float f32x4_t __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + row_out + col) =
-                f32x4_t{v[0], v[1], v[2], v[3]};
+          if constexpr (EPI == EPI_GELU_BWD) {
+            float y[4], h[4];
+            load_bf16x4(aux + row_aux + col, y);
+            static_for<4>([&](auto R) __attribute__((always_inline)) {
+              v[R] *= gelu_grad_f32(y[R]);
+              h[R] = gelu_f32(y[R]);
+            });
+            store_x4<OUT_F32>(ep.out2, row_out + col, h);
           } else {
-            const u32x2_t hi = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + row_out + col) = hi;
-            if (out_lo != nullptr) {
-              const u32x2_t lo = u32x2_t{
-                  pack_bf16x2(v[0] - __uint_as_float(hi[0] << 16), v[1] - __uint_as_float(hi[0] & 0xFFFF0000u)),
-                  pack_bf16x2(v[2] - __uint_as_float(hi[1] << 16), v[3] - __uint_as_float(hi[1] & 0xFFFF0000u))};
-              *reinterpret_cast<u32x2_t*>(out_lo + row_out + col) = lo;
+            if constexpr (kBias) {
+              float b[4];
+              load_bf16x4(bias + n_lane + col, b);
+              static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] += b[R]; });
             }
+            if constexpr (EPI == EPI_GELU) {
+              if constexpr (kExtra) store_x4<OUT_F32>(ep.pre, row_out + col, v);
+              static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] = gelu_f32(v[R]); });
+            }
+            if constexpr (kRes) {
+              float r[4];
+              load_bf16x4(residual + row_res + col, r);
+              static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] += r[R]; });
+            }
+          }
+          store_x4<OUT_F32>(ep.out, row_out + col, v);
+          if constexpr (EPI == EPI_LINEAR && kExtra && !OUT_F32) {
+            float lo[4];
+            static_for<2>([&](auto P) __attribute__((always_inline)) {
+              const uint32_t hi = pack_bf16x2(v[2 * P], v[2 * P + 1]);
+              lo[2 * P] = v[2 * P] - __uint_as_float(hi << 16);
+              lo[2 * P + 1] = v[2 * P + 1] - __uint_as_float(hi & 0xFFFF0000u);
+            });
+            store_x4<false>(out_lo, row_out + col, lo);
           }
         });
         // keep the accumulator reads of one 32x32 block next to its stores
-        // (hoisting all 256 of them ahead of the stores would spill)
+        // (hoisting all of them ahead of the stores would spill)
         sched_fence();
       });
     });
   };
   using T = std::true_type;
   using F = std::false_type;
-  if constexpr (GELU) {
-    if (bias != nullptr) epilogue(T{}, F{}); else epilogue(F{}, F{});
+  if constexpr (EPI == EPI_GELU_BWD) {
+    epilogue(F{}, F{}, F{});
+  } else if constexpr (EPI == EPI_GELU) {
+    if (bias != nullptr) {
+      if (ep.pre != nullptr) epilogue(T{}, F{}, T{}); else epilogue(T{}, F{}, F{});
+    } else {
+      if (ep.pre != nullptr) epilogue(F{}, F{}, T{}); else epilogue(F{}, F{}, F{});
+    }
+  } else if (out_lo != nullptr) {
+    epilogue(F{}, F{}, T{});
   } else if (bias != nullptr) {
-    if (residual != nullptr) epilogue(T{}, T{}); else epilogue(T{}, F{});
+    if (residual != nullptr) epilogue(T{}, T{}, F{}); else epilogue(T{}, F{}, F{});
   } else {
-    if (residual != nullptr) epilogue(F{}, T{}); else epilogue(F{}, F{});
+    if (residual != nullptr) epilogue(F{}, T{}, F{}); else epilogue(F{}, F{}, F{});
   }
 }
 
@@ -187,11 +222,10 @@ __device__ __forceinline__ void interleave_substep() {
 
 // BM x BN tile per workgroup of WGM x WGN waves; each wave owns a
 // (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA blocks.
-template <int BM, int BN, int WGM, int WGN, bool MASKED, bool GELU, bool OUT_F32>
+template <int BM, int BN, int WGM, int WGN, bool MASKED, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    int M, int N, int K, const uint16_t* __restrict__ bias, const uint16_t* __restrict__ residual,
-    int64_t ldr, void* __restrict__ out, int64_t ldo, uint16_t* __restrict__ out_lo) {
+    int M, int N, int K, const Epilogue ep) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -357,35 +391,37 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
     sched_fence();
   }
 
-  store_tile<TM, TN, MASKED, GELU, OUT_F32>(acc, m0 + wm * WM + (lane & 31), n0 + wn * WN + (lane >> 5) * 4,
-                                           M, N, bias, residual, ldr, out, ldo, out_lo);
+  store_tile<TM, TN, MASKED, EPI, OUT_F32>(acc, m0 + wm * WM + (lane & 31), n0 + wn * WN + (lane >> 5) * 4,
+                                          M, N, ep);
 }
 
-template <int BM, int BN, int WGM, int WGN, bool GELU, bool OUT_F32>
+template <int BM, int BN, int WGM, int WGN, int EPI, bool OUT_F32>
 hipError_t launch_tile(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
                        int N, int K, const Epilogue& ep, hipStream_t stream) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const bool masked = (M % BM) || (N % BN) || (K % kBK);
-  const uint16_t* bias = static_cast<const uint16_t*>(ep.bias);
-  const uint16_t* res = static_cast<const uint16_t*>(ep.residual);
   const dim3 block(64 * WGM * WGN);
   if (masked)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, GELU, OUT_F32>), dim3(tiles), block,
-                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo,
-                       static_cast<uint16_t*>(ep.out_lo));
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, EPI, OUT_F32>), dim3(tiles), block,
+                       0, stream, A, lda, B, ldb, M, N, K, ep);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, GELU, OUT_F32>), dim3(tiles), block,
-                       0, stream, A, lda, B, ldb, M, N, K, bias, res, ep.ldr, ep.out, ep.ldo,
-                       static_cast<uint16_t*>(ep.out_lo));
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, EPI, OUT_F32>), dim3(tiles), block,
+                       0, stream, A, lda, B, ldb, M, N, K, ep);
   return hipGetLastError();
 }
 
 }  // namespace gemm_detail
 
-// One explicit instantiation set per (tile shape, GeLU, output type); defined in
-// the gemm_bf16_*.hip translation units.
-template <int BM, int BN, bool GELU, bool OUT_F32>
+// One explicit instantiation set per (tile shape, epilogue kind, output type);
+// defined in the gemm_bf16_*.hip translation units.
+template <int BM, int BN, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                 int M, int N, int K, const Epilogue& ep, hipStream_t stream);
+
+// Tile-aligned products with k-major flags (256 x 256 tiles, copy kernel);
+// defined in the gemm_bf16_256_*.hip translation units.
+template <bool A_KMAJOR, bool B_KMAJOR, int EPI, bool OUT_F32>
+hipError_t launch_gemm_bf16_t_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                  int M, int N, int K, const Epilogue& ep, hipStream_t stream);
 
 }  // namespace tpk

@@ -7,13 +7,21 @@
 
 namespace tpk {
 
-// Epilogue applied to the fp32 accumulator of C = A B, element (m, n):
-//   v = acc + bias[n]            (bias: input dtype, or null)
-//   v = GeLU(v)                  (if gelu)
-//   v = v + residual[m, n]       (residual: input dtype, row stride ldr, or null)
+// Epilogue kinds (compile-time in the kernels).
+enum EpilogueKind : int {
+  EPI_LINEAR = 0,    // v = acc + bias[n]; v += residual[m, n]
+  EPI_GELU = 1,      // y = acc + bias[n]; pre[m, n] = y (if pre); v = GeLU(y)
+  EPI_GELU_BWD = 2,  // y = aux[m, n]; v = acc * GeLU'(y); out2[m, n] = GeLU(y)
+};
+
+// Epilogue applied to the fp32 accumulator of C = A B, element (m, n), then
 //   out[m, n] = v                (fp32, or bf16 rounded to nearest-even)
-//   out_lo[m, n] = v - out[m, n] (bf16 out only, if out_lo is set: v as the
-//                                 pair hi + lo, ~16 significant bits)
+//   out_lo[m, n] = v - out[m, n] (bf16 out, EPI_LINEAR with no bias and no
+//                                 residual, if out_lo is set: v as the pair
+//                                 hi + lo, ~16 significant bits)
+// bias: input dtype or null; residual: input dtype, row stride ldr, or null
+// (EPI_LINEAR only); pre and out2 share out's dtype and row stride ldo; aux
+// is in the input dtype with row stride ldaux.
 struct Epilogue {
   const void* bias;
   const void* residual;
@@ -21,21 +29,50 @@ struct Epilogue {
   void* out;
   int64_t ldo;
   bool out_f32;
-  bool gelu;
+  int kind;
   void* out_lo = nullptr;
+  void* pre = nullptr;
+  const void* aux = nullptr;
+  int64_t ldaux = 0;
+  void* out2 = nullptr;
 };
 
 // bf16 x bf16 -> fp32 accumulate, MFMA.  A [M, K] row-major (lda), B [K, N]
 // row-major (ldb).  Requires N % 8 == 0, K % 8 == 0, lda/ldb/ldr/ldo % 8 == 0
-// (ldo % 4 for fp32 out), 16-byte aligned pointers.
+// (ldo % 4 for fp32 out), 16-byte aligned pointers.  EPI_LINEAR / EPI_GELU.
 hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                             int64_t M, int64_t N, int64_t K, const Epilogue& ep,
                             hipStream_t stream);
 
-// fp32 x fp32 -> fp32 FMA.  Same layout rules with 4-element alignment.
-hipError_t launch_gemm_f32(const float* A, int64_t lda, const float* B, int64_t ldb,
-                           int64_t M, int64_t N, int64_t K, const Epilogue& ep,
+// The same product with either operand stored k-major or not:
+//   a_kmajor: A given as [K, M] row-major (lda >= M), i.e. the product uses Aᵀ of it;
+//   b_kmajor: B given as [K, N] row-major (the usual form); false: B given as
+//             [N, K] row-major (ldb >= K).
+// Tile-aligned shapes only: M % 256 == N % 256 == K % 32 == 0 (else
+// hipErrorInvalidValue).  Every epilogue kind.
+hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B,
+                              int64_t ldb, bool b_kmajor, int64_t M, int64_t N, int64_t K,
+                              const Epilogue& ep, hipStream_t stream);
+
+// fp32 x fp32 -> fp32 FMA, any shape.  Same layout flags as launch_gemm_bf16_t
+// (a_kmajor: A given [K, M]; b_kmajor: B given [K, N], else [N, K]); every
+// epilogue kind except the (hi, lo) pair.
+hipError_t launch_gemm_f32(const float* A, int64_t lda, bool a_kmajor, const float* B, int64_t ldb,
+                           bool b_kmajor, int64_t M, int64_t N, int64_t K, const Epilogue& ep,
                            hipStream_t stream);
+
+// Column sums out[n] = sum_m in[m, n] (fp32 accumulation, in fp32 or bf16 by
+// in_dt 0/1, row stride ld), in two passes over 256-row chunks (deterministic):
+// partial needs colsum_partial_floats(M, N) floats of scratch.
+int64_t colsum_partial_floats(int64_t M, int64_t N);
+hipError_t launch_colsum(const void* in, int64_t ld, int in_dt, int64_t M, int64_t N, float* out,
+                         float* partial, hipStream_t stream);
+
+// p[r, c] = 0 for r < rows, c < cols, row stride ld elements of elt_bytes
+// (2 or 4) bytes: a kernel, not a memset, so that it may sit in a captured
+// graph.
+hipError_t launch_zero_2d(void* p, int64_t rows, int64_t cols, int64_t ld, int elt_bytes,
+                          hipStream_t stream);
 
 // Head-local attention: qkv_hi/qkv_lo [batch*seq, ld_qkv] bf16 pair holding
 // the rank's packed projection (per head [q | k | v], head_dim columns each);

@@ -73,8 +73,23 @@ tp_status run_gemm(tp_dtype in_dt, const void* a, int64_t lda, const void* b, in
     return from_hip(tpk::launch_gemm_bf16(static_cast<const uint16_t*>(a), lda,
                                           static_cast<const uint16_t*>(b), ldb, M, N, K, ep,
                                           stream));
-  return from_hip(tpk::launch_gemm_f32(static_cast<const float*>(a), lda,
-                                       static_cast<const float*>(b), ldb, M, N, K, ep, stream));
+  return from_hip(tpk::launch_gemm_f32(static_cast<const float*>(a), lda, false,
+                                       static_cast<const float*>(b), ldb, true, M, N, K, ep,
+                                       stream));
+}
+
+// The same with k-major flags (A given [K, M] if a_kmajor; B given [K, N] if
+// b_kmajor, else [N, K]).  bf16 needs tile-aligned shapes (checked by callers).
+tp_status run_gemm_t(tp_dtype in_dt, const void* a, int64_t lda, bool a_kmajor, const void* b,
+                     int64_t ldb, bool b_kmajor, int64_t M, int64_t N, int64_t K,
+                     const tpk::Epilogue& ep, hipStream_t stream) {
+  if (in_dt == TP_BF16)
+    return from_hip(tpk::launch_gemm_bf16_t(static_cast<const uint16_t*>(a), lda, a_kmajor,
+                                            static_cast<const uint16_t*>(b), ldb, b_kmajor, M, N,
+                                            K, ep, stream));
+  return from_hip(tpk::launch_gemm_f32(static_cast<const float*>(a), lda, a_kmajor,
+                                       static_cast<const float*>(b), ldb, b_kmajor, M, N, K, ep,
+                                       stream));
 }
 
 size_t round256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -115,7 +130,8 @@ tp_status tp_column_linear(const void* x, int64_t ldx, const void* a_i, int64_t 
   TP_TRY(check_matrix(a_i, lda, f, in_dt));
   TP_TRY(check_matrix(y_i, ldy, f, out_dt));
   TP_TRY(check_optional_vec(bias_i));
-  tpk::Epilogue ep{bias_i, nullptr, 0, y_i, ldy, out_dt == TP_F32, apply_gelu == 1};
+  tpk::Epilogue ep{bias_i, nullptr, 0, y_i, ldy, out_dt == TP_F32,
+                   apply_gelu == 1 ? tpk::EPI_GELU : tpk::EPI_LINEAR};
   return run_gemm(in_dt, x, ldx, a_i, lda, tokens, f, hidden, ep,
                   static_cast<hipStream_t>(stream));
 }
@@ -155,7 +171,7 @@ tp_status tp_row_linear(const void* h_i, int64_t ldh, const void* b_i, int64_t l
   const void* res_use = owner ? residual : nullptr;
   TP_TRY(check_optional_vec(bias_use));
   if (res_use != nullptr) TP_TRY(check_matrix(res_use, ldr, hidden, in_dt));
-  tpk::Epilogue ep{bias_use, res_use, ldr, z_i, ldz, out_dt == TP_F32, false};
+  tpk::Epilogue ep{bias_use, res_use, ldr, z_i, ldz, out_dt == TP_F32, tpk::EPI_LINEAR};
   return run_gemm(in_dt, h_i, ldh, b_i, ldb, tokens, hidden, f, ep,
                   static_cast<hipStream_t>(stream));
 }
@@ -171,7 +187,8 @@ size_t tp_mlp_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
 
 tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const void* b_i,
                            const void* bias_a_i, const void* bias_b, const void* residual,
-                           void* z_i, void* workspace, size_t workspace_bytes, int64_t tokens,
+                           void* z_i, void* y_save, void* workspace, size_t workspace_bytes,
+                           int64_t tokens,
                            int64_t hidden, int64_t ffn, int t, int rank, tp_dtype in_dt,
                            tp_dtype out_dt, void* stream) {
   if (!dtype_known(in_dt) || !dtype_known(out_dt) || !gemm_pair_ok(in_dt, out_dt))
@@ -185,6 +202,7 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
   TP_TRY(check_matrix(a_i, lda, f, in_dt));
   TP_TRY(check_matrix(b_i, hidden, hidden, in_dt));
   TP_TRY(check_matrix(z_i, hidden, hidden, out_dt));
+  if (y_save != nullptr) TP_TRY(check_matrix(y_save, f, f, in_dt));
   TP_TRY(check_optional_vec(bias_a_i));
   const bool owner = rank == 0;
   const void* bias_use = owner ? bias_b : nullptr;
@@ -197,12 +215,111 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   // Column-parallel GEMM with GeLU fused into its epilogue: H_i = GeLU(X A_i + a_i)
-  // stored once in the workspace (bf16 for bf16 inputs, fp32 for fp32).
-  tpk::Epilogue ep1{bias_a_i, nullptr, 0, workspace, f, in_dt == TP_F32, true};
+  // stored once in the workspace (bf16 for bf16 inputs, fp32 for fp32); the
+  // pre-activation also goes to y_save when asked for.
+  tpk::Epilogue ep1{bias_a_i, nullptr, 0, workspace, f, in_dt == TP_F32, tpk::EPI_GELU};
+  ep1.pre = y_save;
   TP_TRY(run_gemm(in_dt, x, hidden, a_i, lda, tokens, f, hidden, ep1, s));
   // Row-parallel GEMM: Z_i = H_i B_i (+ b + R on rank 0).
-  tpk::Epilogue ep2{bias_use, res_use, hidden, z_i, hidden, out_dt == TP_F32, false};
+  tpk::Epilogue ep2{bias_use, res_use, hidden, z_i, hidden, out_dt == TP_F32, tpk::EPI_LINEAR};
   return run_gemm(in_dt, workspace, f, b_i, hidden, tokens, hidden, f, ep2, s);
+}
+
+
+namespace {
+// Workspace of tp_mlp_shard_bwd: dY_i, H_i [tokens, f] (in_dt), then the
+// column-sum partials (fp32) of the bias gradients.
+struct MlpBwdWorkspace {
+  size_t dy, h, partial, total;
+};
+MlpBwdWorkspace mlp_bwd_workspace(int64_t tokens, int64_t hidden, int64_t f, tp_dtype in_dt) {
+  const size_t act = round256(static_cast<size_t>(tokens) * static_cast<size_t>(f) *
+                              static_cast<size_t>(elem_bytes(in_dt)));
+  const int64_t cols = f > hidden ? f : hidden;
+  const size_t part = round256(static_cast<size_t>(tpk::colsum_partial_floats(tokens, cols)) * 4);
+  return {act, act, part, 2 * act + part};
+}
+}  // namespace
+
+size_t tp_mlp_shard_bwd_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int t,
+                                        tp_dtype in_dt) {
+  if (!dtype_known(in_dt) || tokens < 0 || hidden < 1) return 0;
+  int64_t f = 0;
+  if (check_split(ffn, t, 0, &f) != TP_OK) return 0;
+  return mlp_bwd_workspace(tokens, hidden, f, in_dt).total;
+}
+
+tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const void* b_i,
+                           const void* y_i, const void* dz, void* dx_i, void* da_i, void* db_i,
+                           void* dbias_a_i, void* dbias_b, void* workspace,
+                           size_t workspace_bytes, int64_t tokens, int64_t hidden, int64_t ffn,
+                           int t, int rank, tp_dtype in_dt, tp_dtype grad_dt, void* stream) {
+  if (!dtype_known(in_dt) || !dtype_known(grad_dt) || !gemm_pair_ok(in_dt, grad_dt))
+    return TP_ERR_DTYPE;
+  if (tokens < 0 || hidden < 1) return TP_ERR_INVALID_ARG;
+  int64_t f = 0;
+  TP_TRY(check_split(ffn, t, rank, &f));
+  if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(f)) return TP_ERR_UNSUPPORTED;
+  // operands that are read (tokens == 0 reads none of the token-indexed ones)
+  TP_TRY(check_matrix(a_i, lda, f, in_dt));
+  TP_TRY(check_matrix(b_i, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(da_i, lda, f, grad_dt));
+  TP_TRY(check_matrix(db_i, hidden, hidden, grad_dt));
+  TP_TRY(check_optional_vec(dbias_a_i));
+  TP_TRY(check_optional_vec(dbias_b));
+  if (tokens > 0) {
+    TP_TRY(check_matrix(x, hidden, hidden, in_dt));
+    TP_TRY(check_matrix(y_i, f, f, in_dt));
+    TP_TRY(check_matrix(dz, hidden, hidden, in_dt));
+    TP_TRY(check_matrix(dx_i, hidden, hidden, grad_dt));
+  }
+  if (in_dt == TP_BF16 && (tokens % 256 != 0 || hidden % 256 != 0 || f % 256 != 0))
+    return TP_ERR_UNSUPPORTED;
+  const MlpBwdWorkspace ws = mlp_bwd_workspace(tokens, hidden, f, in_dt);
+  if (workspace == nullptr || workspace_bytes < ws.total) return TP_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int geb = static_cast<int>(elem_bytes(grad_dt));
+  const bool g32 = grad_dt == TP_F32;
+  if (tokens == 0) {
+    // sums over no tokens: zero weight and bias gradients
+    TP_TRY(from_hip(tpk::launch_zero_2d(da_i, hidden, f, lda, geb, s)));
+    TP_TRY(from_hip(tpk::launch_zero_2d(db_i, f, hidden, hidden, geb, s)));
+    if (dbias_a_i != nullptr) TP_TRY(from_hip(tpk::launch_zero_2d(dbias_a_i, 1, f, f, 4, s)));
+    if (dbias_b != nullptr) TP_TRY(from_hip(tpk::launch_zero_2d(dbias_b, 1, hidden, hidden, 4, s)));
+    return TP_OK;
+  }
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  void* dy = w;
+  void* h = w + ws.dy;
+  float* partial = reinterpret_cast<float*>(w + ws.dy + ws.h);
+  const bool in32 = in_dt == TP_F32;
+  // 1. dH_i = dz B_i^T (B_i is [f, hidden]: the product reads it as [N, K]),
+  //    with dY_i = dH_i * GeLU'(Y_i) and H_i = GeLU(Y_i) in the epilogue.
+  tpk::Epilogue e1{nullptr, nullptr, 0, dy, f, in32, tpk::EPI_GELU_BWD};
+  e1.aux = y_i;
+  e1.ldaux = f;
+  e1.out2 = h;
+  TP_TRY(run_gemm_t(in_dt, dz, hidden, false, b_i, hidden, false, tokens, f, hidden, e1, s));
+  // 2. db_i = H_i^T dz: A = H_i read as [K = tokens, M = f].
+  tpk::Epilogue e2{nullptr, nullptr, 0, db_i, hidden, g32, tpk::EPI_LINEAR};
+  TP_TRY(run_gemm_t(in_dt, h, f, true, dz, hidden, true, f, hidden, tokens, e2, s));
+  // 3. da_i = X^T dY_i: A = X read as [K = tokens, M = hidden].
+  tpk::Epilogue e3{nullptr, nullptr, 0, da_i, lda, g32, tpk::EPI_LINEAR};
+  TP_TRY(run_gemm_t(in_dt, x, hidden, true, dy, f, true, hidden, f, tokens, e3, s));
+  // 4. dx_i = dY_i A_i^T (A_i is [hidden, f]: read as [N, K]).
+  tpk::Epilogue e4{nullptr, nullptr, 0, dx_i, hidden, g32, tpk::EPI_LINEAR};
+  TP_TRY(run_gemm_t(in_dt, dy, f, false, a_i, lda, false, tokens, hidden, f, e4, s));
+  // 5. bias gradients: column sums over the tokens.
+  const int dt = in_dt == TP_BF16 ? 1 : 0;
+  if (dbias_a_i != nullptr)
+    TP_TRY(from_hip(tpk::launch_colsum(dy, f, dt, tokens, f, static_cast<float*>(dbias_a_i),
+                                       partial, s)));
+  if (dbias_b != nullptr)
+    TP_TRY(from_hip(tpk::launch_colsum(dz, hidden, dt, tokens, hidden,
+                                       static_cast<float*>(dbias_b), partial, s)));
+  return TP_OK;
 }
 
 namespace {
@@ -258,14 +375,14 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
   uint16_t* o = reinterpret_cast<uint16_t*>(w + 2 * ws.qkv_bytes);
   // 1. Column-parallel packed QKV projection of the rank's heads, kept as a
   //    bf16 (hi, lo) pair so that Q K^T keeps ~16 significant bits.
-  tpk::Epilogue ep1{nullptr, nullptr, 0, qkv_hi, 3 * dl, false, false, qkv_lo};
+  tpk::Epilogue ep1{nullptr, nullptr, 0, qkv_hi, 3 * dl, false, tpk::EPI_LINEAR, qkv_lo};
   TP_TRY(run_gemm(in_dt, x, hidden, wqkv_i, 3 * dl, tokens, 3 * dl, hidden, ep1, s));
   // 2. softmax(Q K^T / sqrt(d)) V per local head.
   TP_TRY(from_hip(tpk::launch_attention(qkv_hi, qkv_lo, 3 * dl, o, dl, static_cast<int>(batch),
                                         static_cast<int>(seq), static_cast<int>(hl),
                                         static_cast<int>(head_dim), causal == 1, s)));
   // 3. Row-parallel output projection: the rank's full-hidden partial.
-  tpk::Epilogue ep3{nullptr, nullptr, 0, out_i, hidden, out_dt == TP_F32, false};
+  tpk::Epilogue ep3{nullptr, nullptr, 0, out_i, hidden, out_dt == TP_F32, tpk::EPI_LINEAR};
   return run_gemm(in_dt, o, dl, wo_i, hidden, tokens, hidden, dl, ep3, s);
 }
 

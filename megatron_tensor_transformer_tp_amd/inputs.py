@@ -38,6 +38,7 @@ __all__ = [
     "mlp_bias_a_block",
     "mlp_bias_b",
     "mlp_residual_rows",
+    "mlp_dz_rows",
     "attn_x",
     "attn_wqkv_block",
     "attn_wo_block",
@@ -48,7 +49,7 @@ __all__ = [
 X_ROW_CHUNK = 256
 
 _TENSOR_IDS = {"x": 0, "a": 1, "b": 2, "wqkv": 3, "wo": 4, "residual": 5,
-               "bias_a": 6, "bias_b": 7}
+               "bias_a": 6, "bias_b": 7, "dz": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -101,6 +102,10 @@ MLP_WORKLOADS = {
     # Unsharded (t=1) bf16 MLP, 2048 tokens, h=1024: bf16 final output.
     "t1_h1024_m2048": MlpWorkload("t1_h1024_m2048", 2048, 1024, 4096, 1, "bf16",
                                   1.0, 0.02, 0.02, "bf16"),
+    # Small sharded bf16 MLP, t=4: 1024 tokens, h=1024, F=4096 (f=1024), every
+    # dimension a multiple of the 256 tile (backward and strided-view cases).
+    "t4_h1024_m1024": MlpWorkload("t4_h1024_m1024", 1024, 1024, 4096, 4, "bf16",
+                                  1.0, 0.02, 0.02, "f32"),
     # One rank of t=8 at h=8192, 4096 tokens: fp32 partial sum.
     "t8_h8192_m4096": MlpWorkload("t8_h8192_m4096", 4096, 8192, 32768, 8, "bf16",
                                   1.0, 0.02, 0.02, "f32"),
@@ -206,6 +211,19 @@ def mlp_residual_rows(wl: MlpWorkload, row0: int = 0, rows: Optional[int] = None
     rows = wl.tokens - row0 if rows is None else rows
     c0, c1 = row0 // X_ROW_CHUNK, (row0 + rows + X_ROW_CHUNK - 1) // X_ROW_CHUNK
     parts = [draw(wl.name, "residual", c, (min(X_ROW_CHUNK, wl.tokens - c * X_ROW_CHUNK), wl.hidden),
+                  std, wl.dtype) for c in range(c0, c1)]
+    full = np.concatenate(parts, axis=0)
+    off = row0 - c0 * X_ROW_CHUNK
+    return np.ascontiguousarray(full[off:off + rows])
+
+
+def mlp_dz_rows(wl: MlpWorkload, row0: int = 0, rows: Optional[int] = None,
+                std: float = 1.0) -> np.ndarray:
+    """Rows of the output gradient dZ [tokens, hidden] fed to the backward
+    (N(0, std^2), drawn in 256-row chunks like X)."""
+    rows = wl.tokens - row0 if rows is None else rows
+    c0, c1 = row0 // X_ROW_CHUNK, (row0 + rows + X_ROW_CHUNK - 1) // X_ROW_CHUNK
+    parts = [draw(wl.name, "dz", c, (min(X_ROW_CHUNK, wl.tokens - c * X_ROW_CHUNK), wl.hidden),
                   std, wl.dtype) for c in range(c0, c1)]
     full = np.concatenate(parts, axis=0)
     off = row0 - c0 * X_ROW_CHUNK

@@ -33,20 +33,28 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def errors(got: np.ndarray, ref: np.ndarray):
+def errors(got: np.ndarray, ref: np.ndarray, floor: float = 1.0):
+    """(max |err| / (floor + |ref|), relative Frobenius error)."""
     d = got - ref
-    mx = float(np.max(np.abs(d) / (1.0 + np.abs(ref)))) if d.size else 0.0
+    mx = float(np.max(np.abs(d) / (floor + np.abs(ref)))) if d.size else 0.0
     nr = float(np.linalg.norm(ref))
     fro = float(np.linalg.norm(d) / nr) if nr > 0 else float(np.linalg.norm(d))
     return mx, fro
 
 
-def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str) -> None:
+def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str,
+                 rms_floor: bool = False) -> None:
+    """Both bounds.  The max criterion is max |err| / (1 + |ref|); with
+    rms_floor the "1" is the output's RMS magnitude instead (for outputs far
+    from unit scale, e.g. weight gradients summed over thousands of tokens:
+    the same bound at unit scale)."""
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite values (unwritten tile?)"
-    mx, fro = errors(got, ref)
+    floor = float(np.sqrt(np.mean(ref * ref))) if rms_floor and ref.size else 1.0
+    mx, fro = errors(got, ref, floor)
     lim_mx, lim_fro = (BF16_MAX, BF16_FRO) if dtype == "bf16" else (F32_MAX, F32_FRO)
-    say(f"{what}: max|e|/(1+|r|) = {mx:.3e} (<= {lim_mx}), rel-fro = {fro:.3e} (<= {lim_fro})")
+    label = f"max|e|/({floor:.3g}+|r|)" if rms_floor else "max|e|/(1+|r|)"
+    say(f"{what}: {label} = {mx:.3e} (<= {lim_mx}), rel-fro = {fro:.3e} (<= {lim_fro})")
     assert mx <= lim_mx and fro <= lim_fro, what
 
 

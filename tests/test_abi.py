@@ -115,12 +115,12 @@ def test_gelu_validation(lib):
 
 
 def mlp(lib, **kw):
-    a = dict(x=P, a=P, lda=512, b=P, bias_a=None, bias_b=None, res=None, z=P, ws=P, ws_bytes=1 << 30,
-             tokens=16, hidden=1024, ffn=4096, t=8, rank=0, in_dt=BF16, out_dt=F32)
+    a = dict(x=P, a=P, lda=512, b=P, bias_a=None, bias_b=None, res=None, z=P, y=None, ws=P,
+             ws_bytes=1 << 30, tokens=16, hidden=1024, ffn=4096, t=8, rank=0, in_dt=BF16, out_dt=F32)
     a.update(kw)
     return lib.tp_mlp_shard_fwd(a["x"], a["a"], a["lda"], a["b"], a["bias_a"], a["bias_b"], a["res"],
-                                a["z"], a["ws"], a["ws_bytes"], a["tokens"], a["hidden"], a["ffn"],
-                                a["t"], a["rank"], a["in_dt"], a["out_dt"], None)
+                                a["z"], a["y"], a["ws"], a["ws_bytes"], a["tokens"], a["hidden"],
+                                a["ffn"], a["t"], a["rank"], a["in_dt"], a["out_dt"], None)
 
 
 def test_mlp_shard_validation(lib):
@@ -141,6 +141,42 @@ def test_mlp_shard_validation(lib):
     assert mlp(lib, bias_a=P + 2) == MISALIGNED
     assert mlp(lib, in_dt=F32, out_dt=BF16) == DTYPE
     assert mlp(lib, tokens=0, ws=None) == OK
+    assert mlp(lib, y=P + 8) == MISALIGNED        # the saved pre-activation must be aligned
+
+
+def bwd(lib, **kw):
+    a = dict(x=P, a=P, lda=512, b=P, y=P, dz=P, dx=P, da=P, db=P, dba=None, dbb=None, ws=P,
+             ws_bytes=1 << 30, tokens=256, hidden=1024, ffn=4096, t=8, rank=0, in_dt=BF16,
+             g_dt=F32)
+    a.update(kw)
+    return lib.tp_mlp_shard_bwd(a["x"], a["a"], a["lda"], a["b"], a["y"], a["dz"], a["dx"], a["da"],
+                                a["db"], a["dba"], a["dbb"], a["ws"], a["ws_bytes"], a["tokens"],
+                                a["hidden"], a["ffn"], a["t"], a["rank"], a["in_dt"], a["g_dt"], None)
+
+
+def test_mlp_shard_bwd_validation(lib):
+    need = lib.tp_mlp_shard_bwd_workspace_bytes(256, 1024, 4096, 8, BF16)
+    # dY and H [256, 512] bf16, then one 256-row chunk of fp32 partial sums over max(f, hidden)
+    assert need == 2 * 256 * 512 * 2 + 1024 * 4
+    assert lib.tp_mlp_shard_bwd_workspace_bytes(256, 1024, 4100, 8, BF16) == 0
+    assert bwd(lib, ws_bytes=need - 1) == WORKSPACE
+    assert bwd(lib, ws=None) == WORKSPACE
+    assert bwd(lib, ws=P + 16) == MISALIGNED
+    assert bwd(lib, ffn=4097) == NOT_DIV
+    assert bwd(lib, rank=8) == BAD_RANK
+    assert bwd(lib, in_dt=F32, g_dt=BF16) == DTYPE
+    assert bwd(lib, y=None) == INVALID
+    assert bwd(lib, dz=None) == INVALID
+    assert bwd(lib, da=None) == INVALID
+    assert bwd(lib, lda=500) == INVALID
+    assert bwd(lib, dba=P + 4) == MISALIGNED
+    # the bf16 kernels take tile-aligned shapes only
+    assert bwd(lib, tokens=300) == UNSUPPORTED
+    assert bwd(lib, hidden=1032) == UNSUPPORTED
+    assert bwd(lib, ffn=8 * 264, lda=264) == UNSUPPORTED
+    # fp32 takes any shape: the same call gets past the shape check (and stops
+    # at the workspace size, before any launch)
+    assert bwd(lib, in_dt=F32, tokens=300, hidden=1000, ffn=4000, lda=500, ws_bytes=1) == WORKSPACE
 
 
 def attn(lib, **kw):

@@ -1,0 +1,185 @@
+"""GPU parity of the MLP shard backward (tp_mlp_shard_bwd) and of the
+forward's saved pre-activation against the fp64 oracle.
+
+Every call goes through the C ABI.  Outputs are NaN-filled before each call.
+Tolerances as for the forward, bf16 inputs: max |err| <= 2e-2 (s + |ref|) and
+relative Frobenius <= 5e-3 per output; fp32: both <= 1e-5.  For the
+gradients s is the output's RMS magnitude rather than 1 (they are sums over
+up to 16384 tokens, far from unit scale; at unit scale it is the same bound).
+The sum of the ranks' dX contributions is held to the relative Frobenius
+bound, its normalised max error reported.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_tp_amd import binding, inputs
+from tests.gpu_helpers import (BF16_FRO, assert_close, dev, errors, host64, nan_tensor, say,
+                               to_np)
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def run_fwd_save(wl, r, xd, ad, bd, bias_d=None):
+    """Forward of rank r with the pre-activation saved; returns (z, y)."""
+    td = TORCH_DT[wl.dtype]
+    ws = torch.empty(binding.tp_mlp_shard_workspace_bytes(xd.shape[0], wl.hidden, wl.ffn, wl.t, td),
+                     dtype=torch.uint8, device="cuda")
+    z = nan_tensor((xd.shape[0], wl.hidden), TORCH_DT[wl.out_dtype])
+    y = nan_tensor((xd.shape[0], wl.f), td)
+    binding.tp_mlp_shard_fwd(xd, ad, bd, z, ws, ffn=wl.ffn, t=wl.t, rank=r, bias_a_i=bias_d,
+                             y_save=y)
+    torch.cuda.synchronize()
+    return z, y
+
+
+def run_bwd(wl, r, xd, ad, bd, yd, dzd, grad_dt, with_bias=True, da=None):
+    td = TORCH_DT[wl.dtype]
+    tokens = xd.shape[0]
+    nbytes = binding.tp_mlp_shard_bwd_workspace_bytes(tokens, wl.hidden, wl.ffn, wl.t, td)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    gd = TORCH_DT[grad_dt]
+    dx = nan_tensor((tokens, wl.hidden), gd)
+    da = nan_tensor((wl.hidden, wl.f), gd) if da is None else da
+    db = nan_tensor((wl.f, wl.hidden), gd)
+    dba = nan_tensor((wl.f,), torch.float32) if with_bias else None
+    dbb = nan_tensor((wl.hidden,), torch.float32) if with_bias else None
+    binding.tp_mlp_shard_bwd(xd, ad, bd, yd, dzd, dx, da, db, ws, ffn=wl.ffn, t=wl.t, rank=r,
+                             dbias_a_i=dba, dbias_b=dbb)
+    torch.cuda.synchronize()
+    return dict(dx=dx, da=da, db=db, dbias_a=dba, dbias_b=dbb)
+
+
+def check_grads(got, ref, dtype, what, keys=("dx", "da", "db", "dbias_a", "dbias_b")):
+    for k in keys:
+        if got.get(k) is None:
+            continue
+        # the bias gradients are fp32 sums of the (rounded) row gradients
+        assert_close(to_np(got[k]), ref[k], dtype, f"{what} {k}", rms_floor=True)
+
+
+def shard_ref(x64, a64, b64, dz64, ba64=None):
+    """Oracle backward of one rank given that rank's blocks: with t = 1 the
+    oracle's rank-0 block of [h, f] / [f, h] weights is the whole of them
+    (the partition identity pin ties this to the sharded form)."""
+    return oracle.mlp_shard_bwd(x64, a64, b64, dz64, 1, 0, bias_a=ba64)
+
+
+def test_tiny_f32_all_ranks_save_and_backward():
+    wl = inputs.MLP_WORKLOADS["tiny_f32_t4"]
+    x, dz = inputs.mlp_x_rows(wl), inputs.mlp_dz_rows(wl)
+    a_full = np.concatenate([inputs.mlp_a_block(wl, r) for r in range(wl.t)], axis=1)
+    b_full = np.concatenate([inputs.mlp_b_block(wl, r) for r in range(wl.t)], axis=0)
+    ba_full = np.concatenate([inputs.mlp_bias_a_block(wl, r) for r in range(wl.t)])
+    xd, dzd = dev(x, "f32"), dev(dz, "f32")
+    dx_sum = None
+    for r in range(wl.t):
+        say(f"tiny_f32_t4 backward rank {r}")
+        ad, bd = dev(inputs.mlp_a_block(wl, r), "f32"), dev(inputs.mlp_b_block(wl, r), "f32")
+        bias_d = dev(inputs.mlp_bias_a_block(wl, r), "f32")
+        _z, y = run_fwd_save(wl, r, xd, ad, bd, bias_d)
+        ref = oracle.mlp_shard_bwd(x, a_full, b_full, dz, wl.t, r, bias_a=ba_full)
+        assert_close(to_np(y), ref["y"], "f32", f"tiny rank {r} saved pre-activation")
+        got = run_bwd(wl, r, xd, ad, bd, y, dzd, "f32")
+        check_grads(got, ref, "f32", f"tiny rank {r}")
+        dx = to_np(got["dx"])
+        dx_sum = dx if dx_sum is None else dx_sum + dx
+    full = oracle.mlp_shard_bwd(x, a_full, b_full, dz, 1, 0, bias_a=ba_full)
+    assert_close(dx_sum, full["dx"], "f32", "tiny sum over ranks of dX vs unsharded dX",
+                 rms_floor=True)
+
+
+def test_f32_ragged_tokens():
+    """fp32 takes any shape: 37 tokens."""
+    wl = inputs.MLP_WORKLOADS["tiny_f32_t4"]
+    x, dz = inputs.mlp_x_rows(wl, 0, 37), inputs.mlp_dz_rows(wl, 0, 37)
+    a, b = inputs.mlp_a_block(wl, 2), inputs.mlp_b_block(wl, 2)
+    ref = shard_ref(x, a, b, dz)
+    say("tiny_f32_t4 rank 2, 37 tokens")
+    got = run_bwd(wl, 2, dev(x, "f32"), dev(a, "f32"), dev(b, "f32"), dev(ref["y"].astype(np.float32), "f32"),
+                  dev(dz, "f32"), "f32")
+    check_grads(got, ref, "f32", "ragged f32")
+
+
+@pytest.mark.parametrize("grad_dt", ["f32", "bf16"])
+def test_t1_bf16(grad_dt):
+    wl = inputs.MLP_WORKLOADS["t1_h1024_m2048"]
+    x, dz = inputs.mlp_x_rows(wl), inputs.mlp_dz_rows(wl)
+    a, b = inputs.mlp_a_block(wl, 0), inputs.mlp_b_block(wl, 0)
+    xd, ad, bd = dev(x, "bf16"), dev(a, "bf16"), dev(b, "bf16")
+    say(f"t1_h1024_m2048 backward, grads {grad_dt}")
+    _z, y = run_fwd_save(wl, 0, xd, ad, bd)
+    ref = shard_ref(host64(x, "bf16"), host64(a, "bf16"), host64(b, "bf16"), host64(dz, "bf16"))
+    assert_close(to_np(y), ref["y"], "bf16", "t1 saved pre-activation")
+    got = run_bwd(wl, 0, xd, ad, bd, y, dev(dz, "bf16"), grad_dt)
+    check_grads(got, ref, "bf16", f"t1 grads {grad_dt}")
+
+
+def test_t4_all_ranks_strided_weight_views_and_reconstruction():
+    """A_i and dA_i as column-block views of the full [h, F] tensors (ld = F):
+    the rank writes only its block.  The ranks' dX contributions sum to the
+    unsharded dX."""
+    wl = inputs.MLP_WORKLOADS["t4_h1024_m1024"]
+    x, dz = inputs.mlp_x_rows(wl), inputs.mlp_dz_rows(wl)
+    a_blocks = [inputs.mlp_a_block(wl, r) for r in range(wl.t)]
+    b_blocks = [inputs.mlp_b_block(wl, r) for r in range(wl.t)]
+    xd, dzd = dev(x, "bf16"), dev(dz, "bf16")
+    a_full_d = dev(np.concatenate(a_blocks, axis=1), "bf16")
+    da_full = nan_tensor((wl.hidden, wl.ffn), torch.float32)
+    x64, dz64 = host64(x, "bf16"), host64(dz, "bf16")
+    dx_sum = None
+    for r in range(wl.t):
+        say(f"t4_h1024_m1024 backward rank {r} (strided A_i / dA_i)")
+        cols = slice(r * wl.f, (r + 1) * wl.f)
+        a_view = a_full_d[:, cols]
+        bd = dev(b_blocks[r], "bf16")
+        _z, y = run_fwd_save(wl, r, xd, a_view, bd)
+        got = run_bwd(wl, r, xd, a_view, bd, y, dzd, "f32", da=da_full[:, cols])
+        ref = shard_ref(x64, host64(a_blocks[r], "bf16"), host64(b_blocks[r], "bf16"), dz64)
+        check_grads(got, ref, "bf16", f"t4 rank {r}")
+        if r < wl.t - 1:
+            assert torch.isnan(da_full[:, (r + 1) * wl.f:]).all(), "dA columns of later ranks written"
+        dx = to_np(got["dx"])
+        dx_sum = dx if dx_sum is None else dx_sum + dx
+    a64 = host64(np.concatenate(a_blocks, axis=1), "bf16")
+    b64 = host64(np.concatenate(b_blocks, axis=0), "bf16")
+    full = oracle.mlp_shard_bwd(x64, a64, b64, dz64, 1, 0)
+    assert_close(to_np(da_full), full["da"], "bf16", "t4 assembled dA vs unsharded dA", rms_floor=True)
+    mx, fro = errors(dx_sum, full["dx"])
+    say(f"t4 sum over ranks of dX vs unsharded: rel-fro {fro:.3e} (<= {BF16_FRO}), max {mx:.3e} (reported)")
+    assert fro <= BF16_FRO
+
+
+@pytest.mark.parametrize("name,rank", [("t8_h8192_m4096", 0), ("t8_h8192_m4096", 5),
+                                       ("t8_h8192_m16384", 3)])
+def test_large_rank_shards(name, rank):
+    wl = inputs.MLP_WORKLOADS[name]
+    x, dz = inputs.mlp_x_rows(wl), inputs.mlp_dz_rows(wl)
+    a, b = inputs.mlp_a_block(wl, rank), inputs.mlp_b_block(wl, rank)
+    xd, ad, bd = dev(x, "bf16"), dev(a, "bf16"), dev(b, "bf16")
+    say(f"{name} backward rank {rank}")
+    _z, y = run_fwd_save(wl, rank, xd, ad, bd)
+    got = run_bwd(wl, rank, xd, ad, bd, y, dev(dz, "bf16"), "f32")
+    del xd, ad, bd
+    ref = shard_ref(host64(x, "bf16"), host64(a, "bf16"), host64(b, "bf16"), host64(dz, "bf16"))
+    check_grads(got, ref, "bf16", f"{name} rank {rank}")
+
+
+def test_zero_tokens_and_errors():
+    wl = inputs.MLP_WORKLOADS["t4_h1024_m1024"]
+    ad = dev(inputs.mlp_a_block(wl, 0), "bf16")
+    bd = dev(inputs.mlp_b_block(wl, 0), "bf16")
+    empty = torch.empty((0, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    y0 = torch.empty((0, wl.f), dtype=torch.bfloat16, device="cuda")
+    say("backward with tokens = 0")
+    got = run_bwd(wl, 0, empty, ad, bd, y0, empty, "f32")
+    for k in ("da", "db", "dbias_a", "dbias_b"):
+        assert (got[k] == 0).all(), f"{k} must be zero for zero tokens"
+    # bf16 needs tile-aligned shapes: 300 tokens is refused before any launch
+    x = dev(inputs.mlp_x_rows(wl, 0, 300), "bf16")
+    y = torch.zeros((300, wl.f), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(binding.TpError, match="UNSUPPORTED"):
+        run_bwd(wl, 0, x, ad, bd, y, x, "f32")
