@@ -15,6 +15,9 @@ Also reported:
                 summaries when they match the current kernel source
   cpu_baseline  the fp64 CPU oracle on a bounded sample of rows of the same
                 shard, on this host's cores
+  backward      the MLP shard's backward (rank 0 of the same workload): dX_i,
+                dA_i, dB_i (fp32) and the first-layer bias gradient from dZ and
+                the saved pre-activation, through tp_mlp_shard_bwd
   attention     the head-local attention shard (hidden 8192, 64 heads of 128,
                 t = 8, one sequence of 4096 tokens, rank 0, non-causal): whole
                 shard through tp_attn_shard_fwd, its two projection GEMMs
@@ -42,7 +45,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/" + f for f in (
     "device_common.h", "gemm_bf16_impl.h", "gemm_bf16_dma.h", "gemm_bf16.hip",
-    "gemm_bf16_256_gelu.hip", "gemm_bf16_256_plain.hip", "attention.hip")]
+    "gemm_bf16_256_gelu.hip", "gemm_bf16_256_plain.hip", "gemm_bf16_256_nt.hip",
+    "gemm_bf16_256_tn.hip", "colsum.hip", "attention.hip")]
 
 
 def kernel_source_sha() -> str:
@@ -138,13 +142,13 @@ PROFILE_CMDS = {
 # fp32 output.
 _M, _H, _F = 16384, 8192, 4096          # MLP shard: tokens, hidden, f = ffn / t
 _S, _DL = 4096, 1024                    # attention shard: tokens, local width (8 heads x 128)
-_GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "
+_GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "   # then A k-major, B k-major, epilogue kind, fp32 out
 PROFILED = {
-    "column_gemm_gelu": (_GEMM + "true, false>", (_M // 256) * (_F // 256) * 512,
+    "column_gemm_gelu": (_GEMM + "false, true, 1, false>", (_M // 256) * (_F // 256) * 512,
                          2.0 * _M * _H * _F, 2 * (_M * _H + _H * _F + _M * _F),
                          "MLP rank shard, M=16384, h=8192, f=4096: X, A_i read, H_i written (bf16)",
                          "column_gemm_gelu_t8_h8192_m16384"),
-    "row_gemm": (_GEMM + "false, true>", (_M // 256) * (_H // 256) * 512,
+    "row_gemm": (_GEMM + "false, true, 0, true>", (_M // 256) * (_H // 256) * 512,
                  2.0 * _M * _F * _H, 2 * (_M * _F + _F * _H) + 4 * _M * _H,
                  "MLP rank shard, M=16384, h=8192, f=4096: H_i, B_i read (bf16), Z_i written (fp32)",
                  "row_gemm_t8_h8192_m16384"),
@@ -153,10 +157,25 @@ PROFILED = {
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K as "
                        "bf16 (hi, lo) pairs and V read once, O written (bf16)",
                        "attention_core_t8_h8192_s4096"),
-    "attn_out_gemm": (_GEMM + "false, true>", (_S // 256) * (_H // 256) * 512,
+    "attn_out_gemm": (_GEMM + "false, true, 0, true>", (_S // 256) * (_H // 256) * 512,
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
                       "attention rank shard output projection, M=4096, K=1024, N=8192 (fp32 out)",
                       "attn_out_gemm_t8_h8192_s4096"),
+    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false>", (_M // 256) * (_F // 256) * 512,
+                       2.0 * _M * _H * _F, 2 * (_M * _H + _F * _H + _M * _F) + 2 * 2 * _M * _F,
+                       "MLP shard backward dH = dZ B_i^T with dY_i = dH * GeLU'(Y_i) and H_i = "
+                       "GeLU(Y_i) in the epilogue: dZ, B_i, Y_i read, dY_i and H_i written (bf16)",
+                       "bwd_dgelu_gemm_t8_h8192_m16384"),
+    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true>", (_F // 256) * (_H // 256) * 512,
+                             2.0 * _M * _H * _F, 2 * (_M * _F + _M * _H) + 4 * _F * _H,
+                             "MLP shard backward weight gradients H_i^T dZ and X^T dY_i (one "
+                             "kernel, K = 16384 tokens): two bf16 operands read, fp32 [4096 x 8192] "
+                             "written; both launches averaged",
+                             "bwd_weight_grad_gemm_t8_h8192_m16384"),
+    "bwd_dx_gemm": (_GEMM + "false, false, 0, true>", (_M // 256) * (_H // 256) * 512,
+                    2.0 * _M * _F * _H, 2 * (_M * _F + _H * _F) + 4 * _M * _H,
+                    "MLP shard backward dX_i = dY_i A_i^T: dY_i, A_i read (bf16), dX_i written (fp32)",
+                    "bwd_dx_gemm_t8_h8192_m16384"),
 }
 COPY_KEY = ("copyBuffer", 1 << 30)    # the 1 GiB calibration copy
 
@@ -226,6 +245,55 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str) -> None:
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def bench_backward(wl, x, a0, b0, stream, reps: int):
+    """Time tp_mlp_shard_bwd on rank 0 of the MLP workload (inputs resident)."""
+    import torch
+    from megatron_tensor_transformer_tp_amd import binding, inputs
+
+    dev = x.device
+    dz = torch.from_numpy(inputs.mlp_dz_rows(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((wl.tokens, wl.f), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((wl.tokens, wl.hidden), dtype=torch.float32, device=dev)
+    fws = torch.empty(binding.tp_mlp_shard_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t,
+                                                           torch.bfloat16), dtype=torch.uint8, device=dev)
+    binding.tp_mlp_shard_fwd(x, a0, b0, z, fws, ffn=wl.ffn, t=wl.t, rank=0, y_save=y, stream=stream)
+    del z, fws
+    dx = torch.empty((wl.tokens, wl.hidden), dtype=torch.float32, device=dev)
+    da = torch.empty((wl.hidden, wl.f), dtype=torch.float32, device=dev)
+    db = torch.empty((wl.f, wl.hidden), dtype=torch.float32, device=dev)
+    dba = torch.empty((wl.f,), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.tp_mlp_shard_bwd_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t,
+                                                              torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def call():
+        binding.tp_mlp_shard_bwd(x, a0, b0, y, dz, dx, da, db, ws, ffn=wl.ffn, t=wl.t, rank=0,
+                                 dbias_a_i=dba, stream=stream)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    flops = 8.0 * wl.tokens * wl.hidden * wl.f
+    res = {
+        "workload": (f"{wl.name} rank 0: dH = dZ B_i^T with the GeLU-backward epilogue, "
+                     "dB_i = H_i^T dZ, dA_i = X^T dY_i, dX_i = dY_i A_i^T (fp32 gradients), "
+                     "first-layer bias gradient"),
+        "flops": int(flops),
+        "us": round(us, 2),
+        "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+        "pct_peak": round(100.0 * flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(wl.tokens / (us * 1e-6), 1),
+    }
+    log(f"backward shard {us:.1f} us ({res['tflops']} TFLOP/s)")
+    return res
 
 
 def bench_attention(stream, reps: int, name: str = "attn_t8_h8192_s4096"):
@@ -311,6 +379,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the attention-shard measurement")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the MLP-backward measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the bounded oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -418,6 +488,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log("calibration copy of 1 GiB x3 done")
 
+    backward = None if args.no_backward else bench_backward(wl, x, a[0], b[0], stream,
+                                                            args.kernel_reps)
     attention = None if args.no_attention else bench_attention(stream, args.kernel_reps)
 
     cpu = None
@@ -463,6 +535,7 @@ def main() -> int:
         "kernels": per_kernel,
         "kernel_source_sha": kernel_source_sha(),
         "cpu_baseline": cpu,
+        "backward": backward,
         "attention": attention,
     }
     print(json.dumps(result), flush=True)
