@@ -15,11 +15,12 @@ from .mlp import (ShardError, shard_width, shard_slice, gelu, column_linear, row
 from .attention import (softmax_rows, split_packed_qkv, mha_full, attn_shard, attn_partial_sum,
                         local_heads)
 from .brute import mlp_shard_loops, attention_head_loops
+from .sp import sp_shard_rows, sp_reduce_scatter
 
 __all__ = [
     "ShardError", "shard_width", "shard_slice", "gelu", "column_linear", "row_linear",
     "mlp_full", "mlp_shard", "mlp_partial_sum", "normal_pdf", "gelu_grad", "mlp_shard_bwd",
     "softmax_rows", "split_packed_qkv",
     "mha_full", "attn_shard", "attn_partial_sum", "local_heads", "mlp_shard_loops",
-    "attention_head_loops",
+    "attention_head_loops", "sp_shard_rows", "sp_reduce_scatter",
 ]

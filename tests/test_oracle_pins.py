@@ -416,3 +416,36 @@ def test_mlp_backward_partition_identity():
         parts = _assembled_grads(x, a, b, ba, dz, t)
         for name in full:
             np.testing.assert_allclose(parts[name], full[name], rtol=1e-12, atol=1e-12)
+
+
+# ---- sequence-parallel boundary (Megatron Level 2, M034) ----
+
+def test_sp_shards_gather_to_the_layer_output():
+    """Reduce-scatter then gather = the summed output: the shards of the t
+    partials, stacked in rank order, equal GeLU(X A + a) B + b + R."""
+    rng = np.random.default_rng(50)
+    tokens, hidden, ffn, t = 12, 6, 16, 4
+    x, a, b = rng.standard_normal((tokens, hidden)), rng.standard_normal((hidden, ffn)), \
+        rng.standard_normal((ffn, hidden))
+    ba, bb, res = rng.standard_normal(ffn), rng.standard_normal(hidden), rng.standard_normal((tokens, hidden))
+    parts = [oracle.mlp_shard(x, a, b, t, r, bias_a=ba) for r in range(t)]
+    shards = [oracle.sp_reduce_scatter(parts, t, r, bias=bb,
+                                       residual_r=res[oracle.sp_shard_rows(tokens, t, r)])
+              for r in range(t)]
+    np.testing.assert_allclose(np.concatenate(shards, axis=0),
+                               oracle.mlp_full(x, a, b, ba, bb, res), rtol=1e-12, atol=1e-12)
+
+
+def test_sp_reduce_scatter_by_hand():
+    """Two ranks, four tokens, one column: each rank sums its two rows."""
+    p0 = np.array([[1.0], [2.0], [3.0], [4.0]])
+    p1 = np.array([[10.0], [20.0], [30.0], [40.0]])
+    assert oracle.sp_reduce_scatter([p0, p1], 2, 0).tolist() == [[11.0], [22.0]]
+    assert oracle.sp_reduce_scatter([p0, p1], 2, 1, bias=[0.5]).tolist() == [[33.5], [44.5]]
+
+
+def test_sp_rejects_tokens_not_divisible():
+    with pytest.raises(oracle.ShardError):
+        oracle.sp_shard_rows(10, 4, 0)
+    with pytest.raises(oracle.ShardError):
+        oracle.sp_shard_rows(8, 4, 4)
