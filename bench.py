@@ -18,6 +18,9 @@ Also reported:
   backward      the MLP shard's backward (rank 0 of the same workload): dX_i,
                 dA_i, dB_i (fp32) and the first-layer bias gradient from dZ and
                 the saved pre-activation, through tp_mlp_shard_bwd
+  sp_boundary   the sequence-parallel reduce-scatter of the step's 8 fp32
+                partials into each rank's [M/8, h] shard with bias and
+                residual rows (HBM-bound: GB/s against 8 TB/s)
   attention     the head-local attention shard (hidden 8192, 64 heads of 128,
                 t = 8, one sequence of 4096 tokens, rank 0, non-causal): whole
                 shard through tp_attn_shard_fwd, its two projection GEMMs
@@ -42,11 +45,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s + % bf16 MFMA peak, t=8 MLP shard (h=8192, 16384 tok), 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/" + f for f in (
     "device_common.h", "gemm_bf16_impl.h", "gemm_bf16_dma.h", "gemm_bf16.hip",
     "gemm_bf16_256_gelu.hip", "gemm_bf16_256_plain.hip", "gemm_bf16_256_nt.hip",
-    "gemm_bf16_256_tn.hip", "colsum.hip", "attention.hip")]
+    "gemm_bf16_256_tn.hip", "colsum.hip", "sp_reduce.hip", "attention.hip")]
 
 
 def kernel_source_sha() -> str:
@@ -161,6 +165,12 @@ PROFILED = {
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
                       "attention rank shard output projection, M=4096, K=1024, N=8192 (fp32 out)",
                       "attn_out_gemm_t8_h8192_s4096"),
+    "sp_reduce_scatter": ("sp_reduce_kernel<unsigned short, unsigned short, true, true>", 8192 * 256,
+                          0.0, 8 * (_M // 8) * _H * 4 + 2 * (_M // 8) * _H * 2 + 2 * _H,
+                          "sequence-parallel reduce-scatter of the 8 fp32 MLP partials into one "
+                          "rank's [2048, 8192] shard with bf16 bias and residual rows, bf16 out "
+                          "(HBM-bound: partial rows, residual and bias read, shard written)",
+                          "sp_reduce_scatter_t8_h8192_m16384"),
     "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false>", (_M // 256) * (_F // 256) * 512,
                        2.0 * _M * _H * _F, 2 * (_M * _H + _F * _H + _M * _F) + 2 * 2 * _M * _F,
                        "MLP shard backward dH = dZ B_i^T with dY_i = dH * GeLU'(Y_i) and H_i = "
@@ -233,9 +243,12 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str) -> None:
               f"| dispatches in the trace run | {len(us)} |",
               f"| average duration | {avg_us:.1f} us |",
               f"| median / min / max duration | {statistics.median(us):.1f} / {min(us):.1f} / {max(us):.1f} us |",
-              f"| algorithmic FLOP per launch | {flops / 1e9:.1f} G |",
-              f"| achieved (algorithmic FLOP / avg duration) | {flops / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s "
-              f"({100 * flops / (avg_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS}) |",
+              *([f"| algorithmic FLOP per launch | {flops / 1e9:.1f} G |",
+                 f"| achieved (algorithmic FLOP / avg duration) | {flops / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s "
+                 f"({100 * flops / (avg_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS}) |"]
+                if flops else
+                [f"| achieved (algorithmic bytes / avg duration) | {alg_bytes / (avg_us * 1e-6) / 1e9:.0f} GB/s "
+                 f"({100 * alg_bytes / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f}) |"]),
               f"| FETCH_SIZE per dispatch (median) | {fetch[key]:.0f} KiB (x{f_scale:.3f} from the 1 GiB copy) |",
               f"| WRITE_SIZE per dispatch (median) | {write[key]:.0f} KiB (x{w_scale:.3f}) |",
               f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.1f} MB (fetch {fb / 1e6:.1f}, write {wb / 1e6:.1f}) |",
@@ -245,6 +258,44 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str) -> None:
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def bench_sp(wl, z, stream, reps: int):
+    """Time tp_sp_reduce_scatter over the step's t partials, every rank in
+    turn, bf16 bias / residual rows / output."""
+    import torch
+    from megatron_tensor_transformer_tp_amd import binding, inputs
+
+    dev = z[0].device
+    rows = wl.tokens // wl.t
+    bias = torch.from_numpy(inputs.mlp_bias_b(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    res = torch.from_numpy(inputs.mlp_residual_rows(wl, 0, rows).view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty((rows, wl.hidden), dtype=torch.bfloat16, device=dev)
+
+    def call(r):
+        binding.tp_sp_reduce_scatter(z, out, t=wl.t, rank=r, bias=bias, residual_r=res, stream=stream)
+
+    for r in range(wl.t):
+        call(r)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps * wl.t):
+        call(i % wl.t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * wl.t)
+    nbytes = wl.t * rows * wl.hidden * 4 + 2 * rows * wl.hidden * 2 + 2 * wl.hidden
+    res_d = {
+        "workload": (f"{wl.name}: one rank's sequence shard [{rows}, {wl.hidden}] of the sum of the "
+                     f"{wl.t} fp32 partials, bf16 bias / residual rows / output"),
+        "us": round(us, 2),
+        "algorithmic_bytes": int(nbytes),
+        "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+        "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+    log(f"sp reduce-scatter {us:.1f} us per rank ({res_d['gbs']} GB/s)")
+    return res_d
 
 
 def bench_backward(wl, x, a0, b0, stream, reps: int):
@@ -488,6 +539,7 @@ def main() -> int:
         torch.cuda.synchronize()
         log("calibration copy of 1 GiB x3 done")
 
+    sp_boundary = bench_sp(wl, z, stream, args.kernel_reps)
     backward = None if args.no_backward else bench_backward(wl, x, a[0], b[0], stream,
                                                             args.kernel_reps)
     attention = None if args.no_attention else bench_attention(stream, args.kernel_reps)
@@ -535,6 +587,7 @@ def main() -> int:
         "kernels": per_kernel,
         "kernel_source_sha": kernel_source_sha(),
         "cpu_baseline": cpu,
+        "sp_boundary": sp_boundary,
         "backward": backward,
         "attention": attention,
     }

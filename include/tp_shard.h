@@ -31,6 +31,10 @@
  *     ranks (Megatron Level 2, M025); for the row layer the input gradient
  *     dZ B_i^T is already the rank's input-block gradient and the weight
  *     gradient is local (Megatron Level 2, M026).
+ *   - Sequence-parallel boundary: the row-parallel partials are summed by a
+ *     Reduce-Scatter that leaves each rank its sequence shard [s/t, b, h],
+ *     on which per-token work (bias, residual) runs locally: Megatron
+ *     Level 2, M034.
  *   - Shapes that do not divide are rejected, never padded: 列并行 tutorial,
  *     切分原理; Megatron Level 2, M031.
  *
@@ -225,6 +229,27 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
                             int64_t batch, int64_t seq, int64_t hidden, int64_t heads,
                             int64_t head_dim, int causal, int t, int rank,
                             tp_dtype in_dt, tp_dtype out_dt, void* stream);
+
+/*
+ * Sequence-parallel boundary on one device: the SUM Reduce-Scatter half of
+ * the exchange, fused with the shard's bias and residual.  Rank `rank`
+ * receives its sequence shard of the summed output,
+ *   out_r[m, :] = sum_{j < t} Z_j[rank*M/t + m, :] + bias + residual_r[m, :],
+ * m < M/t, M = tokens (rows ordered sequence-major, so the shard is the
+ * contiguous row block [rank*M/t, (rank+1)*M/t)).
+ *   partials    HOST array of t DEVICE pointers; partials[j] is rank j's
+ *               partial Z_j [tokens, hidden] contiguous, fp32
+ *   bias        [hidden] or NULL                         (in_dt)
+ *   residual_r  [tokens/t, hidden] contiguous or NULL: the rank's rows of
+ *               the (sequence-sharded) residual stream   (in_dt)
+ *   out_r       [tokens/t, hidden] contiguous            (out_dt)
+ * The partials are summed in rank order in fp32 (deterministic).
+ * tokens % t != 0 -> TP_ERR_NOT_DIVISIBLE; t > 16 -> TP_ERR_UNSUPPORTED;
+ * hidden must be a multiple of 4.  in_dt, out_dt: f32 or bf16 (any pair).
+ */
+tp_status tp_sp_reduce_scatter(const void* const* partials, int t, int rank, const void* bias,
+                               const void* residual_r, void* out_r, int64_t tokens,
+                               int64_t hidden, tp_dtype in_dt, tp_dtype out_dt, void* stream);
 
 #ifdef __cplusplus
 }

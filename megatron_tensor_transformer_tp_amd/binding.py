@@ -41,6 +41,7 @@ SIGNATURES = {
     "tp_mlp_shard_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "tp_mlp_shard_bwd": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                                 _I64, _I64, _I64, _INT, _INT, _INT, _INT, _VP]),
+    "tp_sp_reduce_scatter": (_INT, [_VP, _INT, _INT, _VP, _VP, _VP, _I64, _I64, _INT, _INT, _VP]),
     "tp_attn_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I64, _INT, _INT]),
     "tp_attn_shard_fwd": (_INT, [_VP, _VP, _VP, _VP, _VP, _SZ, _I64, _I64, _I64, _I64, _I64,
                                  _INT, _INT, _INT, _INT, _INT, _VP]),
@@ -213,3 +214,23 @@ def tp_attn_shard_fwd(x: torch.Tensor, wqkv_i: torch.Tensor, wo_i: torch.Tensor,
                                    rank, _dt(x), _dt(out_i), _stream(stream)),
            "tp_attn_shard_fwd")
     return out_i
+
+
+def tp_sp_reduce_scatter(partials, out_r: torch.Tensor, *, t: int, rank: int,
+                         bias: Optional[torch.Tensor] = None,
+                         residual_r: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out_r <- rank's sequence shard of sum(partials) (+ bias + residual_r)."""
+    if len(partials) != t:
+        raise ValueError(f"{len(partials)} partials for t={t}")
+    tokens, hidden = partials[0].shape
+    for name, ten in [("out_r", out_r), ("residual_r", residual_r)] + \
+            [(f"partials[{j}]", p) for j, p in enumerate(partials)]:
+        if ten is not None and not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    in_ref = bias if bias is not None else residual_r
+    ptrs = (ctypes.c_void_p * t)(*[p.data_ptr() for p in partials])
+    _check(lib().tp_sp_reduce_scatter(ptrs, t, rank, _ptr(bias), _ptr(residual_r), _ptr(out_r),
+                                      tokens, hidden, _dt(in_ref) if in_ref is not None else TP_F32,
+                                      _dt(out_r), _stream(stream)),
+           "tp_sp_reduce_scatter")
+    return out_r

@@ -31,6 +31,7 @@ SOURCES = [
     "gemm_bf16_256_tn.hip",
     "gemm_f32.hip",
     "colsum.hip",
+    "sp_reduce.hip",
     "gelu.hip",
     "attention.hip",
 ]

@@ -82,6 +82,18 @@ hipError_t launch_attention(const uint16_t* qkv_hi, const uint16_t* qkv_lo, int6
                             uint16_t* o, int64_t ld_o, int batch, int seq, int heads,
                             int head_dim, bool causal, hipStream_t stream);
 
+// Sequence-parallel reduce-scatter on one device: out[m, :] = sum_{j < t}
+// parts.p[j][row0 + m, :] (+ bias) (+ residual[m, :]) for m < rows; partials
+// fp32 [*, hidden] contiguous; bias / residual in in_dt, out in out_dt
+// (0 = f32, 1 = bf16); hidden % 4 == 0, 16-byte aligned pointers.
+constexpr int kSpMaxParts = 16;
+struct SpPartials {
+  const float* p[kSpMaxParts];
+};
+hipError_t launch_sp_reduce(const SpPartials& parts, int t, int64_t row0, int64_t rows,
+                            int64_t hidden, const void* bias, const void* residual, int in_dt,
+                            void* out, int out_dt, hipStream_t stream);
+
 // out[k] = GeLU(in[k]), dtypes 0 = f32, 1 = bf16.
 hipError_t launch_gelu(const void* in, void* out, int64_t n, int in_dt, int out_dt,
                        hipStream_t stream);

@@ -386,4 +386,31 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
   return run_gemm(in_dt, o, dl, wo_i, hidden, tokens, hidden, dl, ep3, s);
 }
 
+tp_status tp_sp_reduce_scatter(const void* const* partials, int t, int rank, const void* bias,
+                               const void* residual_r, void* out_r, int64_t tokens,
+                               int64_t hidden, tp_dtype in_dt, tp_dtype out_dt, void* stream) {
+  if (!dtype_known(in_dt) || !dtype_known(out_dt)) return TP_ERR_DTYPE;
+  if (t < 1 || rank < 0 || rank >= t) return TP_ERR_BAD_RANK;
+  if (t > tpk::kSpMaxParts) return TP_ERR_UNSUPPORTED;
+  if (tokens < 0 || hidden < 1 || partials == nullptr) return TP_ERR_INVALID_ARG;
+  if (tokens % t != 0) return TP_ERR_NOT_DIVISIBLE;
+  if (hidden % 4 != 0) return TP_ERR_MISALIGNED;
+  if (!fits_int32(hidden)) return TP_ERR_UNSUPPORTED;
+  if (tokens == 0) return TP_OK;
+  tpk::SpPartials parts{};
+  for (int j = 0; j < t; ++j) {
+    if (partials[j] == nullptr) return TP_ERR_INVALID_ARG;
+    if (!aligned16(partials[j])) return TP_ERR_MISALIGNED;
+    parts.p[j] = static_cast<const float*>(partials[j]);
+  }
+  if (out_r == nullptr) return TP_ERR_INVALID_ARG;
+  if (!aligned16(out_r)) return TP_ERR_MISALIGNED;
+  TP_TRY(check_optional_vec(bias));
+  TP_TRY(check_optional_vec(residual_r));
+  const int64_t rows = tokens / t;
+  return from_hip(tpk::launch_sp_reduce(parts, t, rank * rows, rows, hidden, bias, residual_r,
+                                        in_dt == TP_BF16 ? 1 : 0, out_r, out_dt == TP_BF16 ? 1 : 0,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

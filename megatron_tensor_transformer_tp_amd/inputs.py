@@ -49,7 +49,7 @@ __all__ = [
 X_ROW_CHUNK = 256
 
 _TENSOR_IDS = {"x": 0, "a": 1, "b": 2, "wqkv": 3, "wo": 4, "residual": 5,
-               "bias_a": 6, "bias_b": 7, "dz": 8}
+               "bias_a": 6, "bias_b": 7, "dz": 8, "partial": 9}
 
 
 @dataclasses.dataclass(frozen=True)

@@ -215,3 +215,26 @@ def test_product_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), fn
                 assert "oracle." not in text.replace("the oracle.", ""), fn
+
+
+def sp(lib, t=4, parts=None, **kw):
+    a = dict(rank=0, bias=None, res=None, out=P, tokens=256, hidden=1024, in_dt=BF16, out_dt=F32)
+    a.update(kw)
+    ptrs = (ctypes.c_void_p * max(t, 1))(*(parts if parts is not None else [P + 4096 * j for j in range(t)]))
+    return lib.tp_sp_reduce_scatter(ptrs, t, a["rank"], a["bias"], a["res"], a["out"], a["tokens"],
+                                    a["hidden"], a["in_dt"], a["out_dt"], None)
+
+
+def test_sp_reduce_scatter_validation(lib):
+    assert sp(lib, t=0, parts=[P]) == BAD_RANK
+    assert sp(lib, rank=4) == BAD_RANK
+    assert sp(lib, t=17) == UNSUPPORTED
+    assert sp(lib, tokens=250) == NOT_DIV
+    assert sp(lib, hidden=1022) == MISALIGNED
+    assert sp(lib, in_dt=5) == DTYPE
+    assert sp(lib, parts=[P, None, P, P]) == INVALID
+    assert sp(lib, parts=[P, P + 8, P, P]) == MISALIGNED
+    assert sp(lib, out=None) == INVALID                 # every partial passed its checks
+    assert sp(lib, bias=P + 2, out=P) == MISALIGNED
+    assert sp(lib, tokens=0) == OK
+    assert lib.tp_sp_reduce_scatter(None, 4, 0, None, None, P, 256, 1024, BF16, F32, None) == INVALID
