@@ -14,13 +14,15 @@ from .mlp import (ShardError, shard_width, shard_slice, gelu, column_linear, row
                   mlp_full, mlp_shard, mlp_partial_sum, normal_pdf, gelu_grad, mlp_shard_bwd)
 from .attention import (softmax_rows, split_packed_qkv, mha_full, attn_shard, attn_partial_sum,
                         local_heads)
-from .brute import mlp_shard_loops, attention_head_loops
+from .brute import mlp_shard_loops, attention_head_loops, swiglu_shard_loops
 from .sp import sp_shard_rows, sp_reduce_scatter
+from .swiglu import silu, swiglu_mlp_full, swiglu_mlp_shard
 
 __all__ = [
     "ShardError", "shard_width", "shard_slice", "gelu", "column_linear", "row_linear",
     "mlp_full", "mlp_shard", "mlp_partial_sum", "normal_pdf", "gelu_grad", "mlp_shard_bwd",
     "softmax_rows", "split_packed_qkv",
     "mha_full", "attn_shard", "attn_partial_sum", "local_heads", "mlp_shard_loops",
-    "attention_head_loops", "sp_shard_rows", "sp_reduce_scatter",
+    "attention_head_loops", "sp_shard_rows", "sp_reduce_scatter", "silu", "swiglu_mlp_full",
+    "swiglu_mlp_shard", "swiglu_shard_loops",
 ]

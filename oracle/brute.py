@@ -71,3 +71,22 @@ def attention_head_loops(q, k, v, causal=False):
             row.append(acc / tot)
         out.append(row)
     return out
+
+
+def swiglu_shard_loops(x, wg, wu, b, t, rank):
+    """Rank ``rank``'s SwiGLU partial with explicit loops and math.exp."""
+    tokens, hidden = len(x), len(x[0])
+    ffn = len(wg[0])
+    f = ffn // t
+    cols = range(rank * f, (rank + 1) * f)
+    out_w = len(b[0])
+    z = [[0.0] * out_w for _ in range(tokens)]
+    for m in range(tokens):
+        h = []
+        for c in cols:
+            g = sum(x[m][k] * wg[k][c] for k in range(hidden))
+            u = sum(x[m][k] * wu[k][c] for k in range(hidden))
+            h.append(g / (1.0 + math.exp(-g)) * u)
+        for n in range(out_w):
+            z[m][n] = sum(h[j] * b[c][n] for j, c in enumerate(cols))
+    return z

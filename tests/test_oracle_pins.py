@@ -449,3 +449,54 @@ def test_sp_rejects_tokens_not_divisible():
         oracle.sp_shard_rows(10, 4, 0)
     with pytest.raises(oracle.ShardError):
         oracle.sp_shard_rows(8, 4, 4)
+
+
+# ---- SwiGLU variant (Megatron Level 2, M027 / M031) ----
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    z = np.linspace(-30, 30, 121)
+    # sigma(z) + sigma(-z) = 1  =>  SiLU(z) - SiLU(-z) = z
+    np.testing.assert_allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=0, atol=1e-13)
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-12 and abs(oracle.silu(-40.0)) < 1e-15
+    # mpmath at 50 digits
+    mpmath.mp.dps = 50
+    for v in (-3.7, -0.2, 0.9, 5.5):
+        assert abs(oracle.silu(v) - float(v / (1 + mpmath.e ** (-v)))) < 1e-15
+
+
+def test_swiglu_partition_identity_and_pairing():
+    """sum over ranks of the paired shards = the unsharded gated MLP; pairing
+    the gate block of one rank with the value block of another breaks it."""
+    rng = np.random.default_rng(60)
+    x = rng.standard_normal((7, 8))
+    wg, wu = rng.standard_normal((8, 24)), rng.standard_normal((8, 24))
+    b = rng.standard_normal((24, 8))
+    bb, res = rng.standard_normal(8), rng.standard_normal((7, 8))
+    full = oracle.swiglu_mlp_full(x, wg, wu, b, bb, res)
+    for t in (1, 2, 3, 4, 6):
+        total = sum(oracle.swiglu_mlp_shard(x, wg, wu, b, t, r, bb, res) for r in range(t))
+        np.testing.assert_allclose(total, full, rtol=1e-12, atol=1e-12)
+    # negative control: value columns of the neighbouring block
+    wu_shift = np.concatenate([wu[:, 6:], wu[:, :6]], axis=1)
+    bad = sum(oracle.swiglu_mlp_shard(x, wg, wu_shift, b, 4, r, bb, res) for r in range(4))
+    assert not np.allclose(bad, full, rtol=1e-6, atol=1e-6)
+
+
+def test_swiglu_brute_force():
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((3, 5))
+    wg, wu = rng.standard_normal((5, 6)), rng.standard_normal((5, 6))
+    b = rng.standard_normal((6, 4))
+    for r in range(3):
+        np.testing.assert_allclose(oracle.swiglu_mlp_shard(x, wg, wu, b, 3, r),
+                                   np.array(oracle.swiglu_shard_loops(x.tolist(), wg.tolist(),
+                                                                      wu.tolist(), b.tolist(), 3, r)),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_swiglu_rejects_undivisible():
+    x = np.zeros((2, 4))
+    with pytest.raises(oracle.ShardError):
+        oracle.swiglu_mlp_shard(x, np.zeros((4, 10)), np.zeros((4, 10)), np.zeros((10, 4)), 4, 0)
