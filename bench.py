@@ -18,6 +18,8 @@ Also reported:
   backward      the MLP shard's backward (rank 0 of the same workload): dX_i,
                 dA_i, dB_i (fp32) and the first-layer bias gradient from dZ and
                 the saved pre-activation, through tp_mlp_shard_bwd
+  swiglu        the SwiGLU variant of the same MLP shard (rank 0): gate and
+                value projections of width f each, through tp_mlp_swiglu_shard_fwd
   sp_boundary   the sequence-parallel reduce-scatter of the step's 8 fp32
                 partials into each rank's [M/8, h] shard with bias and
                 residual rows (HBM-bound: GB/s against 8 TB/s)
@@ -50,7 +52,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/" + f for f in (
     "device_common.h", "gemm_bf16_impl.h", "gemm_bf16_dma.h", "gemm_bf16.hip",
     "gemm_bf16_256_gelu.hip", "gemm_bf16_256_plain.hip", "gemm_bf16_256_nt.hip",
-    "gemm_bf16_256_tn.hip", "colsum.hip", "sp_reduce.hip", "attention.hip")]
+    "gemm_bf16_256_tn.hip", "gemm_bf16_256_swiglu.hip", "colsum.hip", "sp_reduce.hip", "attention.hip")]
 
 
 def kernel_source_sha() -> str:
@@ -171,6 +173,11 @@ PROFILED = {
                           "rank's [2048, 8192] shard with bf16 bias and residual rows, bf16 out "
                           "(HBM-bound: partial rows, residual and bias read, shard written)",
                           "sp_reduce_scatter_t8_h8192_m16384"),
+    "swiglu_gemm": (_GEMM + "false, true, 3, false>", (_M // 256) * (2 * _F // 256) * 512,
+                    2.0 * _M * _H * 2 * _F, 2 * (_M * _H + 2 * _H * _F + _M * _F),
+                    "SwiGLU column layer, both projections in one product with SiLU(gate) * value "
+                    "in the epilogue: X, Wg_i, Wu_i read, H_i written (bf16)",
+                    "swiglu_gemm_t8_h8192_m16384"),
     "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false>", (_M // 256) * (_F // 256) * 512,
                        2.0 * _M * _H * _F, 2 * (_M * _H + _F * _H + _M * _F) + 2 * 2 * _M * _F,
                        "MLP shard backward dH = dZ B_i^T with dY_i = dH * GeLU'(Y_i) and H_i = "
@@ -258,6 +265,47 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str) -> None:
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def bench_swiglu(wl, x, b0, stream, reps: int):
+    """Time tp_mlp_swiglu_shard_fwd on rank 0 of the MLP workload."""
+    import torch
+    from megatron_tensor_transformer_tp_amd import binding, inputs
+
+    dev = x.device
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    wg, wu = up(inputs.mlp_wg_block(wl, 0)), up(inputs.mlp_wu_block(wl, 0))
+    z = torch.empty((wl.tokens, wl.hidden), dtype=torch.float32, device=dev)
+    ws = torch.empty(binding.tp_mlp_swiglu_shard_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t,
+                                                                 torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def call():
+        binding.tp_mlp_swiglu_shard_fwd(x, wg, wu, b0, z, ws, ffn=wl.ffn, t=wl.t, rank=0, stream=stream)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    flops = 6.0 * wl.tokens * wl.hidden * wl.f
+    res = {
+        "workload": (f"{wl.name} rank 0, SwiGLU: H_i = SiLU(X Wg_i) * (X Wu_i) (one product over "
+                     f"both [{wl.hidden}, {wl.f}] projections), Z_i = H_i B_i, fp32 partial"),
+        "flops": int(flops),
+        "us": round(us, 2),
+        "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+        "pct_peak": round(100.0 * flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+    }
+    log(f"swiglu shard {us:.1f} us ({res['tflops']} TFLOP/s)")
+    return res
 
 
 def bench_sp(wl, z, stream, reps: int):
@@ -540,6 +588,7 @@ def main() -> int:
         log("calibration copy of 1 GiB x3 done")
 
     sp_boundary = bench_sp(wl, z, stream, args.kernel_reps)
+    swiglu = bench_swiglu(wl, x, b[0], stream, args.kernel_reps)
     backward = None if args.no_backward else bench_backward(wl, x, a[0], b[0], stream,
                                                             args.kernel_reps)
     attention = None if args.no_attention else bench_attention(stream, args.kernel_reps)
@@ -587,6 +636,7 @@ def main() -> int:
         "kernels": per_kernel,
         "kernel_source_sha": kernel_source_sha(),
         "cpu_baseline": cpu,
+        "swiglu": swiglu,
         "sp_boundary": sp_boundary,
         "backward": backward,
         "attention": attention,

@@ -26,6 +26,8 @@
  *   - Attention shard: heads split over ranks, packed QKV interleaved per
  *     head, local softmax(Q K^T / sqrt(d)) V, row-parallel output projection:
  *     Tencent write-up, attention paragraph; Megatron Level 2, M028.
+ *   - SwiGLU variant: the gated activation acts on paired local shards of
+ *     the two projections (Megatron Level 2, M027, M031).
  *   - Backward: for the column layer the weight gradient X^T dY_i is local
  *     and the input-gradient contributions dY_i A_i^T are summed over the
  *     ranks (Megatron Level 2, M025); for the row layer the input gradient
@@ -160,6 +162,37 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
                            void* z_i, void* y_save, void* workspace, size_t workspace_bytes,
                            int64_t tokens, int64_t hidden, int64_t ffn, int t, int rank,
                            tp_dtype in_dt, tp_dtype out_dt, void* stream);
+
+/*
+ * Bytes of workspace tp_mlp_swiglu_shard_fwd needs: H_i [tokens, f] in in_dt
+ * (fp32 inputs: also the two gated projections), rounded up to 256 bytes;
+ * 0 if invalid.
+ */
+size_t tp_mlp_swiglu_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int t,
+                                           tp_dtype in_dt);
+
+/*
+ * One rank's SwiGLU MLP shard (the gated variant of the MLP; Megatron
+ * Level 2, M027: the gate acts on paired local shards, no other rank is
+ * needed; M031: both projections are split, each must divide):
+ *   H_i = SiLU(X Wg_i) * (X Wu_i),  SiLU(z) = z / (1 + exp(-z)),
+ *   Z_i = H_i B_i (+ b + R on rank 0).
+ *   x         [tokens, hidden] contiguous                  (in_dt)
+ *   wg_i      [hidden, f], ld lda: the rank's column block of the gate
+ *             projection                                   (in_dt)
+ *   wu_i      [hidden, f], ld lda: the SAME columns of the value
+ *             projection                                   (in_dt)
+ *   b_i       [f, hidden] contiguous                       (in_dt)
+ *   bias_b, residual, z_i, workspace: as for tp_mlp_shard_fwd.
+ * f = ffn / t with ffn the width of each projection.  bf16 inputs: tokens a
+ * multiple of 256, f of 128 and hidden of 32 (TP_ERR_UNSUPPORTED
+ * otherwise); fp32: any shape.  dtype pairs as for tp_mlp_shard_fwd.
+ */
+tp_status tp_mlp_swiglu_shard_fwd(const void* x, const void* wg_i, const void* wu_i, int64_t lda,
+                                  const void* b_i, const void* bias_b, const void* residual,
+                                  void* z_i, void* workspace, size_t workspace_bytes,
+                                  int64_t tokens, int64_t hidden, int64_t ffn, int t, int rank,
+                                  tp_dtype in_dt, tp_dtype out_dt, void* stream);
 
 /*
  * Bytes of workspace tp_mlp_shard_bwd needs: dY_i and H_i [tokens, f] in

@@ -38,6 +38,9 @@ SIGNATURES = {
     "tp_mlp_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "tp_mlp_shard_fwd": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I64,
                                 _I64, _I64, _INT, _INT, _INT, _INT, _VP]),
+    "tp_mlp_swiglu_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
+    "tp_mlp_swiglu_shard_fwd": (_INT, [_VP, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _SZ, _I64,
+                                       _I64, _I64, _INT, _INT, _INT, _INT, _VP]),
     "tp_mlp_shard_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "tp_mlp_shard_bwd": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                                 _I64, _I64, _I64, _INT, _INT, _INT, _INT, _VP]),
@@ -234,3 +237,28 @@ def tp_sp_reduce_scatter(partials, out_r: torch.Tensor, *, t: int, rank: int,
                                       _dt(out_r), _stream(stream)),
            "tp_sp_reduce_scatter")
     return out_r
+
+
+def tp_mlp_swiglu_shard_workspace_bytes(tokens: int, hidden: int, ffn: int, t: int, dtype) -> int:
+    dt = TP_BF16 if dtype == torch.bfloat16 else TP_F32
+    return int(lib().tp_mlp_swiglu_shard_workspace_bytes(tokens, hidden, ffn, t, dt))
+
+
+def tp_mlp_swiglu_shard_fwd(x: torch.Tensor, wg_i: torch.Tensor, wu_i: torch.Tensor,
+                            b_i: torch.Tensor, z_i: torch.Tensor, workspace: torch.Tensor, *,
+                            ffn: int, t: int, rank: int, bias_b: Optional[torch.Tensor] = None,
+                            residual: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """z_i <- (SiLU(X Wg_i) * (X Wu_i)) B_i (+ b + R on rank 0)."""
+    tokens, hidden = x.shape
+    for name, ten in (("x", x), ("b_i", b_i), ("z_i", z_i), ("residual", residual)):
+        if ten is not None and not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    lda = _rows(wg_i, "wg_i")
+    if _rows(wu_i, "wu_i") != lda:
+        raise ValueError("wg_i and wu_i must share their row stride")
+    _check(lib().tp_mlp_swiglu_shard_fwd(_ptr(x), _ptr(wg_i), _ptr(wu_i), lda, _ptr(b_i),
+                                         _ptr(bias_b), _ptr(residual), _ptr(z_i), _ptr(workspace),
+                                         _nbytes(workspace), tokens, hidden, ffn, t, rank, _dt(x),
+                                         _dt(z_i), _stream(stream)),
+           "tp_mlp_swiglu_shard_fwd")
+    return z_i

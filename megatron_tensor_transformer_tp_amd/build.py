@@ -29,6 +29,7 @@ SOURCES = [
     "gemm_bf16_128_plain.hip",
     "gemm_bf16_256_nt.hip",
     "gemm_bf16_256_tn.hip",
+    "gemm_bf16_256_swiglu.hip",
     "gemm_f32.hip",
     "colsum.hip",
     "sp_reduce.hip",

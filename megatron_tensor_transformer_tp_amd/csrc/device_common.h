@@ -74,6 +74,13 @@ __device__ __forceinline__ float gelu_grad_f32(float v) {
   return __builtin_fmaf(v * 0.39894228040143268f, n.e, cdf);
 }
 
+// SiLU(z) = z * sigma(z) = z / (1 + exp(-z)), sigma the logistic function
+// (the gate of the SwiGLU variant): one v_exp_f32 and one v_rcp_f32.  For
+// z << 0 the exponential overflows to +inf and the reciprocal gives 0.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
 // ---- global->LDS copies and explicit LDS synchronisation (gfx950) --------
 
 // Workgroup barrier with no memory fence: the compiler may not move memory

@@ -78,7 +78,25 @@ hipError_t launch_typed(const void* in, void* out, int64_t n, hipStream_t stream
   return hipGetLastError();
 }
 
+// fp32 SwiGLU combine for the fp32 path (the bf16 path fuses it into the
+// GEMM epilogue): h = SiLU(g) * u, grid-stride, one element per step.
+__global__ __launch_bounds__(256) void swiglu_combine_kernel(const float* __restrict__ g,
+                                                             const float* __restrict__ u,
+                                                             float* __restrict__ h, int64_t n) {
+  for (int64_t k = blockIdx.x * 256ll + threadIdx.x; k < n; k += 256ll * gridDim.x)
+    h[k] = silu_f32(g[k]) * u[k];
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_combine_f32(const float* g, const float* u, float* h, int64_t n,
+                                     hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  hipLaunchKernelGGL(swiglu_combine_kernel, dim3(static_cast<unsigned>(want < 4096 ? want : 4096)),
+                     dim3(256), 0, stream, g, u, h, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_gelu(const void* in, void* out, int64_t n, int in_dt, int out_dt,
                        hipStream_t stream) {

@@ -55,4 +55,17 @@ hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, con
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_gemm_bf16_swiglu(const uint16_t* A, int64_t lda, const uint16_t* Bg,
+                                   const uint16_t* Bu, int64_t ldb, int64_t M, int64_t F,
+                                   int64_t K, uint16_t* out, int64_t ldo, hipStream_t stream) {
+  if (M == 0 || F == 0) return hipSuccess;
+  if (K <= 0 || M % 256 != 0 || F % 128 != 0 || K % gemm_detail::kBKd != 0)
+    return hipErrorInvalidValue;
+  Epilogue ep{nullptr, nullptr, 0, out, ldo, false, EPI_SWIGLU};
+  ep.b2 = Bu;
+  // the product runs over the 2F interleaved gate / value columns
+  return launch_gemm_bf16_t_cfg<false, true, EPI_SWIGLU, false>(
+      A, lda, Bg, ldb, static_cast<int>(M), static_cast<int>(2 * F), static_cast<int>(K), ep, stream);
+}
+
 }  // namespace tpk

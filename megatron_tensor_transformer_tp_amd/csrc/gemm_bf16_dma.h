@@ -67,6 +67,24 @@ struct OperandTile {
     step = KMAJOR ? static_cast<int64_t>(kBKd) * ld : kBKd;
   }
 
+  // SwiGLU form of a k-major weight tile: LDS columns in 32-column blocks
+  // alternating between the gate projection (even blocks) and the value
+  // projection (odd blocks) of the same 32 features, so an MFMA wave whose
+  // 64 columns start on an even block holds gate and value of 32 features.
+  // Features [f0, f0 + R/2) of both projections (same ld).
+  __device__ __forceinline__ void init_dual(const uint16_t* gate, const uint16_t* value, int64_t ld,
+                                            int f0, int wave, int lane) {
+    static_assert(KMAJOR, "the paired tile is a weight ([K, N]) tile");
+    static_for<Q>([&](auto I) __attribute__((always_inline)) {
+      const int slot = (wave * Q + I) * 64 + lane;
+      const int krow = slot / CB, c = (slot % CB) ^ ((krow & 3) << 2);
+      const int blk = c >> 2;
+      const uint16_t* base = (blk & 1) ? value : gate;
+      src[I] = base + static_cast<int64_t>(krow) * ld + f0 + (blk >> 1) * 32 + (c & 3) * 8;
+    });
+    step = static_cast<int64_t>(kBKd) * ld;
+  }
+
   // Copies of k-tile kc into the LDS region at byte address `lds`.
   __device__ __forceinline__ void issue(int kc, uint32_t lds, int wave) const {
     static_for<Q>([&](auto I) __attribute__((always_inline)) {
@@ -96,6 +114,24 @@ struct OperandTile {
     }
   }
 };
+
+// SwiGLU epilogue: acc[0] holds the gate and acc[1] the value of the same 32
+// features (see OperandTile::init_dual); out[m, n] = SiLU(gate) * value.
+template <int TM, bool OUT_F32>
+__device__ __forceinline__ void store_swiglu(const f32x16_t (&acc)[2][TM], int m_lane, int n_lane,
+                                             const Epilogue& ep) {
+  static_for<TM>([&](auto I) __attribute__((always_inline)) {
+    const int64_t row = static_cast<int64_t>(m_lane + I * 32) * ep.ldo + n_lane;
+    static_for<4>([&](auto G) __attribute__((always_inline)) {
+      float h[4];
+      static_for<4>([&](auto R) __attribute__((always_inline)) {
+        h[R] = silu_f32(acc[0][I][4 * G + R]) * acc[1][I][4 * G + R];
+      });
+      store_x4<OUT_F32>(ep.out, row + G * 8, h);
+    });
+    sched_fence();
+  });
+}
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,
           bool OUT_F32>
@@ -127,7 +163,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   TileA ta;
   TileB tb;
   ta.init(A, lda, m0, wave, lane);
-  tb.init(B, ldb, n0, wave, lane);
+  if constexpr (EPI == EPI_SWIGLU)
+    tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, wave, lane);
+  else
+    tb.init(B, ldb, n0, wave, lane);
 
   // Copies of k-tile kt (clamped to the last tile) into stage kt % STAGES.
   const uint32_t smem_base = lds_address(smem);
@@ -193,8 +232,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   }
   wait_vmcnt<0>();
 
-  store_tile<TM, TN, false, EPI, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
-                                           n0 + wn * WN + (lane >> 5) * 4, M, N, ep);
+  if constexpr (EPI == EPI_SWIGLU) {
+    static_assert(TN == 2, "gate and value blocks per wave");
+    store_swiglu<TM, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
+                              n0 / 2 + wn * (WN / 2) + (lane >> 5) * 4, ep);
+  } else {
+    store_tile<TM, TN, false, EPI, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
+                                             n0 + wn * WN + (lane >> 5) * 4, M, N, ep);
+  }
 }
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,

@@ -12,6 +12,7 @@ enum EpilogueKind : int {
   EPI_LINEAR = 0,    // v = acc + bias[n]; v += residual[m, n]
   EPI_GELU = 1,      // y = acc + bias[n]; pre[m, n] = y (if pre); v = GeLU(y)
   EPI_GELU_BWD = 2,  // y = aux[m, n]; v = acc * GeLU'(y); out2[m, n] = GeLU(y)
+  EPI_SWIGLU = 3,    // gate and value columns of one feature: out = SiLU(g) * u
 };
 
 // Epilogue applied to the fp32 accumulator of C = A B, element (m, n), then
@@ -35,6 +36,7 @@ struct Epilogue {
   const void* aux = nullptr;
   int64_t ldaux = 0;
   void* out2 = nullptr;
+  const void* b2 = nullptr;   // EPI_SWIGLU: the value projection (B is the gate)
 };
 
 // bf16 x bf16 -> fp32 accumulate, MFMA.  A [M, K] row-major (lda), B [K, N]
@@ -53,6 +55,18 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, i
 hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B,
                               int64_t ldb, bool b_kmajor, int64_t M, int64_t N, int64_t K,
                               const Epilogue& ep, hipStream_t stream);
+
+// SwiGLU column layer: out[m, j] = SiLU((A Bg)[m, j]) * (A Bu)[m, j], j < F,
+// A [M, K] row-major, Bg and Bu [K, F] row-major with the same ldb, out bf16
+// [M, F] (ldo).  One product over both projections: M % 256 == 0,
+// F % 128 == 0, K % 32 == 0 (else hipErrorInvalidValue).
+hipError_t launch_gemm_bf16_swiglu(const uint16_t* A, int64_t lda, const uint16_t* Bg,
+                                   const uint16_t* Bu, int64_t ldb, int64_t M, int64_t F,
+                                   int64_t K, uint16_t* out, int64_t ldo, hipStream_t stream);
+
+// fp32 SwiGLU combine: h[k] = SiLU(g[k]) * u[k], k < n.
+hipError_t launch_swiglu_combine_f32(const float* g, const float* u, float* h, int64_t n,
+                                     hipStream_t stream);
 
 // fp32 x fp32 -> fp32 FMA, any shape.  Same layout flags as launch_gemm_bf16_t
 // (a_kmajor: A given [K, M]; b_kmajor: B given [K, N], else [N, K]); every

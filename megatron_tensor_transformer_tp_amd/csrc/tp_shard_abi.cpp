@@ -226,6 +226,68 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
 }
 
 
+size_t tp_mlp_swiglu_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int t,
+                                           tp_dtype in_dt) {
+  if (!dtype_known(in_dt) || tokens < 0 || hidden < 1) return 0;
+  int64_t f = 0;
+  if (check_split(ffn, t, 0, &f) != TP_OK) return 0;
+  const size_t act = round256(static_cast<size_t>(tokens) * static_cast<size_t>(f) *
+                              static_cast<size_t>(elem_bytes(in_dt)));
+  return in_dt == TP_BF16 ? act : 3 * act;   // fp32: gate, value, product
+}
+
+tp_status tp_mlp_swiglu_shard_fwd(const void* x, const void* wg_i, const void* wu_i, int64_t lda,
+                                  const void* b_i, const void* bias_b, const void* residual,
+                                  void* z_i, void* workspace, size_t workspace_bytes,
+                                  int64_t tokens, int64_t hidden, int64_t ffn, int t, int rank,
+                                  tp_dtype in_dt, tp_dtype out_dt, void* stream) {
+  if (!dtype_known(in_dt) || !dtype_known(out_dt) || !gemm_pair_ok(in_dt, out_dt))
+    return TP_ERR_DTYPE;
+  if (tokens < 0 || hidden < 1) return TP_ERR_INVALID_ARG;
+  int64_t f = 0;
+  TP_TRY(check_split(ffn, t, rank, &f));
+  if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(2 * f)) return TP_ERR_UNSUPPORTED;
+  if (tokens == 0) return TP_OK;
+  TP_TRY(check_matrix(x, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(wg_i, lda, f, in_dt));
+  TP_TRY(check_matrix(wu_i, lda, f, in_dt));
+  TP_TRY(check_matrix(b_i, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(z_i, hidden, hidden, out_dt));
+  const bool owner = rank == 0;
+  const void* bias_use = owner ? bias_b : nullptr;
+  const void* res_use = owner ? residual : nullptr;
+  TP_TRY(check_optional_vec(bias_use));
+  TP_TRY(check_optional_vec(res_use));
+  if (in_dt == TP_BF16 && (tokens % 256 != 0 || f % 128 != 0 || hidden % 32 != 0))
+    return TP_ERR_UNSUPPORTED;
+  const size_t need = tp_mlp_swiglu_shard_workspace_bytes(tokens, hidden, ffn, t, in_dt);
+  if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  void* h = w;
+  if (in_dt == TP_BF16) {
+    // Both gated projections in one product, H_i = SiLU(X Wg_i) * (X Wu_i)
+    // formed in the epilogue (one bf16 HBM round trip of H_i).
+    TP_TRY(from_hip(tpk::launch_gemm_bf16_swiglu(
+        static_cast<const uint16_t*>(x), hidden, static_cast<const uint16_t*>(wg_i),
+        static_cast<const uint16_t*>(wu_i), lda, tokens, f, hidden, static_cast<uint16_t*>(h), f, s)));
+  } else {
+    const size_t act = round256(static_cast<size_t>(tokens) * static_cast<size_t>(f) * 4);
+    float* g = reinterpret_cast<float*>(w + act);
+    float* u = reinterpret_cast<float*>(w + 2 * act);
+    tpk::Epilogue eg{nullptr, nullptr, 0, g, f, true, tpk::EPI_LINEAR};
+    TP_TRY(run_gemm(in_dt, x, hidden, wg_i, lda, tokens, f, hidden, eg, s));
+    tpk::Epilogue eu{nullptr, nullptr, 0, u, f, true, tpk::EPI_LINEAR};
+    TP_TRY(run_gemm(in_dt, x, hidden, wu_i, lda, tokens, f, hidden, eu, s));
+    TP_TRY(from_hip(tpk::launch_swiglu_combine_f32(g, u, static_cast<float*>(h), tokens * f, s)));
+  }
+  // Row-parallel GEMM: Z_i = H_i B_i (+ b + R on rank 0).
+  tpk::Epilogue e2{bias_use, res_use, hidden, z_i, hidden, out_dt == TP_F32, tpk::EPI_LINEAR};
+  return run_gemm(in_dt, h, f, b_i, hidden, tokens, hidden, f, e2, s);
+}
+
 namespace {
 // Workspace of tp_mlp_shard_bwd: dY_i, H_i [tokens, f] (in_dt), then the
 // column-sum partials (fp32) of the bias gradients.

@@ -39,6 +39,8 @@ __all__ = [
     "mlp_bias_b",
     "mlp_residual_rows",
     "mlp_dz_rows",
+    "mlp_wg_block",
+    "mlp_wu_block",
     "attn_x",
     "attn_wqkv_block",
     "attn_wo_block",
@@ -49,7 +51,8 @@ __all__ = [
 X_ROW_CHUNK = 256
 
 _TENSOR_IDS = {"x": 0, "a": 1, "b": 2, "wqkv": 3, "wo": 4, "residual": 5,
-               "bias_a": 6, "bias_b": 7, "dz": 8, "partial": 9}
+               "bias_a": 6, "bias_b": 7, "dz": 8, "partial": 9,
+               "wg": 10, "wu": 11}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -215,6 +218,17 @@ def mlp_residual_rows(wl: MlpWorkload, row0: int = 0, rows: Optional[int] = None
     full = np.concatenate(parts, axis=0)
     off = row0 - c0 * X_ROW_CHUNK
     return np.ascontiguousarray(full[off:off + rows])
+
+
+def mlp_wg_block(wl: MlpWorkload, r: int) -> np.ndarray:
+    """Column block r [hidden, f] of the SwiGLU gate projection [hidden, ffn]
+    (same distribution as A)."""
+    return draw(wl.name, "wg", r, (wl.hidden, wl.f), wl.a_std, wl.dtype)
+
+
+def mlp_wu_block(wl: MlpWorkload, r: int) -> np.ndarray:
+    """Column block r [hidden, f] of the SwiGLU value projection."""
+    return draw(wl.name, "wu", r, (wl.hidden, wl.f), wl.a_std, wl.dtype)
 
 
 def mlp_dz_rows(wl: MlpWorkload, row0: int = 0, rows: Optional[int] = None,

@@ -238,3 +238,29 @@ def test_sp_reduce_scatter_validation(lib):
     assert sp(lib, bias=P + 2, out=P) == MISALIGNED
     assert sp(lib, tokens=0) == OK
     assert lib.tp_sp_reduce_scatter(None, 4, 0, None, None, P, 256, 1024, BF16, F32, None) == INVALID
+
+
+def swiglu(lib, **kw):
+    a = dict(x=P, wg=P, wu=P, lda=512, b=P, bias_b=None, res=None, z=P, ws=P, ws_bytes=1 << 30,
+             tokens=256, hidden=1024, ffn=4096, t=8, rank=0, in_dt=BF16, out_dt=F32)
+    a.update(kw)
+    return lib.tp_mlp_swiglu_shard_fwd(a["x"], a["wg"], a["wu"], a["lda"], a["b"], a["bias_b"],
+                                       a["res"], a["z"], a["ws"], a["ws_bytes"], a["tokens"],
+                                       a["hidden"], a["ffn"], a["t"], a["rank"], a["in_dt"],
+                                       a["out_dt"], None)
+
+
+def test_swiglu_validation(lib):
+    need = lib.tp_mlp_swiglu_shard_workspace_bytes(256, 1024, 4096, 8, BF16)
+    assert need == 256 * 512 * 2
+    assert lib.tp_mlp_swiglu_shard_workspace_bytes(64, 64, 256, 4, F32) == 3 * 64 * 64 * 4
+    assert swiglu(lib, ffn=4097) == NOT_DIV
+    assert swiglu(lib, rank=8) == BAD_RANK
+    assert swiglu(lib, wu=None) == INVALID
+    assert swiglu(lib, wg=P + 8) == MISALIGNED
+    assert swiglu(lib, in_dt=F32, out_dt=BF16) == DTYPE
+    assert swiglu(lib, tokens=300) == UNSUPPORTED          # bf16: tokens % 256
+    assert swiglu(lib, ffn=8 * 136, lda=136) == UNSUPPORTED  # bf16: f % 128
+    assert swiglu(lib, ws_bytes=need - 1) == WORKSPACE
+    assert swiglu(lib, in_dt=F32, tokens=300, ws_bytes=1) == WORKSPACE   # fp32: any shape
+    assert swiglu(lib, tokens=0, ws=None) == OK

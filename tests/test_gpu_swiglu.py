@@ -1,0 +1,107 @@
+"""GPU parity of the SwiGLU MLP shard (tp_mlp_swiglu_shard_fwd) against the
+fp64 oracle.  Outputs NaN-filled before each call.  Tolerances as for the
+GeLU MLP, bf16 inputs: max |err| <= 2e-2 (s + |ref|) and relative Frobenius
+<= 5e-3 per shard (the sum over ranks: relative Frobenius, max reported);
+fp32: both <= 1e-5.  s is the output's RMS magnitude rather than 1: the gated
+product of two projections puts the partial at RMS ~3 for the large shard
+(at unit scale it is the same bound)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_tp_amd import binding, inputs
+from tests.gpu_helpers import BF16_FRO, assert_close, dev, errors, host64, nan_tensor, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def run(wl, r, xd, wgd, wud, bd, tokens, **extras):
+    td = TORCH_DT[wl.dtype]
+    ws = torch.empty(binding.tp_mlp_swiglu_shard_workspace_bytes(tokens, wl.hidden, wl.ffn, wl.t, td),
+                     dtype=torch.uint8, device="cuda")
+    z = nan_tensor((tokens, wl.hidden), TORCH_DT[wl.out_dtype])
+    binding.tp_mlp_swiglu_shard_fwd(xd, wgd, wud, bd, z, ws, ffn=wl.ffn, t=wl.t, rank=r, **extras)
+    torch.cuda.synchronize()
+    return z
+
+
+def full_weights(wl):
+    return (np.concatenate([inputs.mlp_wg_block(wl, r) for r in range(wl.t)], axis=1),
+            np.concatenate([inputs.mlp_wu_block(wl, r) for r in range(wl.t)], axis=1),
+            np.concatenate([inputs.mlp_b_block(wl, r) for r in range(wl.t)], axis=0))
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_t4", "t4_h1024_m1024"])
+def test_all_ranks_and_reconstruction(name):
+    wl = inputs.MLP_WORKLOADS[name]
+    dt = wl.dtype
+    x = inputs.mlp_x_rows(wl)
+    wg, wu, b = full_weights(wl)
+    bb, res = inputs.mlp_bias_b(wl), inputs.mlp_residual_rows(wl)
+    x64, wg64, wu64, b64 = (host64(v, dt) for v in (x, wg, wu, b))
+    bb64, res64 = host64(bb, dt), host64(res, dt)
+    xd = dev(x, dt)
+    total = None
+    for r in range(wl.t):
+        say(f"{name} swiglu rank {r}")
+        z = to_np(run(wl, r, xd, dev(inputs.mlp_wg_block(wl, r), dt), dev(inputs.mlp_wu_block(wl, r), dt),
+                      dev(inputs.mlp_b_block(wl, r), dt), wl.tokens, bias_b=dev(bb, dt),
+                      residual=dev(res, dt)))
+        ref = oracle.swiglu_mlp_shard(x64, wg64, wu64, b64, wl.t, r, bb64, res64)
+        assert_close(z, ref, dt, f"{name} swiglu rank {r}", rms_floor=True)
+        total = z if total is None else total + z
+    full = oracle.swiglu_mlp_full(x64, wg64, wu64, b64, bb64, res64)
+    if dt == "f32":
+        assert_close(total, full, dt, f"{name} swiglu sum over ranks", rms_floor=True)
+    else:
+        mx, fro = errors(total, full)
+        say(f"{name} swiglu sum over ranks: rel-fro {fro:.3e} (<= {BF16_FRO}), max {mx:.3e} (reported)")
+        assert fro <= BF16_FRO
+
+
+@pytest.mark.parametrize("rank", [0, 6])
+def test_large_shard_sampled_rows(rank):
+    """t = 8, hidden 8192, 16384 tokens: the whole shard runs on the GPU; the
+    oracle computes sampled rows (each row depends only on its own token)."""
+    wl = inputs.MLP_WORKLOADS["t8_h8192_m16384"]
+    x = inputs.mlp_x_rows(wl)
+    wg, wu, b = inputs.mlp_wg_block(wl, rank), inputs.mlp_wu_block(wl, rank), inputs.mlp_b_block(wl, rank)
+    say(f"t8_h8192_m16384 swiglu rank {rank}")
+    z = run(wl, rank, dev(x, "bf16"), dev(wg, "bf16"), dev(wu, "bf16"), dev(b, "bf16"), wl.tokens)
+    rows = np.r_[0:128, 8000:8128, 16256:16384]
+    got = to_np(z[torch.as_tensor(rows, device="cuda")])
+    assert np.isfinite(to_np(z)).all()
+    # the rank's blocks with t = 1 are the whole of its shard (partition pin)
+    ref = oracle.swiglu_mlp_shard(host64(x[rows], "bf16"), host64(wg, "bf16"), host64(wu, "bf16"),
+                                  host64(b, "bf16"), 1, 0)
+    assert_close(got, ref, "bf16", f"t8 swiglu rank {rank} sampled rows", rms_floor=True)
+
+
+def test_strided_weight_views_and_f32_ragged():
+    wl = inputs.MLP_WORKLOADS["t4_h1024_m1024"]
+    x = inputs.mlp_x_rows(wl)
+    wg, wu, b = full_weights(wl)
+    wgd, wud = dev(wg, "bf16"), dev(wu, "bf16")
+    r = 2
+    cols = slice(r * wl.f, (r + 1) * wl.f)
+    say("t4_h1024_m1024 swiglu rank 2 from column-block views (ld = ffn)")
+    z = to_np(run(wl, r, dev(x, "bf16"), wgd[:, cols], wud[:, cols], dev(inputs.mlp_b_block(wl, r), "bf16"),
+                  wl.tokens))
+    ref = oracle.swiglu_mlp_shard(host64(x, "bf16"), host64(wg, "bf16"), host64(wu, "bf16"),
+                                  host64(b, "bf16"), wl.t, r)
+    assert_close(z, ref, "bf16", "swiglu strided views", rms_floor=True)
+    # fp32 takes any token count
+    wt = inputs.MLP_WORKLOADS["tiny_f32_t4"]
+    xs = inputs.mlp_x_rows(wt, 0, 37)
+    say("tiny_f32_t4 swiglu rank 1, 37 tokens")
+    z = to_np(run(wt, 1, dev(xs, "f32"), dev(inputs.mlp_wg_block(wt, 1), "f32"),
+                  dev(inputs.mlp_wu_block(wt, 1), "f32"), dev(inputs.mlp_b_block(wt, 1), "f32"), 37))
+    fg, fu, fb = full_weights(wt)
+    assert_close(z, oracle.swiglu_mlp_shard(xs, fg, fu, fb, wt.t, 1), "f32", "swiglu fp32 ragged",
+                 rms_floor=True)
+    # bf16 needs 256-token tiles
+    with pytest.raises(binding.TpError, match="UNSUPPORTED"):
+        run(wl, 0, dev(x[:300], "bf16"), wgd[:, :wl.f], wud[:, :wl.f], dev(inputs.mlp_b_block(wl, 0), "bf16"), 300)
