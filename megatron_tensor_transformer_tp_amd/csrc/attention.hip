@@ -5,31 +5,41 @@
 // attention because the softmax reduces over keys).
 //
 // Input: the packed QKV projection of the rank, per token row laid out per
-// local head as [q | k | v] (head_dim columns each), given as a bf16 pair
-// (hi, lo) with hi + lo ~= the fp32 projection: Q K^T is formed from the
-// pairs (hi*hi + hi*lo + lo*hi) so the logits keep ~16 significant bits —
-// with logits of std ~3 a plain bf16 Q/K would alone cost ~5e-3 relative
-// error in the output.  V uses the hi part only.
+// local head as [q | k | v] (head_dim columns each), with the q and k
+// columns in fp16 scaled by 2^-8 and the v columns in bf16: Q K^T runs on
+// the fp16 MFMA (11 significant bits; with logits of std ~3 a bf16 Q/K
+// would alone cost ~5e-3 relative error in the output), the 2^16 going back
+// in the softmax scale.  The scale keeps |q|, |k| in [2^-6, 2^24) at full
+// fp16 precision.
 // Output: O [tokens, heads_local * head_dim] bf16, head j in columns j*d.
 //
 // Flash-style, gfx950:
-//   * workgroup = one (batch, head, 128-query block), 4 waves x 32 queries;
-//     grid ids are ordered head-fastest, so with 8 local heads each XCD
+//   * workgroup = one (batch, head, 128-query block) and 8 waves in two
+//     groups of 4: wave w owns queries 32 (w % 4) .. +31 of the block, and
+//     group g = w / 4 takes the 32-key blocks with index = g (mod 2), so the
+//     two waves on each SIMD alternate between MFMA work and softmax work.
+//     Each wave keeps its own online-softmax state; the two groups' states
+//     are merged through LDS at the end (max, rescale, add);
+//   * grid ids are ordered head-fastest, so with 8 local heads each XCD
 //     serves one head and its K/V stay in that XCD's L2;
-//   * key blocks of 64; K_hi, K_lo, V of a block (48 KiB) arrive by
-//     global->LDS copies, 3 LDS stages (two blocks in flight);
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16, K fragments from LDS (one
-//     ds_read_b128, rows XOR-swizzled by row % 16), Q fragments held in
-//     registers: each lane owns one query and 32 of the block's keys, so the
-//     online-softmax row max needs one exchange with lane ^ 32;
+//   * K and V of a 32-key block (16 KiB) arrive by global->LDS copies (saddr
+//     form: uniform base + 32-bit lane offset); 6 LDS stages: the two blocks
+//     being read, two in flight, two being issued;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_f16, K fragments from LDS (one
+//     ds_read_b128, rows XOR-swizzled by row % 16, read one d-step ahead),
+//     Q fragments held in registers; each lane owns one query and 16 of the
+//     block's 32 keys, so the row max needs one exchange with lane ^ 32; the
+//     logits accumulate in two chains (even / odd d-steps);
 //   * O^T = V^T P^T: each lane keeps 64 of its query's output dimensions, so
-//     the per-query rescale is lane-local; V^T fragments come straight from
-//     the row-major V block with ds_read_b64_tr_b16 (rows XOR-swizzled by
+//     the rescale is lane-local; V^T fragments come straight from the
+//     row-major V block with ds_read_b64_tr_b16 (rows XOR-swizzled by
 //     4 * (row % 4)); P is rounded to bf16 (RNE) for the MFMA; the key order
 //     inside a 16-key MFMA step is permuted identically in P and V;
-//   * exp via v_exp_f32 on log2-scaled logits; running max starts at a large
-//     finite negative value, so fully masked (causal) entries give exp = 0 and
-//     never NaN.
+//   * exp via v_exp_f32 on log2-scaled logits; the running max starts at a
+//     large finite negative value, so fully masked (causal) entries give
+//     exp = 0 and never NaN; it is raised lazily (only when a block's max
+//     exceeds it by more than 8 in log2 units, decided per wave), so the
+//     64-register output rescale is rare.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -39,6 +49,7 @@ namespace tpk {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
@@ -47,17 +58,32 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;                 // head_dim
 constexpr int kBQ = 128;                // queries per workgroup
-constexpr int kBKV = 64;                // keys per block
-constexpr int kStages = 3;
-constexpr int kArr = kBKV * kD * 2;     // one array (K_hi, K_lo or V) of a block: 16 KiB
-constexpr int kStage = 3 * kArr;        // 48 KiB
-constexpr int kWaves = 4;
-constexpr int kCopies = kStage / 1024 / kWaves;  // 12 copy instructions per wave per block
+constexpr int kBKV = 32;                // keys per block
+constexpr int kStages = 6;
+constexpr int kArr = kBKV * kD * 2;     // one array (K or V) of a block: 8 KiB
+constexpr int kStage = 2 * kArr;        // 16 KiB
+constexpr int kWaves = 8;
+constexpr int kCopies = 2 * kStage / 1024 / kWaves;  // two blocks per iteration: 4 per wave
+constexpr int kCopiesPerBlock = kStage / 1024;       // 16
 constexpr float kNegBig = -1.0e30f;
+// log2 units by which the running max may lag the true one before the
+// output accumulator is rescaled (so the softmax weights stay <= 2^8).
+constexpr float kRescaleSlack = 8.0f;
+static_assert(kStages * kStage <= 160 * 1024, "LDS");
+static_assert(kWaves / 2 * 64 * 66 * 4 <= kStages * kStage, "merge area");
+static_assert(kQkvPart == kD, "q / k / v parts of head_dim columns");
+
+// One global->LDS copy with a uniform base (SGPR pair) and a per-lane 32-bit
+// byte offset: lane t's 16 bytes land at LDS byte address lds_addr + 16 t.
+__device__ __forceinline__ void copy_to_lds_off(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_addr)
+               : "m0");
+}
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restrict__ qkv_hi,
-                                                       const uint16_t* __restrict__ qkv_lo,
+__global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
                                                        int64_t ld_qkv, uint16_t* __restrict__ o,
                                                        int64_t ld_o, int seq, int heads,
                                                        float scale_log2) {
@@ -65,6 +91,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int group = wave >> 2;             // which half of the key blocks
   const int nqb = seq / kBQ;
   const int id = blockIdx.x;
   const int head = id % heads;
@@ -74,46 +101,51 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
   const int64_t row0 = static_cast<int64_t>(b) * seq;   // first token row of this batch
   const int col_q = head * 3 * kD, col_k = col_q + kD, col_v = col_q + 2 * kD;
   const int h = lane >> 5;                 // which half of the keys / dims this lane holds
-  const int query = qb * kBQ + wave * 32 + (lane & 31);
+  const int query = qb * kBQ + (wave & 3) * 32 + (lane & 31);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[query][16t + 8h .. +7].
-  bf16x8_t qh[8], ql[8];
+  f16x8_t qf[8];
   {
     const int64_t qoff = (row0 + query) * ld_qkv + col_q + 8 * h;
-    for (int t = 0; t < 8; ++t) {
-      qh[t] = *reinterpret_cast<const bf16x8_t*>(qkv_hi + qoff + 16 * t);
-      ql[t] = *reinterpret_cast<const bf16x8_t*>(qkv_lo + qoff + 16 * t);
-    }
+    static_for<8>([&](auto T) __attribute__((always_inline)) {
+      qf[T] = *reinterpret_cast<const f16x8_t*>(qkv + qoff + 16 * T);
+    });
   }
 
-  // Copy sources: instruction q of this wave moves 4 key rows (1 KiB) of one
-  // array; lane -> (row, physical chunk) with the array's swizzle undone on
-  // the global side.
-  const uint16_t* csrc[kCopies];
+  // Copies of one iteration: two blocks x (K, V) x 8 KiB = 32 copy
+  // instructions of 1 KiB, 4 per wave; copy q moves 4 key rows of one array.
+  // Lane -> (row, physical chunk), the array's swizzle undone on the global
+  // side; the per-lane part is a byte offset from the block's first row.
+  uint32_t coff[kCopies];
   static_for<kCopies>([&](auto Q) __attribute__((always_inline)) {
-    const int q = wave * kCopies + Q;
-    const int arr = q / 16;                        // 0: K_hi, 1: K_lo, 2: V
-    const int slot = (q % 16) * 64 + lane;
+    const int rem = (wave * kCopies + Q) % kCopiesPerBlock;
+    const int arr = rem / 8;                   // 0: K, 1: V
+    const int slot = (rem % 8) * 64 + lane;
     const int row = slot >> 4, p = slot & 15;
-    const int c = arr < 2 ? (p ^ (row & 15)) : (p ^ ((row & 3) << 2));
-    const uint16_t* base = arr == 1 ? qkv_lo : qkv_hi;
-    csrc[Q] = base + (row0 + row) * ld_qkv + (arr < 2 ? col_k : col_v) + 8 * c;
+    const int c = arr == 0 ? (p ^ (row & 15)) : (p ^ ((row & 3) << 2));
+    coff[Q] = static_cast<uint32_t>((row * ld_qkv + (arr == 0 ? col_k : col_v) + 8 * c) * 2);
   });
   const int64_t block_step = static_cast<int64_t>(kBKV) * ld_qkv;
   const uint32_t smem_base = lds_address(smem);
-  const int kb_end = CAUSAL ? min(seq / kBKV, ((qb + 1) * kBQ + kBKV - 1) / kBKV) : seq / kBKV;
+  const int nblk = CAUSAL ? min(seq / kBKV, (qb + 1) * (kBQ / kBKV)) : seq / kBKV;  // even
+  const int nit = nblk / 2;
 
-  auto issue = [&](int kb) __attribute__((always_inline)) {
-    const int kc = min(kb, kb_end - 1);
-    const uint32_t sbase = smem_base + (kb % kStages) * kStage;
+  // Copies of blocks 2 it and 2 it + 1 (clamped to the last block) into
+  // their stages (block j lives in stage j % kStages).
+  auto issue = [&](int it) __attribute__((always_inline)) {
     static_for<kCopies>([&](auto Q) __attribute__((always_inline)) {
       const int q = wave * kCopies + Q;
-      copy_to_lds(csrc[Q] + kc * block_step, sbase + (q / 16) * kArr + (q % 16) * 1024);
+      const int j = 2 * it + q / kCopiesPerBlock;
+      const int kc = min(j, nblk - 1);
+      const int rem = q % kCopiesPerBlock;
+      const uint16_t* base = qkv + row0 * ld_qkv + kc * block_step;
+      copy_to_lds_off(base, coff[Q],
+                      smem_base + (j % kStages) * kStage + (rem / 8) * kArr + (rem % 8) * 1024);
     });
   };
 
   // Fragment addressing.
-  const int k_row = lane & 31;                 // + kt*32
+  const int k_row = lane & 31;
   const int k_sw = lane & 15;                  // row % 16 for the K swizzle
   const int gi = lane & 15;
   const int v_row = 4 * h + (gi >> 2);         // + 16u (+8 for the second read)
@@ -122,120 +154,164 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
   const int v_within = (gi & 1) * 8;
 
   f32x16_t acc_o[4];
-  for (int dt = 0; dt < 4; ++dt) acc_o[dt] = (f32x16_t)(0.0f);
+  static_for<4>([&](auto DT) __attribute__((always_inline)) { acc_o[DT] = (f32x16_t)(0.0f); });
   float m_run = kNegBig, l_run = 0.0f;
 
   issue(0);
   issue(1);
-  for (int kb = 0; kb < kb_end; ++kb) {
+  for (int it = 0; it < nit; ++it) {
+    // blocks 2 it, 2 it + 1 have landed (this wave's copies; the barrier
+    // makes it every wave's); issue blocks 2 it + 4, 2 it + 5 into the stages
+    // that iteration it - 1 read
     wait_vmcnt<kCopies>();
     lds_barrier();
-    issue(kb + 2);
+    issue(it + 2);
+    const int kb = 2 * it + group;
     const uint8_t* st = smem + (kb % kStages) * kStage;
-    const uint8_t* kh = st;
-    const uint8_t* kl = st + kArr;
-    const uint8_t* vv = st + 2 * kArr;
+    const uint8_t* kk = st;
+    const uint8_t* vv = st + kArr;
 
-    // S^T for the block's two 32-key tiles.
-    f32x16_t s[2];
-    static_for<2>([&](auto KT) __attribute__((always_inline)) {
-      s[KT] = (f32x16_t)(0.0f);
-      const int row = KT * 32 + k_row;
-      static_for<8>([&](auto T) __attribute__((always_inline)) {
-        const int off = row * (kD * 2) + (((2 * T + h) ^ k_sw) * 16);
-        const bf16x8_t a_hi = *TPK_LDS(const bf16x8_t, kh + off);
-        const bf16x8_t a_lo = *TPK_LDS(const bf16x8_t, kl + off);
-        s[KT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, qh[T], s[KT], 0, 0, 0);
-        s[KT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, ql[T], s[KT], 0, 0, 0);
-        s[KT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, qh[T], s[KT], 0, 0, 0);
-      });
+    // S^T of the block's 32 keys: two chains (even / odd d-steps), the K
+    // fragments of d-step T+1 read while the MFMAs of d-step T run.
+    f32x16_t s2[2] = {(f32x16_t)(0.0f), (f32x16_t)(0.0f)};
+    f16x8_t kf[2];
+    auto load_k = [&](auto T, auto BUF) __attribute__((always_inline)) {
+      const int off = k_row * (kD * 2) + (((2 * T + h) ^ k_sw) * 16);
+      kf[BUF] = *TPK_LDS(const f16x8_t, kk + off);
+    };
+    load_k(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    static_for<8>([&](auto T) __attribute__((always_inline)) {
+      constexpr int cur = T & 1;
+      if constexpr (T < 7) load_k(std::integral_constant<int, T + 1>{}, std::integral_constant<int, cur ^ 1>{});
+      s2[cur] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[cur], qf[T], s2[cur], 0, 0, 0);
     });
 
-    // Online softmax over the block (this lane: its query, 32 of the 64 keys).
-    float mx = kNegBig;
-    static_for<2>([&](auto KT) __attribute__((always_inline)) {
-      static_for<16>([&](auto R) __attribute__((always_inline)) {
-        float v = s[KT][int(R)] * scale_log2;
-        if constexpr (CAUSAL) {
-          const int key = kb * kBKV + KT * 32 + 8 * (R / 4) + 4 * h + (R % 4);
-          if (key > query) v = -__builtin_inff();
-        }
-        s[KT][int(R)] = v;
-        mx = fmaxf(mx, v);
+    // V^T fragments of the first 32 output dims load under the softmax.
+    i16x4_t vf[2][2][2];
+    auto load_v = [&](auto DT, auto BUF) __attribute__((always_inline)) {
+      const int chunk = (4 * DT + v_chunk) ^ v_sw;
+      static_for<2>([&](auto U) __attribute__((always_inline)) {
+        const int r0 = 16 * U + v_row;
+        vf[BUF][U][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TPK_LDS(i16x4_t, vv + r0 * (kD * 2) + chunk * 16 + v_within));
+        vf[BUF][U][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TPK_LDS(i16x4_t, vv + (r0 + 8) * (kD * 2) + chunk * 16 + v_within));
       });
+    };
+    load_v(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+
+    // Online softmax over the block (this lane: its query, 16 of the 32
+    // keys: S^T rows 8 (R / 4) + 4 h + R % 4).  The running max is raised
+    // (and the accumulator rescaled) only when the block's max exceeds it by
+    // more than kRescaleSlack, decided for the whole wave at once; otherwise
+    // the weights exp2(s - m_run) may grow up to 2^kRescaleSlack.
+    f32x16_t sv = s2[0] + s2[1];
+    float mx = kNegBig;
+    static_for<16>([&](auto R) __attribute__((always_inline)) {
+      float v = sv[int(R)] * scale_log2;
+      if constexpr (CAUSAL) {
+        const int key = kb * kBKV + 8 * (R / 4) + 4 * h + (R % 4);
+        if (key > query) v = -__builtin_inff();
+      }
+      sv[int(R)] = v;
+      mx = fmaxf(mx, v);
     });
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      static_for<4>([&](auto DT) __attribute__((always_inline)) { acc_o[DT] *= alpha; });
+    }
     float lsum = 0.0f;
-    static_for<2>([&](auto KT) __attribute__((always_inline)) {
-      static_for<16>([&](auto R) __attribute__((always_inline)) {
-        const float p = __builtin_amdgcn_exp2f(s[KT][int(R)] - m_new);
-        s[KT][int(R)] = p;
-        lsum += p;
-      });
+    static_for<16>([&](auto R) __attribute__((always_inline)) {
+      const float p = __builtin_amdgcn_exp2f(sv[int(R)] - m_run);
+      sv[int(R)] = p;
+      lsum += p;
     });
-    l_run = l_run * alpha + lsum;
-    for (int dt = 0; dt < 4; ++dt) acc_o[dt] *= alpha;
+    l_run += lsum;
 
-    // P^T fragments: step u covers 16 keys; half h holds keys {4h..4h+3,
-    // 8+4h..8+4h+3} of the step (the S^T rows it owns), V^T uses the same order.
-    bf16x8_t pf[4];
-    static_for<4>([&](auto U) __attribute__((always_inline)) {
-      constexpr int kt = U / 2, g0 = 2 * (U % 2);
+    // P^T fragments: step u covers keys 16u .. 16u+15; half h holds keys
+    // {4h..4h+3, 8+4h..8+4h+3} of the step, V^T uses the same order.
+    bf16x8_t pf[2];
+    static_for<2>([&](auto U) __attribute__((always_inline)) {
       i16x8_t w;
       static_for<4>([&](auto R) __attribute__((always_inline)) {
-        w[int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(s[kt][4 * g0 + int(R)]));
-        w[4 + int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(s[kt][4 * (g0 + 1) + int(R)]));
+        w[int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(sv[8 * U + int(R)]));
+        w[4 + int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(sv[8 * U + 4 + int(R)]));
       });
       pf[U] = __builtin_bit_cast(bf16x8_t, w);
     });
 
-    // O^T += V^T P^T.
+    // O^T += V^T P^T, the next 32 dims' V^T fragments loading under the MFMAs.
     static_for<4>([&](auto DT) __attribute__((always_inline)) {
-      const int chunk = (4 * DT + v_chunk) ^ v_sw;
-      static_for<4>([&](auto U) __attribute__((always_inline)) {
-        const int r0 = 16 * U + v_row;
-        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TPK_LDS(i16x4_t, vv + r0 * (kD * 2) + chunk * 16 + v_within));
-        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TPK_LDS(i16x4_t, vv + (r0 + 8) * (kD * 2) + chunk * 16 + v_within));
-        const i16x8_t w = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        acc_o[DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w),
-                                                             pf[U], acc_o[DT], 0, 0, 0);
+      constexpr int cur = DT & 1;
+      if constexpr (DT < 3) load_v(std::integral_constant<int, DT + 1>{}, std::integral_constant<int, cur ^ 1>{});
+      static_for<2>([&](auto U) __attribute__((always_inline)) {
+        const i16x8_t w = {vf[cur][U][0][0], vf[cur][U][0][1], vf[cur][U][0][2], vf[cur][U][0][3],
+                           vf[cur][U][1][0], vf[cur][U][1][1], vf[cur][U][1][2], vf[cur][U][1][3]};
+        acc_o[DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf[U],
+                                                             acc_o[DT], 0, 0, 0);
       });
     });
   }
   wait_vmcnt<0>();
 
-  // Normalise and store O[query][dt*32 + 8g + 4h + r] (4 consecutive dims per store).
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  uint16_t* orow = o + (row0 + query) * ld_o + head * kD + 4 * h;
-  for (int dt = 0; dt < 4; ++dt) {
-    for (int g = 0; g < 4; ++g) {
-      const u32x2_t w = {pack_bf16x2(acc_o[dt][4 * g] * inv, acc_o[dt][4 * g + 1] * inv),
-                         pack_bf16x2(acc_o[dt][4 * g + 2] * inv, acc_o[dt][4 * g + 3] * inv)};
-      *reinterpret_cast<u32x2_t*>(orow + dt * 32 + 8 * g) = w;
-    }
+  // Merge the two groups: group 1 publishes (m, l, acc) through LDS (the
+  // stages are free once every wave is past its last read), group 0 combines
+  // with its partner wave w + 4 (same queries, same lane layout) and stores.
+  lds_barrier();
+  float* mrg = reinterpret_cast<float*>(smem) + ((wave & 3) * 64 + lane) * 66;
+  if (group == 1) {
+    mrg[0] = m_run;
+    mrg[1] = l_run;
+    static_for<4>([&](auto DT) __attribute__((always_inline)) {
+      static_for<16>([&](auto R) __attribute__((always_inline)) { mrg[2 + 16 * DT + R] = acc_o[DT][int(R)]; });
+    });
+  }
+  lds_barrier();
+  if (group == 0) {
+    const float m1 = mrg[0], l1 = mrg[1];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float l_lane = l_run * a0 + l1 * a1;
+    const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+    const float inv = 1.0f / l_tot;
+    uint16_t* orow = o + (row0 + query) * ld_o + head * kD + 4 * h;
+    static_for<4>([&](auto DT) __attribute__((always_inline)) {
+      float v[16];
+      static_for<16>([&](auto R) __attribute__((always_inline)) {
+        v[R] = (acc_o[DT][int(R)] * a0 + mrg[2 + 16 * DT + R] * a1) * inv;
+      });
+      // O[query][dt*32 + 8g + 4h + r]: 4 consecutive dims per store
+      static_for<4>([&](auto G) __attribute__((always_inline)) {
+        const u32x2_t w = {pack_bf16x2(v[4 * G], v[4 * G + 1]), pack_bf16x2(v[4 * G + 2], v[4 * G + 3])};
+        *reinterpret_cast<u32x2_t*>(orow + DT * 32 + 8 * G) = w;
+      });
+    });
   }
 }
 
 }  // namespace
 
-hipError_t launch_attention(const uint16_t* qkv_hi, const uint16_t* qkv_lo, int64_t ld_qkv,
-                            uint16_t* o, int64_t ld_o, int batch, int seq, int heads,
-                            int head_dim, bool causal, hipStream_t stream) {
+hipError_t launch_attention(const uint16_t* qkv, int64_t ld_qkv, uint16_t* o, int64_t ld_o,
+                            int batch, int seq, int heads, int head_dim, bool causal,
+                            hipStream_t stream) {
   if (batch == 0 || seq == 0) return hipSuccess;
-  const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(static_cast<float>(head_dim));
+  // per-lane copy offsets are 32-bit byte offsets within one key block
+  if (static_cast<int64_t>(kBKV) * ld_qkv * 2 >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+  if (head_dim != kD || seq % kBQ != 0) return hipErrorInvalidValue;
+  // log2(e) / sqrt(d), times 1 / kQkScale^2 for the scaled fp16 Q and K
+  const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(static_cast<float>(head_dim)) /
+                           (kQkScale * kQkScale);
   const dim3 grid(static_cast<unsigned>(batch * heads * (seq / kBQ)));
   if (causal)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, grid, dim3(256), 0, stream, qkv_hi, qkv_lo, ld_qkv,
-                       o, ld_o, seq, heads, scale_log2);
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, grid, dim3(64 * kWaves), 0, stream, qkv, ld_qkv, o,
+                       ld_o, seq, heads, scale_log2);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, grid, dim3(256), 0, stream, qkv_hi, qkv_lo, ld_qkv,
-                       o, ld_o, seq, heads, scale_log2);
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, grid, dim3(64 * kWaves), 0, stream, qkv, ld_qkv, o,
+                       ld_o, seq, heads, scale_log2);
   return hipGetLastError();
 }
 

@@ -10,6 +10,9 @@ hipError_t launch_epi(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t
   if (ep.kind == EPI_GELU)
     return ep.out_f32 ? launch_gemm_bf16_cfg<BM, BN, EPI_GELU, true>(A, lda, B, ldb, M, N, K, ep, stream)
                       : launch_gemm_bf16_cfg<BM, BN, EPI_GELU, false>(A, lda, B, ldb, M, N, K, ep, stream);
+  if (ep.kind == EPI_QKV_F16)
+    return ep.out_f32 ? hipErrorInvalidValue
+                      : launch_gemm_bf16_cfg<BM, BN, EPI_QKV_F16, false>(A, lda, B, ldb, M, N, K, ep, stream);
   if (ep.kind != EPI_LINEAR) return hipErrorInvalidValue;
   return ep.out_f32 ? launch_gemm_bf16_cfg<BM, BN, EPI_LINEAR, true>(A, lda, B, ldb, M, N, K, ep, stream)
                     : launch_gemm_bf16_cfg<BM, BN, EPI_LINEAR, false>(A, lda, B, ldb, M, N, K, ep, stream);

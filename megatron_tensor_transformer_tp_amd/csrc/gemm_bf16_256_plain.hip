@@ -19,4 +19,6 @@ template hipError_t launch_gemm_bf16_cfg<256, 256, EPI_LINEAR, true>(const uint1
 
 template hipError_t launch_gemm_bf16_cfg<256, 256, EPI_LINEAR, false>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);
 
+template hipError_t launch_gemm_bf16_cfg<256, 256, EPI_QKV_F16, false>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);
+
 }  // namespace tpk

@@ -141,7 +141,17 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
           if (MASKED && n_lane + col >= N) return;
           float v[4];
           static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] = acc[J][I][4 * G + R]; });
-          if constexpr (EPI == EPI_GELU_BWD) {
+          if constexpr (EPI == EPI_QKV_F16) {
+            static_assert(!OUT_F32, "the packed projection is 16-bit");
+            if (((n_lane + col) / kQkvPart) % 3 < 2) {
+              typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+              const f16x2_t a = {static_cast<_Float16>(v[0] * kQkScale), static_cast<_Float16>(v[1] * kQkScale)};
+              const f16x2_t b = {static_cast<_Float16>(v[2] * kQkScale), static_cast<_Float16>(v[3] * kQkScale)};
+              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(ep.out) + row_out + col) =
+                  u32x2_t{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+              return;
+            }
+          } else if constexpr (EPI == EPI_GELU_BWD) {
             float y[4], h[4];
             load_bf16x4(aux + row_aux + col, y);
             static_for<4>([&](auto R) __attribute__((always_inline)) {
@@ -184,7 +194,7 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
   };
   using T = std::true_type;
   using F = std::false_type;
-  if constexpr (EPI == EPI_GELU_BWD) {
+  if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_QKV_F16) {
     epilogue(F{}, F{}, F{});
   } else if constexpr (EPI == EPI_GELU) {
     if (bias != nullptr) {

@@ -13,7 +13,14 @@ enum EpilogueKind : int {
   EPI_GELU = 1,      // y = acc + bias[n]; pre[m, n] = y (if pre); v = GeLU(y)
   EPI_GELU_BWD = 2,  // y = aux[m, n]; v = acc * GeLU'(y); out2[m, n] = GeLU(y)
   EPI_SWIGLU = 3,    // gate and value columns of one feature: out = SiLU(g) * u
+  EPI_QKV_F16 = 4,   // packed [q | k | v] projection: q, k columns as fp16(v * 2^-8),
+                     // v columns as bf16 (128-column parts, bf16 out only)
 };
+
+// Scale of the fp16 Q and K columns written by EPI_QKV_F16 (their product
+// carries kQkScale^2, removed again in the softmax scale).
+constexpr float kQkScale = 1.0f / 256.0f;
+constexpr int kQkvPart = 128;
 
 // Epilogue applied to the fp32 accumulator of C = A B, element (m, n), then
 //   out[m, n] = v                (fp32, or bf16 rounded to nearest-even)
@@ -88,13 +95,13 @@ hipError_t launch_colsum(const void* in, int64_t ld, int in_dt, int64_t M, int64
 hipError_t launch_zero_2d(void* p, int64_t rows, int64_t cols, int64_t ld, int elt_bytes,
                           hipStream_t stream);
 
-// Head-local attention: qkv_hi/qkv_lo [batch*seq, ld_qkv] bf16 pair holding
-// the rank's packed projection (per head [q | k | v], head_dim columns each);
-// o [batch*seq, ld_o] bf16, head j at columns j*head_dim.  head_dim == 128,
-// seq % 128 == 0.
-hipError_t launch_attention(const uint16_t* qkv_hi, const uint16_t* qkv_lo, int64_t ld_qkv,
-                            uint16_t* o, int64_t ld_o, int batch, int seq, int heads,
-                            int head_dim, bool causal, hipStream_t stream);
+// Head-local attention: qkv [batch*seq, ld_qkv] holding the rank's packed
+// projection as written by EPI_QKV_F16 (per head [q | k | v], head_dim
+// columns each; q and k fp16 scaled by kQkScale, v bf16); o [batch*seq,
+// ld_o] bf16, head j at columns j*head_dim.  head_dim == 128, seq % 128 == 0.
+hipError_t launch_attention(const uint16_t* qkv, int64_t ld_qkv, uint16_t* o, int64_t ld_o,
+                            int batch, int seq, int heads, int head_dim, bool causal,
+                            hipStream_t stream);
 
 // Sequence-parallel reduce-scatter on one device: out[m, :] = sum_{j < t}
 // parts.p[j][row0 + m, :] (+ bias) (+ residual[m, :]) for m < rows; partials

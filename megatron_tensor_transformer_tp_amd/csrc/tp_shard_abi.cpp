@@ -385,15 +385,16 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const vo
 }
 
 namespace {
-// Workspace of tp_attn_shard_fwd: the rank's packed QKV projection as a bf16
-// (hi, lo) pair [tokens, 3*hl*d] each, then the attention output [tokens, hl*d].
+// Workspace of tp_attn_shard_fwd: the rank's packed QKV projection [tokens,
+// 3*hl*d] (q, k columns fp16 scaled, v columns bf16), then the attention
+// output [tokens, hl*d] bf16.
 struct AttnWorkspace {
   size_t qkv_bytes, o_bytes, total;
 };
 AttnWorkspace attn_workspace(int64_t tokens, int64_t hl, int64_t head_dim) {
   const size_t qkv = round256(static_cast<size_t>(tokens) * 3 * hl * head_dim * 2);
   const size_t o = round256(static_cast<size_t>(tokens) * hl * head_dim * 2);
-  return {qkv, o, 2 * qkv + o};
+  return {qkv, o, qkv + o};
 }
 }  // namespace
 
@@ -432,15 +433,15 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  uint16_t* qkv_hi = reinterpret_cast<uint16_t*>(w);
-  uint16_t* qkv_lo = reinterpret_cast<uint16_t*>(w + ws.qkv_bytes);
-  uint16_t* o = reinterpret_cast<uint16_t*>(w + 2 * ws.qkv_bytes);
-  // 1. Column-parallel packed QKV projection of the rank's heads, kept as a
-  //    bf16 (hi, lo) pair so that Q K^T keeps ~16 significant bits.
-  tpk::Epilogue ep1{nullptr, nullptr, 0, qkv_hi, 3 * dl, false, tpk::EPI_LINEAR, qkv_lo};
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(w);
+  uint16_t* o = reinterpret_cast<uint16_t*>(w + ws.qkv_bytes);
+  // 1. Column-parallel packed QKV projection of the rank's heads; Q and K
+  //    leave the fp32 accumulator as scaled fp16 (11 significant bits for
+  //    Q K^T), V as bf16.
+  tpk::Epilogue ep1{nullptr, nullptr, 0, qkv, 3 * dl, false, tpk::EPI_QKV_F16};
   TP_TRY(run_gemm(in_dt, x, hidden, wqkv_i, 3 * dl, tokens, 3 * dl, hidden, ep1, s));
   // 2. softmax(Q K^T / sqrt(d)) V per local head.
-  TP_TRY(from_hip(tpk::launch_attention(qkv_hi, qkv_lo, 3 * dl, o, dl, static_cast<int>(batch),
+  TP_TRY(from_hip(tpk::launch_attention(qkv, 3 * dl, o, dl, static_cast<int>(batch),
                                         static_cast<int>(seq), static_cast<int>(hl),
                                         static_cast<int>(head_dim), causal == 1, s)));
   // 3. Row-parallel output projection: the rank's full-hidden partial.

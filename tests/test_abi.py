@@ -199,8 +199,8 @@ def test_attn_shard_validation(lib):
     assert attn(lib, x=None) == INVALID
     assert attn(lib, out=P + 8) == MISALIGNED
     need = lib.tp_attn_shard_workspace_bytes(1, 256, 1024, 8, 128, 2, BF16)
-    # (hi, lo) projection pair [256, 3*4*128] bf16 + output [256, 4*128] bf16
-    assert need == 2 * 256 * 1536 * 2 + 256 * 512 * 2
+    # packed projection [256, 3*4*128] (16-bit) + output [256, 4*128] bf16
+    assert need == 256 * 1536 * 2 + 256 * 512 * 2
     assert attn(lib, ws_bytes=need - 1) == WORKSPACE
     assert attn(lib, ws=P + 16) == MISALIGNED
     assert attn(lib, batch=0, ws=None) == OK
