@@ -156,7 +156,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   const int wm = wave / WGN, wn = wave % WGN;
 
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, M / BM, N / BN, tm, tn);
+  if (!(BM == 256 && BN == 256 && tile_coords_rounds(blockIdx.x, gridDim.x, M / BM, N / BN, tm, tn)))
+    tile_coords(blockIdx.x, gridDim.x, M / BM, N / BN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int nk = K / kBKd;
 

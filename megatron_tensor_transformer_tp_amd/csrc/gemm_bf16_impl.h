@@ -71,6 +71,27 @@ __device__ __forceinline__ void tile_coords(int bid, int nblk, int tiles_m, int 
   tn = in_group / gsize;
 }
 
+// Round-synchronous order for one-tile-per-CU grids: workgroup b runs on
+// XCD b % 8 as that XCD's (b / 8)-th tile; an XCD's tiles come in rounds of
+// 32 (one per CU of the XCD), and round r of all XCDs covers one compact
+// block of (256 / tiles_n) x tiles_n tiles, XCD x taking a 4 x 8 sub-block.
+// The operand panels live in one round (A rows of the block + all of B) fit
+// in the last-level (MALL) cache, while each XCD's L2 still sees only 4 + 8
+// panels per round.  Applies when tiles_n is 8, 16 or 32 and tiles_m a
+// multiple of 256 / tiles_n; returns false otherwise.
+__device__ __forceinline__ bool tile_coords_rounds(int bid, int nblk, int tiles_m, int tiles_n,
+                                                   int& tm, int& tn) {
+  if (tiles_n != 8 && tiles_n != 16 && tiles_n != 32) return false;
+  const int rows = 256 / tiles_n;                // tile-rows per round block
+  if (nblk != tiles_m * tiles_n || tiles_m % rows != 0) return false;
+  const int xcd = bid % kXcds, k = bid / kXcds;
+  const int round = k / 32, s = k % 32;
+  const int xr = rows / 4;                       // XCD sub-blocks stacked vertically
+  tm = round * rows + (xcd % xr) * 4 + (s % 4);
+  tn = (xcd / xr) * 8 + s / 4;
+  return true;
+}
+
 __device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
 // Scheduling fence between the k-substeps of the main loop: nothing moves
@@ -194,7 +215,39 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
   };
   using T = std::true_type;
   using F = std::false_type;
-  if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_QKV_F16) {
+  if constexpr (EPI == EPI_GELU_BWD && !MASKED) {
+    // All of the tile's saved pre-activations are loaded first (one memory
+    // latency per tile instead of one per 32 x 32 block), then one sweep
+    // forms acc * GeLU'(y) and GeLU(y).
+    u32x2_t yv[TM][TN][4];
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      const int64_t row_aux = static_cast<int64_t>(m_lane + I * 32) * ep.ldaux + n_lane;
+      static_for<TN>([&](auto J) __attribute__((always_inline)) {
+        static_for<4>([&](auto G) __attribute__((always_inline)) {
+          yv[I][J][G] = *reinterpret_cast<const u32x2_t*>(aux + row_aux + J * 32 + G * 8);
+        });
+      });
+    });
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      const int64_t row_out = static_cast<int64_t>(m_lane + I * 32) * ep.ldo + n_lane;
+      static_for<TN>([&](auto J) __attribute__((always_inline)) {
+        static_for<4>([&](auto G) __attribute__((always_inline)) {
+          const float y[4] = {__uint_as_float(yv[I][J][G][0] << 16),
+                              __uint_as_float(yv[I][J][G][0] & 0xFFFF0000u),
+                              __uint_as_float(yv[I][J][G][1] << 16),
+                              __uint_as_float(yv[I][J][G][1] & 0xFFFF0000u)};
+          float v[4], h[4];
+          static_for<4>([&](auto R) __attribute__((always_inline)) {
+            v[R] = acc[J][I][4 * G + R] * gelu_grad_f32(y[R]);
+            h[R] = gelu_f32(y[R]);
+          });
+          store_x4<OUT_F32>(ep.out, row_out + J * 32 + G * 8, v);
+          store_x4<OUT_F32>(ep.out2, row_out + J * 32 + G * 8, h);
+        });
+        sched_fence();
+      });
+    });
+  } else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_QKV_F16) {
     epilogue(F{}, F{}, F{});
   } else if constexpr (EPI == EPI_GELU) {
     if (bias != nullptr) {
