@@ -24,18 +24,20 @@
 //     serves one head and its K/V stay in that XCD's L2;
 //   * K and V of a 32-key block (16 KiB) arrive by global->LDS copies (saddr
 //     form: uniform base + 32-bit lane offset); 6 LDS stages: the two blocks
-//     being read, two in flight, two being issued;
+//     being read, two in flight, two being issued; the loop is unrolled by 3
+//     so that every LDS fragment address is a loop-invariant register plus
+//     an immediate offset;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_f16, K fragments from LDS (one
 //     ds_read_b128, rows XOR-swizzled by row % 16, read one d-step ahead),
 //     Q fragments held in registers; each lane owns one query and 16 of the
-//     block's 32 keys, so the row max needs one exchange with lane ^ 32; the
-//     logits accumulate in two chains (even / odd d-steps);
+//     block's 32 keys, so the row max needs one exchange with lane ^ 32;
 //   * O^T = V^T P^T: each lane keeps 64 of its query's output dimensions, so
 //     the rescale is lane-local; V^T fragments come straight from the
 //     row-major V block with ds_read_b64_tr_b16 (rows XOR-swizzled by
 //     4 * (row % 4)); P is rounded to bf16 (RNE) for the MFMA; the key order
 //     inside a 16-key MFMA step is permuted identically in P and V;
-//   * exp via v_exp_f32 on log2-scaled logits; the running max starts at a
+//   * exp via v_exp_f32 of fma(score, log2(e) / sqrt(d) * scale, -max) (the
+//     max taken on the raw scores); the running max starts at a
 //     large finite negative value, so fully masked (causal) entries give
 //     exp = 0 and never NaN; it is raised lazily (only when a block's max
 //     exceeds it by more than 8 in log2 units, decided per wave), so the
@@ -130,8 +132,15 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int nblk = CAUSAL ? min(seq / kBKV, (qb + 1) * (kBQ / kBKV)) : seq / kBKV;  // even
   const int nit = nblk / 2;
 
-  // Copies of blocks 2 it and 2 it + 1 (clamped to the last block) into
-  // their stages (block j lives in stage j % kStages).
+  // LDS placement: block j sits in its group's half of the stages (j % 2)
+  // at its iteration's place in a 3-iteration cycle ((j / 2) % 3),
+  //   stage(j) = (j % 2) * 3 * kStage + ((j / 2) % 3) * kStage,
+  // so with the loop unrolled by 3 every fragment address is a per-lane
+  // register (holding the group's 48 KiB) plus a compile-time offset of at
+  // most 32 KiB that the LDS instruction's immediate field carries.
+  auto stage_off = [](int j) { return (j % 2) * 3 * kStage + ((j / 2) % 3) * kStage; };
+
+  // Copies of blocks 2 it and 2 it + 1 (clamped to the last block).
   auto issue = [&](int it) __attribute__((always_inline)) {
     static_for<kCopies>([&](auto Q) __attribute__((always_inline)) {
       const int q = wave * kCopies + Q;
@@ -139,12 +148,11 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
       const int kc = min(j, nblk - 1);
       const int rem = q % kCopiesPerBlock;
       const uint16_t* base = qkv + row0 * ld_qkv + kc * block_step;
-      copy_to_lds_off(base, coff[Q],
-                      smem_base + (j % kStages) * kStage + (rem / 8) * kArr + (rem % 8) * 1024);
+      copy_to_lds_off(base, coff[Q], smem_base + stage_off(j) + (rem / 8) * kArr + (rem % 8) * 1024);
     });
   };
 
-  // Fragment addressing.
+  // Per-lane fragment offsets within the group's stages.
   const int k_row = lane & 31;
   const int k_sw = lane & 15;                  // row % 16 for the K swizzle
   const int gi = lane & 15;
@@ -152,71 +160,69 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int v_sw = (gi >> 2) << 2;             // 4 * (row % 4)
   const int v_chunk = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);  // + 4*dt
   const int v_within = (gi & 1) * 8;
+  const int grp_off = group * 3 * kStage;
+  int k_off[8], v_off[4];
+  static_for<8>([&](auto T) __attribute__((always_inline)) {
+    k_off[T] = grp_off + k_row * (kD * 2) + (((2 * T + h) ^ k_sw) * 16);
+  });
+  static_for<4>([&](auto DT) __attribute__((always_inline)) {
+    v_off[DT] = grp_off + kArr + v_row * (kD * 2) + (((4 * DT + v_chunk) ^ v_sw) * 16) + v_within;
+  });
 
   f32x16_t acc_o[4];
   static_for<4>([&](auto DT) __attribute__((always_inline)) { acc_o[DT] = (f32x16_t)(0.0f); });
   float m_run = kNegBig, l_run = 0.0f;
 
-  issue(0);
-  issue(1);
-  for (int it = 0; it < nit; ++it) {
+  // One iteration: blocks 2 it (group 0) and 2 it + 1 (group 1); U = it % 3.
+  auto step = [&](int it, auto U) __attribute__((always_inline)) {
+    constexpr int ust = U * kStage;
     // blocks 2 it, 2 it + 1 have landed (this wave's copies; the barrier
-    // makes it every wave's); issue blocks 2 it + 4, 2 it + 5 into the stages
-    // that iteration it - 1 read
+    // makes it every wave's); issue blocks 2 it + 4, 2 it + 5 into the
+    // stages that iteration it - 1 read
     wait_vmcnt<kCopies>();
     lds_barrier();
     issue(it + 2);
     const int kb = 2 * it + group;
-    const uint8_t* st = smem + (kb % kStages) * kStage;
-    const uint8_t* kk = st;
-    const uint8_t* vv = st + kArr;
 
-    // S^T of the block's 32 keys: two chains (even / odd d-steps), the K
-    // fragments of d-step T+1 read while the MFMAs of d-step T run.
-    f32x16_t s2[2] = {(f32x16_t)(0.0f), (f32x16_t)(0.0f)};
+    // S^T of the block's 32 keys, the K fragments of d-step T+1 read while
+    // the MFMA of d-step T runs.
+    f32x16_t sv = (f32x16_t)(0.0f);
     f16x8_t kf[2];
-    auto load_k = [&](auto T, auto BUF) __attribute__((always_inline)) {
-      const int off = k_row * (kD * 2) + (((2 * T + h) ^ k_sw) * 16);
-      kf[BUF] = *TPK_LDS(const f16x8_t, kk + off);
-    };
-    load_k(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    kf[0] = *TPK_LDS(const f16x8_t, smem + k_off[0] + ust);
     static_for<8>([&](auto T) __attribute__((always_inline)) {
       constexpr int cur = T & 1;
-      if constexpr (T < 7) load_k(std::integral_constant<int, T + 1>{}, std::integral_constant<int, cur ^ 1>{});
-      s2[cur] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[cur], qf[T], s2[cur], 0, 0, 0);
+      if constexpr (T < 7) kf[cur ^ 1] = *TPK_LDS(const f16x8_t, smem + k_off[T + 1] + ust);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[cur], qf[T], sv, 0, 0, 0);
     });
 
     // V^T fragments of the first 32 output dims load under the softmax.
     i16x4_t vf[2][2][2];
     auto load_v = [&](auto DT, auto BUF) __attribute__((always_inline)) {
-      const int chunk = (4 * DT + v_chunk) ^ v_sw;
-      static_for<2>([&](auto U) __attribute__((always_inline)) {
-        const int r0 = 16 * U + v_row;
-        vf[BUF][U][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TPK_LDS(i16x4_t, vv + r0 * (kD * 2) + chunk * 16 + v_within));
-        vf[BUF][U][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TPK_LDS(i16x4_t, vv + (r0 + 8) * (kD * 2) + chunk * 16 + v_within));
+      static_for<2>([&](auto U2) __attribute__((always_inline)) {
+        vf[BUF][U2][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TPK_LDS(i16x4_t, smem + v_off[DT] + ust + (16 * U2) * (kD * 2)));
+        vf[BUF][U2][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TPK_LDS(i16x4_t, smem + v_off[DT] + ust + (16 * U2 + 8) * (kD * 2)));
       });
     };
     load_v(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
 
     // Online softmax over the block (this lane: its query, 16 of the 32
-    // keys: S^T rows 8 (R / 4) + 4 h + R % 4).  The running max is raised
-    // (and the accumulator rescaled) only when the block's max exceeds it by
-    // more than kRescaleSlack, decided for the whole wave at once; otherwise
-    // the weights exp2(s - m_run) may grow up to 2^kRescaleSlack.
-    f32x16_t sv = s2[0] + s2[1];
-    float mx = kNegBig;
+    // keys: S^T rows 8 (R / 4) + 4 h + R % 4), on the raw scores: the max
+    // commutes with the positive scale, which enters the exponent through
+    // one fma.  The running max is raised (and the accumulator rescaled) only
+    // when the block's max exceeds it by more than kRescaleSlack, decided
+    // for the whole wave at once; otherwise the weights may grow up to
+    // 2^kRescaleSlack.
+    float mraw = kNegBig;
     static_for<16>([&](auto R) __attribute__((always_inline)) {
-      float v = sv[int(R)] * scale_log2;
       if constexpr (CAUSAL) {
         const int key = kb * kBKV + 8 * (R / 4) + 4 * h + (R % 4);
-        if (key > query) v = -__builtin_inff();
+        if (key > query) sv[int(R)] = -__builtin_inff();
       }
-      sv[int(R)] = v;
-      mx = fmaxf(mx, v);
+      mraw = fmaxf(mraw, sv[int(R)]);
     });
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = fmaxf(mraw, __shfl_xor(mraw, 32)) * scale_log2;
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     }
     float lsum = 0.0f;
     static_for<16>([&](auto R) __attribute__((always_inline)) {
-      const float p = __builtin_amdgcn_exp2f(sv[int(R)] - m_run);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[int(R)], scale_log2, -m_run));
       sv[int(R)] = p;
       lsum += p;
     });
@@ -235,26 +241,34 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     // P^T fragments: step u covers keys 16u .. 16u+15; half h holds keys
     // {4h..4h+3, 8+4h..8+4h+3} of the step, V^T uses the same order.
     bf16x8_t pf[2];
-    static_for<2>([&](auto U) __attribute__((always_inline)) {
+    static_for<2>([&](auto U2) __attribute__((always_inline)) {
       i16x8_t w;
       static_for<4>([&](auto R) __attribute__((always_inline)) {
-        w[int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(sv[8 * U + int(R)]));
-        w[4 + int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(sv[8 * U + 4 + int(R)]));
+        w[int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(sv[8 * U2 + int(R)]));
+        w[4 + int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(sv[8 * U2 + 4 + int(R)]));
       });
-      pf[U] = __builtin_bit_cast(bf16x8_t, w);
+      pf[U2] = __builtin_bit_cast(bf16x8_t, w);
     });
 
     // O^T += V^T P^T, the next 32 dims' V^T fragments loading under the MFMAs.
     static_for<4>([&](auto DT) __attribute__((always_inline)) {
       constexpr int cur = DT & 1;
       if constexpr (DT < 3) load_v(std::integral_constant<int, DT + 1>{}, std::integral_constant<int, cur ^ 1>{});
-      static_for<2>([&](auto U) __attribute__((always_inline)) {
-        const i16x8_t w = {vf[cur][U][0][0], vf[cur][U][0][1], vf[cur][U][0][2], vf[cur][U][0][3],
-                           vf[cur][U][1][0], vf[cur][U][1][1], vf[cur][U][1][2], vf[cur][U][1][3]};
-        acc_o[DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf[U],
+      static_for<2>([&](auto U2) __attribute__((always_inline)) {
+        const i16x8_t w = {vf[cur][U2][0][0], vf[cur][U2][0][1], vf[cur][U2][0][2], vf[cur][U2][0][3],
+                           vf[cur][U2][1][0], vf[cur][U2][1][1], vf[cur][U2][1][2], vf[cur][U2][1][3]};
+        acc_o[DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf[U2],
                                                              acc_o[DT], 0, 0, 0);
       });
     });
+  };
+
+  issue(0);
+  issue(1);
+  for (int it = 0; it < nit; it += 3) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 < nit) step(it + 2, std::integral_constant<int, 2>{});
   }
   wait_vmcnt<0>();
 
