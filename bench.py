@@ -163,11 +163,10 @@ PROFILED = {
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K "
                        "(fp16) and V (bf16) read once, O written (bf16)",
                        "attention_core_t8_h8192_s4096"),
-    "attn_qkv_gemm": ("gemm_bf16_dma_kernel<128, 128, 2, 2, 4, false, true, 4, false>",
-                      (_S // 128) * (3 * _DL // 128) * 256,
+    "attn_qkv_gemm": (_GEMM + "false, true, 4, false>", (_S // 256) * (3 * _DL // 256) * 512,
                       2.0 * _S * _H * 3 * _DL, 2 * (_S * _H + _H * 3 * _DL + _S * 3 * _DL),
                       "attention rank shard packed QKV projection, M=4096, K=8192, N=3072 "
-                      "(128 x 128 tiles), q/k written as scaled fp16, v as bf16",
+                      "(one round of 192 256 x 256 tiles), q/k written as scaled fp16, v as bf16",
                       "attn_qkv_gemm_t8_h8192_s4096"),
     "attn_out_gemm": (_GEMM + "false, true, 0, true>", (_S // 256) * (_H // 256) * 512,
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
