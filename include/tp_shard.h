@@ -184,9 +184,8 @@ size_t tp_mlp_swiglu_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64
  *             projection                                   (in_dt)
  *   b_i       [f, hidden] contiguous                       (in_dt)
  *   bias_b, residual, z_i, workspace: as for tp_mlp_shard_fwd.
- * f = ffn / t with ffn the width of each projection.  bf16 inputs: tokens a
- * multiple of 256, f of 128 and hidden of 32 (TP_ERR_UNSUPPORTED
- * otherwise); fp32: any shape.  dtype pairs as for tp_mlp_shard_fwd.
+ * f = ffn / t with ffn the width of each projection.  Any tokens; widths,
+ * leading dimensions, alignment and dtype pairs as for tp_mlp_shard_fwd.
  */
 tp_status tp_mlp_swiglu_shard_fwd(const void* x, const void* wg_i, const void* wu_i, int64_t lda,
                                   const void* b_i, const void* bias_b, const void* residual,
@@ -222,9 +221,8 @@ size_t tp_mlp_shard_bwd_workspace_bytes(int64_t tokens, int64_t hidden, int64_t 
  *   workspace >= tp_mlp_shard_bwd_workspace_bytes(...), 256-byte aligned,
  *   scratch.
  * dtype pairs (in_dt -> grad_dt): bf16 -> f32, bf16 -> bf16, f32 -> f32.
- * bf16 inputs: tokens, hidden and f must be multiples of 256, else
- * TP_ERR_UNSUPPORTED (fp32: any shape).  tokens == 0 gives zero weight and
- * bias gradients.  dY_i and H_i are rounded to in_dt (bf16: nearest-even)
+ * Any tokens; widths, leading dimensions and alignment as for
+ * tp_mlp_shard_fwd.  tokens == 0 gives zero weight and bias gradients.  dY_i and H_i are rounded to in_dt (bf16: nearest-even)
  * before the weight- and input-gradient products.
  */
 tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const void* b_i,

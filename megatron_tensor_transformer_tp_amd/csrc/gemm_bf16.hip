@@ -39,8 +39,7 @@ hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, con
                               int64_t ldb, bool b_kmajor, int64_t M, int64_t N, int64_t K,
                               const Epilogue& ep, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (K <= 0 || M % 256 != 0 || N % 256 != 0 || K % gemm_detail::kBKd != 0)
-    return hipErrorInvalidValue;
+  if (K <= 0) return hipErrorInvalidValue;
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   if (!a_kmajor && b_kmajor) {
     if (ep.kind == EPI_GELU_BWD) return hipErrorInvalidValue;
@@ -64,8 +63,7 @@ hipError_t launch_gemm_bf16_swiglu(const uint16_t* A, int64_t lda, const uint16_
                                    const uint16_t* Bu, int64_t ldb, int64_t M, int64_t F,
                                    int64_t K, uint16_t* out, int64_t ldo, hipStream_t stream) {
   if (M == 0 || F == 0) return hipSuccess;
-  if (K <= 0 || M % 256 != 0 || F % 128 != 0 || K % gemm_detail::kBKd != 0)
-    return hipErrorInvalidValue;
+  if (K <= 0 || F % 8 != 0) return hipErrorInvalidValue;
   Epilogue ep{nullptr, nullptr, 0, out, ldo, false, EPI_SWIGLU};
   ep.b2 = Bu;
   // the product runs over the 2F interleaved gate / value columns

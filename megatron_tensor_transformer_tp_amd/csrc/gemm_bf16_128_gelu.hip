@@ -6,13 +6,10 @@ namespace tpk {
 template <int BM, int BN, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                 int M, int N, int K, const Epilogue& ep, hipStream_t stream) {
-  // Tile-aligned shapes: the global->LDS copy kernel (4 waves of 64 x 64,
-  // 4 LDS stages, 64 KiB: two workgroups per CU); others the register-staged
-  // kernel, which masks every edge.
-  if (K > 0 && M % BM == 0 && N % BN == 0 && K % gemm_detail::kBKd == 0)
-    return gemm_detail::launch_tile_dma<BM, BN, 2, 2, 4, false, true, EPI, OUT_F32>(
-        A, lda, B, ldb, M, N, K, ep, stream);
-  return gemm_detail::launch_tile<BM, BN, 2, 2, EPI, OUT_F32>(A, lda, B, ldb, M, N, K, ep, stream);
+  // global->LDS copy kernel: 4 waves of 64 x 64, 4 LDS stages of 16 KiB (two
+  // workgroups per CU)
+  return gemm_detail::launch_tile_dma<BM, BN, 2, 2, 4, false, true, EPI, OUT_F32>(
+      A, lda, B, ldb, M, N, K, ep, stream);
 }
 
 template hipError_t launch_gemm_bf16_cfg<128, 128, EPI_GELU, true>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);

@@ -1,5 +1,5 @@
 // bf16 GEMM instantiations with k-major flags A false, B false (A [M, K], B given as [N, K]: dH = dZ B_i^T with the GeLU-backward epilogue, dX = dY A_i^T):
-// 256x256 tiles, global->LDS copy kernel, tile-aligned shapes only.
+// 256x256 tiles, global->LDS copy kernel (ragged M, N and K included).
 #include "gemm_bf16_dma.h"
 
 namespace tpk {

@@ -1,5 +1,5 @@
 // bf16 GEMM instantiations with k-major flags A true, B true (A given as [K, M], B [K, N]: the weight gradients H^T dZ and X^T dY):
-// 256x256 tiles, global->LDS copy kernel, tile-aligned shapes only.
+// 256x256 tiles, global->LDS copy kernel (ragged M, N and K included).
 #include "gemm_bf16_dma.h"
 
 namespace tpk {

@@ -1,10 +1,9 @@
 // bf16 GEMM, C[M,N] = A[M,K] . B[K,N], fp32 accumulation on the gfx950 matrix
 // cores, with both operand tiles brought into LDS by the asynchronous
 // global->LDS copy (global_load_lds_dwordx4) instead of through registers.
-// Used for tile-aligned shapes (M % BM == 0, N % BN == 0, K % 32 == 0): the
-// copy cannot zero-fill a K tail.  Each operand is stored either with k
-// contiguous ("row-major in k": A as [M, K], B as [N, K]) or k-major (A as
-// [K, M], B as [K, N]); the two LDS layouts below serve either operand.
+// Each operand is stored either with k contiguous ("row-major in k": A as
+// [M, K], B as [N, K]) or k-major (A as [K, M], B as [K, N]); the two LDS
+// layouts below serve either operand.
 //
 //   * k-tiles of 32, STAGES LDS stages of (BM + BN) x 64 B (32 KiB each for
 //     256 x 256): tiles kt+1 .. kt+STAGES-1 are in flight while tile kt is
@@ -29,6 +28,15 @@
 //     tile, never for the younger tiles in flight; the barrier is a bare
 //     s_barrier with a compiler memory clobber (a workgroup fence would make
 //     the compiler drain every outstanding copy).
+//   * Ragged shapes: the copy cannot zero-fill, so every copy source is
+//     clamped into the operand instead.  Rows (k-contiguous) or 8-column
+//     chunks (k-major) past M or N re-read the last valid one; their products
+//     reach only outputs that the masked epilogue of an edge tile does not
+//     store.  A K that is not a multiple of 32 (KTAIL) leaves krem valid k in
+//     the last k-tile: its copies past krem re-read valid k, and its fragments
+//     are zeroed there before the last MFMAs.  Requirements: 16-byte aligned
+//     bases and leading dimensions, a k-contiguous operand's K and a k-major
+//     operand's row length multiples of 8.
 #pragma once
 
 #include "gemm_bf16_impl.h"
@@ -42,26 +50,35 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
 // One operand's share of a k-tile: R rows (M or N) x kBKd k, copied by NW
 // waves (Q copies of 1 KiB each per wave).
-template <int R, int NW, bool KMAJOR>
+template <int R, int NW, bool KMAJOR, bool KTAIL>
 struct OperandTile {
   static constexpr int kBytes = R * kBKd * 2;
   static constexpr int Q = kBytes / 1024 / NW;
   static constexpr int CB = R / 8;     // 16-byte chunks per k-row (k-major)
   static_assert(Q * NW * 1024 == kBytes && (!KMAJOR || CB >= 16), "operand tile shape");
 
-  const uint16_t* src[Q];
-  int64_t step;   // elements per k-tile
+  const uint16_t* src[Q];               // sources of k-tile 0
+  const uint16_t* last[KTAIL ? Q : 1];  // sources of the partial last k-tile
+  int64_t step;                         // elements per k-tile
 
-  // Per-lane copy sources for k-tile 0 of the rows [r0, r0 + R).
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int r0, int wave, int lane) {
+  // Per-lane copy sources for the rows [r0, r0 + R) of an operand with `rows`
+  // rows (k-contiguous: rows of [rows, K]; k-major: columns of [K, rows],
+  // rows % 8 == 0), clamped to the last row / chunk.  With KTAIL the last
+  // k-tile starts at k = klast and holds krem valid k.
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int r0, int rows,
+                                       int klast, int krem, int wave, int lane) {
     static_for<Q>([&](auto I) __attribute__((always_inline)) {
       const int slot = (wave * Q + I) * 64 + lane;
       if constexpr (!KMAJOR) {
-        const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
-        src[I] = base + static_cast<int64_t>(r0 + row) * ld + 8 * c;
+        const int row = slot >> 2, kin = 8 * ((slot & 3) ^ ((row >> 2) & 3));
+        const uint16_t* p = base + static_cast<int64_t>(min(r0 + row, rows - 1)) * ld;
+        src[I] = p + kin;
+        if constexpr (KTAIL) last[I] = p + klast + min(kin, krem - 8);
       } else {
         const int krow = slot / CB, c = (slot % CB) ^ ((krow & 3) << 2);
-        src[I] = base + static_cast<int64_t>(krow) * ld + r0 + 8 * c;
+        const uint16_t* p = base + min(r0 + 8 * c, rows - 8);
+        src[I] = p + static_cast<int64_t>(krow) * ld;
+        if constexpr (KTAIL) last[I] = p + static_cast<int64_t>(klast + min(krow, krem - 1)) * ld;
       }
     });
     step = KMAJOR ? static_cast<int64_t>(kBKd) * ld : kBKd;
@@ -71,24 +88,31 @@ struct OperandTile {
   // alternating between the gate projection (even blocks) and the value
   // projection (odd blocks) of the same 32 features, so an MFMA wave whose
   // 64 columns start on an even block holds gate and value of 32 features.
-  // Features [f0, f0 + R/2) of both projections (same ld).
+  // Features [f0, f0 + R/2) of both projections (same ld) of `feats`
+  // features, clamped to the last 8-feature chunk.
   __device__ __forceinline__ void init_dual(const uint16_t* gate, const uint16_t* value, int64_t ld,
-                                            int f0, int wave, int lane) {
+                                            int f0, int feats, int klast, int krem, int wave,
+                                            int lane) {
     static_assert(KMAJOR, "the paired tile is a weight ([K, N]) tile");
     static_for<Q>([&](auto I) __attribute__((always_inline)) {
       const int slot = (wave * Q + I) * 64 + lane;
       const int krow = slot / CB, c = (slot % CB) ^ ((krow & 3) << 2);
       const int blk = c >> 2;
-      const uint16_t* base = (blk & 1) ? value : gate;
-      src[I] = base + static_cast<int64_t>(krow) * ld + f0 + (blk >> 1) * 32 + (c & 3) * 8;
+      const uint16_t* p = ((blk & 1) ? value : gate) +
+                          min(f0 + (blk >> 1) * 32 + (c & 3) * 8, feats - 8);
+      src[I] = p + static_cast<int64_t>(krow) * ld;
+      if constexpr (KTAIL) last[I] = p + static_cast<int64_t>(klast + min(krow, krem - 1)) * ld;
     });
     step = static_cast<int64_t>(kBKd) * ld;
   }
 
-  // Copies of k-tile kc into the LDS region at byte address `lds`.
-  __device__ __forceinline__ void issue(int kc, uint32_t lds, int wave) const {
+  // Copies of k-tile kc (the partial last one if `tail`) into the LDS region
+  // at byte address `lds`.
+  __device__ __forceinline__ void issue(int kc, bool tail, uint32_t lds, int wave) const {
     static_for<Q>([&](auto I) __attribute__((always_inline)) {
-      copy_to_lds(src[I] + kc * step, lds + (wave * Q + I) * 1024);
+      const uint16_t* p = src[I] + kc * step;
+      if constexpr (KTAIL) p = tail ? last[I] : p;
+      copy_to_lds(p, lds + (wave * Q + I) * 1024);
     });
   }
 
@@ -116,13 +140,17 @@ struct OperandTile {
 };
 
 // SwiGLU epilogue: acc[0] holds the gate and acc[1] the value of the same 32
-// features (see OperandTile::init_dual); out[m, n] = SiLU(gate) * value.
-template <int TM, bool OUT_F32>
+// features (see OperandTile::init_dual); out[m, n] = SiLU(gate) * value for
+// m < M and n < F (F % 4 == 0).
+template <int TM, bool MASKED, bool OUT_F32>
 __device__ __forceinline__ void store_swiglu(const f32x16_t (&acc)[2][TM], int m_lane, int n_lane,
-                                             const Epilogue& ep) {
+                                             int M, int F, const Epilogue& ep) {
   static_for<TM>([&](auto I) __attribute__((always_inline)) {
-    const int64_t row = static_cast<int64_t>(m_lane + I * 32) * ep.ldo + n_lane;
+    const int m = m_lane + I * 32;
+    if (MASKED && m >= M) return;
+    const int64_t row = static_cast<int64_t>(m) * ep.ldo + n_lane;
     static_for<4>([&](auto G) __attribute__((always_inline)) {
+      if (MASKED && n_lane + G * 8 >= F) return;
       float h[4];
       static_for<4>([&](auto R) __attribute__((always_inline)) {
         h[R] = silu_f32(acc[0][I][4 * G + R]) * acc[1][I][4 * G + R];
@@ -133,16 +161,28 @@ __device__ __forceinline__ void store_swiglu(const f32x16_t (&acc)[2][TM], int m
   });
 }
 
+// Zeroes the bf16 elements of a fragment whose k (counted from the start of
+// the fragment's 8) is >= nvalid.
+__device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int nvalid) {
+  u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+  static_for<4>([&](auto D) __attribute__((always_inline)) {
+    constexpr int d = D;
+    const uint32_t m = nvalid >= 2 * d + 2 ? 0xFFFFFFFFu : (nvalid == 2 * d + 1 ? 0x0000FFFFu : 0u);
+    w[d] &= m;
+  });
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,
-          bool OUT_F32>
+          bool OUT_F32, bool KTAIL>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     int M, int N, int K, const Epilogue ep) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  using TileA = OperandTile<BM, NW, A_KMAJOR>;
-  using TileB = OperandTile<BN, NW, B_KMAJOR>;
+  using TileA = OperandTile<BM, NW, A_KMAJOR, KTAIL>;
+  using TileB = OperandTile<BN, NW, B_KMAJOR, KTAIL>;
   constexpr int A_BYTES = TileA::kBytes;
   constexpr int STAGE = A_BYTES + TileB::kBytes;
   constexpr int L = TileA::Q + TileB::Q;   // copies per wave per k-tile
@@ -155,27 +195,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lives in an SGPR
   const int wm = wave / WGN, wn = wave % WGN;
 
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  if (!(BM == 256 && BN == 256 && tile_coords_rounds(blockIdx.x, gridDim.x, M / BM, N / BN, tm, tn)))
-    tile_coords(blockIdx.x, gridDim.x, M / BM, N / BN, tm, tn);
+  if (!(BM == 256 && BN == 256 && tile_coords_rounds(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn)))
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = K / kBKd;
+  const int nk = (K + kBKd - 1) / kBKd;
+  const int klast = (nk - 1) * kBKd, krem = K - klast;   // krem == kBKd unless KTAIL
 
   TileA ta;
   TileB tb;
-  ta.init(A, lda, m0, wave, lane);
+  ta.init(A, lda, m0, M, klast, krem, wave, lane);
   if constexpr (EPI == EPI_SWIGLU)
-    tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, wave, lane);
+    tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, N / 2, klast, krem, wave, lane);
   else
-    tb.init(B, ldb, n0, wave, lane);
+    tb.init(B, ldb, n0, N, klast, krem, wave, lane);
 
   // Copies of k-tile kt (clamped to the last tile) into stage kt % STAGES.
   const uint32_t smem_base = lds_address(smem);
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const int kc = min(kt, nk - 1);
+    const bool tail = kt >= nk - 1;
     const uint32_t sbase = smem_base + (kt % STAGES) * STAGE;
-    ta.issue(kc, sbase, wave);
-    tb.issue(kc, sbase + A_BYTES, wave);
+    ta.issue(kc, tail, sbase, wave);
+    tb.issue(kc, tail, sbase + A_BYTES, wave);
   };
 
   bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
@@ -214,7 +257,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   lds_barrier();
   read_frags(0, 0, af0, bf0);
 
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = 0; kt < nk - 1; ++kt) {
     // substep 0 of tile kt: fragments of substep 1 load under its MFMAs
     read_frags(kt, 1, af1, bf1);
     mfmas(af0, bf0);
@@ -231,26 +274,62 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     interleave_substep<kMfma, kFrags, 0, 0, 0>();
     sched_fence();
   }
+  // the last k-tile (its substep-0 fragments are in af0 / bf0)
+  read_frags(nk - 1, 1, af1, bf1);
+  if constexpr (KTAIL) {
+    // lane l's fragments hold k 16 s + 8 (l / 32) .. +7 of the tile
+    const int k_lane = 8 * (lane >> 5);
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      af0[I] = keep_first(af0[I], krem - k_lane);
+      af1[I] = keep_first(af1[I], krem - 16 - k_lane);
+    });
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      bf0[J] = keep_first(bf0[J], krem - k_lane);
+      bf1[J] = keep_first(bf1[J], krem - 16 - k_lane);
+    });
+  }
+  mfmas(af0, bf0);
+  mfmas(af1, bf1);
   wait_vmcnt<0>();
 
+  const bool edge = m0 + BM > M || n0 + BN > N;   // workgroup-uniform
+  const int m_lane = m0 + wm * WM + (lane & 31);
   if constexpr (EPI == EPI_SWIGLU) {
     static_assert(TN == 2, "gate and value blocks per wave");
-    store_swiglu<TM, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
-                              n0 / 2 + wn * (WN / 2) + (lane >> 5) * 4, ep);
+    const int n_lane = n0 / 2 + wn * (WN / 2) + (lane >> 5) * 4;
+    if (edge)
+      store_swiglu<TM, true, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
+    else
+      store_swiglu<TM, false, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
   } else {
-    store_tile<TM, TN, false, EPI, OUT_F32>(acc, m0 + wm * WM + (lane & 31),
-                                             n0 + wn * WN + (lane >> 5) * 4, M, N, ep);
+    const int n_lane = n0 + wn * WN + (lane >> 5) * 4;
+    if (edge)
+      store_tile<TM, TN, true, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
+    else
+      store_tile<TM, TN, false, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
   }
 }
 
+// Any M, N >= 1 and K >= 1 within the requirements above (the shape ones
+// are checked here; the caller guarantees alignment).
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,
           bool OUT_F32>
 hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
                            int N, int K, const Epilogue& ep, hipStream_t stream) {
-  const int tiles = (M / BM) * (N / BN);
-  hipLaunchKernelGGL(
-      (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32>),
-      dim3(tiles), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
+  const int b_rows = EPI == EPI_SWIGLU ? N / 2 : N;   // paired tiles: features
+  if (M <= 0 || N <= 0 || K <= 0 || ((!A_KMAJOR || !B_KMAJOR) && K % 8 != 0) ||
+      (A_KMAJOR && M % 8 != 0) || (B_KMAJOR && b_rows % 8 != 0) ||
+      (EPI == EPI_SWIGLU && N % 2 != 0))
+    return hipErrorInvalidValue;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (K % kBKd != 0)
+    hipLaunchKernelGGL(
+        (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, true>),
+        dim3(tiles), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
+  else
+    hipLaunchKernelGGL(
+        (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, false>),
+        dim3(tiles), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
   return hipGetLastError();
 }
 

@@ -1,9 +1,10 @@
-// bf16 GEMM with fp32 accumulation on gfx950 matrix cores, with the
-// column-/row-parallel epilogues fused in (kernel template; the launch
-// configurations are instantiated in gemm_bf16_*.hip, one translation unit
-// per tile shape and output type, so that they compile in parallel).
+// bf16 GEMM with fp32 accumulation on gfx950 matrix cores: the pieces shared
+// by the kernel (gemm_bf16_dma.h) and its instantiation units
+// (gemm_bf16_*.hip, one per tile shape and operand layout, so that they
+// compile in parallel): workgroup -> tile maps, scheduling helpers and the
+// fused epilogues.
 //
-//   C[M, N] = A[M, K] . B[K, N]      A, B row-major bf16, C fp32 accumulators
+//   C[M, N] = A[M, K] . B[K, N]      bf16 operands, fp32 accumulators
 //
 // The column-parallel linear of a tensor-parallel MLP calls it with
 // A = X [tokens, hidden], B = A_i [hidden, f] and the GeLU epilogue; the
@@ -11,25 +12,10 @@
 // bias/residual epilogue (列并行 tutorial, 数学基础 and MLP 应用; Megatron
 // expert interview Level 2, M025/M026).
 //
-// Design (gfx950, 256 CUs in 8 XCDs, 160 KiB LDS per CU, wave64):
-//   * Workgroup = 4 waves (256 threads) computing a BM x BN tile, BK = 64.
-//     The 4 waves form a 2 x 2 grid; each owns a (BM/2) x (BN/2) sub-tile as
-//     a grid of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16).
-//   * Operand roles inside the MFMA are swapped (the weight fragment is the
-//     MFMA's first operand, the activation fragment the second), so each lane
-//     ends up owning 4 CONSECUTIVE output columns of one row: the epilogue
-//     stores 16-byte fp32 or 8-byte bf16 vectors.
-//   * Both operands are staged in LDS as [row][k] with k contiguous and a
-//     row pitch of 72 elements (144 B = 9 x 16 B).  An MFMA fragment is one
-//     16-byte ds_read per lane; 16 lanes reading 16 consecutive rows at the
-//     same k hit 16 distinct 16-byte bank groups.
-//   * The row-major weight tile [BK, BN] has n contiguous in memory but the
-//     MFMA wants k contiguous per lane: each loader thread fetches an 8x8
-//     block (8 rows of 16 B) and transposes it in registers with v_perm_b32
-//     before the 16-byte LDS stores.
-//   * Two LDS stages (2 x (BM + BN) x 144 B; 144 KiB for 256 x 256) and a
-//     register prefetch of the next k-tile: global loads for k-tile t+1 are
-//     in flight while the MFMAs consume k-tile t; one barrier per k-tile.
+//   * Operand roles inside the MFMA (v_mfma_f32_32x32x16_bf16) are swapped
+//     (the B fragment is the MFMA's first operand, the A fragment the second),
+//     so each lane ends up owning 4 CONSECUTIVE output columns of one row: the
+//     epilogue stores 16-byte fp32 or 8-byte bf16 vectors.
 //   * Workgroup -> tile mapping is XCD-aware: consecutive workgroup ids are
 //     dealt round-robin to the 8 XCDs, so ids are first regrouped so that
 //     each XCD owns a contiguous range of logical tiles, then tiles are
@@ -52,8 +38,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;
-constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 elements (144 B)
 constexpr int kBKd = 32;         // k-tile of the global->LDS copy kernel
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
@@ -91,8 +75,6 @@ __device__ __forceinline__ bool tile_coords_rounds(int bid, int nblk, int tiles_
   tn = (xcd / xr) * 8 + s / 4;
   return true;
 }
-
-__device__ __forceinline__ u32x4_t zero4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
 // Scheduling fence between the k-substeps of the main loop: nothing moves
 // across it, so the LDS reads issued in substep s for substep s+1 stay ahead
@@ -285,196 +267,6 @@ __device__ __forceinline__ void interleave_substep() {
   });
 }
 
-// BM x BN tile per workgroup of WGM x WGN waves; each wave owns a
-// (BM/WGM) x (BN/WGN) sub-tile of 32x32 MFMA blocks.
-template <int BM, int BN, int WGM, int WGN, bool MASKED, int EPI, bool OUT_F32>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    int M, int N, int K, const Epilogue ep) {
-  constexpr int NT = 64 * WGM * WGN;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_CHUNKS = BM * kBK / 8 / NT;  // 16-byte chunks of the A tile per thread
-  constexpr int RB = kBK * BN / 8 / NT;        // k-rows of the B tile per thread (x 8 columns)
-  constexpr int KG = kBK / RB;                 // k-groups of RB rows
-  static_assert(A_CHUNKS >= 1 && (RB == 2 || RB == 4 || RB == 8) && KG * (BN / 8) == NT,
-                "tile / thread shape");
-
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kPitch];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lives in an SGPR
-  const int wm = wave / WGN, wn = wave % WGN;
-
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = (K + kBK - 1) / kBK;
-
-  // A loader: chunk i of thread t is row i*(NT/8) + t/8, k-chunk t%8.
-  const int a_row = tid >> 3, a_kc = tid & 7;
-  // B loader: thread t covers k-rows (t%KG)*RB .. +RB-1 of columns (t/KG)*8 .. +7.
-  const int b_kb = tid % KG, b_nb = tid / KG;
-
-  u32x4_t ra[A_CHUNKS];
-  u32x4_t rb[RB];
-
-  auto load_a = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * kBK;
-    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
-      const int gm = m0 + I * (NT / 8) + a_row, gk = k0 + a_kc * 8;
-      if (!MASKED || (gm < M && gk < K))
-        ra[I] = *reinterpret_cast<const u32x4_t*>(A + static_cast<int64_t>(gm) * lda + gk);
-      else
-        ra[I] = zero4();
-    });
-  };
-  auto load_b = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * kBK;
-    static_for<RB>([&](auto J) __attribute__((always_inline)) {
-      const int gk = k0 + b_kb * RB + J, gn = n0 + b_nb * 8;
-      if (!MASKED || (gk < K && gn < N))
-        rb[J] = *reinterpret_cast<const u32x4_t*>(B + static_cast<int64_t>(gk) * ldb + gn);
-      else
-        rb[J] = zero4();
-    });
-  };
-  auto store_a = [&](int buf) __attribute__((always_inline)) {
-    static_for<A_CHUNKS>([&](auto I) __attribute__((always_inline)) {
-      *reinterpret_cast<u32x4_t*>(&sA[buf][(I * (NT / 8) + a_row) * kPitch + a_kc * 8]) = ra[I];
-    });
-  };
-  auto store_b = [&](int buf) __attribute__((always_inline)) {
-    // rb[j] holds B[k0 + kb*RB + j][n0 + nb*8 .. +7]; column e of this RB x 8
-    // block becomes RB consecutive k values of LDS row n = nb*8 + e.
-    static_for<8>([&](auto E) __attribute__((always_inline)) {
-      constexpr int q = E >> 1;
-      constexpr uint32_t sel = (E & 1) ? 0x07060302u : 0x05040100u;
-      uint16_t* dst = &sB[buf][(b_nb * 8 + E) * kPitch + b_kb * RB];
-      if constexpr (RB == 8) {
-        u32x4_t t;
-        t[0] = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
-        t[1] = __builtin_amdgcn_perm(rb[3][q], rb[2][q], sel);
-        t[2] = __builtin_amdgcn_perm(rb[5][q], rb[4][q], sel);
-        t[3] = __builtin_amdgcn_perm(rb[7][q], rb[6][q], sel);
-        *reinterpret_cast<u32x4_t*>(dst) = t;
-      } else if constexpr (RB == 4) {
-        u32x2_t t;
-        t[0] = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
-        t[1] = __builtin_amdgcn_perm(rb[3][q], rb[2][q], sel);
-        *reinterpret_cast<u32x2_t*>(dst) = t;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(rb[1][q], rb[0][q], sel);
-      }
-    });
-  };
-
-  // MFMA operand fragments, double-buffered by k-substep parity.
-  const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
-  const int a_frag = (wm * WM + frag_row) * kPitch + frag_k;
-  const int b_frag = (wn * WN + frag_row) * kPitch + frag_k;
-  bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
-  auto read_frags = [&](int buf, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
-      __attribute__((always_inline)) {
-    const uint16_t* a_s = sA[buf] + a_frag + s * 16;
-    const uint16_t* b_s = sB[buf] + b_frag + s * 16;
-    static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      af[I] = *reinterpret_cast<const bf16x8_t*>(a_s + I * 32 * kPitch);
-    });
-    static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      bf[J] = *reinterpret_cast<const bf16x8_t*>(b_s + J * 32 * kPitch);
-    });
-  };
-
-  f32x16_t acc[TN][TM];
-  static_for<TN>([&](auto J) __attribute__((always_inline)) {
-    static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      acc[J][I] = (f32x16_t)(0.0f);
-    });
-  });
-  auto mfmas = [&](const bf16x8_t(&af)[TM], const bf16x8_t(&bf)[TN]) __attribute__((always_inline)) {
-    static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      static_for<TM>([&](auto I) __attribute__((always_inline)) {
-        acc[J][I] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[J], af[I], acc[J][I], 0, 0, 0);
-      });
-    });
-  };
-
-  // Software pipeline over k-tiles (4 k-substeps of 16 each).  In iteration kt
-  // the registers ra/rb hold k-tile kt+1 (loaded one iteration earlier):
-  //   s0: LDS-store A of tile kt+1 into the other stage, issue global loads of
-  //       A for tile kt+2, read fragments of s1, MFMAs of s0
-  //   s1: same for B (with the in-register transposes), fragments of s2, MFMAs of s1
-  //   s2: fragments of s3, MFMAs of s2
-  //   s3: barrier (tile kt+1 complete in the other stage, all reads of this
-  //       stage done), fragments of tile kt+1 s0, MFMAs of s3
-  // The prefetch index is clamped to the last tile, so the loop body has no
-  // branches; the clamped loads re-read a tile that is never consumed.
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  store_b(0);
-  const int k_second = nk > 1 ? 1 : 0;
-  load_a(k_second);
-  load_b(k_second);
-  __syncthreads();
-  read_frags(0, 0, af0, bf0);
-
-  constexpr int kFrags = TM + TN;
-  constexpr int kMfma = TM * TN;
-  constexpr int kPermsB = 8 * (RB / 2);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
-    const int kpre = min(kt + 2, nk - 1);
-    // s0
-    read_frags(cur, 1, af1, bf1);
-    store_a(nxt);
-    load_a(kpre);
-    mfmas(af0, bf0);
-    interleave_substep<kMfma, kFrags, 0, A_CHUNKS, A_CHUNKS>();
-    sched_fence();
-    // s1
-    read_frags(cur, 2, af0, bf0);
-    store_b(nxt);
-    load_b(kpre);
-    mfmas(af1, bf1);
-    interleave_substep<kMfma, kFrags, kPermsB, 8, RB>();
-    sched_fence();
-    // s2
-    read_frags(cur, 3, af1, bf1);
-    mfmas(af0, bf0);
-    interleave_substep<kMfma, kFrags, 0, 0, 0>();
-    sched_fence();
-    // s3: tile kt+1 is complete in the other stage after the barrier
-    __syncthreads();
-    read_frags(nxt, 0, af0, bf0);
-    mfmas(af1, bf1);
-    interleave_substep<kMfma, kFrags, 0, 0, 0>();
-    sched_fence();
-  }
-
-  store_tile<TM, TN, MASKED, EPI, OUT_F32>(acc, m0 + wm * WM + (lane & 31), n0 + wn * WN + (lane >> 5) * 4,
-                                          M, N, ep);
-}
-
-template <int BM, int BN, int WGM, int WGN, int EPI, bool OUT_F32>
-hipError_t launch_tile(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int M,
-                       int N, int K, const Epilogue& ep, hipStream_t stream) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const bool masked = (M % BM) || (N % BN) || (K % kBK);
-  const dim3 block(64 * WGM * WGN);
-  if (masked)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, true, EPI, OUT_F32>), dim3(tiles), block,
-                       0, stream, A, lda, B, ldb, M, N, K, ep);
-  else
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, false, EPI, OUT_F32>), dim3(tiles), block,
-                       0, stream, A, lda, B, ldb, M, N, K, ep);
-  return hipGetLastError();
-}
-
 }  // namespace gemm_detail
 
 // One explicit instantiation set per (tile shape, epilogue kind, output type);
@@ -483,8 +275,8 @@ template <int BM, int BN, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                 int M, int N, int K, const Epilogue& ep, hipStream_t stream);
 
-// Tile-aligned products with k-major flags (256 x 256 tiles, copy kernel);
-// defined in the gemm_bf16_256_*.hip translation units.
+// Products with k-major flags (256 x 256 tiles, copy kernel); defined in the
+// gemm_bf16_256_*.hip translation units.
 template <bool A_KMAJOR, bool B_KMAJOR, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_t_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                   int M, int N, int K, const Epilogue& ep, hipStream_t stream);

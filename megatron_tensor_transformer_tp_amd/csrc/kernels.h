@@ -47,8 +47,10 @@ struct Epilogue {
 };
 
 // bf16 x bf16 -> fp32 accumulate, MFMA.  A [M, K] row-major (lda), B [K, N]
-// row-major (ldb).  Requires N % 8 == 0, K % 8 == 0, lda/ldb/ldr/ldo % 8 == 0
-// (ldo % 4 for fp32 out), 16-byte aligned pointers.  EPI_LINEAR / EPI_GELU.
+// row-major (ldb).  Any M, N and K >= 1 with N % 8 == 0, K % 8 == 0,
+// lda/ldb/ldr/ldo % 8 == 0 (ldo % 4 for fp32 out), 16-byte aligned pointers
+// (else hipErrorInvalidValue where checked).  EPI_LINEAR / EPI_GELU /
+// EPI_QKV_F16.
 hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                             int64_t M, int64_t N, int64_t K, const Epilogue& ep,
                             hipStream_t stream);
@@ -57,16 +59,19 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, i
 //   a_kmajor: A given as [K, M] row-major (lda >= M), i.e. the product uses Aᵀ of it;
 //   b_kmajor: B given as [K, N] row-major (the usual form); false: B given as
 //             [N, K] row-major (ldb >= K).
-// Tile-aligned shapes only: M % 256 == N % 256 == K % 32 == 0 (else
-// hipErrorInvalidValue).  Every epilogue kind.
+// Any M, N and K >= 1 with the dimension that is contiguous in memory a
+// multiple of 8 for each operand (K for a k-contiguous one, M or N for a
+// k-major one), alignment as above.  Layout pairs and epilogues: (false,
+// true) as launch_gemm_bf16; (false, false) EPI_LINEAR and bf16 EPI_GELU_BWD;
+// (true, true) EPI_LINEAR (else hipErrorInvalidValue).
 hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B,
                               int64_t ldb, bool b_kmajor, int64_t M, int64_t N, int64_t K,
                               const Epilogue& ep, hipStream_t stream);
 
 // SwiGLU column layer: out[m, j] = SiLU((A Bg)[m, j]) * (A Bu)[m, j], j < F,
 // A [M, K] row-major, Bg and Bu [K, F] row-major with the same ldb, out bf16
-// [M, F] (ldo).  One product over both projections: M % 256 == 0,
-// F % 128 == 0, K % 32 == 0 (else hipErrorInvalidValue).
+// [M, F] (ldo).  One product over both projections: any M, F % 8 == 0,
+// K % 8 == 0, K >= 1 (else hipErrorInvalidValue).
 hipError_t launch_gemm_bf16_swiglu(const uint16_t* A, int64_t lda, const uint16_t* Bg,
                                    const uint16_t* Bu, int64_t ldb, int64_t M, int64_t F,
                                    int64_t K, uint16_t* out, int64_t ldo, hipStream_t stream);

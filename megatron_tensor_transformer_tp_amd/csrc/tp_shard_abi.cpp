@@ -79,7 +79,7 @@ tp_status run_gemm(tp_dtype in_dt, const void* a, int64_t lda, const void* b, in
 }
 
 // The same with k-major flags (A given [K, M] if a_kmajor; B given [K, N] if
-// b_kmajor, else [N, K]).  bf16 needs tile-aligned shapes (checked by callers).
+// b_kmajor, else [N, K]).
 tp_status run_gemm_t(tp_dtype in_dt, const void* a, int64_t lda, bool a_kmajor, const void* b,
                      int64_t ldb, bool b_kmajor, int64_t M, int64_t N, int64_t K,
                      const tpk::Epilogue& ep, hipStream_t stream) {
@@ -258,8 +258,6 @@ tp_status tp_mlp_swiglu_shard_fwd(const void* x, const void* wg_i, const void* w
   const void* res_use = owner ? residual : nullptr;
   TP_TRY(check_optional_vec(bias_use));
   TP_TRY(check_optional_vec(res_use));
-  if (in_dt == TP_BF16 && (tokens % 256 != 0 || f % 128 != 0 || hidden % 32 != 0))
-    return TP_ERR_UNSUPPORTED;
   const size_t need = tp_mlp_swiglu_shard_workspace_bytes(tokens, hidden, ffn, t, in_dt);
   if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;
@@ -335,8 +333,6 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const vo
     TP_TRY(check_matrix(dz, hidden, hidden, in_dt));
     TP_TRY(check_matrix(dx_i, hidden, hidden, grad_dt));
   }
-  if (in_dt == TP_BF16 && (tokens % 256 != 0 || hidden % 256 != 0 || f % 256 != 0))
-    return TP_ERR_UNSUPPORTED;
   const MlpBwdWorkspace ws = mlp_bwd_workspace(tokens, hidden, f, in_dt);
   if (workspace == nullptr || workspace_bytes < ws.total) return TP_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;

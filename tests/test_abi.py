@@ -170,12 +170,12 @@ def test_mlp_shard_bwd_validation(lib):
     assert bwd(lib, da=None) == INVALID
     assert bwd(lib, lda=500) == INVALID
     assert bwd(lib, dba=P + 4) == MISALIGNED
-    # the bf16 kernels take tile-aligned shapes only
-    assert bwd(lib, tokens=300) == UNSUPPORTED
-    assert bwd(lib, hidden=1032) == UNSUPPORTED
-    assert bwd(lib, ffn=8 * 264, lda=264) == UNSUPPORTED
-    # fp32 takes any shape: the same call gets past the shape check (and stops
-    # at the workspace size, before any launch)
+    # widths must be multiples of 8 (bf16) / 4 (fp32)
+    assert bwd(lib, hidden=1028) == MISALIGNED
+    assert bwd(lib, ffn=8 * 260, lda=260) == MISALIGNED
+    # any token count and 8-aligned widths get past the shape checks (and
+    # stop at the workspace size, before any launch)
+    assert bwd(lib, tokens=300, hidden=1032, ffn=8 * 264, lda=264, ws_bytes=1) == WORKSPACE
     assert bwd(lib, in_dt=F32, tokens=300, hidden=1000, ffn=4000, lda=500, ws_bytes=1) == WORKSPACE
 
 
@@ -259,8 +259,9 @@ def test_swiglu_validation(lib):
     assert swiglu(lib, wu=None) == INVALID
     assert swiglu(lib, wg=P + 8) == MISALIGNED
     assert swiglu(lib, in_dt=F32, out_dt=BF16) == DTYPE
-    assert swiglu(lib, tokens=300) == UNSUPPORTED          # bf16: tokens % 256
-    assert swiglu(lib, ffn=8 * 136, lda=136) == UNSUPPORTED  # bf16: f % 128
+    assert swiglu(lib, ffn=8 * 132, lda=132) == MISALIGNED   # f % 8
+    # any token count and 8-aligned widths get past the shape checks
+    assert swiglu(lib, tokens=300, ffn=8 * 136, lda=136, hidden=1000, ws_bytes=1) == WORKSPACE
     assert swiglu(lib, ws_bytes=need - 1) == WORKSPACE
     assert swiglu(lib, in_dt=F32, tokens=300, ws_bytes=1) == WORKSPACE   # fp32: any shape
     assert swiglu(lib, tokens=0, ws=None) == OK

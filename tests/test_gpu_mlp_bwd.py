@@ -104,6 +104,29 @@ def test_f32_ragged_tokens():
     check_grads(got, ref, "f32", "ragged f32")
 
 
+@pytest.mark.parametrize("tokens,hidden,f,grad_dt", [
+    (1, 64, 64, "f32"),
+    (77, 136, 200, "f32"),
+    (300, 264, 360, "bf16"),
+    (513, 1024, 520, "f32"),
+])
+def test_bf16_ragged_shapes(tokens, hidden, f, grad_dt):
+    """bf16 shapes off every tile: token counts that are ragged against the
+    256-row tiles and, as the k extent of the weight-gradient products,
+    against the 32-deep k-tiles; hidden and f ragged against both."""
+    wl = inputs.MlpWorkload(f"bwd_{tokens}_{hidden}_{f}", tokens, hidden, 2 * f, 2, "bf16", 1.0,
+                            0.05, 0.05, "f32")
+    x, dz = inputs.mlp_x_rows(wl), inputs.mlp_dz_rows(wl)
+    a, b = inputs.mlp_a_block(wl, 1), inputs.mlp_b_block(wl, 1)
+    xd, ad, bd = dev(x, "bf16"), dev(a, "bf16"), dev(b, "bf16")
+    say(f"backward tokens={tokens} hidden={hidden} f={f} grads {grad_dt}")
+    _z, y = run_fwd_save(wl, 1, xd, ad, bd)
+    ref = shard_ref(host64(x, "bf16"), host64(a, "bf16"), host64(b, "bf16"), host64(dz, "bf16"))
+    assert_close(to_np(y), ref["y"], "bf16", "ragged saved pre-activation")
+    got = run_bwd(wl, 1, xd, ad, bd, y, dev(dz, "bf16"), grad_dt)
+    check_grads(got, ref, "bf16", f"ragged {tokens}x{hidden}x{f} grads {grad_dt}")
+
+
 @pytest.mark.parametrize("grad_dt", ["f32", "bf16"])
 def test_t1_bf16(grad_dt):
     wl = inputs.MLP_WORKLOADS["t1_h1024_m2048"]
@@ -178,8 +201,9 @@ def test_zero_tokens_and_errors():
     got = run_bwd(wl, 0, empty, ad, bd, y0, empty, "f32")
     for k in ("da", "db", "dbias_a", "dbias_b"):
         assert (got[k] == 0).all(), f"{k} must be zero for zero tokens"
-    # bf16 needs tile-aligned shapes: 300 tokens is refused before any launch
-    x = dev(inputs.mlp_x_rows(wl, 0, 300), "bf16")
-    y = torch.zeros((300, wl.f), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(binding.TpError, match="UNSUPPORTED"):
-        run_bwd(wl, 0, x, ad, bd, y, x, "f32")
+    # a width that is not a multiple of 8 is refused before any launch
+    wm = inputs.MlpWorkload("misaligned", 16, 1028, 2 * 1028, 2, "bf16", 1.0, 0.05, 0.05, "f32")
+    x = torch.zeros((16, 1028), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((1028, 1028), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(binding.TpError, match="MISALIGNED"):
+        run_bwd(wm, 0, x, w, w, w[:16], x, "f32")

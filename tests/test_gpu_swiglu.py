@@ -102,6 +102,22 @@ def test_strided_weight_views_and_f32_ragged():
     fg, fu, fb = full_weights(wt)
     assert_close(z, oracle.swiglu_mlp_shard(xs, fg, fu, fb, wt.t, 1), "f32", "swiglu fp32 ragged",
                  rms_floor=True)
-    # bf16 needs 256-token tiles
-    with pytest.raises(binding.TpError, match="UNSUPPORTED"):
-        run(wl, 0, dev(x[:300], "bf16"), wgd[:, :wl.f], wud[:, :wl.f], dev(inputs.mlp_b_block(wl, 0), "bf16"), 300)
+
+
+@pytest.mark.parametrize("tokens,hidden,f", [(1, 64, 64), (77, 136, 200), (300, 264, 360), (513, 1024, 520)])
+def test_bf16_ragged_shapes(tokens, hidden, f):
+    """bf16 shapes off every tile: ragged tokens, a feature count that ends
+    inside a paired gate / value tile, and k extents (hidden, f) that end
+    inside a 32-deep k-tile."""
+    wl = inputs.MlpWorkload(f"swiglu_{tokens}_{hidden}_{f}", tokens, hidden, 2 * f, 2, "bf16", 1.0,
+                            0.05, 0.05, "f32")
+    x = inputs.mlp_x_rows(wl)
+    wg, wu, b = full_weights(wl)
+    bb, res = inputs.mlp_bias_b(wl), inputs.mlp_residual_rows(wl)
+    say(f"swiglu tokens={tokens} hidden={hidden} f={f} rank 0")
+    z = to_np(run(wl, 0, dev(x, "bf16"), dev(inputs.mlp_wg_block(wl, 0), "bf16"),
+                  dev(inputs.mlp_wu_block(wl, 0), "bf16"), dev(inputs.mlp_b_block(wl, 0), "bf16"),
+                  tokens, bias_b=dev(bb, "bf16"), residual=dev(res, "bf16")))
+    ref = oracle.swiglu_mlp_shard(host64(x, "bf16"), host64(wg, "bf16"), host64(wu, "bf16"),
+                                  host64(b, "bf16"), wl.t, 0, host64(bb, "bf16"), host64(res, "bf16"))
+    assert_close(z, ref, "bf16", f"swiglu ragged {tokens}x{hidden}x{f}", rms_floor=True)
