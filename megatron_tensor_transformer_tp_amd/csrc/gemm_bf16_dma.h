@@ -161,6 +161,63 @@ __device__ __forceinline__ void store_swiglu(const f32x16_t (&acc)[2][TM], int m
   });
 }
 
+// fp32 linear epilogue (bias and residual optional) of an interior tile,
+// restaged through LDS: the MFMA layout gives each lane 4 columns of one row,
+// so a direct store instruction writes 16-byte pieces of 32 different rows
+// (32 cache lines).  Here each wave writes one 32-row slab of its
+// accumulators into its own LDS region (rows padded by 16 bytes, so both the
+// slab writes and the row reads are free of bank conflicts), reads it back
+// row by row and stores whole row segments: WN/4 lanes per row, each
+// instruction covering 64*16/(WN*4) rows of WN*4 contiguous bytes.  The
+// caller has drained every copy and passed a barrier (the stage area is free).
+template <int TM, int TN>
+__device__ __forceinline__ void store_linear_f32_staged(const f32x16_t (&acc)[TN][TM], uint8_t* lds,
+                                                        int lane, int m_w, int n_w,
+                                                        const Epilogue& ep) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int W = TN * 32;            // columns of the wave's sub-tile
+  constexpr int PITCH = W * 4 + 16;     // bytes per staged row
+  constexpr int LPR = W / 4;            // lanes per row
+  constexpr int RPI = 64 / LPR;         // rows per store instruction
+  const uint16_t* __restrict__ bias = static_cast<const uint16_t*>(ep.bias);
+  const uint16_t* __restrict__ residual = static_cast<const uint16_t*>(ep.residual);
+  const int col = (lane % LPR) * 4, rsub = lane / LPR;
+  auto body = [&](auto has_bias, auto has_res) __attribute__((always_inline)) {
+    constexpr bool kBias = decltype(has_bias)::value;
+    constexpr bool kRes = decltype(has_res)::value;
+    float b[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kBias) load_bf16x4(bias + n_w + col, b);
+    static_for<TM>([&](auto I) __attribute__((always_inline)) {
+      static_for<TN>([&](auto J) __attribute__((always_inline)) {
+        static_for<4>([&](auto G) __attribute__((always_inline)) {
+          const f32x4_t v = {acc[J][I][4 * G], acc[J][I][4 * G + 1], acc[J][I][4 * G + 2],
+                             acc[J][I][4 * G + 3]};
+          *TPK_LDS(f32x4_t, lds + (lane & 31) * PITCH + (J * 32 + G * 8 + (lane >> 5) * 4) * 4) = v;
+        });
+      });
+      static_for<32 / RPI>([&](auto Q) __attribute__((always_inline)) {
+        const int r = Q * RPI + rsub;
+        const f32x4_t v = *TPK_LDS(const f32x4_t, lds + r * PITCH + col * 4);
+        const int64_t m = m_w + I * 32 + r;
+        float o[4] = {v[0] + b[0], v[1] + b[1], v[2] + b[2], v[3] + b[3]};
+        if constexpr (kRes) {
+          float rr[4];
+          load_bf16x4(residual + m * ep.ldr + n_w + col, rr);
+          static_for<4>([&](auto R) __attribute__((always_inline)) { o[R] += rr[R]; });
+        }
+        store_x4<true>(ep.out, m * ep.ldo + n_w + col, o);
+      });
+    });
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (bias != nullptr) {
+    if (residual != nullptr) body(T{}, T{}); else body(T{}, F{});
+  } else {
+    if (residual != nullptr) body(F{}, T{}); else body(F{}, F{});
+  }
+}
+
 // Zeroes the bf16 elements of a fragment whose k (counted from the start of
 // the fragment's 8) is >= nvalid.
 __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int nvalid) {
@@ -301,6 +358,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
       store_swiglu<TM, true, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
     else
       store_swiglu<TM, false, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
+  } else if (EPI == EPI_LINEAR && OUT_F32 && !edge) {
+    static_assert(NW * 32 * (WN * 4 + 16) <= STAGES * STAGE, "staging slabs fit in the stages");
+    // the stage area is free once every wave's copies have landed (waited
+    // above) and its fragment reads of the last stage have returned
+    sched_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    lds_barrier();
+    store_linear_f32_staged<TM, TN>(acc, smem + wave * 32 * (WN * 4 + 16), lane, m0 + wm * WM,
+                                    n0 + wn * WN, ep);
   } else {
     const int n_lane = n0 + wn * WN + (lane >> 5) * 4;
     if (edge)
