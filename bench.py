@@ -144,17 +144,17 @@ PROFILE_CMDS = {
 # Profiled kernels: name pattern in the rocprofv3 output and grid size in
 # work-items (one kernel serves several GEMM shapes), with the per-launch
 # algorithmic work (FLOP, bytes), the workload, and the summary's file stem.
-# GEMM template arguments: tile BM, BN, wave grid, LDS stages, GeLU epilogue,
-# fp32 output.
+# GEMM template arguments: tile BM, BN, wave grid, LDS stages, A k-major,
+# B k-major, epilogue kind, fp32 output, K tail (false: K % 32 == 0).
 _M, _H, _F = 16384, 8192, 4096          # MLP shard: tokens, hidden, f = ffn / t
 _S, _DL = 4096, 1024                    # attention shard: tokens, local width (8 heads x 128)
-_GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "   # then A k-major, B k-major, epilogue kind, fp32 out
+_GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "   # then A k-major, B k-major, epilogue kind, fp32 out, K tail
 PROFILED = {
-    "column_gemm_gelu": (_GEMM + "false, true, 1, false>", (_M // 256) * (_F // 256) * 512,
+    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false>", (_M // 256) * (_F // 256) * 512,
                          2.0 * _M * _H * _F, 2 * (_M * _H + _H * _F + _M * _F),
                          "MLP rank shard, M=16384, h=8192, f=4096: X, A_i read, H_i written (bf16)",
                          "column_gemm_gelu_t8_h8192_m16384"),
-    "row_gemm": (_GEMM + "false, true, 0, true>", (_M // 256) * (_H // 256) * 512,
+    "row_gemm": (_GEMM + "false, true, 0, true, false>", (_M // 256) * (_H // 256) * 512,
                  2.0 * _M * _F * _H, 2 * (_M * _F + _F * _H) + 4 * _M * _H,
                  "MLP rank shard, M=16384, h=8192, f=4096: H_i, B_i read (bf16), Z_i written (fp32)",
                  "row_gemm_t8_h8192_m16384"),
@@ -163,12 +163,12 @@ PROFILED = {
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K "
                        "(fp16) and V (bf16) read once, O written (bf16)",
                        "attention_core_t8_h8192_s4096"),
-    "attn_qkv_gemm": (_GEMM + "false, true, 4, false>", (_S // 256) * (3 * _DL // 256) * 512,
+    "attn_qkv_gemm": (_GEMM + "false, true, 4, false, false>", (_S // 256) * (3 * _DL // 256) * 512,
                       2.0 * _S * _H * 3 * _DL, 2 * (_S * _H + _H * 3 * _DL + _S * 3 * _DL),
                       "attention rank shard packed QKV projection, M=4096, K=8192, N=3072 "
                       "(one round of 192 256 x 256 tiles), q/k written as scaled fp16, v as bf16",
                       "attn_qkv_gemm_t8_h8192_s4096"),
-    "attn_out_gemm": (_GEMM + "false, true, 0, true>", (_S // 256) * (_H // 256) * 512,
+    "attn_out_gemm": (_GEMM + "false, true, 0, true, false>", (_S // 256) * (_H // 256) * 512,
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
                       "attention rank shard output projection, M=4096, K=1024, N=8192 (fp32 out)",
                       "attn_out_gemm_t8_h8192_s4096"),
@@ -178,23 +178,23 @@ PROFILED = {
                           "rank's [2048, 8192] shard with bf16 bias and residual rows, bf16 out "
                           "(HBM-bound: partial rows, residual and bias read, shard written)",
                           "sp_reduce_scatter_t8_h8192_m16384"),
-    "swiglu_gemm": (_GEMM + "false, true, 3, false>", (_M // 256) * (2 * _F // 256) * 512,
+    "swiglu_gemm": (_GEMM + "false, true, 3, false, false>", (_M // 256) * (2 * _F // 256) * 512,
                     2.0 * _M * _H * 2 * _F, 2 * (_M * _H + 2 * _H * _F + _M * _F),
                     "SwiGLU column layer, both projections in one product with SiLU(gate) * value "
                     "in the epilogue: X, Wg_i, Wu_i read, H_i written (bf16)",
                     "swiglu_gemm_t8_h8192_m16384"),
-    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false>", (_M // 256) * (_F // 256) * 512,
+    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false, false>", (_M // 256) * (_F // 256) * 512,
                        2.0 * _M * _H * _F, 2 * (_M * _H + _F * _H + _M * _F) + 2 * 2 * _M * _F,
                        "MLP shard backward dH = dZ B_i^T with dY_i = dH * GeLU'(Y_i) and H_i = "
                        "GeLU(Y_i) in the epilogue: dZ, B_i, Y_i read, dY_i and H_i written (bf16)",
                        "bwd_dgelu_gemm_t8_h8192_m16384"),
-    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true>", (_F // 256) * (_H // 256) * 512,
+    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true, false>", (_F // 256) * (_H // 256) * 512,
                              2.0 * _M * _H * _F, 2 * (_M * _F + _M * _H) + 4 * _F * _H,
                              "MLP shard backward weight gradients H_i^T dZ and X^T dY_i (one "
                              "kernel, K = 16384 tokens): two bf16 operands read, fp32 [4096 x 8192] "
                              "written; both launches averaged",
                              "bwd_weight_grad_gemm_t8_h8192_m16384"),
-    "bwd_dx_gemm": (_GEMM + "false, false, 0, true>", (_M // 256) * (_H // 256) * 512,
+    "bwd_dx_gemm": (_GEMM + "false, false, 0, true, false>", (_M // 256) * (_H // 256) * 512,
                     2.0 * _M * _F * _H, 2 * (_M * _F + _H * _F) + 4 * _M * _H,
                     "MLP shard backward dX_i = dY_i A_i^T: dY_i, A_i read (bf16), dX_i written (fp32)",
                     "bwd_dx_gemm_t8_h8192_m16384"),
