@@ -18,8 +18,12 @@
 //     groups of 4: wave w owns queries 32 (w % 4) .. +31 of the block, and
 //     group g = w / 4 takes the 32-key blocks with index = g (mod 2), so the
 //     two waves on each SIMD alternate between MFMA work and softmax work.
-//     Each wave keeps its own online-softmax state; the two groups' states
-//     are merged through LDS at the end (max, rescale, add);
+//     A wave raises its issue priority (s_setprio) for its two MFMA
+//     sections, so the SIMD's arbiter keeps the matrix pipe fed first and the
+//     partner wave's softmax fills the remaining issue slots (7% faster than
+//     equal priority, non-causal).  Each wave keeps its own online-softmax
+//     state; the two groups' states are merged through LDS at the end (max,
+//     rescale, add);
 //   * grid ids are ordered head-fastest, so with 8 local heads each XCD
 //     serves one head and its K/V stay in that XCD's L2;
 //   * K and V of a 32-key block (16 KiB) arrive by global->LDS copies (saddr
@@ -188,6 +192,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     // the MFMA of d-step T runs.
     f32x16_t sv = (f32x16_t)(0.0f);
     f16x8_t kf[2];
+    __builtin_amdgcn_s_setprio(1);
     kf[0] = *TPK_LDS(const f16x8_t, smem + k_off[0] + ust);
     static_for<8>([&](auto T) __attribute__((always_inline)) {
       constexpr int cur = T & 1;
@@ -195,6 +200,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
       sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[cur], qf[T], sv, 0, 0, 0);
     });
 
+    __builtin_amdgcn_s_setprio(0);
     // V^T fragments of the first 32 output dims load under the softmax.
     i16x4_t vf[2][2][2];
     auto load_v = [&](auto DT, auto BUF) __attribute__((always_inline)) {
@@ -251,6 +257,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     });
 
     // O^T += V^T P^T, the next 32 dims' V^T fragments loading under the MFMAs.
+    __builtin_amdgcn_s_setprio(1);
     static_for<4>([&](auto DT) __attribute__((always_inline)) {
       constexpr int cur = DT & 1;
       if constexpr (DT < 3) load_v(std::integral_constant<int, DT + 1>{}, std::integral_constant<int, cur ^ 1>{});
@@ -261,6 +268,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
                                                              acc_o[DT], 0, 0, 0);
       });
     });
+    __builtin_amdgcn_s_setprio(0);
   };
 
   issue(0);
