@@ -16,21 +16,21 @@
 // Flash-style, gfx950:
 //   * workgroup = one (batch, head, 128-query block) and 8 waves in two
 //     groups of 4: wave w owns queries 32 (w % 4) .. +31 of the block, and
-//     group g = w / 4 takes the 32-key blocks with index = g (mod 2), so the
-//     two waves on each SIMD alternate between MFMA work and softmax work.
-//     A wave raises its issue priority (s_setprio) for its two MFMA
-//     sections, so the SIMD's arbiter keeps the matrix pipe fed first and the
-//     partner wave's softmax fills the remaining issue slots (7% faster than
-//     equal priority, non-causal).  Each wave keeps its own online-softmax
-//     state; the two groups' states are merged through LDS at the end (max,
-//     rescale, add);
+//     group g = w / 4 takes the 32-key blocks with index = g (mod 2).  Each
+//     wave keeps its own online-softmax state; the two groups' states are
+//     merged through LDS at the end (max, rescale, add);
+//   * each wave software-pipelines its blocks: one iteration computes the
+//     scores of its next block (MFMA) while the same wave forms the softmax
+//     weights of the current block (VALU), then O += P V of the current
+//     block (MFMA) while it takes the max of the next block; the wave raises
+//     its issue priority (s_setprio) for the first of the two phases;
 //   * grid ids are ordered head-fastest, so with 8 local heads each XCD
 //     serves one head and its K/V stay in that XCD's L2;
 //   * K and V of a 32-key block (16 KiB) arrive by global->LDS copies (saddr
-//     form: uniform base + 32-bit lane offset); 6 LDS stages: the two blocks
-//     being read, two in flight, two being issued; the loop is unrolled by 3
-//     so that every LDS fragment address is a loop-invariant register plus
-//     an immediate offset;
+//     form: uniform base + 32-bit lane offset); 8 LDS stages, 4 per group:
+//     the current block, the next block, one in flight and one being issued;
+//     the loop is unrolled by 4 so that every LDS fragment address is a
+//     loop-invariant register plus an immediate offset;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_f16, K fragments from LDS (one
 //     ds_read_b128, rows XOR-swizzled by row % 16, read one d-step ahead),
 //     Q fragments held in registers; each lane owns one query and 16 of the
@@ -65,7 +65,8 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kD = 128;                 // head_dim
 constexpr int kBQ = 128;                // queries per workgroup
 constexpr int kBKV = 32;                // keys per block
-constexpr int kStages = 6;
+constexpr int kStages = 8;
+constexpr int kCycle = kStages / 2;      // iterations per stage cycle (per group half)
 constexpr int kArr = kBKV * kD * 2;     // one array (K or V) of a block: 8 KiB
 constexpr int kStage = 2 * kArr;        // 16 KiB
 constexpr int kWaves = 8;
@@ -137,12 +138,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int nit = nblk / 2;
 
   // LDS placement: block j sits in its group's half of the stages (j % 2)
-  // at its iteration's place in a 3-iteration cycle ((j / 2) % 3),
-  //   stage(j) = (j % 2) * 3 * kStage + ((j / 2) % 3) * kStage,
-  // so with the loop unrolled by 3 every fragment address is a per-lane
-  // register (holding the group's 48 KiB) plus a compile-time offset of at
-  // most 32 KiB that the LDS instruction's immediate field carries.
-  auto stage_off = [](int j) { return (j % 2) * 3 * kStage + ((j / 2) % 3) * kStage; };
+  // at its iteration's place in a kCycle-iteration cycle ((j / 2) % kCycle),
+  //   stage(j) = (j % 2) * kCycle * kStage + ((j / 2) % kCycle) * kStage,
+  // so with the loop unrolled by kCycle every fragment address is a per-lane
+  // register (holding the group's base) plus a compile-time offset that the
+  // LDS instruction's immediate field carries.
+  auto stage_off = [](int j) { return (j % 2) * kCycle * kStage + ((j / 2) % kCycle) * kStage; };
 
   // Copies of blocks 2 it and 2 it + 1 (clamped to the last block).
   auto issue = [&](int it) __attribute__((always_inline)) {
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int v_sw = (gi >> 2) << 2;             // 4 * (row % 4)
   const int v_chunk = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);  // + 4*dt
   const int v_within = (gi & 1) * 8;
-  const int grp_off = group * 3 * kStage;
+  const int grp_off = group * kCycle * kStage;
   int k_off[8], v_off[4];
   static_for<8>([&](auto T) __attribute__((always_inline)) {
     k_off[T] = grp_off + k_row * (kD * 2) + (((2 * T + h) ^ k_sw) * 16);
@@ -177,49 +178,25 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   static_for<4>([&](auto DT) __attribute__((always_inline)) { acc_o[DT] = (f32x16_t)(0.0f); });
   float m_run = kNegBig, l_run = 0.0f;
 
-  // One iteration: blocks 2 it (group 0) and 2 it + 1 (group 1); U = it % 3.
-  auto step = [&](int it, auto U) __attribute__((always_inline)) {
-    constexpr int ust = U * kStage;
-    // blocks 2 it, 2 it + 1 have landed (this wave's copies; the barrier
-    // makes it every wave's); issue blocks 2 it + 4, 2 it + 5 into the
-    // stages that iteration it - 1 read
-    wait_vmcnt<kCopies>();
-    lds_barrier();
-    issue(it + 2);
-    const int kb = 2 * it + group;
-
-    // S^T of the block's 32 keys, the K fragments of d-step T+1 read while
-    // the MFMA of d-step T runs.
+  // S^T of one 32-key block from the stage at `so` (8 MFMAs, the K fragment
+  // of d-step T+1 read ahead of the MFMA of d-step T).
+  auto qk = [&](int so) __attribute__((always_inline)) {
     f32x16_t sv = (f32x16_t)(0.0f);
     f16x8_t kf[2];
-    __builtin_amdgcn_s_setprio(1);
-    kf[0] = *TPK_LDS(const f16x8_t, smem + k_off[0] + ust);
+    kf[0] = *TPK_LDS(const f16x8_t, smem + k_off[0] + so);
     static_for<8>([&](auto T) __attribute__((always_inline)) {
       constexpr int cur = T & 1;
-      if constexpr (T < 7) kf[cur ^ 1] = *TPK_LDS(const f16x8_t, smem + k_off[T + 1] + ust);
+      if constexpr (T < 7) kf[cur ^ 1] = *TPK_LDS(const f16x8_t, smem + k_off[T + 1] + so);
       sv = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf[cur], qf[T], sv, 0, 0, 0);
     });
+    return sv;
+  };
 
-    __builtin_amdgcn_s_setprio(0);
-    // V^T fragments of the first 32 output dims load under the softmax.
-    i16x4_t vf[2][2][2];
-    auto load_v = [&](auto DT, auto BUF) __attribute__((always_inline)) {
-      static_for<2>([&](auto U2) __attribute__((always_inline)) {
-        vf[BUF][U2][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TPK_LDS(i16x4_t, smem + v_off[DT] + ust + (16 * U2) * (kD * 2)));
-        vf[BUF][U2][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            TPK_LDS(i16x4_t, smem + v_off[DT] + ust + (16 * U2 + 8) * (kD * 2)));
-      });
-    };
-    load_v(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-
-    // Online softmax over the block (this lane: its query, 16 of the 32
-    // keys: S^T rows 8 (R / 4) + 4 h + R % 4), on the raw scores: the max
-    // commutes with the positive scale, which enters the exponent through
-    // one fma.  The running max is raised (and the accumulator rescaled) only
-    // when the block's max exceeds it by more than kRescaleSlack, decided
-    // for the whole wave at once; otherwise the weights may grow up to
-    // 2^kRescaleSlack.
+  // Causal mask and the block's max (log2 units; this lane: its query and
+  // 16 of the 32 keys, S^T rows 8 (R / 4) + 4 h + R % 4).  The max is taken
+  // on the raw scores: it commutes with the positive scale, which enters the
+  // exponent through one fma.
+  auto block_max = [&](f32x16_t& sv, int kb) __attribute__((always_inline)) {
     float mraw = kNegBig;
     static_for<16>([&](auto R) __attribute__((always_inline)) {
       if constexpr (CAUSAL) {
@@ -228,7 +205,13 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
       }
       mraw = fmaxf(mraw, sv[int(R)]);
     });
-    const float mx = fmaxf(mraw, __shfl_xor(mraw, 32)) * scale_log2;
+    return fmaxf(mraw, __shfl_xor(mraw, 32)) * scale_log2;
+  };
+
+  // The running max is raised (and the accumulator rescaled) only when a
+  // block's max exceeds it by more than kRescaleSlack, decided for the whole
+  // wave at once; otherwise the weights may grow up to 2^kRescaleSlack.
+  auto raise_max = [&](float mx) __attribute__((always_inline)) {
     if (__any(mx > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -236,28 +219,42 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
       l_run *= alpha;
       static_for<4>([&](auto DT) __attribute__((always_inline)) { acc_o[DT] *= alpha; });
     }
+  };
+
+  // Softmax weights of a masked block against the running max, their sum,
+  // and P^T fragments: step u covers keys 16u .. 16u+15; half h holds keys
+  // {4h..4h+3, 8+4h..8+4h+3} of the step, V^T uses the same order.
+  auto weights = [&](const f32x16_t& sv, bf16x8_t (&pf)[2]) __attribute__((always_inline)) {
+    float p[16];
     float lsum = 0.0f;
     static_for<16>([&](auto R) __attribute__((always_inline)) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[int(R)], scale_log2, -m_run));
-      sv[int(R)] = p;
-      lsum += p;
+      p[R] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[int(R)], scale_log2, -m_run));
+      lsum += p[R];
     });
     l_run += lsum;
-
-    // P^T fragments: step u covers keys 16u .. 16u+15; half h holds keys
-    // {4h..4h+3, 8+4h..8+4h+3} of the step, V^T uses the same order.
-    bf16x8_t pf[2];
     static_for<2>([&](auto U2) __attribute__((always_inline)) {
       i16x8_t w;
       static_for<4>([&](auto R) __attribute__((always_inline)) {
-        w[int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(sv[8 * U2 + int(R)]));
-        w[4 + int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(sv[8 * U2 + 4 + int(R)]));
+        w[int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(p[8 * U2 + R]));
+        w[4 + int(R)] = __builtin_bit_cast(short, static_cast<__bf16>(p[8 * U2 + 4 + R]));
       });
       pf[U2] = __builtin_bit_cast(bf16x8_t, w);
     });
+  };
 
-    // O^T += V^T P^T, the next 32 dims' V^T fragments loading under the MFMAs.
-    __builtin_amdgcn_s_setprio(1);
+  // O^T += V^T P^T from the stage at `so`, the V^T fragments of the next 32
+  // dims loading under the MFMAs of the current ones.
+  auto pv = [&](const bf16x8_t (&pf)[2], int so) __attribute__((always_inline)) {
+    i16x4_t vf[2][2][2];
+    auto load_v = [&](auto DT, auto BUF) __attribute__((always_inline)) {
+      static_for<2>([&](auto U2) __attribute__((always_inline)) {
+        vf[BUF][U2][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TPK_LDS(i16x4_t, smem + v_off[DT] + so + (16 * U2) * (kD * 2)));
+        vf[BUF][U2][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            TPK_LDS(i16x4_t, smem + v_off[DT] + so + (16 * U2 + 8) * (kD * 2)));
+      });
+    };
+    load_v(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     static_for<4>([&](auto DT) __attribute__((always_inline)) {
       constexpr int cur = DT & 1;
       if constexpr (DT < 3) load_v(std::integral_constant<int, DT + 1>{}, std::integral_constant<int, cur ^ 1>{});
@@ -268,15 +265,49 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
                                                              acc_o[DT], 0, 0, 0);
       });
     });
-    __builtin_amdgcn_s_setprio(0);
   };
 
+  // Software pipeline over this wave's blocks b = 2 it + group: iteration it
+  // runs S of block b+2 (the next one) under the softmax weights of block b,
+  // then P V of block b under the max of block b+2; the running max is raised
+  // for block b+2 after P V of block b.  Per block the arithmetic and its
+  // order are those of the plain sequence max -> raise -> weights -> P V.
+  // Copies: iteration it needs blocks 2 it (+ group) and 2 it + 2 (+ group)
+  // resident and issues blocks 2 it + 6, 2 it + 7 into the stages of blocks
+  // 2 it - 2, 2 it - 1 (read for the last time in iteration it - 1).
   issue(0);
   issue(1);
-  for (int it = 0; it < nit; it += 3) {
+  issue(2);
+  wait_vmcnt<2 * kCopies>();
+  lds_barrier();
+  f32x16_t s_cur = qk(0);                       // block group: stage offset 0 in the group's half
+  raise_max(block_max(s_cur, group));
+
+  auto step = [&](int it, auto U) __attribute__((always_inline)) {
+    constexpr int ust = U * kStage;                        // block 2 it + group
+    constexpr int nst = ((U + 1) % kCycle) * kStage;       // block 2 it + 2 + group
+    // Nothing of the previous iteration (its MFMAs and their LDS waits)
+    // moves past the barrier; blocks 2 it + 2, 2 it + 3 have landed.
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<kCopies>();
+    lds_barrier();
+    issue(it + 3);
+    bf16x8_t pf[2];
+    __builtin_amdgcn_s_setprio(1);
+    f32x16_t s_next = qk(nst);
+    weights(s_cur, pf);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    pv(pf, ust);
+    const float mx = block_max(s_next, 2 * it + 2 + group);
+    if (it + 1 < nit) raise_max(mx);
+    s_cur = s_next;
+  };
+  for (int it = 0; it < nit; it += kCycle) {
     step(it, std::integral_constant<int, 0>{});
     if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
     if (it + 2 < nit) step(it + 2, std::integral_constant<int, 2>{});
+    if (it + 3 < nit) step(it + 3, std::integral_constant<int, 3>{});
   }
   wait_vmcnt<0>();
 
