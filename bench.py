@@ -52,7 +52,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/" + f for f in (
     "device_common.h", "gemm_bf16_impl.h", "gemm_bf16_dma.h", "gemm_bf16.hip",
     "gemm_bf16_256_gelu.hip", "gemm_bf16_256_plain.hip", "gemm_bf16_256_nt.hip",
-    "gemm_bf16_256_tn.hip", "gemm_bf16_256_swiglu.hip", "colsum.hip", "sp_reduce.hip", "attention.hip")]
+    "gemm_bf16_256_tn.hip", "gemm_bf16_256_swiglu.hip", "gemm_bf16_384_plain.hip", "colsum.hip",
+    "sp_reduce.hip", "attention.hip")]
 
 
 def kernel_source_sha() -> str:
@@ -163,10 +164,11 @@ PROFILED = {
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K "
                        "(fp16) and V (bf16) read once, O written (bf16)",
                        "attention_core_t8_h8192_s4096"),
-    "attn_qkv_gemm": (_GEMM + "false, true, 4, false, false>", (_S // 256) * (3 * _DL // 256) * 512,
+    "attn_qkv_gemm": ("gemm_bf16_dma_kernel<128, 384, 2, 4, 4, false, true, 4, false, false>",
+                      (_S // 128) * (3 * _DL // 384) * 512,
                       2.0 * _S * _H * 3 * _DL, 2 * (_S * _H + _H * 3 * _DL + _S * 3 * _DL),
                       "attention rank shard packed QKV projection, M=4096, K=8192, N=3072 "
-                      "(one round of 192 256 x 256 tiles), q/k written as scaled fp16, v as bf16",
+                      "(one round of 256 128 x 384 tiles), q/k written as scaled fp16, v as bf16",
                       "attn_qkv_gemm_t8_h8192_s4096"),
     "attn_out_gemm": (_GEMM + "false, true, 0, true, false>", (_S // 256) * (_H // 256) * 512,
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,

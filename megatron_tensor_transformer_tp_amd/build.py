@@ -27,6 +27,8 @@ SOURCES = [
     "gemm_bf16_256_plain.hip",
     "gemm_bf16_128_gelu.hip",
     "gemm_bf16_128_plain.hip",
+    "gemm_bf16_384_gelu.hip",
+    "gemm_bf16_384_plain.hip",
     "gemm_bf16_256_nt.hip",
     "gemm_bf16_256_tn.hip",
     "gemm_bf16_256_swiglu.hip",

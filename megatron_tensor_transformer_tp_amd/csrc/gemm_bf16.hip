@@ -19,20 +19,35 @@ hipError_t launch_epi(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t
 }
 }  // namespace
 
+// Tile shape by an estimate of the launch time in units of one 256 x 256
+// tile's time, from the tile counts (one workgroup per CU for 256 x 256 and
+// 128 x 384, two for 128 x 128) and relative per-CU throughputs measured on
+// the 4096 x 8192 x {3072, 1536} products (128 x 384: 0.84, 128 x 128: 0.82
+// of the 256 x 256 rate; a last 128 x 128 round with one workgroup per CU
+// costs 0.73 of a full one).
+static int gemm_tile_choice(int64_t M, int64_t N) {
+  constexpr int64_t kCUs = 256;
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  const int64_t t256 = tiles(256, 256), t384 = tiles(128, 384), t128 = tiles(128, 128);
+  const double c256 = static_cast<double>((t256 + kCUs - 1) / kCUs);
+  const double c384 = static_cast<double>((t384 + kCUs - 1) / kCUs) * (128.0 * 384.0) / (256.0 * 256.0) / 0.84;
+  const int64_t rem = t128 % (2 * kCUs);
+  const double c128 = (static_cast<double>(t128 / (2 * kCUs)) + (rem == 0 ? 0.0 : rem <= kCUs ? 0.73 : 1.0)) *
+                      2.0 * (128.0 * 128.0) / (256.0 * 256.0) / 0.82;
+  if (c256 <= c384 && c256 <= c128) return 256;
+  return c384 < c128 ? 384 : 128;
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                             int64_t M, int64_t N, int64_t K, const Epilogue& ep,
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
-  // Large problems: 256x256 tiles (one workgroup per CU); a single round of
-  // at least 192 of them (3/4 of the CUs at full per-tile speed) still beats
-  // 128x128 tiles (measured on the 4096 x 3072 x 8192 attention projection).
-  // Smaller ones: 128x128 tiles so that the 256 CUs still get work.
-  if (tiles256 >= 192)
-    return launch_epi<256, 256>(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
-                                static_cast<int>(K), ep, stream);
-  return launch_epi<128, 128>(A, lda, B, ldb, static_cast<int>(M), static_cast<int>(N),
-                              static_cast<int>(K), ep, stream);
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  switch (gemm_tile_choice(M, N)) {
+    case 256: return launch_epi<256, 256>(A, lda, B, ldb, m, n, k, ep, stream);
+    case 384: return launch_epi<128, 384>(A, lda, B, ldb, m, n, k, ep, stream);
+    default: return launch_epi<128, 128>(A, lda, B, ldb, m, n, k, ep, stream);
+  }
 }
 
 hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B,

@@ -179,6 +179,7 @@ __device__ __forceinline__ void store_linear_f32_staged(const f32x16_t (&acc)[TN
   constexpr int PITCH = W * 4 + 16;     // bytes per staged row
   constexpr int LPR = W / 4;            // lanes per row
   constexpr int RPI = 64 / LPR;         // rows per store instruction
+  static_assert(LPR * RPI == 64 && 32 % RPI == 0, "whole rows per store instruction");
   const uint16_t* __restrict__ bias = static_cast<const uint16_t*>(ep.bias);
   const uint16_t* __restrict__ residual = static_cast<const uint16_t*>(ep.residual);
   const int col = (lane % LPR) * 4, rsub = lane / LPR;
@@ -238,6 +239,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave sub-tiles of whole 32 x 32 MFMA blocks");
   using TileA = OperandTile<BM, NW, A_KMAJOR, KTAIL>;
   using TileB = OperandTile<BN, NW, B_KMAJOR, KTAIL>;
   constexpr int A_BYTES = TileA::kBytes;
@@ -358,21 +360,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
       store_swiglu<TM, true, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
     else
       store_swiglu<TM, false, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
-  } else if (EPI == EPI_LINEAR && OUT_F32 && !edge) {
-    static_assert(NW * 32 * (WN * 4 + 16) <= STAGES * STAGE, "staging slabs fit in the stages");
-    // the stage area is free once every wave's copies have landed (waited
-    // above) and its fragment reads of the last stage have returned
-    sched_fence();
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    lds_barrier();
-    store_linear_f32_staged<TM, TN>(acc, smem + wave * 32 * (WN * 4 + 16), lane, m0 + wm * WM,
-                                    n0 + wn * WN, ep);
   } else {
-    const int n_lane = n0 + wn * WN + (lane >> 5) * 4;
-    if (edge)
-      store_tile<TM, TN, true, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
-    else
-      store_tile<TM, TN, false, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
+    // fp32 linear outputs of interior tiles go through the LDS restaging
+    // (wave widths whose rows split evenly over the 64 lanes)
+    constexpr bool kStaged = EPI == EPI_LINEAR && OUT_F32 && 64 % (WN / 4) == 0;
+    bool stored = false;
+    if constexpr (kStaged) {
+      if (!edge) {
+        static_assert(NW * 32 * (WN * 4 + 16) <= STAGES * STAGE, "staging slabs fit in the stages");
+        // the stage area is free once every wave's copies have landed
+        // (waited above) and its fragment reads of the last stage have returned
+        sched_fence();
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        lds_barrier();
+        store_linear_f32_staged<TM, TN>(acc, smem + wave * 32 * (WN * 4 + 16), lane, m0 + wm * WM,
+                                        n0 + wn * WN, ep);
+        stored = true;
+      }
+    }
+    if (!stored) {
+      const int n_lane = n0 + wn * WN + (lane >> 5) * 4;
+      if (edge)
+        store_tile<TM, TN, true, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
+      else
+        store_tile<TM, TN, false, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
+    }
   }
 }
 

@@ -152,6 +152,7 @@ def test_headline_reconstruction_sampled_rows(headline):
     (300, 256, 1000, False, "bf16"),
     (513, 1024, 520, True, "bf16"),
     (4000, 1000, 4096, True, "bf16"),   # 256x256 tile path, ragged M and K
+    (4000, 1000, 3000, True, "bf16"),   # 128x384 tile path, ragged M, N and K
 ])
 def test_column_linear_ragged(tokens, hidden, f, gelu, out):
     t = 2
@@ -173,6 +174,7 @@ def test_column_linear_ragged(tokens, hidden, f, gelu, out):
     (129, 200, 136, 1, "f32"),
     (1000, 520, 1024, 0, "f32"),
     (4000, 1000, 4096, 0, "f32"),       # 256x256 tile path, ragged M and K, residual
+    (4000, 1000, 3000, 0, "f32"),       # 128x384 tile path, ragged M, N and K, residual
 ])
 def test_row_linear_ragged(tokens, f, hidden, rank, out):
     t = 2
