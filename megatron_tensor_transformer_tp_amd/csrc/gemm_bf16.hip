@@ -1,4 +1,6 @@
 // Dispatch of the bf16 GEMM to its tile shape and epilogue instantiation.
+#include <atomic>
+
 #include "gemm_bf16_impl.h"
 
 namespace tpk {
@@ -25,8 +27,24 @@ hipError_t launch_epi(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t
 // the 4096 x 8192 x {3072, 1536} products (128 x 384: 0.84, 128 x 128: 0.82
 // of the 256 x 256 rate; a last 128 x 128 round with one workgroup per CU
 // costs 0.73 of a full one).
+// Compute units of the current device (cached per device, safe to call
+// from several threads; 256 on a whole MI355X, fewer on a partition).
+static int64_t device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 static int gemm_tile_choice(int64_t M, int64_t N) {
-  constexpr int64_t kCUs = 256;
+  const int64_t kCUs = device_cus();
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   const int64_t t256 = tiles(256, 256), t384 = tiles(128, 384), t128 = tiles(128, 128);
   const double c256 = static_cast<double>((t256 + kCUs - 1) / kCUs);
