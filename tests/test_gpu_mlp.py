@@ -147,6 +147,8 @@ def test_headline_reconstruction_sampled_rows(headline):
 
 
 @pytest.mark.parametrize("tokens,hidden,f,gelu,out", [
+    (5, 8, 64, True, "f32"),            # K = 8: the only k-tile is a partial one
+    (33, 24, 72, False, "bf16"),        # K = 24
     (1, 64, 64, True, "bf16"),
     (77, 136, 200, True, "f32"),
     (300, 256, 1000, False, "bf16"),

@@ -105,6 +105,7 @@ def test_f32_ragged_tokens():
 
 
 @pytest.mark.parametrize("tokens,hidden,f,grad_dt", [
+    (9, 24, 16, "f32"),                 # every k extent below one 32-deep k-tile
     (1, 64, 64, "f32"),
     (77, 136, 200, "f32"),
     (300, 264, 360, "bf16"),

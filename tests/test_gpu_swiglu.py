@@ -104,7 +104,8 @@ def test_strided_weight_views_and_f32_ragged():
                  rms_floor=True)
 
 
-@pytest.mark.parametrize("tokens,hidden,f", [(1, 64, 64), (77, 136, 200), (300, 264, 360), (513, 1024, 520)])
+@pytest.mark.parametrize("tokens,hidden,f", [(9, 24, 16), (1, 64, 64), (77, 136, 200), (300, 264, 360),
+                                             (513, 1024, 520)])
 def test_bf16_ragged_shapes(tokens, hidden, f):
     """bf16 shapes off every tile: ragged tokens, a feature count that ends
     inside a paired gate / value tile, and k extents (hidden, f) that end
