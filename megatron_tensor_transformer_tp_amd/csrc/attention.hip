@@ -309,11 +309,13 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     if (it + 2 < nit) step(it + 2, std::integral_constant<int, 2>{});
     if (it + 3 < nit) step(it + 3, std::integral_constant<int, 3>{});
   }
-  wait_vmcnt<0>();
-
   // Merge the two groups: group 1 publishes (m, l, acc) through LDS (the
-  // stages are free once every wave is past its last read), group 0 combines
-  // with its partner wave w + 4 (same queries, same lane layout) and stores.
+  // stages are free once every wave's copies have landed and its last
+  // fragment reads have returned), group 0 combines with its partner wave
+  // w + 4 (same queries, same lane layout) and stores.
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   lds_barrier();
   float* mrg = reinterpret_cast<float*>(smem) + ((wave & 3) * 64 + lane) * 66;
   if (group == 1) {
