@@ -1,0 +1,90 @@
+"""Graph capture of the C-ABI entry points.  Every launch the library makes
+is an ordinary kernel launch on the caller's stream (no allocation, no
+memset, no synchronisation), so a captured sequence of calls replays to the
+same bits as the eager calls.  Each graph is replayed several times, with
+outputs poisoned before each replay and eager calls of the same entry points
+in between, and every replay is compared with the eager result bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from megatron_tensor_transformer_tp_amd import binding, inputs
+from tests.gpu_helpers import dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _replay_matches(run, outs, reps=3):
+    """Eager reference, capture of `run`, then `reps` replays checked bit for
+    bit against the reference with an eager `run` between replays."""
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    # warm-up on a side stream, as graph capture requires
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        for t in outs:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(t, r), f"replay {rep}: output {i} differs from the eager result"
+        run()                                   # eager work between replays
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(t, r), f"eager call after replay {rep}: output {i} differs"
+
+
+def test_mlp_forward_and_backward_replay():
+    wl = inputs.MLP_WORKLOADS["t4_h1024_m1024"]
+    r = 1
+    say("graph: t4_h1024_m1024 rank 1 forward (pre-activation saved) + backward")
+    xd, dzd = dev(inputs.mlp_x_rows(wl), "bf16"), dev(inputs.mlp_dz_rows(wl), "bf16")
+    ad, bd = dev(inputs.mlp_a_block(wl, r), "bf16"), dev(inputs.mlp_b_block(wl, r), "bf16")
+    ws = torch.empty(binding.tp_mlp_shard_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(binding.tp_mlp_shard_bwd_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t,
+                                                               torch.bfloat16), dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    z = torch.empty((wl.tokens, wl.hidden), **f32)
+    y = torch.empty((wl.tokens, wl.f), dtype=torch.bfloat16, device="cuda")
+    dx, da, db = (torch.empty(s, **f32) for s in ((wl.tokens, wl.hidden), (wl.hidden, wl.f), (wl.f, wl.hidden)))
+    dba, dbb = torch.empty((wl.f,), **f32), torch.empty((wl.hidden,), **f32)
+
+    def run():
+        binding.tp_mlp_shard_fwd(xd, ad, bd, z, ws, ffn=wl.ffn, t=wl.t, rank=r, y_save=y)
+        binding.tp_mlp_shard_bwd(xd, ad, bd, y, dzd, dx, da, db, wsb, ffn=wl.ffn, t=wl.t, rank=r,
+                                 dbias_a_i=dba, dbias_b=dbb)
+
+    _replay_matches(run, [z, y, dx, da, db, dba, dbb])
+
+
+def test_attention_and_sp_replay():
+    wl = inputs.ATTN_WORKLOADS["attn_t2_h1024_b2_s384"]
+    r = 0
+    say("graph: attn_t2_h1024_b2_s384 rank 0 attention shard + SP reduce-scatter of two partials")
+    tokens = wl.batch * wl.seq
+    xd = dev(np.stack([inputs.attn_x(wl, b) for b in range(wl.batch)]), "bf16")
+    wqkv = dev(inputs.attn_wqkv_block(wl, r), "bf16")
+    wo = dev(inputs.attn_wo_block(wl, r), "bf16")
+    ws = torch.empty(binding.tp_attn_shard_workspace_bytes(wl.batch, wl.seq, wl.hidden, wl.heads, wl.head_dim,
+                                                           wl.t, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    out = torch.empty((tokens, wl.hidden), dtype=torch.float32, device="cuda")
+    other = torch.randn((tokens, wl.hidden), dtype=torch.float32, device="cuda")
+    sp_out = torch.empty((tokens // 2, wl.hidden), dtype=torch.float32, device="cuda")
+
+    def run():
+        binding.tp_attn_shard_fwd(xd, wqkv, wo, out, ws, heads=wl.heads, head_dim=wl.head_dim, t=wl.t,
+                                  rank=r)
+        binding.tp_sp_reduce_scatter([out, other], sp_out, t=2, rank=1)
+
+    _replay_matches(run, [out, sp_out])
