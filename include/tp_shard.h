@@ -60,6 +60,9 @@
  *     launch returns TP_ERR_HIP.  Nothing is printed, no exception crosses
  *     the ABI.  Calls are stateless and thread-safe; calls that write the
  *     same output buffer concurrently race, as with any kernel.
+ *   - Sizes: tokens, hidden and each shard width up to 2^30 (larger ones
+ *     return TP_ERR_UNSUPPORTED); a product whose tile count or fp32 grid
+ *     exceeds the launch limits fails with TP_ERR_HIP before it runs.
  *   - Numerics: bf16 inputs are multiplied with fp32 accumulation (MFMA);
  *     fp32 inputs with fp32 FMA.  GeLU is applied to the fp32 accumulator;
  *     a bf16 output is rounded to nearest-even.  Inputs must be finite.

@@ -30,13 +30,13 @@ template <typename T>
 __global__ __launch_bounds__(kCols) void colsum_chunk_kernel(const T* __restrict__ in, int64_t ld,
                                                             int M, int N,
                                                             float* __restrict__ partial) {
-  const int n = blockIdx.x * kCols + threadIdx.x;
+  const int n = blockIdx.y * kCols + threadIdx.x;
   if (n >= N) return;
-  const int r0 = blockIdx.y * kRows;
+  const int r0 = blockIdx.x * kRows;
   const int r1 = min(M, r0 + kRows);
   float s = 0.0f;
   for (int r = r0; r < r1; ++r) s += load_f(in + static_cast<int64_t>(r) * ld + n);
-  partial[static_cast<int64_t>(blockIdx.y) * N + n] = s;
+  partial[static_cast<int64_t>(blockIdx.x) * N + n] = s;
 }
 
 __global__ __launch_bounds__(kCols) void colsum_finish_kernel(const float* __restrict__ partial,
@@ -81,8 +81,10 @@ hipError_t launch_colsum(const void* in, int64_t ld, int in_dt, int64_t M, int64
   if (N == 0) return hipSuccess;
   const int chunks = static_cast<int>((M + kRows - 1) / kRows);
   const unsigned col_blocks = static_cast<unsigned>((N + kCols - 1) / kCols);
+  if (col_blocks > 65535) return hipErrorInvalidValue;   // grid y limit
   if (chunks > 0) {
-    const dim3 grid(col_blocks, static_cast<unsigned>(chunks));
+    // row chunks on x (no 65535 limit), column blocks on y
+    const dim3 grid(static_cast<unsigned>(chunks), col_blocks);
     if (in_dt == 1)
       hipLaunchKernelGGL(colsum_chunk_kernel<uint16_t>, grid, dim3(kCols), 0, stream,
                          static_cast<const uint16_t*>(in), ld, static_cast<int>(M),

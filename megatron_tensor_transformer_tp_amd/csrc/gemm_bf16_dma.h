@@ -399,15 +399,16 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
       (A_KMAJOR && M % 8 != 0) || (B_KMAJOR && b_rows % 8 != 0) ||
       (EPI == EPI_SWIGLU && N % 2 != 0))
     return hipErrorInvalidValue;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t tiles = ((static_cast<int64_t>(M) + BM - 1) / BM) * ((static_cast<int64_t>(N) + BN - 1) / BN);
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;     // one workgroup per tile in grid x
   if (K % kBKd != 0)
     hipLaunchKernelGGL(
         (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, true>),
-        dim3(tiles), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
+        dim3(static_cast<unsigned>(tiles)), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
   else
     hipLaunchKernelGGL(
         (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, false>),
-        dim3(tiles), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
+        dim3(static_cast<unsigned>(tiles)), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   __shared__ float sB[kBKf][kBN + 4];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;   // M tiles on x: no 65535 limit
 
   float acc[4][4];
   for (int i = 0; i < 4; ++i)
@@ -101,8 +101,9 @@ hipError_t launch_gemm_f32(const float* A, int64_t lda, bool a_kmajor, const flo
                            bool b_kmajor, int64_t M, int64_t N, int64_t K, const Epilogue& ep,
                            hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((N + kBN - 1) / kBN),
-                  static_cast<unsigned>((M + kBM - 1) / kBM));
+  const int64_t tiles_n = (N + kBN - 1) / kBN;
+  if (tiles_n > 65535) return hipErrorInvalidValue;     // grid y limit
+  const dim3 grid(static_cast<unsigned>((M + kBM - 1) / kBM), static_cast<unsigned>(tiles_n));
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   switch (ep.kind) {
     case EPI_LINEAR:

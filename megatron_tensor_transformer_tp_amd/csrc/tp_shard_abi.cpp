@@ -56,7 +56,9 @@ tp_status check_optional_vec(const void* p) {
   return TP_OK;
 }
 
-bool fits_int32(int64_t v) { return v <= static_cast<int64_t>(INT_MAX); }
+// Dimensions are handled as 32-bit ints inside the kernels, with room for a
+// tile's worth of index arithmetic past the end.
+bool fits_int32(int64_t v) { return v <= (int64_t{1} << 30); }
 
 tp_status from_hip(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
 

@@ -142,6 +142,10 @@ def test_mlp_shard_validation(lib):
     assert mlp(lib, in_dt=F32, out_dt=BF16) == DTYPE
     assert mlp(lib, tokens=0, ws=None) == OK
     assert mlp(lib, y=P + 8) == MISALIGNED        # the saved pre-activation must be aligned
+    # sizes past 2^30 are refused before anything is enqueued
+    assert mlp(lib, tokens=(1 << 30) + 8) == UNSUPPORTED
+    assert mlp(lib, hidden=(1 << 30) + 8, ws_bytes=1 << 62) == UNSUPPORTED
+    assert bwd(lib, tokens=(1 << 30) + 8) == UNSUPPORTED
 
 
 def bwd(lib, **kw):
