@@ -320,7 +320,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     // substep 0 of tile kt: fragments of substep 1 load under its MFMAs
     read_frags(kt, 1, af1, bf1);
     mfmas(af0, bf0);
-    interleave_substep<kMfma, kFrags, 0, 0, 0>();
+    interleave_substep<kMfma, kFrags>();
     sched_fence();
     // substep 1: publish tile kt+1, start tile kt+STAGES-1 (into the stage
     // tile kt-1 occupied: every wave finished reading it before this
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     issue(kt + STAGES - 1);
     read_frags(kt + 1, 0, af0, bf0);
     mfmas(af1, bf1);
-    interleave_substep<kMfma, kFrags, 0, 0, 0>();
+    interleave_substep<kMfma, kFrags>();
     sched_fence();
   }
   // the last k-tile (its substep-0 fragments are in af0 / bf0)

@@ -83,12 +83,9 @@ __device__ __forceinline__ bool tile_coords_rounds(int bid, int nblk, int tiles_
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Within a substep, an explicit interleave: each MFMA is followed by one of
-// the substep's memory operations, LDS reads for the next substep first.
-constexpr int kSchedValu = 0x002;
+// the LDS fragment reads for the next substep (sched_group_barrier masks).
 constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
 constexpr int kSchedDsRead = 0x100;
-constexpr int kSchedDsWrite = 0x200;
 
 template <int MASK, int N>
 __device__ __forceinline__ void sched_group() {
@@ -249,21 +246,14 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
 }
 
 // Interleave for one k-substep: kM MFMAs; before MFMA i the scheduler is asked
-// for the substep's next LDS fragment reads (front-loaded, kR in total), and a
-// proportional share of its VALU ops (kP), LDS stores (kW) and global loads (kV).
-template <int kM, int kR, int kP, int kW, int kV>
+// for the next substep's LDS fragment reads (front-loaded, kR in total).
+template <int kM, int kR>
 __device__ __forceinline__ void interleave_substep() {
   static_for<kM>([&](auto I) __attribute__((always_inline)) {
     constexpr int i = I;
     sched_group<kSchedMfma, 1>();
     constexpr int r = (i == kM - 1) ? (kR > i ? kR - i : 0) : (i < kR ? 1 : 0);
     if constexpr (r > 0) sched_group<kSchedDsRead, r>();
-    constexpr int p = (i + 1) * kP / kM - i * kP / kM;
-    if constexpr (p > 0) sched_group<kSchedValu, p>();
-    constexpr int w = (i + 1) * kW / kM - i * kW / kM;
-    if constexpr (w > 0) sched_group<kSchedDsWrite, w>();
-    constexpr int v = (i + 1) * kV / kM - i * kV / kM;
-    if constexpr (v > 0) sched_group<kSchedVmemRead, v>();
   });
 }
 
