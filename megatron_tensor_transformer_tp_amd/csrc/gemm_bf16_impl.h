@@ -124,11 +124,10 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
   const uint16_t* __restrict__ bias = static_cast<const uint16_t*>(ep.bias);
   const uint16_t* __restrict__ residual = static_cast<const uint16_t*>(ep.residual);
   const uint16_t* __restrict__ aux = static_cast<const uint16_t*>(ep.aux);
-  uint16_t* __restrict__ out_lo = static_cast<uint16_t*>(ep.out_lo);
   auto epilogue = [&](auto has_bias, auto has_res, auto has_extra) __attribute__((always_inline)) {
     constexpr bool kBias = decltype(has_bias)::value;
     constexpr bool kRes = decltype(has_res)::value;
-    constexpr bool kExtra = decltype(has_extra)::value;   // pre (GeLU) or out_lo (linear)
+    constexpr bool kExtra = decltype(has_extra)::value;   // pre (GeLU)
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
       const int m = m_lane + I * 32;
       if (MASKED && m >= M) return;
@@ -178,15 +177,6 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
             }
           }
           store_x4<OUT_F32>(ep.out, row_out + col, v);
-          if constexpr (EPI == EPI_LINEAR && kExtra && !OUT_F32) {
-            float lo[4];
-            static_for<2>([&](auto P) __attribute__((always_inline)) {
-              const uint32_t hi = pack_bf16x2(v[2 * P], v[2 * P + 1]);
-              lo[2 * P] = v[2 * P] - __uint_as_float(hi << 16);
-              lo[2 * P + 1] = v[2 * P + 1] - __uint_as_float(hi & 0xFFFF0000u);
-            });
-            store_x4<false>(out_lo, row_out + col, lo);
-          }
         });
         // keep the accumulator reads of one 32x32 block next to its stores
         // (hoisting all of them ahead of the stores would spill)
@@ -236,8 +226,6 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
     } else {
       if (ep.pre != nullptr) epilogue(F{}, F{}, T{}); else epilogue(F{}, F{}, F{});
     }
-  } else if (out_lo != nullptr) {
-    epilogue(F{}, F{}, T{});
   } else if (bias != nullptr) {
     if (residual != nullptr) epilogue(T{}, T{}, F{}); else epilogue(T{}, F{}, F{});
   } else {

@@ -24,9 +24,6 @@ constexpr int kQkvPart = 128;
 
 // Epilogue applied to the fp32 accumulator of C = A B, element (m, n), then
 //   out[m, n] = v                (fp32, or bf16 rounded to nearest-even)
-//   out_lo[m, n] = v - out[m, n] (bf16 out, EPI_LINEAR with no bias and no
-//                                 residual, if out_lo is set: v as the pair
-//                                 hi + lo, ~16 significant bits)
 // bias: input dtype or null; residual: input dtype, row stride ldr, or null
 // (EPI_LINEAR only); pre and out2 share out's dtype and row stride ldo; aux
 // is in the input dtype with row stride ldaux.
@@ -38,7 +35,6 @@ struct Epilogue {
   int64_t ldo;
   bool out_f32;
   int kind;
-  void* out_lo = nullptr;
   void* pre = nullptr;
   const void* aux = nullptr;
   int64_t ldaux = 0;
@@ -82,7 +78,7 @@ hipError_t launch_swiglu_combine_f32(const float* g, const float* u, float* h, i
 
 // fp32 x fp32 -> fp32 FMA, any shape.  Same layout flags as launch_gemm_bf16_t
 // (a_kmajor: A given [K, M]; b_kmajor: B given [K, N], else [N, K]); every
-// epilogue kind except the (hi, lo) pair.
+// epilogue kind.
 hipError_t launch_gemm_f32(const float* A, int64_t lda, bool a_kmajor, const float* B, int64_t ldb,
                            bool b_kmajor, int64_t M, int64_t N, int64_t K, const Epilogue& ep,
                            hipStream_t stream);
