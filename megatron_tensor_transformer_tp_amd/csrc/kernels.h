@@ -84,8 +84,10 @@ hipError_t launch_gemm_f32(const float* A, int64_t lda, bool a_kmajor, const flo
                            hipStream_t stream);
 
 // Column sums out[n] = sum_m in[m, n] (fp32 accumulation, in fp32 or bf16 by
-// in_dt 0/1, row stride ld), in two passes over 256-row chunks (deterministic):
-// partial needs colsum_partial_floats(M, N) floats of scratch.
+// in_dt 0/1, row stride ld), in two passes over 64-row chunks (deterministic):
+// partial needs colsum_partial_floats(M, N) floats of scratch.  N and ld are
+// multiples of 16 bytes' worth of elements, in 16-byte aligned (else
+// hipErrorInvalidValue).
 int64_t colsum_partial_floats(int64_t M, int64_t N);
 hipError_t launch_colsum(const void* in, int64_t ld, int in_dt, int64_t M, int64_t N, float* out,
                          float* partial, hipStream_t stream);

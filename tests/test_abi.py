@@ -160,8 +160,8 @@ def bwd(lib, **kw):
 
 def test_mlp_shard_bwd_validation(lib):
     need = lib.tp_mlp_shard_bwd_workspace_bytes(256, 1024, 4096, 8, BF16)
-    # dY and H [256, 512] bf16, then one 256-row chunk of fp32 partial sums over max(f, hidden)
-    assert need == 2 * 256 * 512 * 2 + 1024 * 4
+    # dY and H [256, 512] bf16, then four 64-row chunks of fp32 partial sums over max(f, hidden)
+    assert need == 2 * 256 * 512 * 2 + 4 * 1024 * 4
     assert lib.tp_mlp_shard_bwd_workspace_bytes(256, 1024, 4100, 8, BF16) == 0
     assert bwd(lib, ws_bytes=need - 1) == WORKSPACE
     assert bwd(lib, ws=None) == WORKSPACE
