@@ -316,23 +316,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   lds_barrier();
   read_frags(0, 0, af0, bf0);
 
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    // substep 0 of tile kt: fragments of substep 1 load under its MFMAs
-    read_frags(kt, 1, af1, bf1);
+  // One k-tile: substep 0 of tile kt (fragments of substep 1 load under its
+  // MFMAs), then substep 1: publish tile kt+1, start tile kt+STAGES-1 (into
+  // the stage tile kt-1 occupied: every wave finished reading it before this
+  // barrier), fragments of tile kt+1.  `stage(d)` gives the stage of tile
+  // kt + d: a compile-time value in the unrolled loop, so every LDS address
+  // is a loop-invariant register plus an immediate offset and the stage
+  // arithmetic disappears (+4-6% on the headline shapes).
+  auto ktile = [&](int kt, auto stage) __attribute__((always_inline)) {
+    const uint8_t* cur = smem + stage(0) * STAGE;
+    const uint8_t* nxt = smem + stage(1) * STAGE;
+    auto frags = [&](const uint8_t* st, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
+        __attribute__((always_inline)) {
+      static_for<TM>([&](auto I) __attribute__((always_inline)) {
+        af[I] = ta.frag(st, wm * WM + I * 32, s, lane);
+      });
+      static_for<TN>([&](auto J) __attribute__((always_inline)) {
+        bf[J] = tb.frag(st + A_BYTES, wn * WN + J * 32, s, lane);
+      });
+    };
+    frags(cur, 1, af1, bf1);
     mfmas(af0, bf0);
     interleave_substep<kMfma, kFrags>();
     sched_fence();
-    // substep 1: publish tile kt+1, start tile kt+STAGES-1 (into the stage
-    // tile kt-1 occupied: every wave finished reading it before this
-    // barrier), fragments of tile kt+1
     wait_vmcnt<(STAGES - 3) * L>();
     lds_barrier();
-    issue(kt + STAGES - 1);
-    read_frags(kt + 1, 0, af0, bf0);
+    const int kn = kt + STAGES - 1;
+    const uint32_t sbase = smem_base + stage(STAGES - 1) * STAGE;
+    ta.issue(min(kn, nk - 1), kn >= nk - 1, sbase, wave);
+    tb.issue(min(kn, nk - 1), kn >= nk - 1, sbase + A_BYTES, wave);
+    frags(nxt, 0, af0, bf0);
     mfmas(af1, bf1);
     interleave_substep<kMfma, kFrags>();
     sched_fence();
+  };
+  int kt = 0;
+  for (; kt + STAGES <= nk - 1; kt += STAGES) {
+    static_for<STAGES>([&](auto U) __attribute__((always_inline)) {
+      ktile(kt + U, [](int d) { return (static_cast<int>(decltype(U)::value) + d) % STAGES; });
+    });
   }
+  for (; kt < nk - 1; ++kt) ktile(kt, [kt](int d) { return (kt + d) % STAGES; });
   // the last k-tile (its substep-0 fragments are in af0 / bf0)
   read_frags(nk - 1, 1, af1, bf1);
   if constexpr (KTAIL) {
