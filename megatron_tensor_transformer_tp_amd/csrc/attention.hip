@@ -287,8 +287,11 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   issue(2);
   wait_vmcnt<2 * kCopies>();
   lds_barrier();
-  f32x16_t s_cur = qk(0);                       // block group: stage offset 0 in the group's half
-  raise_max(block_max(s_cur, group));
+  // scores of the current and the next block, alternating roles by step
+  // parity (the unroll factor is even), so no copy passes them on
+  f32x16_t s_buf[2];
+  s_buf[0] = qk(0);                             // block group: stage offset 0 in the group's half
+  raise_max(block_max(s_buf[0], group));
 
   auto step = [&](int it, auto U) __attribute__((always_inline)) {
     constexpr int ust = U * kStage;                        // block 2 it + group
@@ -299,17 +302,18 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     wait_vmcnt<kCopies>();
     lds_barrier();
     issue(it + 3);
+    constexpr int C = U & 1, N = C ^ 1;                     // current / next score buffer
     bf16x8_t pf[2];
     __builtin_amdgcn_s_setprio(1);
-    f32x16_t s_next = qk(nst);
-    weights(s_cur, pf);
+    s_buf[N] = qk(nst);
+    weights(s_buf[C], pf);
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     pv(pf, ust);
-    const float mx = block_max(s_next, 2 * it + 2 + group);
+    const float mx = block_max(s_buf[N], 2 * it + 2 + group);
     if (it + 1 < nit) raise_max(mx);
-    s_cur = s_next;
   };
+  static_assert(kCycle % 2 == 0, "score buffers alternate within one unrolled group");
   for (int it = 0; it < nit; it += kCycle) {
     step(it, std::integral_constant<int, 0>{});
     if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
