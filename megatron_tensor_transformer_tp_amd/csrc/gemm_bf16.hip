@@ -21,15 +21,9 @@ hipError_t launch_epi(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t
 }
 }  // namespace
 
-// Tile shape by an estimate of the launch time in units of one 256 x 256
-// tile's time, from the tile counts (one workgroup per CU for 256 x 256 and
-// 128 x 384, two for 128 x 128) and relative per-CU throughputs measured on
-// the 4096 x 8192 x {3072, 1536} products (128 x 384: 0.84, 128 x 128: 0.82
-// of the 256 x 256 rate; a last 128 x 128 round with one workgroup per CU
-// costs 0.73 of a full one).
 // Compute units of the current device (cached per device, safe to call
 // from several threads; 256 on a whole MI355X, fewer on a partition).
-static int64_t device_cus() {
+int64_t device_cus() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cus[kMaxDevices];
   int dev = 0;
@@ -43,6 +37,12 @@ static int64_t device_cus() {
   return n;
 }
 
+// Tile shape by an estimate of the launch time in units of one 256 x 256
+// tile's time, from the tile counts (one workgroup per CU for 256 x 256 and
+// 128 x 384, two for 128 x 128) and relative per-CU throughputs measured on
+// the 4096 x 8192 x {3072, 1536} products (128 x 384: 0.84, 128 x 128: 0.82
+// of the 256 x 256 rate; a last 128 x 128 round with one workgroup per CU
+// costs 0.73 of a full one).
 static int gemm_tile_choice(int64_t M, int64_t N) {
   const int64_t kCUs = device_cus();
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };

@@ -165,21 +165,28 @@ __device__ __forceinline__ void store_swiglu(const f32x16_t (&acc)[2][TM], int m
 // restaged through LDS: the MFMA layout gives each lane 4 columns of one row,
 // so a direct store instruction writes 16-byte pieces of 32 different rows
 // (32 cache lines).  Here each wave writes one 32-row slab of its
-// accumulators into its own LDS region (rows padded by 16 bytes, so both the
-// slab writes and the row reads are free of bank conflicts), reads it back
+// accumulators into its own LDS region of kStagedSlabBytes, reads it back
 // row by row and stores whole row segments: WN/4 lanes per row, each
 // instruction covering 64*16/(WN*4) rows of WN*4 contiguous bytes.  The
-// caller has drained every copy and passed a barrier (the stage area is free).
+// 16-byte chunk c of slab row r sits at chunk c ^ (r & 15) (for W = 64: the
+// 16 rows written by 16 consecutive lanes, and the 16 chunks of one row read
+// by 16 consecutive lanes, fall in distinct bank groups).  The caller
+// guarantees that nothing else reads or writes the region meanwhile.
+template <int TN>
+constexpr int kStagedSlabBytes = 32 * TN * 32 * 4;
 template <int TM, int TN>
 __device__ __forceinline__ void store_linear_f32_staged(const f32x16_t (&acc)[TN][TM], uint8_t* lds,
                                                         int lane, int m_w, int n_w,
                                                         const Epilogue& ep) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   constexpr int W = TN * 32;            // columns of the wave's sub-tile
-  constexpr int PITCH = W * 4 + 16;     // bytes per staged row
-  constexpr int LPR = W / 4;            // lanes per row
+  constexpr int PITCH = W * 4;          // bytes per staged row
+  constexpr int CPR = W / 4;            // 16-byte chunks per row
+  constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+  constexpr int LPR = CPR;              // lanes per row
   constexpr int RPI = 64 / LPR;         // rows per store instruction
-  static_assert(LPR * RPI == 64 && 32 % RPI == 0, "whole rows per store instruction");
+  static_assert(LPR * RPI == 64 && 32 % RPI == 0 && (CPR & (CPR - 1)) == 0,
+                "whole rows per store instruction");
   const uint16_t* __restrict__ bias = static_cast<const uint16_t*>(ep.bias);
   const uint16_t* __restrict__ residual = static_cast<const uint16_t*>(ep.residual);
   const int col = (lane % LPR) * 4, rsub = lane / LPR;
@@ -193,12 +200,13 @@ __device__ __forceinline__ void store_linear_f32_staged(const f32x16_t (&acc)[TN
         static_for<4>([&](auto G) __attribute__((always_inline)) {
           const f32x4_t v = {acc[J][I][4 * G], acc[J][I][4 * G + 1], acc[J][I][4 * G + 2],
                              acc[J][I][4 * G + 3]};
-          *TPK_LDS(f32x4_t, lds + (lane & 31) * PITCH + (J * 32 + G * 8 + (lane >> 5) * 4) * 4) = v;
+          const int r = lane & 31, c = J * 8 + G * 2 + (lane >> 5);
+          *TPK_LDS(f32x4_t, lds + r * PITCH + ((c ^ (r & SWZ)) * 16)) = v;
         });
       });
       static_for<32 / RPI>([&](auto Q) __attribute__((always_inline)) {
         const int r = Q * RPI + rsub;
-        const f32x4_t v = *TPK_LDS(const f32x4_t, lds + r * PITCH + col * 4);
+        const f32x4_t v = *TPK_LDS(const f32x4_t, lds + r * PITCH + (((col >> 2) ^ (r & SWZ)) * 16));
         const int64_t m = m_w + I * 32 + r;
         float o[4] = {v[0] + b[0], v[1] + b[1], v[2] + b[2], v[3] + b[3]};
         if constexpr (kRes) {
@@ -231,6 +239,25 @@ __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int nvalid) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// LDS of one workgroup: STAGES stages of (BM + BN) x 64 bytes; with the fp32
+// restaging (linear fp32 epilogue, wave widths whose rows split evenly over
+// the 64 lanes) the slabs sit in the last stage and the bytes past the
+// stages, so that the next tile's first STAGES-1 k-tiles can be in flight
+// during the epilogue.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int EPI, bool OUT_F32>
+struct DmaLayout {
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kTN = BN / WGN / 32;
+  static constexpr int kStage = (BM + BN) * kBKd * 2;
+  static constexpr bool kStaged = EPI == EPI_LINEAR && OUT_F32 && 64 % (BN / WGN / 4) == 0;
+  static constexpr int kStagingAt = (STAGES - 1) * kStage;
+  static constexpr int kStagingEnd = kStagingAt + kWaves * kStagedSlabBytes<kTN>;
+  static constexpr int kLdsBytes =
+      kStaged && kStagingEnd > STAGES * kStage ? kStagingEnd : STAGES * kStage;
+  static constexpr int kPerCu = 160 * 1024 / kLdsBytes;   // resident workgroups per CU
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
+
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,
           bool OUT_F32, bool KTAIL>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
@@ -247,7 +274,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   constexpr int L = TileA::Q + TileB::Q;   // copies per wave per k-tile
   static_assert(STAGES >= 3 && STAGES * STAGE <= 160 * 1024, "LDS stages");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+  using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32>;
+  static_assert(Layout::kStage == STAGE, "stage size");
+  constexpr bool kStaged = Layout::kStaged;
+  constexpr int kStagingAt = Layout::kStagingAt;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Layout::kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -255,20 +286,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   const int wm = wave / WGN, wn = wave % WGN;
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  if (!(BM == 256 && BN == 256 && tile_coords_rounds(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn)))
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int ntiles = tiles_m * tiles_n;
   const int nk = (K + kBKd - 1) / kBKd;
   const int klast = (nk - 1) * kBKd, krem = K - klast;   // krem == kBKd unless KTAIL
 
+  // Workgroup b computes tiles b, b + gridDim.x, ...; tile t takes the place
+  // workgroup t of a one-tile-per-workgroup grid would (XCD t % 8, round
+  // order), so a grid of whole rounds changes no tile's neighbours.
   TileA ta;
   TileB tb;
-  ta.init(A, lda, m0, M, klast, krem, wave, lane);
-  if constexpr (EPI == EPI_SWIGLU)
-    tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, N / 2, klast, krem, wave, lane);
-  else
-    tb.init(B, ldb, n0, N, klast, krem, wave, lane);
+  int m0, n0;
+  auto setup = [&](int t) __attribute__((always_inline)) {
+    int tm, tn;
+    if (!(BM == 256 && BN == 256 && tile_coords_rounds(t, ntiles, tiles_m, tiles_n, tm, tn)))
+      tile_coords(t, ntiles, tiles_m, tiles_n, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    ta.init(A, lda, m0, M, klast, krem, wave, lane);
+    if constexpr (EPI == EPI_SWIGLU)
+      tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, N / 2, klast, krem, wave,
+                   lane);
+    else
+      tb.init(B, ldb, n0, N, klast, krem, wave, lane);
+  };
 
   // Copies of k-tile kt (clamped to the last tile) into stage kt % STAGES.
   const uint32_t smem_base = lds_address(smem);
@@ -280,22 +320,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     tb.issue(kc, tail, sbase + A_BYTES, wave);
   };
 
+  // The lane index of the fragment reads, renewed (opaquely) for every tile:
+  // their loop-invariant LDS addresses are then computed per tile instead of
+  // being hoisted out of the tile loop and held live through the epilogue.
+  int flane = lane;
   bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
   auto read_frags = [&](int kt, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
       __attribute__((always_inline)) {
     const uint8_t* st = smem + (kt % STAGES) * STAGE;
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      af[I] = ta.frag(st, wm * WM + I * 32, s, lane);
+      af[I] = ta.frag(st, wm * WM + I * 32, s, flane);
     });
     static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      bf[J] = tb.frag(st + A_BYTES, wn * WN + J * 32, s, lane);
+      bf[J] = tb.frag(st + A_BYTES, wn * WN + J * 32, s, flane);
     });
   };
 
   f32x16_t acc[TN][TM];
-  static_for<TN>([&](auto J) __attribute__((always_inline)) {
-    static_for<TM>([&](auto I) __attribute__((always_inline)) { acc[J][I] = (f32x16_t)(0.0f); });
-  });
   auto mfmas = [&](const bf16x8_t(&af)[TM], const bf16x8_t(&bf)[TN]) __attribute__((always_inline)) {
     static_for<TN>([&](auto J) __attribute__((always_inline)) {
       static_for<TM>([&](auto I) __attribute__((always_inline)) {
@@ -307,15 +348,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   constexpr int kFrags = TM + 2 * TN;
   constexpr int kMfma = TM * TN;
 
-  // Every iteration issues exactly L copies per wave (the copies of tiles past
-  // the end re-read the last tile into a stage that is never read again), so
-  // "tile kt+1 has landed" is always vmcnt <= (STAGES-3)*L: only the tiles
-  // kt+2 .. kt+STAGES-2 may still be in flight when tile kt+1 is published.
-  static_for<STAGES - 1>([&](auto T) __attribute__((always_inline)) { issue(T); });
-  wait_vmcnt<(STAGES - 2) * L>();
-  lds_barrier();
-  read_frags(0, 0, af0, bf0);
-
   // One k-tile: substep 0 of tile kt (fragments of substep 1 load under its
   // MFMAs), then substep 1: publish tile kt+1, start tile kt+STAGES-1 (into
   // the stage tile kt-1 occupied: every wave finished reading it before this
@@ -323,16 +355,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   // kt + d: a compile-time value in the unrolled loop, so every LDS address
   // is a loop-invariant register plus an immediate offset and the stage
   // arithmetic disappears (+4-6% on the headline shapes).
+  //
+  // Every iteration issues exactly L copies per wave (the copies of tiles past
+  // the end re-read the last tile into a stage that is never read again), so
+  // "tile kt+1 has landed" is always vmcnt <= (STAGES-3)*L: only the tiles
+  // kt+2 .. kt+STAGES-2 may still be in flight when tile kt+1 is published.
   auto ktile = [&](int kt, auto stage) __attribute__((always_inline)) {
     const uint8_t* cur = smem + stage(0) * STAGE;
     const uint8_t* nxt = smem + stage(1) * STAGE;
     auto frags = [&](const uint8_t* st, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
         __attribute__((always_inline)) {
       static_for<TM>([&](auto I) __attribute__((always_inline)) {
-        af[I] = ta.frag(st, wm * WM + I * 32, s, lane);
+        af[I] = ta.frag(st, wm * WM + I * 32, s, flane);
       });
       static_for<TN>([&](auto J) __attribute__((always_inline)) {
-        bf[J] = tb.frag(st + A_BYTES, wn * WN + J * 32, s, lane);
+        bf[J] = tb.frag(st + A_BYTES, wn * WN + J * 32, s, flane);
       });
     };
     frags(cur, 1, af1, bf1);
@@ -350,65 +387,105 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     interleave_substep<kMfma, kFrags>();
     sched_fence();
   };
-  int kt = 0;
-  for (; kt + STAGES <= nk - 1; kt += STAGES) {
-    static_for<STAGES>([&](auto U) __attribute__((always_inline)) {
-      ktile(kt + U, [](int d) { return (static_cast<int>(decltype(U)::value) + d) % STAGES; });
-    });
-  }
-  for (; kt < nk - 1; ++kt) ktile(kt, [kt](int d) { return (kt + d) % STAGES; });
-  // the last k-tile (its substep-0 fragments are in af0 / bf0)
-  read_frags(nk - 1, 1, af1, bf1);
-  if constexpr (KTAIL) {
-    // lane l's fragments hold k 16 s + 8 (l / 32) .. +7 of the tile
-    const int k_lane = 8 * (lane >> 5);
-    static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      af0[I] = keep_first(af0[I], krem - k_lane);
-      af1[I] = keep_first(af1[I], krem - 16 - k_lane);
-    });
-    static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      bf0[J] = keep_first(bf0[J], krem - k_lane);
-      bf1[J] = keep_first(bf1[J], krem - 16 - k_lane);
-    });
-  }
-  mfmas(af0, bf0);
-  mfmas(af1, bf1);
-  wait_vmcnt<0>();
 
-  const bool edge = m0 + BM > M || n0 + BN > N;   // workgroup-uniform
-  const int m_lane = m0 + wm * WM + (lane & 31);
-  if constexpr (EPI == EPI_SWIGLU) {
-    static_assert(TN == 2, "gate and value blocks per wave");
-    const int n_lane = n0 / 2 + wn * (WN / 2) + (lane >> 5) * 4;
-    if (edge)
-      store_swiglu<TM, true, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
-    else
-      store_swiglu<TM, false, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
-  } else {
-    // fp32 linear outputs of interior tiles go through the LDS restaging
-    // (wave widths whose rows split evenly over the 64 lanes)
-    constexpr bool kStaged = EPI == EPI_LINEAR && OUT_F32 && 64 % (WN / 4) == 0;
-    bool stored = false;
-    if constexpr (kStaged) {
-      if (!edge) {
-        static_assert(NW * 32 * (WN * 4 + 16) <= STAGES * STAGE, "staging slabs fit in the stages");
-        // the stage area is free once every wave's copies have landed
-        // (waited above) and its fragment reads of the last stage have returned
-        sched_fence();
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        lds_barrier();
-        store_linear_f32_staged<TM, TN>(acc, smem + wave * 32 * (WN * 4 + 16), lane, m0 + wm * WM,
-                                        n0 + wn * WN, ep);
-        stored = true;
+  int tile = blockIdx.x;
+  setup(tile);
+  static_for<STAGES - 1>([&](auto T) __attribute__((always_inline)) { issue(T); });
+  wait_vmcnt<(STAGES - 2) * L>();
+  for (;;) {
+    // k-tile 0 of the current tile has landed (each wave waited for its own copies)
+    flane = lane;
+    asm volatile("" : "+v"(flane));
+    lds_barrier();
+    read_frags(0, 0, af0, bf0);
+    static_for<TN>([&](auto J) __attribute__((always_inline)) {
+      static_for<TM>([&](auto I) __attribute__((always_inline)) { acc[J][I] = (f32x16_t)(0.0f); });
+    });
+    int kt = 0;
+    for (; kt + STAGES <= nk - 1; kt += STAGES) {
+      static_for<STAGES>([&](auto U) __attribute__((always_inline)) {
+        ktile(kt + U, [](int d) { return (static_cast<int>(decltype(U)::value) + d) % STAGES; });
+      });
+    }
+    for (; kt < nk - 1; ++kt) ktile(kt, [kt](int d) { return (kt + d) % STAGES; });
+    // the last k-tile (its substep-0 fragments are in af0 / bf0)
+    read_frags(nk - 1, 1, af1, bf1);
+    if constexpr (KTAIL) {
+      // lane l's fragments hold k 16 s + 8 (l / 32) .. +7 of the tile
+      const int k_lane = 8 * (flane >> 5);
+      static_for<TM>([&](auto I) __attribute__((always_inline)) {
+        af0[I] = keep_first(af0[I], krem - k_lane);
+        af1[I] = keep_first(af1[I], krem - 16 - k_lane);
+      });
+      static_for<TN>([&](auto J) __attribute__((always_inline)) {
+        bf0[J] = keep_first(bf0[J], krem - k_lane);
+        bf1[J] = keep_first(bf1[J], krem - 16 - k_lane);
+      });
+    }
+    mfmas(af0, bf0);
+    mfmas(af1, bf1);
+
+    // Every stage is free once each wave's copies have landed (the clamped
+    // re-reads past the last k-tile included) and its fragment reads have
+    // returned, and all waves have passed the barrier after that.  Then the
+    // next tile's first STAGES-1 k-tiles are started before this tile's
+    // epilogue, which they overlap.
+    const int cm0 = m0, cn0 = n0;
+    const int next = tile + static_cast<int>(gridDim.x);
+    const bool more = next < ntiles;   // workgroup-uniform
+    wait_vmcnt<0>();
+    if (more || kStaged) {
+      sched_fence();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      lds_barrier();
+    }
+    if (more) {
+      setup(next);
+      static_for<STAGES - 1>([&](auto T) __attribute__((always_inline)) { issue(T); });
+    }
+
+    // The epilogue's per-lane addresses are loop-invariant; computed from an
+    // opaque copy of the lane index they are not hoisted out of the tile
+    // loop, where they would stay live through the main loop.
+    int elane = lane;
+    asm volatile("" : "+v"(elane));
+    const bool edge = cm0 + BM > M || cn0 + BN > N;   // workgroup-uniform
+    const int m_lane = cm0 + wm * WM + (elane & 31);
+    if constexpr (EPI == EPI_SWIGLU) {
+      static_assert(TN == 2, "gate and value blocks per wave");
+      const int n_lane = cn0 / 2 + wn * (WN / 2) + (elane >> 5) * 4;
+      if (edge)
+        store_swiglu<TM, true, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
+      else
+        store_swiglu<TM, false, OUT_F32>(acc, m_lane, n_lane, M, N / 2, ep);
+    } else {
+      bool stored = false;
+      if constexpr (kStaged) {
+        if (!edge) {
+          store_linear_f32_staged<TM, TN>(acc, smem + kStagingAt + wave * kStagedSlabBytes<TN>, elane,
+                                          cm0 + wm * WM, cn0 + wn * WN, ep);
+          stored = true;
+        }
+      }
+      if (!stored) {
+        const int n_lane = cn0 + wn * WN + (elane >> 5) * 4;
+        if (edge)
+          store_tile<TM, TN, true, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
+        else
+          store_tile<TM, TN, false, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
       }
     }
-    if (!stored) {
-      const int n_lane = n0 + wn * WN + (lane >> 5) * 4;
-      if (edge)
-        store_tile<TM, TN, true, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
-      else
-        store_tile<TM, TN, false, EPI, OUT_F32>(acc, m_lane, n_lane, M, N, ep);
-    }
+    if (!more) break;
+    // The copy sources are rebuilt from an opaque copy of the tile index, so
+    // that the ones used for the prefetch above are not kept live across
+    // the epilogue.
+    tile = next;
+    asm volatile("" : "+s"(tile));
+    setup(tile);
+    // the next tile's first k-tile (and everything before it) has landed;
+    // waiting for the epilogue's stores as well keeps the count simple
+    sched_fence();
+    wait_vmcnt<0>();
   }
 }
 
@@ -424,15 +501,21 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
       (EPI == EPI_SWIGLU && N % 2 != 0))
     return hipErrorInvalidValue;
   const int64_t tiles = ((static_cast<int64_t>(M) + BM - 1) / BM) * ((static_cast<int64_t>(N) + BN - 1) / BN);
-  if (tiles > INT32_MAX) return hipErrorInvalidValue;     // one workgroup per tile in grid x
+  if (tiles > INT32_MAX) return hipErrorInvalidValue;     // tile indices are ints
+  // one round of resident workgroups (whole XCD rounds: a multiple of 8),
+  // each looping over its tiles
+  using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32>;
+  int64_t cap = device_cus() * Layout::kPerCu / 8 * 8;
+  if (cap < 8) cap = 8;
+  const unsigned grid = static_cast<unsigned>(tiles < cap ? tiles : cap);
   if (K % kBKd != 0)
     hipLaunchKernelGGL(
         (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, true>),
-        dim3(static_cast<unsigned>(tiles)), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
+        dim3(grid), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
   else
     hipLaunchKernelGGL(
         (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, false>),
-        dim3(static_cast<unsigned>(tiles)), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
+        dim3(grid), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
   return hipGetLastError();
 }
 

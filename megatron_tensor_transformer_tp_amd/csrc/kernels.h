@@ -42,6 +42,10 @@ struct Epilogue {
   const void* b2 = nullptr;   // EPI_SWIGLU: the value projection (B is the gate)
 };
 
+// Compute units of the current device (cached per device; 256 on a whole
+// MI355X).  The GEMM kernels size their grids by it.
+int64_t device_cus();
+
 // bf16 x bf16 -> fp32 accumulate, MFMA.  A [M, K] row-major (lda), B [K, N]
 // row-major (ldb).  Any M, N and K >= 1 with N % 8 == 0, K % 8 == 0,
 // lda/ldb/ldr/ldo % 8 == 0 (ldo % 4 for fp32 out), 16-byte aligned pointers
