@@ -139,6 +139,49 @@ struct OperandTile {
   }
 };
 
+// A k-contiguous operand copied two k-tiles at a time: R rows of 64 k, 128
+// bytes each, so every copy instruction reads 8 whole 128-byte lines (a
+// single k-tile's 64-byte row pieces cost the texture addresser about twice
+// as much per byte, which limits a product whose operands are both
+// k-contiguous).  Logical chunk c (8 k) of row r sits at chunk
+// c ^ ((r >> 1) & 7): the 16 rows read by 16 consecutive lanes of a fragment
+// fall in distinct 16-byte bank groups.  K % 64 == 0 (no partial tiles).
+template <int R, int NW>
+struct OperandPairTile {
+  static constexpr int kBytes = R * 2 * kBKd * 2;
+  static constexpr int Q = kBytes / 1024 / NW;
+  static_assert(Q * NW * 1024 == kBytes, "pair tile shape");
+
+  const uint16_t* src[Q];   // sources of k-tiles 0 and 1
+
+  // Rows [r0, r0 + R) of an operand [rows, K] (row stride ld), clamped to
+  // the last row.
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int r0, int rows, int wave,
+                                       int lane) {
+    static_for<Q>([&](auto I) __attribute__((always_inline)) {
+      const int slot = (wave * Q + I) * 64 + lane;
+      const int row = slot >> 3, kin = 8 * ((slot & 7) ^ ((row >> 1) & 7));
+      src[I] = base + static_cast<int64_t>(min(r0 + row, rows - 1)) * ld + kin;
+    });
+  }
+
+  // Copies of k-tiles 2j and 2j + 1 into the LDS region at byte address lds.
+  __device__ __forceinline__ void issue(int j, uint32_t lds, int wave) const {
+    static_for<Q>([&](auto I) __attribute__((always_inline)) {
+      copy_to_lds(src[I] + static_cast<int64_t>(j) * (2 * kBKd), lds + (wave * Q + I) * 1024);
+    });
+  }
+
+  // MFMA fragment of 32 rows starting at row0 (a multiple of 32) from the
+  // k-tile half h of the pair, k-substep s: lane l gets row row0 + l % 32,
+  // k 16 s + 8 (l / 32) .. +7 of that k-tile.
+  __device__ __forceinline__ bf16x8_t frag(const uint8_t* st, int row0, int h, int s, int lane) const {
+    const int r = lane & 31;
+    const int chunk = (4 * h + 2 * s + (lane >> 5)) ^ ((r >> 1) & 7);
+    return *TPK_LDS(const bf16x8_t, st + (row0 + r) * 128 + chunk * 16);
+  }
+};
+
 // SwiGLU epilogue: acc[0] holds the gate and acc[1] the value of the same 32
 // features (see OperandTile::init_dual); out[m, n] = SiLU(gate) * value for
 // m < M and n < F (F % 4 == 0).
@@ -239,27 +282,45 @@ __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int nvalid) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
-// LDS of one workgroup: STAGES stages of (BM + BN) x 64 bytes; with the fp32
-// restaging (linear fp32 epilogue, wave widths whose rows split evenly over
-// the 64 lanes) the slabs sit in the last stage and the bytes past the
-// stages, so that the next tile's first STAGES-1 k-tiles can be in flight
-// during the epilogue.
-template <int BM, int BN, int WGM, int WGN, int STAGES, int EPI, bool OUT_F32>
+// LDS of one workgroup.  Single k-tile stages: STAGES stages of
+// (BM + BN) x 64 bytes; with the fp32 restaging (linear fp32 epilogue, wave
+// widths whose rows split evenly over the 64 lanes) the slabs sit in the
+// last stage and the bytes past the stages, so that the next tile's first
+// STAGES-1 k-tiles can be in flight during the epilogue.  BPAIR (B
+// k-contiguous, K % 64 == 0): STAGES single stages of A (BM x 64 bytes),
+// then kPairs stages of B holding two k-tiles each (BN x 128 bytes); the
+// slabs reuse the stage area, so the next tile starts after the epilogue.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int EPI, bool OUT_F32, bool BPAIR>
 struct DmaLayout {
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kTN = BN / WGN / 32;
+  static constexpr int kABytes = BM * kBKd * 2;
   static constexpr int kStage = (BM + BN) * kBKd * 2;
+  static constexpr int kPairs = 3;
+  static constexpr int kPairBytes = BN * 2 * kBKd * 2;
+  static constexpr int kPairAt = STAGES * kABytes;
   static constexpr bool kStaged = EPI == EPI_LINEAR && OUT_F32 && 64 % (BN / WGN / 4) == 0;
-  static constexpr int kStagingAt = (STAGES - 1) * kStage;
+  static constexpr bool kPrefetch = !BPAIR;   // next tile's copies during the epilogue
+  static constexpr int kStagingAt = BPAIR ? 0 : (STAGES - 1) * kStage;
   static constexpr int kStagingEnd = kStagingAt + kWaves * kStagedSlabBytes<kTN>;
+  static constexpr int kStageBytes = BPAIR ? kPairAt + kPairs * kPairBytes : STAGES * kStage;
   static constexpr int kLdsBytes =
-      kStaged && kStagingEnd > STAGES * kStage ? kStagingEnd : STAGES * kStage;
+      kStaged && kStagingEnd > kStageBytes ? kStagingEnd : kStageBytes;
   static constexpr int kPerCu = 160 * 1024 / kLdsBytes;   // resident workgroups per CU
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
+// LDS places of one k-tile in the main loop: A stage, B pair stage and half
+// of the pair; KNOWN: the k-tile's parity is a compile-time EVEN.
+template <bool KNOWN, bool EVEN>
+struct KPlace {
+  static constexpr bool kParityKnown = KNOWN;
+  static constexpr bool kEven = EVEN;
+  int a, p, h;
+};
+
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,
-          bool OUT_F32, bool KTAIL>
+          bool OUT_F32, bool KTAIL, bool BPAIR>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     int M, int N, int K, const Epilogue ep) {
@@ -267,17 +328,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave sub-tiles of whole 32 x 32 MFMA blocks");
+  static_assert(!BPAIR || (!B_KMAJOR && !KTAIL && EPI != EPI_SWIGLU && STAGES == 4),
+                "paired B stages: k-contiguous B, whole 64-k pairs, 4 A stages");
   using TileA = OperandTile<BM, NW, A_KMAJOR, KTAIL>;
   using TileB = OperandTile<BN, NW, B_KMAJOR, KTAIL>;
+  using TileP = OperandPairTile<BN, NW>;
   constexpr int A_BYTES = TileA::kBytes;
   constexpr int STAGE = A_BYTES + TileB::kBytes;
-  constexpr int L = TileA::Q + TileB::Q;   // copies per wave per k-tile
+  constexpr int L = TileA::Q + TileB::Q;   // copies per wave per k-tile (single stages)
   static_assert(STAGES >= 3 && STAGES * STAGE <= 160 * 1024, "LDS stages");
 
-  using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32>;
-  static_assert(Layout::kStage == STAGE, "stage size");
+  using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32, BPAIR>;
+  static_assert(Layout::kStage == STAGE && Layout::kABytes == A_BYTES &&
+                Layout::kPairBytes == TileP::kBytes, "stage sizes");
   constexpr bool kStaged = Layout::kStaged;
+  constexpr bool kPrefetch = Layout::kPrefetch;
   constexpr int kStagingAt = Layout::kStagingAt;
+  constexpr int kPairs = Layout::kPairs;
+  constexpr int kPairAt = Layout::kPairAt;
+  constexpr int kPairBytes = Layout::kPairBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Layout::kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -289,12 +358,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   const int ntiles = tiles_m * tiles_n;
   const int nk = (K + kBKd - 1) / kBKd;
   const int klast = (nk - 1) * kBKd, krem = K - klast;   // krem == kBKd unless KTAIL
+  const int npairs = nk / 2;                             // BPAIR: nk is even
 
   // Workgroup b computes tiles b, b + gridDim.x, ...; tile t takes the place
   // workgroup t of a one-tile-per-workgroup grid would (XCD t % 8, round
   // order), so a grid of whole rounds changes no tile's neighbours.
   TileA ta;
   TileB tb;
+  TileP tp;
   int m0, n0;
   auto setup = [&](int t) __attribute__((always_inline)) {
     int tm, tn;
@@ -303,37 +374,80 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     m0 = tm * BM;
     n0 = tn * BN;
     ta.init(A, lda, m0, M, klast, krem, wave, lane);
-    if constexpr (EPI == EPI_SWIGLU)
+    if constexpr (BPAIR)
+      tp.init(B, ldb, n0, N, wave, lane);
+    else if constexpr (EPI == EPI_SWIGLU)
       tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, N / 2, klast, krem, wave,
                    lane);
     else
       tb.init(B, ldb, n0, N, klast, krem, wave, lane);
   };
 
-  // Copies of k-tile kt (clamped to the last tile) into stage kt % STAGES.
+  // LDS places of k-tile kt: A in stage kt % STAGES; B in the same stage
+  // (single stages) or in pair stage (kt / 2) % kPairs, half kt % 2.
   const uint32_t smem_base = lds_address(smem);
-  auto issue = [&](int kt) __attribute__((always_inline)) {
-    const int kc = min(kt, nk - 1);
-    const bool tail = kt >= nk - 1;
-    const uint32_t sbase = smem_base + (kt % STAGES) * STAGE;
-    ta.issue(kc, tail, sbase, wave);
-    tb.issue(kc, tail, sbase + A_BYTES, wave);
+  auto a_at = [](int sa) { return BPAIR ? sa * A_BYTES : sa * STAGE; };
+  auto b_at = [](int sa, int sp) { return BPAIR ? kPairAt + sp * kPairBytes : sa * STAGE + A_BYTES; };
+  // Copies of k-tile kt's A (clamped to the last tile), and of kt's B
+  // (single stages) or of pair j's B (clamped to the last pair).
+  auto issue_a = [&](int kt) __attribute__((always_inline)) {
+    ta.issue(min(kt, nk - 1), kt >= nk - 1, smem_base + a_at(kt % STAGES), wave);
   };
+  auto issue_b = [&](int kt) __attribute__((always_inline)) {
+    tb.issue(min(kt, nk - 1), kt >= nk - 1, smem_base + b_at(kt % STAGES, 0), wave);
+  };
+  auto issue_pair = [&](int j) __attribute__((always_inline)) {
+    tp.issue(min(j, npairs - 1), smem_base + b_at(0, j % kPairs), wave);
+  };
+  // The first k-tiles of the current tile, and the vmcnt that says k-tile 0
+  // has landed.  Single stages: k-tiles 0 .. STAGES-2.  Pairs: A 0, pair 0,
+  // A 1, A 2, pair 1 (k-tiles 0 .. 3 of B).
+  auto prologue = [&]() __attribute__((always_inline)) {
+    if constexpr (BPAIR) {
+      issue_a(0);
+      issue_pair(0);
+      issue_a(1);
+      issue_a(2);
+      issue_pair(1);
+    } else {
+      static_for<STAGES - 1>([&](auto T) __attribute__((always_inline)) {
+        issue_a(T);
+        issue_b(T);
+      });
+    }
+  };
+  constexpr int kFirstWait = BPAIR ? 2 * TileA::Q + TileP::Q : (STAGES - 2) * L;
+  // "k-tile kt+1 has landed" inside the main loop.  Single stages: every
+  // iteration issues L copies per wave (past the end they re-read the last
+  // tile into a stage never read again), so only tiles kt+2 .. kt+STAGES-2
+  // may be in flight.  Pairs: iteration kt issues A(kt+3), and for even kt
+  // the pair of k-tiles kt+4, kt+5 (into the pair stage k-tiles kt-2, kt-1
+  // left); A(kt+1) was issued in iteration kt-2 and its pair earlier, and
+  // after it exactly one A and one pair have been issued.
+  constexpr int kLoopWait = BPAIR ? TileA::Q + TileP::Q : (STAGES - 3) * L;
 
   // The lane index of the fragment reads, renewed (opaquely) for every tile:
   // their loop-invariant LDS addresses are then computed per tile instead of
   // being hoisted out of the tile loop and held live through the epilogue.
   int flane = lane;
   bf16x8_t af0[TM], bf0[TN], af1[TM], bf1[TN];
-  auto read_frags = [&](int kt, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
+  // Fragments of substep s of the k-tile whose A sits at LDS offset ao and
+  // whose B sits at offset bo (half h of a pair).
+  auto frags = [&](int ao, int bo, int h, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
       __attribute__((always_inline)) {
-    const uint8_t* st = smem + (kt % STAGES) * STAGE;
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      af[I] = ta.frag(st, wm * WM + I * 32, s, flane);
+      af[I] = ta.frag(smem + ao, wm * WM + I * 32, s, flane);
     });
     static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      bf[J] = tb.frag(st + A_BYTES, wn * WN + J * 32, s, flane);
+      if constexpr (BPAIR)
+        bf[J] = tp.frag(smem + bo, wn * WN + J * 32, h, s, flane);
+      else
+        bf[J] = tb.frag(smem + bo, wn * WN + J * 32, s, flane);
     });
+  };
+  auto read_frags = [&](int kt, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
+      __attribute__((always_inline)) {
+    frags(a_at(kt % STAGES), b_at(kt % STAGES, (kt / 2) % kPairs), kt & 1, s, af, bf);
   };
 
   f32x16_t acc[TN][TM];
@@ -349,49 +463,48 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   constexpr int kMfma = TM * TN;
 
   // One k-tile: substep 0 of tile kt (fragments of substep 1 load under its
-  // MFMAs), then substep 1: publish tile kt+1, start tile kt+STAGES-1 (into
-  // the stage tile kt-1 occupied: every wave finished reading it before this
-  // barrier), fragments of tile kt+1.  `stage(d)` gives the stage of tile
-  // kt + d: a compile-time value in the unrolled loop, so every LDS address
-  // is a loop-invariant register plus an immediate offset and the stage
-  // arithmetic disappears (+4-6% on the headline shapes).
-  //
-  // Every iteration issues exactly L copies per wave (the copies of tiles past
-  // the end re-read the last tile into a stage that is never read again), so
-  // "tile kt+1 has landed" is always vmcnt <= (STAGES-3)*L: only the tiles
-  // kt+2 .. kt+STAGES-2 may still be in flight when tile kt+1 is published.
-  auto ktile = [&](int kt, auto stage) __attribute__((always_inline)) {
-    const uint8_t* cur = smem + stage(0) * STAGE;
-    const uint8_t* nxt = smem + stage(1) * STAGE;
-    auto frags = [&](const uint8_t* st, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
-        __attribute__((always_inline)) {
-      static_for<TM>([&](auto I) __attribute__((always_inline)) {
-        af[I] = ta.frag(st, wm * WM + I * 32, s, flane);
-      });
-      static_for<TN>([&](auto J) __attribute__((always_inline)) {
-        bf[J] = tb.frag(st + A_BYTES, wn * WN + J * 32, s, flane);
-      });
-    };
-    frags(cur, 1, af1, bf1);
+  // MFMAs), then substep 1: publish tile kt+1, start the copies that reuse
+  // the places of tile kt-1 (every wave finished reading them before this
+  // barrier), fragments of tile kt+1.  `sel(d)` gives the (A stage, B pair
+  // stage) of tile kt + d: compile-time values in the unrolled loop, so
+  // every LDS address is a loop-invariant register plus an immediate offset
+  // and the stage arithmetic disappears (+4-6% on the headline shapes).
+  auto ktile = [&](int kt, auto sel) __attribute__((always_inline)) {
+    constexpr bool kEvenKnown = decltype(sel(0))::kParityKnown;
+    frags(a_at(sel(0).a), b_at(sel(0).a, sel(0).p), sel(0).h, 1, af1, bf1);
     mfmas(af0, bf0);
     interleave_substep<kMfma, kFrags>();
     sched_fence();
-    wait_vmcnt<(STAGES - 3) * L>();
+    wait_vmcnt<kLoopWait>();
     lds_barrier();
     const int kn = kt + STAGES - 1;
-    const uint32_t sbase = smem_base + stage(STAGES - 1) * STAGE;
-    ta.issue(min(kn, nk - 1), kn >= nk - 1, sbase, wave);
-    tb.issue(min(kn, nk - 1), kn >= nk - 1, sbase + A_BYTES, wave);
-    frags(nxt, 0, af0, bf0);
+    ta.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + a_at(sel(STAGES - 1).a), wave);
+    if constexpr (BPAIR) {
+      // the pair of k-tiles kt+4, kt+5 goes where kt-2, kt-1 were
+      if constexpr (kEvenKnown) {
+        if constexpr (decltype(sel(0))::kEven)
+          tp.issue(min(kt / 2 + 2, npairs - 1), smem_base + b_at(0, sel(4).p), wave);
+      } else {
+        if ((kt & 1) == 0) tp.issue(min(kt / 2 + 2, npairs - 1), smem_base + b_at(0, sel(4).p), wave);
+      }
+    } else {
+      tb.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + b_at(sel(STAGES - 1).a, 0), wave);
+    }
+    frags(a_at(sel(1).a), b_at(sel(1).a, sel(1).p), sel(1).h, 0, af0, bf0);
     mfmas(af1, bf1);
     interleave_substep<kMfma, kFrags>();
     sched_fence();
   };
+  // Places of tile kt + d: compile-time from the position U in the unrolled
+  // cycle (a multiple of the cycle is a multiple of STAGES, of 2 and of
+  // 2 kPairs), or computed at run time.
+  constexpr int kCycle = BPAIR ? 12 : STAGES;
+  static_assert(!BPAIR || (kCycle % STAGES == 0 && kCycle % (2 * kPairs) == 0), "unroll cycle");
 
   int tile = blockIdx.x;
   setup(tile);
-  static_for<STAGES - 1>([&](auto T) __attribute__((always_inline)) { issue(T); });
-  wait_vmcnt<(STAGES - 2) * L>();
+  prologue();
+  wait_vmcnt<kFirstWait>();
   for (;;) {
     // k-tile 0 of the current tile has landed (each wave waited for its own copies)
     flane = lane;
@@ -402,12 +515,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
       static_for<TM>([&](auto I) __attribute__((always_inline)) { acc[J][I] = (f32x16_t)(0.0f); });
     });
     int kt = 0;
-    for (; kt + STAGES <= nk - 1; kt += STAGES) {
-      static_for<STAGES>([&](auto U) __attribute__((always_inline)) {
-        ktile(kt + U, [](int d) { return (static_cast<int>(decltype(U)::value) + d) % STAGES; });
+    for (; kt + kCycle <= nk - 1; kt += kCycle) {
+      static_for<kCycle>([&](auto U) __attribute__((always_inline)) {
+        ktile(kt + decltype(U)::value, [](int d) {
+          constexpr int u = decltype(U)::value;
+          return KPlace<true, u % 2 == 0>{(u + d) % STAGES, ((u + d) / 2) % kPairs, (u + d) & 1};
+        });
       });
     }
-    for (; kt < nk - 1; ++kt) ktile(kt, [kt](int d) { return (kt + d) % STAGES; });
+    for (; kt < nk - 1; ++kt)
+      ktile(kt, [kt](int d) {
+        return KPlace<false, false>{(kt + d) % STAGES, ((kt + d) / 2) % kPairs, (kt + d) & 1};
+      });
     // the last k-tile (its substep-0 fragments are in af0 / bf0)
     read_frags(nk - 1, 1, af1, bf1);
     if constexpr (KTAIL) {
@@ -427,9 +546,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
 
     // Every stage is free once each wave's copies have landed (the clamped
     // re-reads past the last k-tile included) and its fragment reads have
-    // returned, and all waves have passed the barrier after that.  Then the
-    // next tile's first STAGES-1 k-tiles are started before this tile's
-    // epilogue, which they overlap.
+    // returned, and all waves have passed the barrier after that.  With
+    // single stages the next tile's first STAGES-1 k-tiles are then started
+    // before this tile's epilogue, which they overlap.
     const int cm0 = m0, cn0 = n0;
     const int next = tile + static_cast<int>(gridDim.x);
     const bool more = next < ntiles;   // workgroup-uniform
@@ -439,9 +558,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       lds_barrier();
     }
-    if (more) {
-      setup(next);
-      static_for<STAGES - 1>([&](auto T) __attribute__((always_inline)) { issue(T); });
+    if constexpr (kPrefetch) {
+      if (more) {
+        setup(next);
+        prologue();
+      }
     }
 
     // The epilogue's per-lane addresses are loop-invariant; computed from an
@@ -482,10 +603,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     tile = next;
     asm volatile("" : "+s"(tile));
     setup(tile);
-    // the next tile's first k-tile (and everything before it) has landed;
-    // waiting for the epilogue's stores as well keeps the count simple
-    sched_fence();
-    wait_vmcnt<0>();
+    if constexpr (kPrefetch) {
+      // the next tile's first k-tile (and everything before it) has landed;
+      // waiting for the epilogue's stores as well keeps the count simple
+      sched_fence();
+      wait_vmcnt<0>();
+    } else {
+      if constexpr (kStaged) {
+        // every wave is done with the slabs before the copies overwrite them
+        sched_fence();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        lds_barrier();
+      }
+      prologue();
+      wait_vmcnt<kFirstWait>();
+    }
   }
 }
 
@@ -504,18 +636,30 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
   if (tiles > INT32_MAX) return hipErrorInvalidValue;     // tile indices are ints
   // one round of resident workgroups (whole XCD rounds: a multiple of 8),
   // each looping over its tiles
-  using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32>;
-  int64_t cap = device_cus() * Layout::kPerCu / 8 * 8;
-  if (cap < 8) cap = 8;
-  const unsigned grid = static_cast<unsigned>(tiles < cap ? tiles : cap);
-  if (K % kBKd != 0)
+  auto launch = [&](auto ktail, auto bpair) {
+    constexpr bool kTail = decltype(ktail)::value, kPair = decltype(bpair)::value;
+    using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32, kPair>;
+    int64_t cap = device_cus() * Layout::kPerCu / 8 * 8;
+    if (cap < 8) cap = 8;
+    const unsigned grid = static_cast<unsigned>(tiles < cap ? tiles : cap);
     hipLaunchKernelGGL(
-        (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, true>),
+        (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, kTail, kPair>),
         dim3(grid), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
-  else
-    hipLaunchKernelGGL(
-        (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, false>),
-        dim3(grid), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (K % kBKd != 0) {
+    launch(T{}, F{});
+  } else {
+    // a k-contiguous B in whole 64-k pairs takes the paired stages
+    if constexpr (!B_KMAJOR && EPI != EPI_SWIGLU && STAGES == 4) {
+      if (K % (2 * kBKd) == 0) {
+        launch(F{}, T{});
+        return hipGetLastError();
+      }
+    }
+    launch(F{}, F{});
+  }
   return hipGetLastError();
 }
 

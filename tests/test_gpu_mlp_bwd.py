@@ -110,6 +110,7 @@ def test_f32_ragged_tokens():
     (77, 136, 200, "f32"),
     (300, 264, 360, "bf16"),
     (513, 1024, 520, "f32"),
+    (16000, 2112, 1088, "f32"),         # dH / dX: paired B stages over 2 / 3 rounds, ragged M and N
 ])
 def test_bf16_ragged_shapes(tokens, hidden, f, grad_dt):
     """bf16 shapes off every tile: token counts that are ragged against the
