@@ -213,8 +213,9 @@ __device__ __forceinline__ void store_swiglu(const f32x16_t (&acc)[2][TM], int m
 // instruction covering 64*16/(WN*4) rows of WN*4 contiguous bytes.  The
 // 16-byte chunk c of slab row r sits at chunk c ^ (r & 15) (for W = 64: the
 // 16 rows written by 16 consecutive lanes, and the 16 chunks of one row read
-// by 16 consecutive lanes, fall in distinct bank groups).  The caller
-// guarantees that nothing else reads or writes the region meanwhile.
+// by 16 consecutive lanes, fall in distinct bank groups).  The stores carry
+// the non-temporal hint.  The caller guarantees that nothing else reads or
+// writes the region meanwhile.
 template <int TN>
 constexpr int kStagedSlabBytes = 32 * TN * 32 * 4;
 template <int TM, int TN>
@@ -257,7 +258,13 @@ __device__ __forceinline__ void store_linear_f32_staged(const f32x16_t (&acc)[TN
           load_bf16x4(residual + m * ep.ldr + n_w + col, rr);
           static_for<4>([&](auto R) __attribute__((always_inline)) { o[R] += rr[R]; });
         }
-        store_x4<true>(ep.out, m * ep.ldo + n_w + col, o);
+        // non-temporal: the output is not read again, and its 64 MB per round
+        // (row GEMM) would otherwise evict the next round's operand panels
+        // from L2 (+2.6-3.8% on the 8-round fp32 products; whole-line stores
+        // only: the scattered direct stores lose with this hint)
+        __builtin_nontemporal_store(f32x4_t{o[0], o[1], o[2], o[3]},
+                                    reinterpret_cast<f32x4_t*>(static_cast<float*>(ep.out) +
+                                                               m * ep.ldo + n_w + col));
       });
     });
   };
