@@ -10,9 +10,11 @@ rate: 8 shards of 4*M*h*f FLOP in the step's time).
 
 Also reported:
   roofline      the dominant kernel (column GEMM + GeLU, or row GEMM), timed
-                live with HIP events on the launch stream, against the bf16
-                dense MFMA peak; ``traffic`` from committed rocprofv3 counter
-                summaries when they match the current kernel source
+                live with HIP events on the launch stream around each of its
+                launches in the step's order (column and row GEMM for every
+                rank), against the bf16 dense MFMA peak; ``traffic`` from
+                committed rocprofv3 counter summaries when they match the
+                current kernel source
   cpu_baseline  the fp64 CPU oracle on a bounded sample of rows of the same
                 shard, on this host's cores
   backward      the MLP shard's backward (rank 0 of the same workload): dX_i,
@@ -489,7 +491,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="t8_h8192_m16384")
     ap.add_argument("--kernel-reps", type=int, default=10,
-                    help="launches per kernel for the live per-kernel timing")
+                    help="passes over the step's launches (and launches per kernel elsewhere) "
+                         "for the live per-kernel timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the attention-shard measurement")
@@ -563,34 +566,43 @@ def main() -> int:
     tflops = flops_step / (ms_step * 1e-3) / 1e12
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (events), wall {wall * 1e3 / args.steps:.3f} ms/step")
 
-    # ---- per-kernel live timing (same launches as inside the step, rank 0 operands)
+    # ---- per-kernel live timing, in the step's context: the step's launches
+    # in the step's order (column then row GEMM for every rank's operands,
+    # the same kernels tp_mlp_shard_fwd runs), an event pair around each on
+    # the launch stream; a kernel repeated alone runs a few percent faster
+    # than between the other one's launches.
     h_view = ws[: wl.tokens * wl.f * 2].view(torch.bfloat16).view(wl.tokens, wl.f)
     kernels = {
-        "column_gemm_gelu": (lambda: binding.tp_column_linear(x, a[0], h_view, ffn=wl.ffn, t=wl.t, rank=0,
-                                                              apply_gelu=True, stream=stream),
+        "column_gemm_gelu": (lambda r: binding.tp_column_linear(x, a[r], h_view, ffn=wl.ffn, t=wl.t, rank=r,
+                                                                apply_gelu=True, stream=stream),
                              2.0 * wl.tokens * wl.hidden * wl.f,
                              # algorithmic bytes: X + A_i read, H written (bf16)
                              2.0 * (wl.tokens * wl.hidden + wl.hidden * wl.f + wl.tokens * wl.f)),
-        "row_gemm": (lambda: binding.tp_row_linear(h_view, b[0], z[0], ffn=wl.ffn, t=wl.t, rank=0,
-                                                   stream=stream),
+        "row_gemm": (lambda r: binding.tp_row_linear(h_view, b[r], z[r], ffn=wl.ffn, t=wl.t, rank=r,
+                                                     stream=stream),
                      2.0 * wl.tokens * wl.f * wl.hidden,
                      # H + B_i read (bf16), Z written (fp32)
                      2.0 * (wl.tokens * wl.f + wl.f * wl.hidden) + 4.0 * wl.tokens * wl.hidden),
     }
+    step()
+    torch.cuda.synchronize()
+    events = {name: [] for name in kernels}
+    for _ in range(args.kernel_reps):
+        for r in range(wl.t):
+            for name, (fn, _f, _b) in kernels.items():
+                k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                k0.record(stream)
+                fn(r)
+                k1.record(stream)
+                events[name].append((k0, k1))
+    torch.cuda.synchronize()
     per_kernel = {}
     for name, (fn, flops, nbytes) in kernels.items():
-        fn()
-        torch.cuda.synchronize()
-        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        k0.record(stream)
-        for _ in range(args.kernel_reps):
-            fn()
-        k1.record(stream)
-        torch.cuda.synchronize()
-        us = k0.elapsed_time(k1) * 1e3 / args.kernel_reps
+        us = sum(k0.elapsed_time(k1) for k0, k1 in events[name]) * 1e3 / len(events[name])
         per_kernel[name] = {"avg_us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
-                            "algorithmic_bytes": int(nbytes), "flops": int(flops)}
-        log(f"kernel {name}: {us:.1f} us/launch, {flops / (us * 1e-6) / 1e12:.1f} TFLOP/s")
+                            "algorithmic_bytes": int(nbytes), "flops": int(flops),
+                            "launches": len(events[name])}
+        log(f"kernel {name}: {us:.1f} us/launch in the step's order, {flops / (us * 1e-6) / 1e12:.1f} TFLOP/s")
     dom = max(per_kernel, key=lambda k: per_kernel[k]["avg_us"])
     achieved = per_kernel[dom]["tflops"]
 
