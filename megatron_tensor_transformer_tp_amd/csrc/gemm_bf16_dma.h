@@ -28,6 +28,14 @@
 //     tile, never for the younger tiles in flight; the barrier is a bare
 //     s_barrier with a compiler memory clobber (a workgroup fence would make
 //     the compiler drain every outstanding copy).
+//   * A k-contiguous B with K % 64 == 0 (the backward's products against a
+//     weight stored [N, K]) is copied two k-tiles at a time into pair stages
+//     of 128-byte rows (OperandPairTile), so that each copy instruction
+//     reads whole cache lines; A keeps single stages.
+//   * The grid is one round of resident workgroups; each loops over the tiles
+//     a one-tile-per-workgroup grid would give it, in the same order, and
+//     starts the next tile's first k-tiles before the current epilogue when
+//     the epilogue leaves their stages alone.
 //   * Ragged shapes: the copy cannot zero-fill, so every copy source is
 //     clamped into the operand instead.  Rows (k-contiguous) or 8-column
 //     chunks (k-major) past M or N re-read the last valid one; their products

@@ -1,0 +1,233 @@
+"""CPU models of the bf16 GEMM kernel's index maps (csrc/gemm_bf16_dma.h,
+csrc/gemm_bf16_impl.h), checked before any GPU run.
+
+The kernel moves operand tiles into LDS with 1 KiB global->LDS copies (lane t's
+16 bytes land at base + 16 t, so the LDS layout is fixed by which global 16
+bytes each lane fetches) and reads MFMA fragments back with ds_read_b128 or
+ds_read_b64_tr_b16.  These tests restate the kernel's per-lane formulas in
+Python and check, over all waves, lanes and k-tiles:
+
+  * the tile orders are bijections onto the tile grid;
+  * every copy source lies inside its operand, ragged shapes included;
+  * every fragment read returns exactly the (row, k) elements the MFMA
+    operand layout asks for (lane l: row row0 + l % 32, k 16 s + 8 (l / 32)
+    .. +7), and the 16 lanes of a read group hit distinct 16-byte bank groups;
+  * the paired B stages' issue schedule never overwrites a stage that is
+    still to be read, and the constant vmcnt waits cover every published
+    k-tile under in-order completion.
+
+The transposing read follows its measured behaviour: within each 16-lane
+group, lane 4r + c supplies the address of 4 consecutive bf16 of row r of a
+4 x 16 block (columns 4c .. 4c+3), and lane i receives column i.
+"""
+import itertools
+import random
+
+import pytest
+
+KBK = 32        # k per k-tile
+XCDS = 8
+
+
+# ---- tile orders (tile_coords / tile_coords_rounds) ---------------------------
+
+def tile_coords(bid, nblk, tiles_m, tiles_n, group_m=8):
+    pid = bid
+    if nblk % XCDS == 0:
+        pid = (bid % XCDS) * (nblk // XCDS) + bid // XCDS
+    width = group_m * tiles_n
+    group = pid // width
+    first_m = group * group_m
+    gsize = min(tiles_m - first_m, group_m)
+    in_group = pid - group * width
+    return first_m + in_group % gsize, in_group // gsize
+
+
+def tile_coords_rounds(bid, nblk, tiles_m, tiles_n):
+    if tiles_n not in (8, 16, 32):
+        return None
+    rows = 256 // tiles_n
+    if nblk != tiles_m * tiles_n or tiles_m % rows:
+        return None
+    xcd, k = bid % XCDS, bid // XCDS
+    rnd, s = k // 32, k % 32
+    xr = rows // 4
+    return rnd * rows + (xcd % xr) * 4 + s % 4, (xcd // xr) * 8 + s // 4
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n", [(64, 16), (64, 32), (16, 16), (32, 8), (63, 9), (17, 3), (1, 1)])
+def test_tile_orders_are_bijections(tiles_m, tiles_n):
+    n = tiles_m * tiles_n
+    got = {tile_coords(b, n, tiles_m, tiles_n) for b in range(n)}
+    assert len(got) == n and all(0 <= a < tiles_m and 0 <= c < tiles_n for a, c in got)
+    if tile_coords_rounds(0, n, tiles_m, tiles_n) is not None:
+        got = {tile_coords_rounds(b, n, tiles_m, tiles_n) for b in range(n)}
+        assert len(got) == n and all(0 <= a < tiles_m and 0 <= c < tiles_n for a, c in got)
+
+
+# ---- single k-tile stages (OperandTile) ----------------------------------------
+
+def single_copies(R, NW, kmajor, r0, rows, K, kc):
+    """{LDS 16-byte chunk index: (row or k-row, first k or first column)} of
+    k-tile kc's copies (KTAIL clamping for a partial last k-tile)."""
+    nk = -(-K // KBK)
+    klast, krem = (nk - 1) * KBK, K - (nk - 1) * KBK
+    tail = K % KBK != 0 and kc == nk - 1
+    Q = R * KBK * 2 // 1024 // NW
+    cb = R // 8
+    lds = {}
+    for wave, i, lane in itertools.product(range(NW), range(Q), range(64)):
+        slot = (wave * Q + i) * 64 + lane
+        if not kmajor:
+            row = slot >> 2
+            kin = 8 * ((slot & 3) ^ ((row >> 2) & 3))
+            k = klast + min(kin, krem - 8) if tail else kc * KBK + kin
+            lds[slot] = (min(r0 + row, rows - 1), k)
+        else:
+            krow = slot // cb
+            c = (slot % cb) ^ ((krow & 3) << 2)
+            kr = klast + min(krow, krem - 1) if tail else kc * KBK + krow
+            lds[slot] = (kr, min(r0 + 8 * c, rows - 8))
+    assert len(lds) == R * KBK * 2 // 16
+    return lds
+
+
+@pytest.mark.parametrize("R,NW,kmajor,rows,K", [
+    (256, 8, False, 300, 200), (256, 8, False, 16, 8), (256, 8, True, 264, 300), (256, 8, True, 8, 1),
+    (128, 4, False, 300, 136), (128, 4, True, 1000, 40), (256, 8, False, 257, 40), (384, 8, True, 3072, 8192),
+])
+def test_single_stage_sources_in_bounds(R, NW, kmajor, rows, K):
+    nk = -(-K // KBK)
+    for r0 in range(0, rows, R):
+        for kc in sorted({0, nk - 1, nk // 2}):
+            for a, b in single_copies(R, NW, kmajor, r0, rows, K, kc).values():
+                if not kmajor:
+                    assert 0 <= a < rows and 0 <= b and b + 8 <= K
+                else:
+                    assert 0 <= a < K and 0 <= b and b + 8 <= rows
+
+
+def test_kcontig_fragments():
+    R, NW = 256, 8
+    lds = single_copies(R, NW, False, 0, 10**6, 1024, 3)
+    for row0, s in itertools.product(range(0, R, 32), range(2)):
+        banks = {}
+        for lane in range(64):
+            chunk = (2 * s + (lane >> 5)) ^ ((lane >> 2) & 3)
+            off = (row0 + (lane & 31)) * 64 + chunk * 16
+            assert lds[off // 16] == (row0 + (lane & 31), 3 * KBK + 16 * s + 8 * (lane >> 5))
+            banks.setdefault(lane // 16, set()).add((off // 16) % 16)
+        assert all(len(b) == 16 for b in banks.values())
+
+
+def test_kmajor_fragments_through_the_transposing_read():
+    R, NW = 256, 8
+    cb = R // 8
+    lds = single_copies(R, NW, True, 0, 10**6, 1024, 5)
+
+    def element(krow, byte):               # (k, column) of the bf16 at byte `byte` of LDS k-row `krow`
+        kr, col0 = lds[(krow * R * 2 + byte) // 16]
+        return kr, col0 + (byte % 16) // 2
+
+    for row0, s in itertools.product(range(0, R, 32), range(2)):
+        for H in range(2):
+            addr = {}
+            for lane in range(64):
+                gi = lane & 15
+                row_lane = (lane >> 5) * 8 + (gi >> 2)
+                chunk = ((row0 >> 3) + ((lane >> 4) & 1) * 2 + ((gi & 3) >> 1)) ^ ((gi >> 2) << 2)
+                addr[lane] = (s * 16 + H * 4 + row_lane, chunk * 16 + (gi & 1) * 8)
+            for lane in range(64):
+                g0, gi = lane & ~15, lane & 15
+                for r in range(4):             # lane gi receives column gi of the 4 x 16 block
+                    src = g0 + 4 * r + (gi >> 2)
+                    krow, byte = addr[src]
+                    k, col = element(krow, byte + 2 * (gi & 3))
+                    assert (k, col) == (5 * KBK + 16 * s + 8 * (lane >> 5) + 4 * H + r, row0 + (lane & 31))
+            # the four k-rows of one read fall in four different 64-byte bank windows
+            for g in range(4):
+                wins = {((addr[g * 16 + 4 * r][0] * R * 2 + addr[g * 16 + 4 * r][1]) // 64) % 4 for r in range(4)}
+                assert len(wins) == 4
+
+
+# ---- paired B stages (OperandPairTile) ------------------------------------------
+
+def pair_copies(R, NW, r0, rows, K, j):
+    Q = R * 2 * KBK * 2 // 1024 // NW
+    lds = {}
+    for wave, i, lane in itertools.product(range(NW), range(Q), range(64)):
+        slot = (wave * Q + i) * 64 + lane
+        row = slot >> 3
+        kin = 8 * ((slot & 7) ^ ((row >> 1) & 7))
+        src_row, k = min(r0 + row, rows - 1), j * 2 * KBK + kin
+        assert 0 <= src_row < rows and 0 <= k and k + 8 <= K
+        lds[slot] = (src_row, k)
+    assert len(lds) == R * 128 // 16
+    return lds
+
+
+@pytest.mark.parametrize("rows,K,r0,j", [(8192, 4096, 0, 0), (8192, 4096, 7936, 63), (300, 128, 256, 1), (260, 64, 256, 0)])
+def test_pair_fragments(rows, K, r0, j):
+    R, NW = 256, 8
+    lds = pair_copies(R, NW, r0, rows, K, j)
+    for row0, h, s in itertools.product(range(0, R, 32), range(2), range(2)):
+        banks = {}
+        for lane in range(64):
+            r = lane & 31
+            chunk = (4 * h + 2 * s + (lane >> 5)) ^ ((r >> 1) & 7)
+            off = (row0 + r) * 128 + chunk * 16
+            assert lds[off // 16] == (min(r0 + row0 + r, rows - 1), j * 64 + 32 * h + 16 * s + 8 * (lane >> 5))
+            banks.setdefault(lane // 16, set()).add((off // 16) % 16)
+        assert all(len(b) == 16 for b in banks.values())
+
+
+@pytest.mark.parametrize("nk", [2, 4, 6, 8, 10, 12, 14, 16, 24, 26, 30, 128, 256])
+def test_pair_schedule_and_waits(nk):
+    """Iteration kt publishes k-tile kt+1, then issues A(kt+3) and, for even
+    kt, the B pair (kt+4, kt+5) into pair stage (kt/2 + 2) % 3; pairs past the
+    end re-read the last one.  Prologue: A0, pair 0, A1, A2, pair 1."""
+    QA, QP, pairs = 2, 4, nk // 2
+    held = {}                                   # pair stage -> requested pair index
+    queue = []                                  # issued copies in order: (kind, requested index)
+
+    def issue_a(t):
+        queue.extend([("A", t)] * QA)
+
+    def issue_pair(jr):
+        st = jr % 3
+        if st in held:                          # everything in the old pair has been read
+            for t in (2 * held[st], 2 * held[st] + 1):
+                assert t >= nk or t <= last_read[0], ("overwritten before read", nk, jr)
+        held[st] = jr
+        queue.extend([("P", jr)] * QP)
+
+    def wait(n, t):                             # in-order completion: all but the last n landed
+        landed = queue[:len(queue) - n]
+        for kind, idx in (("A", t), ("P", t // 2)):
+            assert queue.count((kind, idx)) and landed.count((kind, idx)) == queue.count((kind, idx))
+        st = (t // 2) % 3
+        assert held[st] == t // 2 and t // 2 < pairs
+
+    last_read = [-1]
+    issue_a(0); issue_pair(0); issue_a(1); issue_a(2); issue_pair(1)
+    wait(2 * QA + QP, 0)
+    for kt in range(nk - 1):
+        wait(QA + QP, kt + 1)                   # the barrier of iteration kt
+        last_read[0] = kt - 1                   # every wave has read tile kt-1 by now
+        issue_a(kt + 3)
+        if kt % 2 == 0:
+            issue_pair(kt // 2 + 2)
+
+
+def test_random_ragged_sources():
+    rng = random.Random(1)
+    for _ in range(12):
+        R, NW = rng.choice([(256, 8), (128, 4)])
+        kmajor = rng.random() < 0.5
+        rows = 8 * rng.randint(1, 90) if kmajor else rng.randint(1, 700)
+        K = rng.randint(1, 300) if kmajor else 8 * rng.randint(1, 40)
+        nk = -(-K // KBK)
+        r0 = R * rng.randrange(-(-rows // R))
+        for kc in (0, nk - 1):
+            for a, b in single_copies(R, NW, kmajor, r0, rows, K, kc).values():
+                assert (0 <= a < K and 0 <= b and b + 8 <= rows) if kmajor else (0 <= a < rows and 0 <= b and b + 8 <= K)
