@@ -151,17 +151,17 @@ PROFILE_CMDS = {
 # shape, so their grids do not tell shapes apart), with the per-launch
 # algorithmic work (FLOP, bytes), the workload, and the summary's file stem.
 # GEMM template arguments: tile BM, BN, wave grid, LDS stages, A k-major,
-# B k-major, epilogue kind, fp32 output, K tail (false: K % 32 == 0), paired B
-# stages (k-contiguous B, K % 64 == 0).
+# B k-major, epilogue kind, fp32 output, K tail (false: K % 32 == 0), paired
+# stages (0: none, 1: B, 2: A; a k-contiguous operand with K % 64 == 0).
 _M, _H, _F = 16384, 8192, 4096          # MLP shard: tokens, hidden, f = ffn / t
 _S, _DL = 4096, 1024                    # attention shard: tokens, local width (8 heads x 128)
-_GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "   # then A k-major, B k-major, epilogue kind, fp32 out, K tail, B pairs
+_GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "   # then A k-major, B k-major, epilogue kind, fp32 out, K tail, pairs
 PROFILED = {
-    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false, false>", None,
+    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0>", None,
                          2.0 * _M * _H * _F, 2 * (_M * _H + _H * _F + _M * _F),
                          "MLP rank shard, M=16384, h=8192, f=4096: X, A_i read, H_i written (bf16)",
                          "column_gemm_gelu_t8_h8192_m16384"),
-    "row_gemm": (_GEMM + "false, true, 0, true, false, false>", ("us", 300.0, 1e9),
+    "row_gemm": (_GEMM + "false, true, 0, true, false, 0>", ("us", 300.0, 1e9),
                  2.0 * _M * _F * _H, 2 * (_M * _F + _F * _H) + 4 * _M * _H,
                  "MLP rank shard, M=16384, h=8192, f=4096: H_i, B_i read (bf16), Z_i written (fp32)",
                  "row_gemm_t8_h8192_m16384"),
@@ -170,12 +170,12 @@ PROFILED = {
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K "
                        "(fp16) and V (bf16) read once, O written (bf16)",
                        "attention_core_t8_h8192_s4096"),
-    "attn_qkv_gemm": ("gemm_bf16_dma_kernel<128, 384, 2, 4, 4, false, true, 4, false, false, false>", None,
+    "attn_qkv_gemm": ("gemm_bf16_dma_kernel<128, 384, 2, 4, 4, false, true, 4, false, false, 2>", None,
                       2.0 * _S * _H * 3 * _DL, 2 * (_S * _H + _H * 3 * _DL + _S * 3 * _DL),
                       "attention rank shard packed QKV projection, M=4096, K=8192, N=3072 "
                       "(one round of 256 128 x 384 tiles), q/k written as scaled fp16, v as bf16",
                       "attn_qkv_gemm_t8_h8192_s4096"),
-    "attn_out_gemm": (_GEMM + "false, true, 0, true, false, false>", ("us", 0.0, 300.0),
+    "attn_out_gemm": (_GEMM + "false, true, 0, true, false, 0>", ("us", 0.0, 300.0),
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
                       "attention rank shard output projection, M=4096, K=1024, N=8192 (fp32 out)",
                       "attn_out_gemm_t8_h8192_s4096"),
@@ -185,23 +185,23 @@ PROFILED = {
                           "rank's [2048, 8192] shard with bf16 bias and residual rows, bf16 out "
                           "(HBM-bound: partial rows, residual and bias read, shard written)",
                           "sp_reduce_scatter_t8_h8192_m16384"),
-    "swiglu_gemm": (_GEMM + "false, true, 3, false, false, false>", None,
+    "swiglu_gemm": (_GEMM + "false, true, 3, false, false, 0>", None,
                     2.0 * _M * _H * 2 * _F, 2 * (_M * _H + 2 * _H * _F + _M * _F),
                     "SwiGLU column layer, both projections in one product with SiLU(gate) * value "
                     "in the epilogue: X, Wg_i, Wu_i read, H_i written (bf16)",
                     "swiglu_gemm_t8_h8192_m16384"),
-    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false, false, true>", None,
+    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false, false, 1>", None,
                        2.0 * _M * _H * _F, 2 * (_M * _H + _F * _H + _M * _F) + 2 * 2 * _M * _F,
                        "MLP shard backward dH = dZ B_i^T with dY_i = dH * GeLU'(Y_i) and H_i = "
                        "GeLU(Y_i) in the epilogue: dZ, B_i, Y_i read, dY_i and H_i written (bf16)",
                        "bwd_dgelu_gemm_t8_h8192_m16384"),
-    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true, false, false>", None,
+    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true, false, 0>", None,
                              2.0 * _M * _H * _F, 2 * (_M * _F + _M * _H) + 4 * _F * _H,
                              "MLP shard backward weight gradients H_i^T dZ and X^T dY_i (one "
                              "kernel, K = 16384 tokens): two bf16 operands read, fp32 [4096 x 8192] "
                              "written; both launches averaged",
                              "bwd_weight_grad_gemm_t8_h8192_m16384"),
-    "bwd_dx_gemm": (_GEMM + "false, false, 0, true, false, true>", None,
+    "bwd_dx_gemm": (_GEMM + "false, false, 0, true, false, 1>", None,
                     2.0 * _M * _F * _H, 2 * (_M * _F + _H * _F) + 4 * _M * _H,
                     "MLP shard backward dX_i = dY_i A_i^T: dY_i, A_i read (bf16), dX_i written (fp32)",
                     "bwd_dx_gemm_t8_h8192_m16384"),

@@ -301,32 +301,34 @@ __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int nvalid) {
 // (BM + BN) x 64 bytes; with the fp32 restaging (linear fp32 epilogue, wave
 // widths whose rows split evenly over the 64 lanes) the slabs sit in the
 // last stage and the bytes past the stages, so that the next tile's first
-// STAGES-1 k-tiles can be in flight during the epilogue.  BPAIR (B
-// k-contiguous, K % 64 == 0): STAGES single stages of A (BM x 64 bytes),
-// then kPairs stages of B holding two k-tiles each (BN x 128 bytes); the
-// slabs reuse the stage area, so the next tile starts after the epilogue.
-template <int BM, int BN, int WGM, int WGN, int STAGES, int EPI, bool OUT_F32, bool BPAIR>
+// STAGES-1 k-tiles can be in flight during the epilogue.  PAIR 1 (B
+// k-contiguous) or 2 (A k-contiguous), K % 64 == 0: STAGES single stages of
+// the other operand (rows x 64 bytes), then kPairs stages of the paired
+// operand holding two k-tiles each (rows x 128 bytes); the slabs reuse the
+// stage area, so with them the next tile starts after the epilogue.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int EPI, bool OUT_F32, int PAIR>
 struct DmaLayout {
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kTN = BN / WGN / 32;
   static constexpr int kABytes = BM * kBKd * 2;
+  static constexpr int kBBytes = BN * kBKd * 2;
   static constexpr int kStage = (BM + BN) * kBKd * 2;
   static constexpr int kPairs = 3;
-  static constexpr int kPairBytes = BN * 2 * kBKd * 2;
-  static constexpr int kPairAt = STAGES * kABytes;
+  static constexpr int kPairBytes = (PAIR == 2 ? BM : BN) * 2 * kBKd * 2;
+  static constexpr int kPairAt = STAGES * (PAIR == 2 ? kBBytes : kABytes);
   static constexpr bool kStaged = EPI == EPI_LINEAR && OUT_F32 && 64 % (BN / WGN / 4) == 0;
-  static constexpr bool kPrefetch = !BPAIR;   // next tile's copies during the epilogue
-  static constexpr int kStagingAt = BPAIR ? 0 : (STAGES - 1) * kStage;
+  static constexpr bool kPrefetch = PAIR == 0 || !kStaged;   // next tile's copies during the epilogue
+  static constexpr int kStagingAt = PAIR ? 0 : (STAGES - 1) * kStage;
   static constexpr int kStagingEnd = kStagingAt + kWaves * kStagedSlabBytes<kTN>;
-  static constexpr int kStageBytes = BPAIR ? kPairAt + kPairs * kPairBytes : STAGES * kStage;
+  static constexpr int kStageBytes = PAIR ? kPairAt + kPairs * kPairBytes : STAGES * kStage;
   static constexpr int kLdsBytes =
       kStaged && kStagingEnd > kStageBytes ? kStagingEnd : kStageBytes;
   static constexpr int kPerCu = 160 * 1024 / kLdsBytes;   // resident workgroups per CU
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
-// LDS places of one k-tile in the main loop: A stage, B pair stage and half
-// of the pair; KNOWN: the k-tile's parity is a compile-time EVEN.
+// LDS places of one k-tile in the main loop: single stage, pair stage and
+// half of the pair; KNOWN: the k-tile's parity is a compile-time EVEN.
 template <bool KNOWN, bool EVEN>
 struct KPlace {
   static constexpr bool kParityKnown = KNOWN;
@@ -335,7 +337,7 @@ struct KPlace {
 };
 
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KMAJOR, int EPI,
-          bool OUT_F32, bool KTAIL, bool BPAIR>
+          bool OUT_F32, bool KTAIL, int PAIR>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     int M, int N, int K, const Epilogue ep) {
@@ -343,17 +345,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave sub-tiles of whole 32 x 32 MFMA blocks");
-  static_assert(!BPAIR || (!B_KMAJOR && !KTAIL && EPI != EPI_SWIGLU && STAGES == 4),
-                "paired B stages: k-contiguous B, whole 64-k pairs, 4 A stages");
+  static_assert(PAIR == 0 || (!KTAIL && EPI != EPI_SWIGLU && STAGES == 4 &&
+                              (PAIR == 1 ? !B_KMAJOR : PAIR == 2 && !A_KMAJOR)),
+                "paired stages: a k-contiguous operand, whole 64-k pairs, 4 single stages");
   using TileA = OperandTile<BM, NW, A_KMAJOR, KTAIL>;
   using TileB = OperandTile<BN, NW, B_KMAJOR, KTAIL>;
-  using TileP = OperandPairTile<BN, NW>;
+  using TileP = OperandPairTile<PAIR == 2 ? BM : BN, NW>;
   constexpr int A_BYTES = TileA::kBytes;
+  constexpr int B_BYTES = TileB::kBytes;
+  constexpr int QS = PAIR == 2 ? TileB::Q : TileA::Q;   // copies per wave of the single operand
   constexpr int STAGE = A_BYTES + TileB::kBytes;
   constexpr int L = TileA::Q + TileB::Q;   // copies per wave per k-tile (single stages)
   static_assert(STAGES >= 3 && STAGES * STAGE <= 160 * 1024, "LDS stages");
 
-  using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32, BPAIR>;
+  using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32, PAIR>;
   static_assert(Layout::kStage == STAGE && Layout::kABytes == A_BYTES &&
                 Layout::kPairBytes == TileP::kBytes, "stage sizes");
   constexpr bool kStaged = Layout::kStaged;
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   const int ntiles = tiles_m * tiles_n;
   const int nk = (K + kBKd - 1) / kBKd;
   const int klast = (nk - 1) * kBKd, krem = K - klast;   // krem == kBKd unless KTAIL
-  const int npairs = nk / 2;                             // BPAIR: nk is even
+  const int npairs = nk / 2;                             // PAIR: nk is even
 
   // Workgroup b computes tiles b, b + gridDim.x, ...; tile t takes the place
   // workgroup t of a one-tile-per-workgroup grid would (XCD t % 8, round
@@ -388,8 +393,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
       tile_coords(t, ntiles, tiles_m, tiles_n, tm, tn);
     m0 = tm * BM;
     n0 = tn * BN;
-    ta.init(A, lda, m0, M, klast, krem, wave, lane);
-    if constexpr (BPAIR)
+    if constexpr (PAIR == 2)
+      tp.init(A, lda, m0, M, wave, lane);
+    else
+      ta.init(A, lda, m0, M, klast, krem, wave, lane);
+    if constexpr (PAIR == 1)
       tp.init(B, ldb, n0, N, wave, lane);
     else if constexpr (EPI == EPI_SWIGLU)
       tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, N / 2, klast, krem, wave,
@@ -398,31 +406,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
       tb.init(B, ldb, n0, N, klast, krem, wave, lane);
   };
 
-  // LDS places of k-tile kt: A in stage kt % STAGES; B in the same stage
-  // (single stages) or in pair stage (kt / 2) % kPairs, half kt % 2.
+  // LDS places of k-tile kt: a single-stage operand in stage kt % STAGES
+  // (both operands share that stage when nothing is paired), the paired one
+  // in pair stage (kt / 2) % kPairs, half kt % 2.
   const uint32_t smem_base = lds_address(smem);
-  auto a_at = [](int sa) { return BPAIR ? sa * A_BYTES : sa * STAGE; };
-  auto b_at = [](int sa, int sp) { return BPAIR ? kPairAt + sp * kPairBytes : sa * STAGE + A_BYTES; };
-  // Copies of k-tile kt's A (clamped to the last tile), and of kt's B
-  // (single stages) or of pair j's B (clamped to the last pair).
+  auto a_at = [](int ss, int sp) {
+    return PAIR == 2 ? kPairAt + sp * kPairBytes : PAIR == 1 ? ss * A_BYTES : ss * STAGE;
+  };
+  auto b_at = [](int ss, int sp) {
+    return PAIR == 1 ? kPairAt + sp * kPairBytes : PAIR == 2 ? ss * B_BYTES : ss * STAGE + A_BYTES;
+  };
+  // Copies of k-tile kt of a single-stage operand (clamped to the last
+  // tile), and of pair j of the paired one (clamped to the last pair).
   auto issue_a = [&](int kt) __attribute__((always_inline)) {
-    ta.issue(min(kt, nk - 1), kt >= nk - 1, smem_base + a_at(kt % STAGES), wave);
+    ta.issue(min(kt, nk - 1), kt >= nk - 1, smem_base + a_at(kt % STAGES, 0), wave);
   };
   auto issue_b = [&](int kt) __attribute__((always_inline)) {
     tb.issue(min(kt, nk - 1), kt >= nk - 1, smem_base + b_at(kt % STAGES, 0), wave);
   };
+  auto issue_single = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (PAIR == 2) issue_b(kt); else issue_a(kt);
+  };
   auto issue_pair = [&](int j) __attribute__((always_inline)) {
-    tp.issue(min(j, npairs - 1), smem_base + b_at(0, j % kPairs), wave);
+    const int sp = j % kPairs;
+    tp.issue(min(j, npairs - 1), smem_base + (PAIR == 2 ? a_at(0, sp) : b_at(0, sp)), wave);
   };
   // The first k-tiles of the current tile, and the vmcnt that says k-tile 0
-  // has landed.  Single stages: k-tiles 0 .. STAGES-2.  Pairs: A 0, pair 0,
-  // A 1, A 2, pair 1 (k-tiles 0 .. 3 of B).
+  // has landed.  Single stages: k-tiles 0 .. STAGES-2.  Pairs: single 0,
+  // pair 0, single 1, single 2, pair 1 (k-tiles 0 .. 3 of the paired operand).
   auto prologue = [&]() __attribute__((always_inline)) {
-    if constexpr (BPAIR) {
-      issue_a(0);
+    if constexpr (PAIR != 0) {
+      issue_single(0);
       issue_pair(0);
-      issue_a(1);
-      issue_a(2);
+      issue_single(1);
+      issue_single(2);
       issue_pair(1);
     } else {
       static_for<STAGES - 1>([&](auto T) __attribute__((always_inline)) {
@@ -431,15 +448,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
       });
     }
   };
-  constexpr int kFirstWait = BPAIR ? 2 * TileA::Q + TileP::Q : (STAGES - 2) * L;
+  constexpr int kFirstWait = PAIR ? 2 * QS + TileP::Q : (STAGES - 2) * L;
   // "k-tile kt+1 has landed" inside the main loop.  Single stages: every
   // iteration issues L copies per wave (past the end they re-read the last
   // tile into a stage never read again), so only tiles kt+2 .. kt+STAGES-2
-  // may be in flight.  Pairs: iteration kt issues A(kt+3), and for even kt
-  // the pair of k-tiles kt+4, kt+5 (into the pair stage k-tiles kt-2, kt-1
-  // left); A(kt+1) was issued in iteration kt-2 and its pair earlier, and
-  // after it exactly one A and one pair have been issued.
-  constexpr int kLoopWait = BPAIR ? TileA::Q + TileP::Q : (STAGES - 3) * L;
+  // may be in flight.  Pairs: iteration kt issues the single operand's
+  // k-tile kt+3 and, for even kt, the pair of k-tiles kt+4, kt+5 (into the
+  // pair stage k-tiles kt-2, kt-1 left); k-tile kt+1 of the single operand
+  // was issued in iteration kt-2 and its pair earlier, and after it exactly
+  // one single k-tile and one pair have been issued.
+  constexpr int kLoopWait = PAIR ? QS + TileP::Q : (STAGES - 3) * L;
 
   // The lane index of the fragment reads, renewed (opaquely) for every tile:
   // their loop-invariant LDS addresses are then computed per tile instead of
@@ -451,10 +469,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   auto frags = [&](int ao, int bo, int h, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
       __attribute__((always_inline)) {
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      af[I] = ta.frag(smem + ao, wm * WM + I * 32, s, flane);
+      if constexpr (PAIR == 2)
+        af[I] = tp.frag(smem + ao, wm * WM + I * 32, h, s, flane);
+      else
+        af[I] = ta.frag(smem + ao, wm * WM + I * 32, s, flane);
     });
     static_for<TN>([&](auto J) __attribute__((always_inline)) {
-      if constexpr (BPAIR)
+      if constexpr (PAIR == 1)
         bf[J] = tp.frag(smem + bo, wn * WN + J * 32, h, s, flane);
       else
         bf[J] = tb.frag(smem + bo, wn * WN + J * 32, s, flane);
@@ -462,7 +483,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   };
   auto read_frags = [&](int kt, int s, bf16x8_t(&af)[TM], bf16x8_t(&bf)[TN])
       __attribute__((always_inline)) {
-    frags(a_at(kt % STAGES), b_at(kt % STAGES, (kt / 2) % kPairs), kt & 1, s, af, bf);
+    frags(a_at(kt % STAGES, (kt / 2) % kPairs), b_at(kt % STAGES, (kt / 2) % kPairs), kt & 1, s, af,
+          bf);
   };
 
   f32x16_t acc[TN][TM];
@@ -480,32 +502,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   // One k-tile: substep 0 of tile kt (fragments of substep 1 load under its
   // MFMAs), then substep 1: publish tile kt+1, start the copies that reuse
   // the places of tile kt-1 (every wave finished reading them before this
-  // barrier), fragments of tile kt+1.  `sel(d)` gives the (A stage, B pair
-  // stage) of tile kt + d: compile-time values in the unrolled loop, so
+  // barrier), fragments of tile kt+1.  `sel(d)` gives the (single stage, pair
+  // stage, half) of tile kt + d: compile-time values in the unrolled loop, so
   // every LDS address is a loop-invariant register plus an immediate offset
   // and the stage arithmetic disappears (+4-6% on the headline shapes).
   auto ktile = [&](int kt, auto sel) __attribute__((always_inline)) {
     constexpr bool kEvenKnown = decltype(sel(0))::kParityKnown;
-    frags(a_at(sel(0).a), b_at(sel(0).a, sel(0).p), sel(0).h, 1, af1, bf1);
+    frags(a_at(sel(0).a, sel(0).p), b_at(sel(0).a, sel(0).p), sel(0).h, 1, af1, bf1);
     mfmas(af0, bf0);
     interleave_substep<kMfma, kFrags>();
     sched_fence();
     wait_vmcnt<kLoopWait>();
     lds_barrier();
     const int kn = kt + STAGES - 1;
-    ta.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + a_at(sel(STAGES - 1).a), wave);
-    if constexpr (BPAIR) {
+    if constexpr (PAIR != 2)
+      ta.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + a_at(sel(STAGES - 1).a, 0), wave);
+    if constexpr (PAIR != 0) {
       // the pair of k-tiles kt+4, kt+5 goes where kt-2, kt-1 were
+      const int sp = sel(4).p;
+      const uint32_t pair_lds = smem_base + (PAIR == 2 ? a_at(0, sp) : b_at(0, sp));
+      if constexpr (PAIR == 2)
+        tb.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + b_at(sel(STAGES - 1).a, 0), wave);
       if constexpr (kEvenKnown) {
-        if constexpr (decltype(sel(0))::kEven)
-          tp.issue(min(kt / 2 + 2, npairs - 1), smem_base + b_at(0, sel(4).p), wave);
+        if constexpr (decltype(sel(0))::kEven) tp.issue(min(kt / 2 + 2, npairs - 1), pair_lds, wave);
       } else {
-        if ((kt & 1) == 0) tp.issue(min(kt / 2 + 2, npairs - 1), smem_base + b_at(0, sel(4).p), wave);
+        if ((kt & 1) == 0) tp.issue(min(kt / 2 + 2, npairs - 1), pair_lds, wave);
       }
     } else {
       tb.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + b_at(sel(STAGES - 1).a, 0), wave);
     }
-    frags(a_at(sel(1).a), b_at(sel(1).a, sel(1).p), sel(1).h, 0, af0, bf0);
+    frags(a_at(sel(1).a, sel(1).p), b_at(sel(1).a, sel(1).p), sel(1).h, 0, af0, bf0);
     mfmas(af1, bf1);
     interleave_substep<kMfma, kFrags>();
     sched_fence();
@@ -513,8 +539,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_dma_kernel(
   // Places of tile kt + d: compile-time from the position U in the unrolled
   // cycle (a multiple of the cycle is a multiple of STAGES, of 2 and of
   // 2 kPairs), or computed at run time.
-  constexpr int kCycle = BPAIR ? 12 : STAGES;
-  static_assert(!BPAIR || (kCycle % STAGES == 0 && kCycle % (2 * kPairs) == 0), "unroll cycle");
+  constexpr int kCycle = PAIR ? 12 : STAGES;
+  static_assert(!PAIR || (kCycle % STAGES == 0 && kCycle % (2 * kPairs) == 0), "unroll cycle");
 
   int tile = blockIdx.x;
   setup(tile);
@@ -651,8 +677,9 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
   if (tiles > INT32_MAX) return hipErrorInvalidValue;     // tile indices are ints
   // one round of resident workgroups (whole XCD rounds: a multiple of 8),
   // each looping over its tiles
-  auto launch = [&](auto ktail, auto bpair) {
-    constexpr bool kTail = decltype(ktail)::value, kPair = decltype(bpair)::value;
+  auto launch = [&](auto ktail, auto pair) {
+    constexpr bool kTail = decltype(ktail)::value;
+    constexpr int kPair = decltype(pair)::value;
     using Layout = DmaLayout<BM, BN, WGM, WGN, STAGES, EPI, OUT_F32, kPair>;
     int64_t cap = device_cus() * Layout::kPerCu / 8 * 8;
     if (cap < 8) cap = 8;
@@ -663,17 +690,24 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
   };
   using T = std::true_type;
   using F = std::false_type;
+  using P0 = std::integral_constant<int, 0>;
   if (K % kBKd != 0) {
-    launch(T{}, F{});
+    launch(T{}, P0{});
   } else {
-    // a k-contiguous B in whole 64-k pairs takes the paired stages
-    if constexpr (!B_KMAJOR && EPI != EPI_SWIGLU && STAGES == 4) {
+    // Whole 64-k pairs of a k-contiguous operand: a k-contiguous B takes the
+    // paired stages, and so does the k-contiguous A of a 128-row tile (whose
+    // copies per MFMA are a third more than a 256 x 256 tile's)
+    constexpr int kPair = EPI == EPI_SWIGLU || STAGES != 4 ? 0
+                          : !B_KMAJOR                       ? 1
+                          : !A_KMAJOR && BM == 128          ? 2
+                                                            : 0;
+    if constexpr (kPair != 0) {
       if (K % (2 * kBKd) == 0) {
-        launch(F{}, T{});
+        launch(F{}, std::integral_constant<int, kPair>{});
         return hipGetLastError();
       }
     }
-    launch(F{}, F{});
+    launch(F{}, P0{});
   }
   return hipGetLastError();
 }

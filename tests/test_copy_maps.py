@@ -12,7 +12,7 @@ Python and check, over all waves, lanes and k-tiles:
   * every fragment read returns exactly the (row, k) elements the MFMA
     operand layout asks for (lane l: row row0 + l % 32, k 16 s + 8 (l / 32)
     .. +7), and the 16 lanes of a read group hit distinct 16-byte bank groups;
-  * the paired B stages' issue schedule never overwrites a stage that is
+  * the paired stages' issue schedule never overwrites a stage that is
     still to be read, and the constant vmcnt waits cover every published
     k-tile under in-order completion.
 
@@ -150,7 +150,7 @@ def test_kmajor_fragments_through_the_transposing_read():
                 assert len(wins) == 4
 
 
-# ---- paired B stages (OperandPairTile) ------------------------------------------
+# ---- paired stages (OperandPairTile) --------------------------------------------
 
 def pair_copies(R, NW, r0, rows, K, j):
     Q = R * 2 * KBK * 2 // 1024 // NW
@@ -166,9 +166,11 @@ def pair_copies(R, NW, r0, rows, K, j):
     return lds
 
 
+@pytest.mark.parametrize("R,NW", [(256, 8), (128, 8), (128, 4)])
 @pytest.mark.parametrize("rows,K,r0,j", [(8192, 4096, 0, 0), (8192, 4096, 7936, 63), (300, 128, 256, 1), (260, 64, 256, 0)])
-def test_pair_fragments(rows, K, r0, j):
-    R, NW = 256, 8
+def test_pair_fragments(R, NW, rows, K, r0, j):
+    """B pairs of the 256 x 256 tile (8 waves), A pairs of the 128 x 384 (8
+    waves) and 128 x 128 (4 waves) tiles."""
     lds = pair_copies(R, NW, r0, rows, K, j)
     for row0, h, s in itertools.product(range(0, R, 32), range(2), range(2)):
         banks = {}
@@ -181,12 +183,16 @@ def test_pair_fragments(rows, K, r0, j):
         assert all(len(b) == 16 for b in banks.values())
 
 
+@pytest.mark.parametrize("QA,QP", [(2, 4), (3, 2)])
 @pytest.mark.parametrize("nk", [2, 4, 6, 8, 10, 12, 14, 16, 24, 26, 30, 128, 256])
-def test_pair_schedule_and_waits(nk):
-    """Iteration kt publishes k-tile kt+1, then issues A(kt+3) and, for even
-    kt, the B pair (kt+4, kt+5) into pair stage (kt/2 + 2) % 3; pairs past the
-    end re-read the last one.  Prologue: A0, pair 0, A1, A2, pair 1."""
-    QA, QP, pairs = 2, 4, nk // 2
+def test_pair_schedule_and_waits(nk, QA, QP):
+    """Iteration kt publishes k-tile kt+1, then issues the single-stage
+    operand's k-tile kt+3 ("A" below) and, for even kt, the pair (kt+4, kt+5)
+    into pair stage (kt/2 + 2) % 3; pairs past the end re-read the last one.
+    Prologue: single 0, pair 0, single 1, single 2, pair 1.  Copies per wave:
+    (single, pair) = (2, 4) for B pairs of 256 x 256 and A pairs of 128 x 128,
+    (3, 2) for A pairs of 128 x 384."""
+    pairs = nk // 2
     held = {}                                   # pair stage -> requested pair index
     queue = []                                  # issued copies in order: (kind, requested index)
 
