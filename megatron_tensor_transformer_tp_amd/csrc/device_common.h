@@ -101,6 +101,10 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // left to itself it would make later LDS reads of *other* stages wait for
 // every copy in flight (s_waitcnt vmcnt(0)), which defeats the pipeline.
 // Ordering against LDS reads is explicit instead: wait_vmcnt + lds_barrier.
+// The compiler warns that M0 is a reserved register in the clobber list: it
+// keeps no value of its own in M0 in these kernels (gfx950 LDS instructions
+// do not use it; in the generated code of every kernel that copies, each M0
+// reference is this sequence's write), so nothing live is overwritten.
 __device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
