@@ -39,6 +39,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -58,11 +59,21 @@ KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/" + f for f in (
     "sp_reduce.hip", "attention.hip")]
 
 
+def _code_only(text: str) -> str:
+    """A C++ source without its comments and blank lines (what the compiler
+    sees of it, up to formatting)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_sha() -> str:
+    """Hash of the kernel sources' code (comments do not count: a comment
+    edit leaves the committed counter summaries valid)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
