@@ -122,3 +122,25 @@ def test_bf16_ragged_shapes(tokens, hidden, f):
     ref = oracle.swiglu_mlp_shard(host64(x, "bf16"), host64(wg, "bf16"), host64(wu, "bf16"),
                                   host64(b, "bf16"), wl.t, 0, host64(bb, "bf16"), host64(res, "bf16"))
     assert_close(z, ref, "bf16", f"swiglu ragged {tokens}x{hidden}x{f}", rms_floor=True)
+
+
+def test_bf16_ragged_multiround_sampled_rows():
+    """Nearly the headline size with every extent ragged: the gated product
+    (2048 paired 256 x 256 tiles, 8 rounds of resident workgroups, features
+    ending inside a paired tile, K % 32 = 24) and the row GEMM (8 rounds,
+    K % 32 = 24) of rank 0; sampled rows (first tile row, middle, the partial
+    last tile row), every column.  The oracle takes rank 0's weight blocks as
+    a t = 1 shard, the same arithmetic."""
+    tokens, hidden, f = 16376, 8184, 4088
+    wl = inputs.MlpWorkload("swiglu_multiround", tokens, hidden, 2 * f, 2, "bf16", 1.0, 0.02, 0.02, "f32")
+    x = inputs.mlp_x_rows(wl)
+    wg, wu, b = inputs.mlp_wg_block(wl, 0), inputs.mlp_wu_block(wl, 0), inputs.mlp_b_block(wl, 0)
+    bb, res = inputs.mlp_bias_b(wl), inputs.mlp_residual_rows(wl)
+    say(f"swiglu multi-round tokens={tokens} hidden={hidden} f={f} rank 0")
+    z = to_np(run(wl, 0, dev(x, "bf16"), dev(wg, "bf16"), dev(wu, "bf16"), dev(b, "bf16"), tokens,
+                  bias_b=dev(bb, "bf16"), residual=dev(res, "bf16")))
+    assert not np.isnan(z).any(), "unwritten outputs"
+    rows = np.r_[0:3, 255:258, 8190:8194, 16128:16131, 16370:16376]
+    ref = oracle.swiglu_mlp_shard(host64(x[rows], "bf16"), host64(wg, "bf16"), host64(wu, "bf16"),
+                                  host64(b, "bf16"), 1, 0, host64(bb, "bf16"), host64(res[rows], "bf16"))
+    assert_close(z[rows], ref, "bf16", "swiglu multi-round", rms_floor=True)
