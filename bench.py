@@ -523,7 +523,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's shard only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "this build has no multi-GPU path: the exchange step (a SUM All-Reduce of the "
+              "the library has no multi-GPU path: the exchange step (a SUM All-Reduce of the "
               "partials) is not implemented.", file=sys.stderr)
         return 2
 
