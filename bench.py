@@ -148,11 +148,11 @@ def cpu_baseline(wl, target_s: float):
 
 
 PROFILE_CMDS = {
-    "trace": ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktrace -o kt -- "
+    "trace": ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/ktrace -o kt -- "
               "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline"),
-    "fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o pmc -- "
+    "fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc_fetch -o pmc -- "
               "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
-    "write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o pmc -- "
+    "write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc_write -o pmc -- "
               "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
 }
 # Profiled kernels: name pattern in the rocprofv3 output and, where one
@@ -272,7 +272,7 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str) -> None:
         md = [f"# {key} — {stem}", "",
               f"Workload: {what}.", "",
               f"kernel: `{durs[key][0][1][:120]}`", f"kernel source sha: {out['source_sha']}", "",
-              "Commands (run from the repository root on the GPU box):", "",
+              "Commands (run from the repository root on the MI355X):", "",
               *[f"    {c}" for c in PROFILE_CMDS.values()], "",
               "| figure | value |", "|---|---|",
               f"| dispatches in the trace run | {len(us)} |",
