@@ -1,0 +1,92 @@
+"""Seeded random shapes through the GEMM-based entry points, against the fp64
+oracle on every output element.
+
+The shapes are drawn to reach every kernel variant the tile choice and the
+launcher select: 128 x 128, 128 x 384 and 256 x 256 tiles, one or several
+rounds of resident workgroups, ragged M and N, a partial last k-tile, and
+(when a k extent is a multiple of 64) the paired stages of a k-contiguous
+operand: A for the 128-row tiles of the forward products, B for the
+backward's dX and dH products.  Tolerances as in the other GPU parity tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_tp_amd import binding, inputs
+from tests.gpu_helpers import assert_close, dev, host64, nan_tensor, say, to_np
+from tests.test_gpu_mlp_bwd import check_grads, run_bwd, run_fwd_save, shard_ref
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(seed, n, large_every=0):
+    """n shapes; every `large_every`-th one (if set) at 3000-16384 tokens and
+    1024-8192 wide, where the tile choice takes 128 x 384 or 256 x 256 tiles
+    over one or several rounds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        if large_every and i % large_every == 0:
+            tokens = int(rng.integers(3000, 16385))
+            hidden = 8 * int(rng.integers(128, 1025))
+            f = 8 * int(rng.integers(128, 1025))
+        else:
+            tokens = int(rng.integers(1, 2500))
+            hidden = 8 * int(rng.integers(1, 200))
+            f = 8 * int(rng.integers(1, 200))
+        if rng.random() < 0.4:
+            hidden = 64 * max(1, hidden // 64)          # k extents that pair
+        if rng.random() < 0.4:
+            f = 64 * max(1, f // 64)
+        out.append((tokens, hidden, f))
+    return out
+
+
+def _rows(tokens):
+    """Rows checked: all of a small output, else a spread sample with the
+    first and the last (partial) tile rows."""
+    if tokens <= 2500:
+        return np.arange(tokens)
+    return np.unique(np.r_[0:3, 128:131, 256:259, np.arange(0, tokens, 97), tokens - 130:tokens])
+
+
+@pytest.mark.parametrize("tokens,hidden,f", _shapes(2024, 16, large_every=2))
+def test_column_and_row_linear(tokens, hidden, f):
+    t = 2
+    wl = inputs.MlpWorkload(f"rand_{tokens}_{hidden}_{f}", tokens, hidden, f * t, t, "bf16", 1.0, 0.05, 0.05,
+                            "f32")
+    x, a, bias_a = inputs.mlp_x_rows(wl), inputs.mlp_a_block(wl, 1), inputs.mlp_bias_a_block(wl, 1)
+    b, bias_b, res = inputs.mlp_b_block(wl, 1), inputs.mlp_bias_b(wl), inputs.mlp_residual_rows(wl)
+    say(f"random shapes: column / row linear tokens={tokens} hidden={hidden} f={f}")
+    y = nan_tensor((tokens, f), torch.bfloat16)
+    binding.tp_column_linear(dev(x, "bf16"), dev(a, "bf16"), y, ffn=f * t, t=t, rank=1,
+                             bias_i=dev(bias_a, "bf16"), apply_gelu=True)
+    z = nan_tensor((tokens, hidden), torch.float32)
+    binding.tp_row_linear(y, dev(b, "bf16"), z, ffn=f * t, t=t, rank=0, bias=dev(bias_b, "bf16"),
+                          residual=dev(res, "bf16"))
+    torch.cuda.synchronize()
+    rows = _rows(tokens)
+    h, zz = to_np(y), to_np(z)
+    assert not np.isnan(h).any() and not np.isnan(zz).any(), "unwritten outputs"
+    ref_h = oracle.column_linear(host64(x[rows], "bf16"), host64(a, "bf16"), host64(bias_a, "bf16"),
+                                 apply_gelu=True)
+    assert_close(h[rows], ref_h, "bf16", "random column_linear")
+    # the row layer against the oracle applied to the kernel's own (bf16) H
+    ref_z = oracle.row_linear(h[rows].astype(np.float64), host64(b, "bf16"), host64(bias_b, "bf16"),
+                              host64(res[rows], "bf16"), rank=0)
+    assert_close(zz[rows], ref_z, "bf16", "random row_linear")
+
+
+@pytest.mark.parametrize("tokens,hidden,f", _shapes(7, 8))
+def test_backward(tokens, hidden, f):
+    wl = inputs.MlpWorkload(f"rand_bwd_{tokens}_{hidden}_{f}", tokens, hidden, 2 * f, 2, "bf16", 1.0,
+                            0.05, 0.05, "f32")
+    x, dz = inputs.mlp_x_rows(wl), inputs.mlp_dz_rows(wl)
+    a, b = inputs.mlp_a_block(wl, 1), inputs.mlp_b_block(wl, 1)
+    xd, ad, bd = dev(x, "bf16"), dev(a, "bf16"), dev(b, "bf16")
+    say(f"random shapes: backward tokens={tokens} hidden={hidden} f={f}")
+    _z, y = run_fwd_save(wl, 1, xd, ad, bd)
+    ref = shard_ref(host64(x, "bf16"), host64(a, "bf16"), host64(b, "bf16"), host64(dz, "bf16"))
+    got = run_bwd(wl, 1, xd, ad, bd, y, dev(dz, "bf16"), "f32")
+    check_grads(got, ref, "bf16", f"random {tokens}x{hidden}x{f}")
