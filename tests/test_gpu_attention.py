@@ -110,3 +110,35 @@ def test_errors_and_empty():
     out0 = torch.empty((0, 128, wl.hidden), dtype=torch.float32, device="cuda")
     binding.tp_attn_shard_fwd(x0, wqkv, wo, out0, None, heads=8, head_dim=128, t=2, rank=0)
     torch.cuda.synchronize()
+
+
+def _attn_shapes(seed, n):
+    """n seeded shard shapes: batch 1-3, seq a multiple of 128 up to 1152
+    (1-36 key blocks of 32, so the loop unrolled by 4 ends at every phase),
+    1-6 local heads, t in 1-4, hidden = heads x 128, causal or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        t = int(rng.integers(1, 5))
+        hl = int(rng.integers(1, 7))
+        while hl * t > 16:
+            hl -= 1
+        out.append((int(rng.integers(1, 4)), 128 * int(rng.integers(1, 10)), hl, t,
+                    int(rng.integers(0, t)), bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("batch,seq,hl,t,rank,causal", _attn_shapes(11, 10))
+def test_random_shapes(batch, seq, hl, t, rank, causal):
+    heads = hl * t
+    hidden = heads * 128
+    # QKV weight std keeps the logits' std near 3, as in the fixed workloads
+    wl = inputs.AttnWorkload(f"attn_rand_{batch}_{seq}_{hl}_{t}", batch, seq, hidden, heads, 128, t,
+                             "bf16", 1.0, 1.8 / np.sqrt(hidden), "f32", 0.02)
+    x = x_all(wl)
+    wqkv, wo = inputs.attn_wqkv_block(wl, rank), inputs.attn_wo_block(wl, rank)
+    say(f"random attention: batch={batch} seq={seq} local heads={hl} t={t} rank={rank} causal={causal}")
+    out = to_np(run(wl, rank, dev(x, "bf16"), dev(wqkv, "bf16"), dev(wo, "bf16"), causal))
+    ref = oracle.attn_shard(host64(x, "bf16"), host64(wqkv, "bf16"), host64(wo, "bf16"), heads, 128, t,
+                            rank, causal)
+    assert_close(out, ref, "bf16", f"random attention {wl.name} rank {rank} causal={causal}")
