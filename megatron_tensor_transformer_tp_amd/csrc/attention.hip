@@ -34,7 +34,8 @@
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_f16, K fragments from LDS (one
 //     ds_read_b128, rows XOR-swizzled by row % 16, read one d-step ahead),
 //     Q fragments held in registers; each lane owns one query and 16 of the
-//     block's 32 keys, so the row max needs one exchange with lane ^ 32;
+//     block's 32 keys, so the row max needs one exchange with lane ^ 32,
+//     done by v_permlane32_swap in the VALU (no LDS round trip);
 //   * O^T = V^T P^T: each lane keeps 64 of its query's output dimensions, so
 //     the rescale is lane-local; V^T fragments come straight from the
 //     row-major V block with ds_read_b64_tr_b16 (rows XOR-swizzled by
@@ -87,6 +88,18 @@ __device__ __forceinline__ void copy_to_lds_off(const void* base, uint32_t voff,
                :
                : "v"(voff), "s"(base), "s"(lds_addr)
                : "m0");
+}
+
+// The values of lanes l % 32 and l % 32 + 32 (lane l and its partner l ^ 32),
+// in that order in every lane.  v_permlane32_swap with both operands v
+// exchanges lanes 32..63 of the first with lanes 0..31 of the second
+// (measured), leaving lane l's pair in the two results.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair lane_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
 template <bool CAUSAL>
@@ -210,7 +223,8 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     });
     m5[5] = fmaxf(sv[15], kNegBig);
     const float mraw = fmaxf(fmaxf(fmaxf(m5[0], m5[1]), m5[2]), fmaxf(fmaxf(m5[3], m5[4]), m5[5]));
-    return fmaxf(mraw, __shfl_xor(mraw, 32)) * scale_log2;
+    const LanePair mp = lane_pair(mraw);
+    return fmaxf(mp.lo, mp.hi) * scale_log2;
   };
 
   // The running max is raised (and the accumulator rescaled) only when a
@@ -342,7 +356,8 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     const float m = fmaxf(m_run, m1);
     const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
     const float l_lane = l_run * a0 + l1 * a1;
-    const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+    const LanePair lp = lane_pair(l_lane);
+    const float l_tot = lp.lo + lp.hi;
     const float inv = 1.0f / l_tot;
     uint16_t* orow = o + (row0 + query) * ld_o + head * kD + 4 * h;
     static_for<4>([&](auto DT) __attribute__((always_inline)) {
