@@ -216,13 +216,8 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
         if (key > query) sv[int(R)] = -__builtin_inff();
       }
     });
-    // max as a tree of 3-input maxima (exact in any order)
-    float m5[6];
-    static_for<5>([&](auto R) __attribute__((always_inline)) {
-      m5[R] = fmaxf(fmaxf(sv[3 * R], sv[3 * R + 1]), sv[3 * R + 2]);
-    });
-    m5[5] = fmaxf(sv[15], kNegBig);
-    const float mraw = fmaxf(fmaxf(fmaxf(m5[0], m5[1]), m5[2]), fmaxf(fmaxf(m5[3], m5[4]), m5[5]));
+    float mraw = kNegBig;
+    static_for<16>([&](auto R) __attribute__((always_inline)) { mraw = fmaxf(mraw, sv[int(R)]); });
     const LanePair mp = lane_pair(mraw);
     return fmaxf(mp.lo, mp.hi) * scale_log2;
   };
@@ -248,11 +243,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     static_for<16>([&](auto R) __attribute__((always_inline)) {
       p[R] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[int(R)], scale_log2, -m_run));
     });
-    // pairwise sum: 4 dependent adds instead of 16
-    float q8[8], q4[4];
-    static_for<8>([&](auto R) __attribute__((always_inline)) { q8[R] = p[2 * R] + p[2 * R + 1]; });
-    static_for<4>([&](auto R) __attribute__((always_inline)) { q4[R] = q8[2 * R] + q8[2 * R + 1]; });
-    l_run += (q4[0] + q4[1]) + (q4[2] + q4[3]);
+    static_for<16>([&](auto R) __attribute__((always_inline)) { l_run += p[R]; });
     static_for<2>([&](auto U2) __attribute__((always_inline)) {
       i16x8_t w;
       static_for<4>([&](auto R) __attribute__((always_inline)) {
