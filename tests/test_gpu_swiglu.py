@@ -144,3 +144,42 @@ def test_bf16_ragged_multiround_sampled_rows():
     ref = oracle.swiglu_mlp_shard(host64(x[rows], "bf16"), host64(wg, "bf16"), host64(wu, "bf16"),
                                   host64(b, "bf16"), 1, 0, host64(bb, "bf16"), host64(res[rows], "bf16"))
     assert_close(z[rows], ref, "bf16", "swiglu multi-round", rms_floor=True)
+
+
+def _swiglu_shapes(seed, n):
+    """n seeded shard shapes: every third at 3000-9000 tokens and 1024-5600
+    wide (several rounds of paired gate / value tiles), the rest small;
+    ragged everywhere, k extents (hidden) a multiple of 64 about half the
+    time; rank 0 or 1 of t = 2."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        if i % 3 == 0:
+            tokens, hidden, f = (int(rng.integers(3000, 9001)), 8 * int(rng.integers(128, 701)),
+                                 8 * int(rng.integers(128, 701)))
+        else:
+            tokens, hidden, f = (int(rng.integers(1, 2000)), 8 * int(rng.integers(1, 151)),
+                                 8 * int(rng.integers(1, 151)))
+        if rng.random() < 0.5:
+            hidden = 64 * max(1, hidden // 64)
+        out.append((tokens, hidden, f, int(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("tokens,hidden,f,rank", _swiglu_shapes(31, 9))
+def test_bf16_random_shapes(tokens, hidden, f, rank):
+    wl = inputs.MlpWorkload(f"swiglu_rand_{tokens}_{hidden}_{f}", tokens, hidden, 2 * f, 2, "bf16", 1.0,
+                            0.05, 0.05, "f32")
+    x = inputs.mlp_x_rows(wl)
+    wg, wu, b = full_weights(wl)
+    bb, res = inputs.mlp_bias_b(wl), inputs.mlp_residual_rows(wl)
+    say(f"swiglu random shapes: tokens={tokens} hidden={hidden} f={f} rank {rank}")
+    z = to_np(run(wl, rank, dev(x, "bf16"), dev(inputs.mlp_wg_block(wl, rank), "bf16"),
+                  dev(inputs.mlp_wu_block(wl, rank), "bf16"), dev(inputs.mlp_b_block(wl, rank), "bf16"),
+                  tokens, bias_b=dev(bb, "bf16"), residual=dev(res, "bf16")))
+    assert not np.isnan(z).any(), "unwritten outputs"
+    rows = (np.arange(tokens) if tokens <= 2500 else
+            np.unique(np.r_[0:3, 255:258, np.arange(0, tokens, 131), tokens - 130:tokens]))
+    ref = oracle.swiglu_mlp_shard(host64(x[rows], "bf16"), host64(wg, "bf16"), host64(wu, "bf16"),
+                                  host64(b, "bf16"), wl.t, rank, host64(bb, "bf16"), host64(res[rows], "bf16"))
+    assert_close(z[rows], ref, "bf16", f"swiglu random {tokens}x{hidden}x{f} rank {rank}", rms_floor=True)
