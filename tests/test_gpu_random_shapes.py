@@ -1,12 +1,14 @@
 """Seeded random shapes through the GEMM-based entry points, against the fp64
-oracle on every output element.
+oracle: every output element of the smaller shapes, sampled rows (every
+column) of the larger ones.
 
 The shapes are drawn to reach every kernel variant the tile choice and the
 launcher select: 128 x 128, 128 x 384 and 256 x 256 tiles, one or several
 rounds of resident workgroups, ragged M and N, a partial last k-tile, and
 (when a k extent is a multiple of 64) the paired stages of a k-contiguous
 operand: A for the 128-row tiles of the forward products, B for the
-backward's dX and dH products.  Tolerances as in the other GPU parity tests.
+backward's dX and dH products; and small fp32 shapes through the fp32
+GEMM.  Tolerances as in the other GPU parity tests.
 """
 import numpy as np
 import pytest
@@ -90,3 +92,34 @@ def test_backward(tokens, hidden, f):
     ref = shard_ref(host64(x, "bf16"), host64(a, "bf16"), host64(b, "bf16"), host64(dz, "bf16"))
     got = run_bwd(wl, 1, xd, ad, bd, y, dev(dz, "bf16"), "f32")
     check_grads(got, ref, "bf16", f"random {tokens}x{hidden}x{f}")
+
+
+def _f32_shapes(seed, n):
+    """Small fp32 shapes: any token count, widths a multiple of 4 (the row
+    alignment the ABI asks of fp32 operands); the fp32 GEMM masks every
+    tile edge."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 700)), 4 * int(rng.integers(1, 75)), 4 * int(rng.integers(1, 75)))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("tokens,hidden,f", _f32_shapes(5, 6))
+def test_f32_column_and_row_linear(tokens, hidden, f):
+    t = 2
+    wl = inputs.MlpWorkload(f"rand_f32_{tokens}_{hidden}_{f}", tokens, hidden, f * t, t, "f32", 1.0,
+                            1.0 / np.sqrt(hidden), 1.0 / np.sqrt(f * t), "f32")
+    x, a, bias_a = inputs.mlp_x_rows(wl), inputs.mlp_a_block(wl, 0), inputs.mlp_bias_a_block(wl, 0)
+    b, bias_b, res = inputs.mlp_b_block(wl, 0), inputs.mlp_bias_b(wl), inputs.mlp_residual_rows(wl)
+    say(f"random shapes: fp32 column / row linear tokens={tokens} hidden={hidden} f={f}")
+    y = nan_tensor((tokens, f), torch.float32)
+    binding.tp_column_linear(dev(x, "f32"), dev(a, "f32"), y, ffn=f * t, t=t, rank=0,
+                             bias_i=dev(bias_a, "f32"), apply_gelu=True)
+    z = nan_tensor((tokens, hidden), torch.float32)
+    binding.tp_row_linear(y, dev(b, "f32"), z, ffn=f * t, t=t, rank=0, bias=dev(bias_b, "f32"),
+                          residual=dev(res, "f32"))
+    torch.cuda.synchronize()
+    h, zz = to_np(y), to_np(z)
+    ref_h = oracle.column_linear(host64(x, "f32"), host64(a, "f32"), host64(bias_a, "f32"), apply_gelu=True)
+    assert_close(h, ref_h, "f32", "random fp32 column_linear")
+    ref_z = oracle.row_linear(h, host64(b, "f32"), host64(bias_b, "f32"), host64(res, "f32"), rank=0)
+    assert_close(zz, ref_z, "f32", "random fp32 row_linear")
