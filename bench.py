@@ -52,11 +52,16 @@ METRIC = "TFLOP/s + % bf16 MFMA peak, t=8 MLP shard (h=8192, 16384 tok), 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["megatron_tensor_transformer_tp_amd/csrc/" + f for f in (
-    "device_common.h", "gemm_bf16_impl.h", "gemm_bf16_dma.h", "gemm_bf16.hip",
-    "gemm_bf16_256_gelu.hip", "gemm_bf16_256_plain.hip", "gemm_bf16_256_nt.hip",
-    "gemm_bf16_256_tn.hip", "gemm_bf16_256_swiglu.hip", "gemm_bf16_384_plain.hip", "colsum.hip",
-    "sp_reduce.hip", "attention.hip")]
+CSRC_DIR = os.path.join(ROOT, "megatron_tensor_transformer_tp_amd", "csrc")
+
+
+def kernel_sources():
+    """Every source the library is built from (csrc/ and the C-ABI header),
+    in a fixed order: a change to any of them invalidates the committed
+    counter summaries."""
+    files = sorted(os.path.join("megatron_tensor_transformer_tp_amd", "csrc", f)
+                   for f in os.listdir(CSRC_DIR) if f.endswith((".h", ".hip", ".cpp")))
+    return files + [os.path.join("include", "tp_shard.h")]
 
 
 def _code_only(text: str) -> str:
@@ -71,7 +76,7 @@ def kernel_source_sha() -> str:
     """Hash of the kernel sources' code (comments do not count: a comment
     edit leaves the committed counter summaries valid)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in kernel_sources():
         with open(os.path.join(ROOT, rel), encoding="utf-8") as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]

@@ -6,15 +6,6 @@
 
 namespace tpk {
 
-template <int BM, int BN, int EPI, bool OUT_F32>
-hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                                int M, int N, int K, const Epilogue& ep, hipStream_t stream) {
-  // global->LDS copy kernel: 8 waves (2 per SIMD) of 64 x 96, 4 LDS stages of
-  // 32 KiB
-  return gemm_detail::launch_tile_dma<BM, BN, 2, 4, 4, false, true, EPI, OUT_F32>(
-      A, lda, B, ldb, M, N, K, ep, stream);
-}
-
 template hipError_t launch_gemm_bf16_cfg<128, 384, EPI_LINEAR, true>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);
 
 template hipError_t launch_gemm_bf16_cfg<128, 384, EPI_LINEAR, false>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);

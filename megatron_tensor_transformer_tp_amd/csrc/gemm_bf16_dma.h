@@ -715,4 +715,25 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
 #undef TPK_LDS
 
 }  // namespace gemm_detail
+
+// The launchers declared in gemm_bf16_impl.h, defined once here; each
+// gemm_bf16_*.hip unit only instantiates its share of them.  256 x 256 and
+// 128 x 384 tiles run 8 waves (2 per SIMD: 256 x 256 as 2 x 4 waves of
+// 128 x 64, 128 x 384 as 2 x 4 of 64 x 96), 128 x 128 tiles 4 waves of
+// 64 x 64 (two workgroups per CU); 4 LDS stages throughout.
+template <int BM, int BN, int EPI, bool OUT_F32>
+hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                int M, int N, int K, const Epilogue& ep, hipStream_t stream) {
+  constexpr int kWgn = BM == 128 && BN == 128 ? 2 : 4;
+  return gemm_detail::launch_tile_dma<BM, BN, 2, kWgn, 4, false, true, EPI, OUT_F32>(
+      A, lda, B, ldb, M, N, K, ep, stream);
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR, int EPI, bool OUT_F32>
+hipError_t launch_gemm_bf16_t_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                  int M, int N, int K, const Epilogue& ep, hipStream_t stream) {
+  return gemm_detail::launch_tile_dma<256, 256, 2, 4, 4, A_KMAJOR, B_KMAJOR, EPI, OUT_F32>(
+      A, lda, B, ldb, M, N, K, ep, stream);
+}
+
 }  // namespace tpk

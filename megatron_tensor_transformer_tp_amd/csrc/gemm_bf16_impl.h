@@ -247,14 +247,17 @@ __device__ __forceinline__ void interleave_substep() {
 
 }  // namespace gemm_detail
 
-// One explicit instantiation set per (tile shape, epilogue kind, output type);
-// defined in the gemm_bf16_*.hip translation units.
+// One explicit instantiation set per (tile shape, epilogue kind, output type).
+// Both launchers are defined once, in gemm_bf16_dma.h; each gemm_bf16_*.hip
+// unit instantiates its share of them (so that the units compile in
+// parallel), and callers that see only these declarations link to those
+// instantiations.
 template <int BM, int BN, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                 int M, int N, int K, const Epilogue& ep, hipStream_t stream);
 
-// Products with k-major flags (256 x 256 tiles, copy kernel); defined in the
-// gemm_bf16_256_*.hip translation units.
+// Products with k-major flags (256 x 256 tiles, copy kernel); instantiated in
+// the gemm_bf16_256_{nt,tn,swiglu}.hip units.
 template <bool A_KMAJOR, bool B_KMAJOR, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_t_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                   int M, int N, int K, const Epilogue& ep, hipStream_t stream);

@@ -4,9 +4,9 @@ the fp64 oracle.
 Every call goes through the C ABI.  Outputs and workspace are NaN-filled
 first, so an unwritten tile cannot pass.  Tolerance as for the bf16 MLP path:
 max |err| / (1 + |ref|) <= 2e-2 and relative Frobenius <= 5e-3 per shard; the
-sum over ranks is held to the relative Frobenius bound, and its normalised
-max error is reported (the shards' bf16 rounding errors add over the ranks,
-the "1 +" floor does not grow with them).
+sum over ranks to both bounds with the max criterion's floor sqrt(t) (the
+shards' independent bf16 rounding errors add in quadrature; the stated-floor
+figure is printed beside it).
 """
 import numpy as np
 import pytest
@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from megatron_tensor_transformer_tp_amd import binding, inputs
-from tests.gpu_helpers import BF16_FRO, assert_close, dev, errors, host64, nan_tensor, say, to_np
+from tests.gpu_helpers import assert_close, dev, host64, nan_tensor, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -60,10 +60,10 @@ def test_small_all_ranks_and_reconstruction(name, causal):
                                          wl.head_dim)
     full = oracle.mha_full(x64, wq, wk, wv, host64(np.concatenate(wo, axis=0), "bf16"), wl.heads,
                            causal)
-    mx, fro = errors(total, full)
-    say(f"{name} sum over ranks vs unsharded attention: rel-fro = {fro:.3e} (<= {BF16_FRO}), "
-        f"max|e|/(1+|r|) = {mx:.3e} (reported)")
-    assert np.isfinite(total).all() and fro <= BF16_FRO
+    # the ranks' bf16 rounding errors are independent: they add in
+    # quadrature, so the max criterion's floor is sqrt(t)
+    assert_close(total, full, "bf16", f"{name} sum over ranks vs unsharded attention causal={causal}",
+                 floor=float(np.sqrt(wl.t)))
 
 
 def test_small_bf16_output():

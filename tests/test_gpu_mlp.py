@@ -11,8 +11,7 @@ import torch
 
 import oracle
 from megatron_tensor_transformer_tp_amd import binding, inputs
-from tests.gpu_helpers import (assert_close, dev, errors, host64, nan_tensor, say, to_np,
-                               BF16_FRO)
+from tests.gpu_helpers import assert_close, dev, host64, nan_tensor, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -91,7 +90,8 @@ def test_t8_h8192_m4096_rank0_full():
 @pytest.fixture(scope="module")
 def headline():
     """All 8 ranks of the t=8, h=8192, 16384-token workload, computed back to back on
-    the GPU exactly as the benchmark launches them."""
+    the GPU exactly as the benchmark launches them (partials stay on the device),
+    and a host-side record of the oracle's partials summed so far."""
     wl = inputs.MLP_WORKLOADS["t8_h8192_m16384"]
     say("headline: generating inputs")
     xd = dev(inputs.mlp_x_rows(wl), "bf16")
@@ -106,44 +106,53 @@ def headline():
         binding.tp_mlp_shard_fwd(xd, ad, bd, z, ws, ffn=wl.ffn, t=wl.t, rank=r)
         zs.append(z)
     torch.cuda.synchronize()
-    # sampled rows: first tile, a middle tile-crossing range, the last rows
-    rows = np.r_[0:96, 8160:8256, 16288:16384]
-    return wl, zs, rows
+    del ws, xd
+    state = {"x64": host64(inputs.mlp_x_rows(wl), "bf16"), "ref_sum": None, "ranks": set()}
+    return wl, zs, state
 
 
-def test_headline_each_rank_sampled_rows(headline):
-    wl, zs, rows = headline
-    xs = host64(inputs.mlp_x_rows(wl)[rows], "bf16")
-    for r in (0, 3, 7):
-        z = zs[r][torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
-        ref = oracle.row_linear(oracle.column_linear(xs, host64(inputs.mlp_a_block(wl, r), "bf16"),
-                                                     apply_gelu=True),
-                                host64(inputs.mlp_b_block(wl, r), "bf16"), rank=r)
-        assert_close(z, ref, "bf16", f"headline rank {r}, {len(rows)} sampled rows")
-    # every element of every shard written and finite
-    for r, z in enumerate(zs):
-        assert torch.isfinite(z).all().item(), f"rank {r} has unwritten / non-finite values"
+def _headline_ref(wl, state, r):
+    """The oracle's partial Z_r of the whole shard (fp64, every token), added
+    once into the running sum of the ranks' partials."""
+    ref = oracle.row_linear(oracle.column_linear(state["x64"], host64(inputs.mlp_a_block(wl, r), "bf16"),
+                                                 apply_gelu=True),
+                            host64(inputs.mlp_b_block(wl, r), "bf16"), rank=r)
+    if r not in state["ranks"]:
+        state["ref_sum"] = ref.copy() if state["ref_sum"] is None else state["ref_sum"] + ref
+        state["ranks"].add(r)
+    return ref
 
 
-def test_headline_reconstruction_sampled_rows(headline):
-    """sum_r Z_r on the device (the untimed local stand-in for the All-Reduce)
-    against the unsharded GeLU(X A) B on the sampled rows."""
-    wl, zs, rows = headline
-    total = torch.zeros_like(zs[0][:1]).expand(len(rows), -1).clone()
-    idx = torch.from_numpy(rows).cuda()
-    for z in zs:
-        total += z[idx]
-    got = total.cpu().numpy().astype(np.float64)
-    xs = host64(inputs.mlp_x_rows(wl)[rows], "bf16")
-    ref = None
+@pytest.mark.parametrize("rank", range(8))
+def test_headline_rank_full(headline, rank):
+    """Every element of rank r's partial Z_r [16384, 8192] against the oracle:
+    both bounds as stated, per shard."""
+    wl, zs, state = headline
+    say(f"headline rank {rank}: oracle over all {wl.tokens} tokens")
+    ref = _headline_ref(wl, state, rank)
+    got = zs[rank].cpu().numpy().astype(np.float64)
+    assert_close(got, ref, "bf16", f"headline rank {rank}, all {got.size} elements")
+
+
+def test_headline_reconstruction_full(headline):
+    """sum_r Z_r formed on the device (the untimed local stand-in for the
+    All-Reduce) against the unsharded GeLU(X A) B, every element.  Relative
+    Frobenius as stated; the max criterion with floor sqrt(t): the t shards'
+    bf16 rounding errors are independent and add in quadrature, so the sum's
+    absolute error floor is sqrt(t) times a shard's (the stated-floor figure
+    is printed beside it)."""
+    wl, zs, state = headline
     for r in range(wl.t):
-        part = oracle.row_linear(oracle.column_linear(xs, host64(inputs.mlp_a_block(wl, r), "bf16"),
-                                                      apply_gelu=True),
-                                 host64(inputs.mlp_b_block(wl, r), "bf16"), rank=r)
-        ref = part if ref is None else ref + part
-    mx, fro = errors(got, ref)
-    say(f"headline reconstruction: max|e|/(1+|r|) = {mx:.3e} (reported), rel-fro = {fro:.3e}")
-    assert fro <= BF16_FRO
+        if r not in state["ranks"]:
+            say(f"headline reconstruction: oracle rank {r}")
+            _headline_ref(wl, state, r)
+    total = torch.zeros_like(zs[0])
+    for z in zs:
+        total += z
+    got = total.cpu().numpy().astype(np.float64)
+    del total
+    assert_close(got, state["ref_sum"], "bf16", f"headline reconstruction of {wl.t} shards, all elements",
+                 floor=float(np.sqrt(wl.t)))
 
 
 @pytest.mark.parametrize("tokens,hidden,f,gelu,out", [

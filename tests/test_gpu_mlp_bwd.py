@@ -15,8 +15,7 @@ import torch
 
 import oracle
 from megatron_tensor_transformer_tp_amd import binding, inputs
-from tests.gpu_helpers import (BF16_FRO, assert_close, dev, errors, host64, nan_tensor, say,
-                               to_np)
+from tests.gpu_helpers import assert_close, dev, host64, nan_tensor, rms, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -54,11 +53,15 @@ def run_bwd(wl, r, xd, ad, bd, yd, dzd, grad_dt, with_bias=True, da=None):
 
 
 def check_grads(got, ref, dtype, what, keys=("dx", "da", "db", "dbias_a", "dbias_b")):
+    """fp32: every gradient to the stated bound.  bf16: dX (near unit scale)
+    to the stated bound in its own units (floor max(1, rms)); the weight and
+    bias gradients, sums over all the tokens (RMS in the tens to hundreds),
+    with the RMS as the floor."""
     for k in keys:
         if got.get(k) is None:
             continue
-        # the bias gradients are fp32 sums of the (rounded) row gradients
-        assert_close(to_np(got[k]), ref[k], dtype, f"{what} {k}", rms_floor=True)
+        floor = "one" if dtype == "f32" else ("scale" if k == "dx" else "rms")
+        assert_close(to_np(got[k]), ref[k], dtype, f"{what} {k}", floor=floor)
 
 
 def shard_ref(x64, a64, b64, dz64, ba64=None):
@@ -88,8 +91,7 @@ def test_tiny_f32_all_ranks_save_and_backward():
         dx = to_np(got["dx"])
         dx_sum = dx if dx_sum is None else dx_sum + dx
     full = oracle.mlp_shard_bwd(x, a_full, b_full, dz, 1, 0, bias_a=ba_full)
-    assert_close(dx_sum, full["dx"], "f32", "tiny sum over ranks of dX vs unsharded dX",
-                 rms_floor=True)
+    assert_close(dx_sum, full["dx"], "f32", "tiny sum over ranks of dX vs unsharded dX")
 
 
 def test_f32_ragged_tokens():
@@ -172,10 +174,11 @@ def test_t4_all_ranks_strided_weight_views_and_reconstruction():
     a64 = host64(np.concatenate(a_blocks, axis=1), "bf16")
     b64 = host64(np.concatenate(b_blocks, axis=0), "bf16")
     full = oracle.mlp_shard_bwd(x64, a64, b64, dz64, 1, 0)
-    assert_close(to_np(da_full), full["da"], "bf16", "t4 assembled dA vs unsharded dA", rms_floor=True)
-    mx, fro = errors(dx_sum, full["dx"])
-    say(f"t4 sum over ranks of dX vs unsharded: rel-fro {fro:.3e} (<= {BF16_FRO}), max {mx:.3e} (reported)")
-    assert fro <= BF16_FRO
+    assert_close(to_np(da_full), full["da"], "bf16", "t4 assembled dA vs unsharded dA", floor="rms")
+    # the t contributions carry independent bf16 rounding errors, which add
+    # in quadrature: the floor of the max criterion grows by sqrt(t)
+    assert_close(dx_sum, full["dx"], "bf16", "t4 sum over ranks of dX vs unsharded dX",
+                 floor=max(np.sqrt(wl.t), rms(full["dx"])))
 
 
 @pytest.mark.parametrize("name,rank", [("t8_h8192_m4096", 0), ("t8_h8192_m4096", 5),
