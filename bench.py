@@ -51,7 +51,6 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s + % bf16 MFMA peak, t=8 MLP shard (h=8192, 16384 tok), 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CSRC_DIR = os.path.join(ROOT, "megatron_tensor_transformer_tp_amd", "csrc")
 
 
@@ -84,20 +83,6 @@ def kernel_source_sha() -> str:
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-
-def load_traffic(kernel: str):
-    """HBM bytes per launch of ``kernel`` from the committed counter summary, or
-    None if there is none or it was taken on a different kernel source."""
-    try:
-        with open(TRAFFIC_FILE) as fh:
-            data = json.load(fh)
-    except (OSError, ValueError):
-        return None
-    if data.get("source_sha") != kernel_source_sha():
-        return None
-    entry = data.get("kernels", {}).get(kernel)
-    return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(wl, target_s: float):
@@ -154,150 +139,358 @@ def cpu_baseline(wl, target_s: float):
 
 PROFILE_CMDS = {
     "trace": ("rocprofv3 --kernel-trace --stats --output-format csv -d rocprof_out/ktrace -o kt -- "
-              "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline"),
+              "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --json-out rocprof_out/ktrace/line.json"),
     "fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d rocprof_out/pmc_fetch -o pmc -- "
               "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
     "write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc_write -o pmc -- "
               "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
+    "mfma": ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE "
+             "GRBM_COUNT --output-format csv -d rocprof_out/pmc_mfma -o pmc -- "
+             "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2"),
 }
-# Profiled kernels: name pattern in the rocprofv3 output and, where one
-# kernel serves several of the benchmark's shapes, a selector of the dispatch
-# (an int: grid size in work-items; ("us", lo, hi): duration band in
-# microseconds — the GEMMs run one round of resident workgroups whatever the
-# shape, so their grids do not tell shapes apart), with the per-launch
-# algorithmic work (FLOP, bytes), the workload, and the summary's file stem.
-# GEMM template arguments: tile BM, BN, wave grid, LDS stages, A k-major,
-# B k-major, epilogue kind, fp32 output, K tail (false: K % 32 == 0), paired
-# stages (0: none, 1: B, 2: A; a k-contiguous operand with K % 64 == 0).
+# The device's SIMD count and XCD count (MI355X: 256 CUs x 4 SIMDs, 8 XCDs):
+# MFMA utilisation = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (GPU-active
+# cycles x SIMDs), rocprofv3's own MfmaUtil expression; the GRBM counters are
+# summed over the XCDs in the per-dispatch rows, so one XCD's active cycles
+# are the sum / 8, and those cycles over the dispatch's duration are its
+# average shader clock.
+N_SIMD, N_XCD = 1024, 8
+# Profiled kernels: name pattern in the rocprofv3 output and a duration band
+# in microseconds that tells the benchmark's shapes of one kernel apart (the
+# GEMMs launch one round of resident workgroups whatever the shape, so their
+# grids do not), with the per-launch algorithmic work (FLOP, bytes), the
+# workload, and the summary's file stem.  GEMM template arguments: tile BM,
+# BN, wave grid, LDS stages, A k-major, B k-major, epilogue kind, fp32 output,
+# K tail (false: K % 32 == 0), paired stages (0: none, 1: B, 2: A; a
+# k-contiguous operand with K % 64 == 0).
 _M, _H, _F = 16384, 8192, 4096          # MLP shard: tokens, hidden, f = ffn / t
+_M3 = 4096                              # the 4096-token rank shard
+_M2, _H2, _F2 = 2048, 1024, 4096        # the t = 1 MLP: tokens, hidden, ffn
 _S, _DL = 4096, 1024                    # attention shard: tokens, local width (8 heads x 128)
 _GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "   # then A k-major, B k-major, epilogue kind, fp32 out, K tail, pairs
+_GEMM128 = "gemm_bf16_dma_kernel<128, 128, 2, 2, 4, "
+_INF = 1e9
 PROFILED = {
-    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0>", None,
+    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0>", (500.0, _INF),
                          2.0 * _M * _H * _F, 2 * (_M * _H + _H * _F + _M * _F),
                          "MLP rank shard, M=16384, h=8192, f=4096: X, A_i read, H_i written (bf16)",
                          "column_gemm_gelu_t8_h8192_m16384"),
-    "row_gemm": (_GEMM + "false, true, 0, true, false, 0>", ("us", 300.0, 1e9),
+    "row_gemm": (_GEMM + "false, true, 0, true, false, 0>", (500.0, _INF),
                  2.0 * _M * _F * _H, 2 * (_M * _F + _F * _H) + 4 * _M * _H,
                  "MLP rank shard, M=16384, h=8192, f=4096: H_i, B_i read (bf16), Z_i written (fp32)",
                  "row_gemm_t8_h8192_m16384"),
-    "attention_core": ("attn_fwd_kernel<false>", None,
+    "t8_h8192_m4096:column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0>", (100.0, 500.0),
+                                        2.0 * _M3 * _H * _F, 2 * (_M3 * _H + _H * _F + _M3 * _F),
+                                        "rank 0 of t=8, M=4096, h=8192, f=4096: X, A_0 read, H_0 written (bf16)",
+                                        "column_gemm_gelu_t8_h8192_m4096"),
+    "t8_h8192_m4096:row_gemm": (_GEMM + "false, true, 0, true, false, 0>", (140.0, 500.0),
+                                2.0 * _M3 * _F * _H, 2 * (_M3 * _F + _F * _H) + 4 * _M3 * _H,
+                                "rank 0 of t=8, M=4096, h=8192, f=4096: H_0, B_0 read (bf16), Z_0 written (fp32)",
+                                "row_gemm_t8_h8192_m4096"),
+    "t1_h1024_m2048:column_gemm_gelu": (_GEMM128 + "false, true, 1, false, false, 2>", (0.0, _INF),
+                                        2.0 * _M2 * _H2 * _F2, 2 * (_M2 * _H2 + _H2 * _F2 + _M2 * _F2),
+                                        "t=1 MLP, M=2048, h=1024, ffn=4096 (128 x 128 tiles): X, A read, "
+                                        "H written (bf16)",
+                                        "column_gemm_gelu_t1_h1024_m2048"),
+    "t1_h1024_m2048:row_gemm": (_GEMM128 + "false, true, 0, false, false, 2>", (0.0, _INF),
+                                2.0 * _M2 * _F2 * _H2, 2 * (_M2 * _F2 + _F2 * _H2) + 2 * _M2 * _H2,
+                                "t=1 MLP, M=2048, ffn=4096, h=1024 (128 x 128 tiles): H, B read, "
+                                "Z written (bf16 final output)",
+                                "row_gemm_t1_h1024_m2048"),
+    "attention_core": ("attn_fwd_kernel<false>", (0.0, _INF),
                        4.0 * _S * _S * _DL, 2 * (3 * _S * _DL + _S * _DL),
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K "
                        "(fp16) and V (bf16) read once, O written (bf16)",
                        "attention_core_t8_h8192_s4096"),
-    "attn_qkv_gemm": ("gemm_bf16_dma_kernel<128, 384, 2, 4, 4, false, true, 4, false, false, 2>", None,
+    "attn_qkv_gemm": ("gemm_bf16_dma_kernel<128, 384, 2, 4, 4, false, true, 4, false, false, 2>", (0.0, _INF),
                       2.0 * _S * _H * 3 * _DL, 2 * (_S * _H + _H * 3 * _DL + _S * 3 * _DL),
                       "attention rank shard packed QKV projection, M=4096, K=8192, N=3072 "
                       "(one round of 256 128 x 384 tiles), q/k written as scaled fp16, v as bf16",
                       "attn_qkv_gemm_t8_h8192_s4096"),
-    "attn_out_gemm": (_GEMM + "false, true, 0, true, false, 0>", ("us", 0.0, 300.0),
+    "attn_out_gemm": (_GEMM + "false, true, 0, true, false, 0>", (0.0, 140.0),
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
                       "attention rank shard output projection, M=4096, K=1024, N=8192 (fp32 out)",
                       "attn_out_gemm_t8_h8192_s4096"),
-    "sp_reduce_scatter": ("sp_reduce_kernel<unsigned short, unsigned short, true, true>", 8192 * 256,
+    "sp_reduce_scatter": ("sp_reduce_kernel<unsigned short, unsigned short, true, true>", (0.0, _INF),
                           0.0, 8 * (_M // 8) * _H * 4 + 2 * (_M // 8) * _H * 2 + 2 * _H,
                           "sequence-parallel reduce-scatter of the 8 fp32 MLP partials into one "
                           "rank's [2048, 8192] shard with bf16 bias and residual rows, bf16 out "
                           "(HBM-bound: partial rows, residual and bias read, shard written)",
                           "sp_reduce_scatter_t8_h8192_m16384"),
-    "swiglu_gemm": (_GEMM + "false, true, 3, false, false, 0>", None,
+    "swiglu_gemm": (_GEMM + "false, true, 3, false, false, 0>", (0.0, _INF),
                     2.0 * _M * _H * 2 * _F, 2 * (_M * _H + 2 * _H * _F + _M * _F),
                     "SwiGLU column layer, both projections in one product with SiLU(gate) * value "
                     "in the epilogue: X, Wg_i, Wu_i read, H_i written (bf16)",
                     "swiglu_gemm_t8_h8192_m16384"),
-    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false, false, 1>", None,
+    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false, false, 1>", (0.0, _INF),
                        2.0 * _M * _H * _F, 2 * (_M * _H + _F * _H + _M * _F) + 2 * 2 * _M * _F,
                        "MLP shard backward dH = dZ B_i^T with dY_i = dH * GeLU'(Y_i) and H_i = "
                        "GeLU(Y_i) in the epilogue: dZ, B_i, Y_i read, dY_i and H_i written (bf16)",
                        "bwd_dgelu_gemm_t8_h8192_m16384"),
-    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true, false, 0>", None,
+    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true, false, 0>", (0.0, _INF),
                              2.0 * _M * _H * _F, 2 * (_M * _F + _M * _H) + 4 * _F * _H,
                              "MLP shard backward weight gradients H_i^T dZ and X^T dY_i (one "
                              "kernel, K = 16384 tokens): two bf16 operands read, fp32 [4096 x 8192] "
                              "written; both launches averaged",
                              "bwd_weight_grad_gemm_t8_h8192_m16384"),
-    "bwd_dx_gemm": (_GEMM + "false, false, 0, true, false, 1>", None,
+    "bwd_dx_gemm": (_GEMM + "false, false, 0, true, false, 1>", (0.0, _INF),
                     2.0 * _M * _F * _H, 2 * (_M * _F + _H * _F) + 4 * _M * _H,
                     "MLP shard backward dX_i = dY_i A_i^T: dY_i, A_i read (bf16), dX_i written (fp32)",
                     "bwd_dx_gemm_t8_h8192_m16384"),
 }
 COPY_KEY = ("copyBuffer", 1 << 30)    # the 1 GiB calibration copy
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
-def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str) -> None:
-    """Turn the rocprofv3 CSVs of the three PROFILE_CMDS runs (the per-dispatch
-    kernel trace and the two counter collections) into the committed
-    summaries: profiles/<file stem>.md per profiled kernel and
-    profiles/traffic_counters.json.  HBM bytes = FETCH_SIZE x (1 GiB / FETCH_SIZE
-    of the 1 GiB copy) + the same for WRITE_SIZE (both counters report KiB per
-    dispatch)."""
+def load_counters() -> dict:
+    """Per-kernel counter figures from the committed summary (profiles/
+    counters.json), or {} if there is none or it was taken on a different
+    kernel source."""
+    try:
+        with open(COUNTERS_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return {}
+    if data.get("source_sha") != kernel_source_sha():
+        return {}
+    return data.get("kernels", {})
+
+
+def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str, mfma_csv: str,
+                       line_json: str) -> None:
+    """Turn the rocprofv3 CSVs of the PROFILE_CMDS runs (the per-dispatch
+    kernel trace and the three counter collections) and the bench line the
+    traced run printed into the committed summaries: profiles/<file stem>.md
+    per profiled kernel and profiles/counters.json.
+      HBM bytes = FETCH_SIZE x (1 GiB / FETCH_SIZE of the 1 GiB copy) + the
+                  same for WRITE_SIZE (both counters report KiB per dispatch);
+      MFMA utilisation, shader clock and MFMA FLOP from the "mfma" pass;
+      the dominant kernels' trace durations over exactly the launches the
+      bench line's per-kernel figures were timed on (its kernel-timing
+      phase), next to those figures."""
     import csv
     import statistics
 
-    def key_of(name, grid, us):
-        for key, (pat, sel, *_rest) in PROFILED.items():
-            if pat not in name:
-                continue
-            if sel is None or (isinstance(sel, int) and sel == grid) or \
-                    (isinstance(sel, tuple) and sel[1] <= us < sel[2]):
+    def key_of(name, us):
+        for key, (pat, band, *_rest) in PROFILED.items():
+            if pat in name and band[0] <= us < band[1]:
                 return key
         return "copy_1GiB" if COPY_KEY[0] in name else None
 
     def dur_us(row):
         return (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
 
-    def per_kernel_counter(path):
-        vals = {}
+    def per_dispatch(path):
+        """{dispatch id: (kernel name, duration us, {counter: value summed over rows})}"""
+        out = {}
         for row in csv.DictReader(open(path)):
-            key = key_of(row["Kernel_Name"], int(row["Grid_Size"]), dur_us(row))
-            if key is not None:
-                vals.setdefault(key, []).append(float(row["Counter_Value"]))
-        return {k: statistics.median(v) for k, v in vals.items()}
+            d = out.setdefault(row["Dispatch_Id"], [row["Kernel_Name"], dur_us(row), {}])
+            c = d[2]
+            c[row["Counter_Name"]] = c.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        return out
 
-    fetch, write = per_kernel_counter(fetch_csv), per_kernel_counter(write_csv)
+    def by_key(path):
+        vals = {}
+        for name, us, ctr in per_dispatch(path).values():
+            key = key_of(name, us)
+            if key is not None:
+                vals.setdefault(key, []).append((us, ctr))
+        return vals
+
+    fetch, write, mfma = by_key(fetch_csv), by_key(write_csv), by_key(mfma_csv)
+
+    def med(vals, key, fn):
+        return statistics.median(fn(us, c) for us, c in vals[key]) if key in vals else None
+
     gib_kib = float(1 << 20)
-    f_scale, w_scale = gib_kib / fetch["copy_1GiB"], gib_kib / write["copy_1GiB"]
+    f_scale = gib_kib / med(fetch, "copy_1GiB", lambda us, c: c["FETCH_SIZE"])
+    w_scale = gib_kib / med(write, "copy_1GiB", lambda us, c: c["WRITE_SIZE"])
+    # the trace: dispatches in time order, per key
     durs = {}
-    for row in csv.DictReader(open(trace_csv)):
-        grid = int(row["Grid_Size_X"]) * int(row["Grid_Size_Y"]) * int(row["Grid_Size_Z"])
-        key = key_of(row["Kernel_Name"], grid, dur_us(row))
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    for row in rows:
+        key = key_of(row["Kernel_Name"], dur_us(row))
         if key is not None:
             durs.setdefault(key, []).append((dur_us(row), row["Kernel_Name"]))
+    with open(line_json) as fh:
+        line = json.load(fh)
+    tm = line["timing"]
+    # launches of each headline GEMM before its kernel-timing phase: warmup
+    # steps, timed steps and one step in between, t launches each
+    t = line["config"]["t"]
+    first = (tm["warmup"] + tm["steps"] + 1) * t
+    phase = slice(first, first + tm["kernel_reps"] * t)
+
     out = {"source_sha": kernel_source_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
-           "commands": PROFILE_CMDS, "kernels": {}}
-    for key, (_pat, _grid, flops, alg_bytes, what, stem) in PROFILED.items():
-        fb = fetch[key] * 1024 * f_scale
-        wb = write[key] * 1024 * w_scale
+           "n_simd": N_SIMD, "n_xcd": N_XCD, "commands": PROFILE_CMDS, "kernels": {},
+           "traced_bench_line": {k: line[k] for k in ("value", "ms_per_step", "roofline", "kernels")}}
+    for key, (_pat, _band, flops, alg_bytes, what, stem) in PROFILED.items():
+        if key not in durs:
+            continue
+        fb = med(fetch, key, lambda us, c: c["FETCH_SIZE"]) * 1024 * f_scale
+        wb = med(write, key, lambda us, c: c["WRITE_SIZE"]) * 1024 * w_scale
+        util = med(mfma, key, lambda us, c: c["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                   (c["GRBM_GUI_ACTIVE"] / N_XCD * N_SIMD))
+        sclk = med(mfma, key, lambda us, c: c["GRBM_GUI_ACTIVE"] / N_XCD / (us * 1e3))
+        mflops = med(mfma, key, lambda us, c: c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0)
         us = [d for d, _ in durs[key]]
         avg_us = statistics.mean(us)
-        out["kernels"][key] = {"hbm_bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb),
-                               "write_bytes": int(wb), "algorithmic_bytes": int(alg_bytes),
-                               "avg_us": round(avg_us, 2), "calls": len(us)}
+        ent = {"hbm_bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb), "write_bytes": int(wb),
+               "algorithmic_bytes": int(alg_bytes), "avg_us": round(avg_us, 2), "calls": len(us),
+               "mfma_util": None if util is None else round(util, 4),
+               "sclk_ghz": None if sclk is None else round(sclk, 3),
+               "mfma_flops_per_launch": None if mflops is None else int(mflops)}
+        phase_us = us[phase] if key in line.get("kernels", {}) else []
+        if phase_us:
+            ent["phase_avg_us"] = round(statistics.mean(phase_us), 2)
+            ent["phase_calls"] = len(phase_us)
+        out["kernels"][key] = ent
         md = [f"# {key} — {stem}", "",
               f"Workload: {what}.", "",
               f"kernel: `{durs[key][0][1][:120]}`", f"kernel source sha: {out['source_sha']}", "",
-              "Commands (run from the repository root on the MI355X):", "",
+              "Commands (run from the repository root on the MI355X; the summary is written by "
+              "`python3 bench.py --summarize-profiles` from their CSV files):", "",
               *[f"    {c}" for c in PROFILE_CMDS.values()], "",
               "| figure | value |", "|---|---|",
               f"| dispatches in the trace run | {len(us)} |",
               f"| average duration | {avg_us:.1f} us |",
-              f"| median / min / max duration | {statistics.median(us):.1f} / {min(us):.1f} / {max(us):.1f} us |",
-              *([f"| algorithmic FLOP per launch | {flops / 1e9:.1f} G |",
-                 f"| achieved (algorithmic FLOP / avg duration) | {flops / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s "
-                 f"({100 * flops / (avg_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS}) |"]
-                if flops else
-                [f"| achieved (algorithmic bytes / avg duration) | {alg_bytes / (avg_us * 1e-6) / 1e9:.0f} GB/s "
-                 f"({100 * alg_bytes / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f}) |"]),
-              f"| FETCH_SIZE per dispatch (median) | {fetch[key]:.0f} KiB (x{f_scale:.3f} from the 1 GiB copy) |",
-              f"| WRITE_SIZE per dispatch (median) | {write[key]:.0f} KiB (x{w_scale:.3f}) |",
-              f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.1f} MB (fetch {fb / 1e6:.1f}, write {wb / 1e6:.1f}) |",
-              f"| algorithmic bytes per launch | {alg_bytes / 1e6:.1f} MB |", ""]
+              f"| median / min / max duration | {statistics.median(us):.1f} / {min(us):.1f} / {max(us):.1f} us |"]
+        if flops:
+            md += [f"| algorithmic FLOP per launch | {flops / 1e9:.1f} G |",
+                   f"| achieved (algorithmic FLOP / avg duration) | {flops / (avg_us * 1e-6) / 1e12:.1f} TFLOP/s "
+                   f"({100 * flops / (avg_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS}) |"]
+        else:
+            md += [f"| achieved (algorithmic bytes / avg duration) | {alg_bytes / (avg_us * 1e-6) / 1e9:.0f} GB/s "
+                   f"({100 * alg_bytes / (avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f}) |"]
+        if phase_us:
+            live = line["kernels"][key]
+            pf = flops / (ent["phase_avg_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+            md += [f"| trace average over the bench's kernel-timing launches ({len(phase_us)}) | "
+                   f"{ent['phase_avg_us']:.1f} us -> frac {pf:.4f} |",
+                   f"| the same launches timed live by bench.py (HIP events, its JSON line in this run) | "
+                   f"{live['avg_us']:.1f} us -> frac {flops / (live['avg_us'] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f} |"]
+        if util is not None:
+            md += [f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs), median) | "
+                   f"{100 * util:.1f}% |",
+                   f"| shader clock (GRBM_GUI_ACTIVE / 8 / duration, median) | {sclk:.3f} GHz |"]
+            if flops:
+                md += [f"| MFMA FLOP per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {mflops / 1e9:.1f} G "
+                       f"({mflops / flops:.3f} x algorithmic) |",
+                       f"| peak at that clock (2516.6 x clock / 2.4 GHz) | {PEAK_BF16_TFLOPS * sclk / 2.4:.1f} TFLOP/s |"]
+        md += [f"| FETCH_SIZE per dispatch (median) | {fb / 1024 / f_scale:.0f} KiB (x{f_scale:.3f} from the 1 GiB copy) |",
+               f"| WRITE_SIZE per dispatch (median) | {wb / 1024 / w_scale:.0f} KiB (x{w_scale:.3f}) |",
+               f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.1f} MB (fetch {fb / 1e6:.1f}, write {wb / 1e6:.1f}) |",
+               f"| algorithmic bytes per launch | {alg_bytes / 1e6:.1f} MB |", ""]
         with open(os.path.join(ROOT, "profiles", f"{stem}.md"), "w") as fh:
             fh.write("\n".join(md))
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(COUNTERS_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def _stats(samples):
+    """median / min / max of a list of per-call times (us)."""
+    return {"median": round(float(np.median(samples)), 2), "min": round(float(min(samples)), 2),
+            "max": round(float(max(samples)), 2)}
+
+
+def time_repeats(call, stream, reps: int, repeats: int = 3, warm: int = 3):
+    """Per-call time (us) of ``call`` in ``repeats`` windows of ``reps`` calls
+    each, queued back to back on ``stream`` after ``warm`` untimed calls
+    (warmup, then three repeats: the fair-benchmark practice of Megatron
+    Level 2, M039)."""
+    import torch
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    marks = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        marks.append((e0, e1))
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e3 / reps for e0, e1 in marks]
+
+
+def time_launches(calls, stream, reps: int):
+    """Per-launch times (us) of each named call, the calls interleaved in the
+    given order ``reps`` times, an event pair around every launch on the
+    launch stream."""
+    import torch
+    events = {name: [] for name in calls}
+    for _ in range(reps):
+        for name, fn in calls.items():
+            k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k0.record(stream)
+            fn()
+            k1.record(stream)
+            events[name].append((k0, k1))
+    torch.cuda.synchronize()
+    return {name: [k0.elapsed_time(k1) * 1e3 for k0, k1 in ev] for name, ev in events.items()}
+
+
+def bench_mlp_config(name: str, rank: int, stream, reps: int, traffic: dict):
+    """One MLP workload's shard on its own: tp_mlp_shard_fwd timed in three
+    repeats, and its two GEMMs (tp_column_linear with GeLU, tp_row_linear)
+    per launch, with algorithmic and (from the committed counters) measured
+    HBM bytes per launch."""
+    import torch
+    from megatron_tensor_transformer_tp_amd import binding, inputs
+
+    wl = inputs.MLP_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    out_dt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    ob = 4 if wl.out_dtype == "f32" else 2
+    x, a, b = up(inputs.mlp_x_rows(wl)), up(inputs.mlp_a_block(wl, rank)), up(inputs.mlp_b_block(wl, rank))
+    z = torch.empty((wl.tokens, wl.hidden), dtype=out_dt, device=dev)
+    ws = torch.empty(binding.tp_mlp_shard_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t,
+                                                          torch.bfloat16), dtype=torch.uint8, device=dev)
+    h = ws[: wl.tokens * wl.f * 2].view(torch.bfloat16).view(wl.tokens, wl.f)
+    shard = time_repeats(lambda: binding.tp_mlp_shard_fwd(x, a, b, z, ws, ffn=wl.ffn, t=wl.t, rank=rank,
+                                                          stream=stream), stream, reps)
+    per = time_launches({
+        "column_gemm_gelu": lambda: binding.tp_column_linear(x, a, h, ffn=wl.ffn, t=wl.t, rank=rank,
+                                                             apply_gelu=True, stream=stream),
+        "row_gemm": lambda: binding.tp_row_linear(h, b, z, ffn=wl.ffn, t=wl.t, rank=rank, stream=stream),
+    }, stream, reps)
+    flops = wl.flops_per_shard()
+    gemm_flops = 2.0 * wl.tokens * wl.hidden * wl.f
+    alg = {"column_gemm_gelu": 2.0 * (wl.tokens * wl.hidden + wl.hidden * wl.f + wl.tokens * wl.f),
+           "row_gemm": 2.0 * (wl.tokens * wl.f + wl.f * wl.hidden) + ob * wl.tokens * wl.hidden}
+    med = float(np.median(shard))
+    kernels = {}
+    for k, us_list in per.items():
+        us = float(np.mean(us_list))
+        ent = {"avg_us": round(us, 2), "tflops": round(gemm_flops / (us * 1e-6) / 1e12, 2),
+               "algorithmic_bytes": int(alg[k]),
+               "algorithmic_gbs": round(alg[k] / (us * 1e-6) / 1e9, 1)}
+        hbm = traffic.get(f"{name}:{k}")
+        if hbm is not None:
+            ent["hbm_bytes"] = int(hbm)
+            ent["hbm_gbs"] = round(hbm / (us * 1e-6) / 1e9, 1)
+            ent["frac_hbm"] = round(hbm / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        kernels[k] = ent
+    res = {
+        "workload": (f"{wl.name}: rank {rank} of t={wl.t}, {wl.tokens} tokens, hidden {wl.hidden}, "
+                     f"ffn {wl.ffn} (f {wl.f}), {wl.out_dtype} "
+                     f"{'final output' if wl.t == 1 else 'partial'}"),
+        "flops": int(flops),
+        "us": _stats(shard),
+        "tflops": round(flops / (med * 1e-6) / 1e12, 2),
+        "pct_peak": round(100.0 * flops / (med * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(wl.tokens / (med * 1e-6), 1),
+        "kernels": kernels,
+    }
+    log(f"{name} rank {rank}: shard {med:.1f} us (min {min(shard):.1f}, max {max(shard):.1f}), "
+        f"{res['tflops']} TFLOP/s; " + ", ".join(f"{k} {v['avg_us']} us" for k, v in kernels.items()))
+    return res
 
 
 def bench_swiglu(wl, x, b0, stream, reps: int):
@@ -526,11 +719,15 @@ def main() -> int:
                     help="skip the attention-shard measurement")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the MLP-backward measurement")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the t=1 2048-token and the 4096-token rank-shard workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the bounded oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+    ap.add_argument("--json-out", help="also write the JSON line to this file")
+    ap.add_argument("--summarize-profiles", nargs=5,
+                    metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV", "MFMA_CSV", "TRACED_LINE_JSON"),
                     help="write profiles/ summaries from the rocprofv3 CSVs of PROFILE_CMDS and exit")
     args = ap.parse_args()
     if args.summarize_profiles:
@@ -555,6 +752,7 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    counters = load_counters()
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -580,19 +778,26 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The K timed steps, one window bracketed by synchronisations; events at
+    # the thirds of the window give three repeats of the same steps (median,
+    # min, max of their per-step times), without timing any step twice.
+    cuts = sorted({0, args.steps // 3, (2 * args.steps) // 3, args.steps})
+    evs = [torch.cuda.Event(enable_timing=True) for _ in cuts]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
+    for i in range(args.steps + 1):
+        if i in cuts:
+            evs[cuts.index(i)].record(stream)
+        if i < args.steps:
+            step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    sub = [evs[j].elapsed_time(evs[j + 1]) / (cuts[j + 1] - cuts[j]) for j in range(len(cuts) - 1)]
     flops_step = wl.flops_per_shard() * wl.t
     tflops = flops_step / (ms_step * 1e-3) / 1e12
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (events), wall {wall * 1e3 / args.steps:.3f} ms/step")
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (events), wall {wall * 1e3 / args.steps:.3f} ms/step; "
+        f"thirds {', '.join(f'{v:.3f}' for v in sub)} ms/step")
 
     # ---- per-kernel live timing, in the step's context: the step's launches
     # in the step's order (column then row GEMM for every rank's operands,
@@ -633,6 +838,31 @@ def main() -> int:
         log(f"kernel {name}: {us:.1f} us/launch in the step's order, {flops / (us * 1e-6) / 1e12:.1f} TFLOP/s")
     dom = max(per_kernel, key=lambda k: per_kernel[k]["avg_us"])
     achieved = per_kernel[dom]["tflops"]
+    ctr = counters.get(dom, {})
+    roofline = {
+        "bound": "mfma",
+        "kernel": dom,
+        "achieved": achieved,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": ctr.get("hbm_bytes_per_launch"),
+        "algorithmic_bytes": per_kernel[dom]["algorithmic_bytes"],
+        "avg_us": per_kernel[dom]["avg_us"],
+    }
+    if ctr.get("sclk_ghz"):
+        # counter evidence from the committed profile of the same kernel
+        # source: the matrix pipes' busy fraction and the shader clock the
+        # part held during the kernel (it is power-limited under MFMA load),
+        # and the achieved rate against the peak at that clock
+        at_clk = PEAK_BF16_TFLOPS * ctr["sclk_ghz"] / 2.4
+        roofline.update({"mfma_util": ctr.get("mfma_util"), "sclk_ghz": ctr["sclk_ghz"],
+                         "peak_at_sclk": round(at_clk, 1), "frac_at_sclk": round(achieved / at_clk, 4)})
+    for name, ent in per_kernel.items():
+        c = counters.get(name, {})
+        for k in ("mfma_util", "sclk_ghz", "hbm_bytes_per_launch"):
+            if c.get(k) is not None:
+                ent[k] = c[k]
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -640,13 +870,22 @@ def main() -> int:
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
         log("calibration copy of 1 GiB x3 done")
 
     sp_boundary = bench_sp(wl, z, stream, args.kernel_reps)
     swiglu = bench_swiglu(wl, x, b[0], stream, args.kernel_reps)
     backward = None if args.no_backward else bench_backward(wl, x, a[0], b[0], stream,
                                                             args.kernel_reps)
+    del a[1:], b[1:], z[1:]
     attention = None if args.no_attention else bench_attention(stream, args.kernel_reps)
+    secondary = None
+    if not args.no_secondary:
+        hbm = {k: v.get("hbm_bytes_per_launch") for k, v in counters.items() if ":" in k}
+        secondary = {
+            "t1_h1024_m2048": bench_mlp_config("t1_h1024_m2048", 0, stream, max(args.kernel_reps, 20) * 5, hbm),
+            "t8_h8192_m4096": bench_mlp_config("t8_h8192_m4096", 0, stream, max(args.kernel_reps, 10), hbm),
+        }
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -677,26 +916,26 @@ def main() -> int:
         "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "ms_per_shard": round(ms_step / wl.t, 4),
         "tokens_per_s_per_shard": round(wl.tokens / (ms_step / wl.t * 1e-3), 1),
-        "roofline": {
-            "bound": "mfma",
-            "kernel": dom,
-            "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(dom),
-            "algorithmic_bytes": per_kernel[dom]["algorithmic_bytes"],
-            "avg_us": per_kernel[dom]["avg_us"],
-        },
+        "repeats": {"windows": len(sub), "ms_per_step": [round(v, 4) for v in sub],
+                    **{k: round(v / 1e3, 4) for k, v in _stats([u * 1e3 for u in sub]).items()},
+                    "tflops_median": round(flops_step / (float(np.median(sub)) * 1e-3) / 1e12, 2)},
+        "timing": {"warmup": args.warmup, "steps": args.steps, "kernel_reps": args.kernel_reps},
+        "roofline": roofline,
         "kernels": per_kernel,
         "kernel_source_sha": kernel_source_sha(),
+        "counters_valid": bool(counters),
         "cpu_baseline": cpu,
+        "secondary": secondary,
         "swiglu": swiglu,
         "sp_boundary": sp_boundary,
         "backward": backward,
         "attention": attention,
     }
-    print(json.dumps(result), flush=True)
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as fh:
+            fh.write(line + "\n")
     return 0
 
 

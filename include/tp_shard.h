@@ -40,6 +40,22 @@
  *   - Shapes that do not divide are rejected, never padded: 列并行 tutorial,
  *     切分原理; Megatron Level 2, M031.
  *
+ * What this interface adds to the method's five operations (column linear,
+ * GeLU, row linear, MLP shard, attention shard, each taking shard shapes, t
+ * and rank), and why:
+ *   - Leading dimensions (ldx, lda, ldy, ldh, ldb, ldr, ldz): a rank's weight
+ *     block may be a column-block VIEW of the full weight (lda = F), and
+ *     activations may be row-strided views; the pages' shapes are the
+ *     logical ones.
+ *   - y_save (tp_mlp_shard_fwd): the pre-activation the backward needs.
+ *   - Workspace arguments and their *_workspace_bytes queries: the library
+ *     never allocates, so the caller hands in the scratch for H_i (the
+ *     intermediate's one HBM round trip) and the attention's Q/K/V/O.
+ *   - tp_mlp_shard_bwd, tp_mlp_swiglu_shard_fwd, tp_sp_reduce_scatter: the
+ *     backward, the gated variant and the sequence-parallel boundary that the
+ *     pages name beside the forward MLP (passages at each declaration).
+ *   - tp_status_string, tp_version: error text and versioning.
+ *
  * Conventions shared by every entry point.
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
  *     never allocates, frees or synchronises; it enqueues kernels on
@@ -99,6 +115,10 @@ int tp_version(void);
 
 /*
  * Column-parallel linear: Y_i = X A_i (+ a_i), then GeLU if apply_gelu.
+ * Passages: 列并行 tutorial, 切分原理 and 数学基础 (W split by output
+ * columns, X replicated, Y = [X W^(1) | ... | X W^(p)]); Megatron Level 2,
+ * M025 (W_i [h, 4h/t], output [s, b, 4h/t] with no gather when the next op
+ * consumes the shard).
  *   x      [tokens, hidden], ld ldx          (in_dt)
  *   a_i    [hidden, f], ld lda, f = ffn / t  (in_dt) -- the rank's column block
  *   bias_i [f] or NULL                       (in_dt) -- the rank's block of a
@@ -111,7 +131,9 @@ tp_status tp_column_linear(const void* x, int64_t ldx, const void* a_i, int64_t 
                            tp_dtype in_dt, tp_dtype out_dt, int apply_gelu, void* stream);
 
 /*
- * Elementwise exact GeLU, out[k] = in[k] * Phi(in[k]), k < n.  in and out may
+ * Elementwise exact GeLU, out[k] = in[k] * Phi(in[k]), k < n.  Passage:
+ * 列并行 tutorial, MLP 应用 (GeLU(z) = z Phi(z), Phi the standard normal CDF;
+ * being elementwise it acts on each column block with no communication).  in and out may
  * alias exactly (in place) when in_dt == out_dt; partial overlap is not
  * allowed.  dtype pairs: any of f32/bf16 -> f32/bf16.  n >= 0; pointers
  * 16-byte aligned.
@@ -121,6 +143,11 @@ tp_status tp_gelu(const void* in, void* out, int64_t n, tp_dtype in_dt, tp_dtype
 
 /*
  * Row-parallel linear: Z_i = H_i B_i, plus (rank 0 only) bias and residual.
+ * Passages: Megatron Level 2, M026 (W split by input rows, the input split
+ * on its last dimension, each rank's output a full-shape partial that the
+ * ranks sum); distributed-parallelism overview, 考点 2 (Z = Z_1 + Z_2 by one
+ * All-Reduce); the bias placed once outside the partials: Megatron Level 2,
+ * M025 (the bias boundary).
  *   h_i      [tokens, f], ld ldh, f = ffn / t (in_dt) -- the rank's input block
  *   b_i      [f, hidden], ld ldb              (in_dt) -- the rank's row block
  *   bias     [hidden] or NULL                 (in_dt) -- added by rank 0 only
@@ -136,7 +163,8 @@ tp_status tp_row_linear(const void* h_i, int64_t ldh, const void* b_i, int64_t l
                         tp_dtype in_dt, tp_dtype out_dt, void* stream);
 
 /*
- * Bytes of workspace tp_mlp_shard_fwd needs: the GeLU intermediate
+ * Bytes of workspace tp_mlp_shard_fwd needs (this interface's addition: the
+ * library does not allocate): the GeLU intermediate
  * H_i [tokens, f] in in_dt (bf16 for bf16 inputs, f32 for f32), rounded up to
  * 256 bytes.  Returns 0 for invalid arguments (and for tokens == 0).
  */
@@ -145,6 +173,11 @@ size_t tp_mlp_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
 
 /*
  * One rank's MLP shard: Z_i = GeLU(X A_i + a_i) B_i (+ b + R on rank 0).
+ * Passages: Tencent write-up, FFN paragraph (column layer, GeLU, row layer,
+ * one All-Reduce at the end); 列并行 tutorial, MLP 应用 (no All-Gather
+ * between the layers: f/g fusion); Megatron Level 2, M027; overview page,
+ * 第三章 (contiguous column slices of the first weight and row slices of the
+ * second with the same indices).
  *   x         [tokens, hidden] contiguous (ld = hidden)  (in_dt)
  *   a_i       [hidden, f], ld lda                          (in_dt)
  *   b_i       [f, hidden] contiguous (ld = hidden)         (in_dt)
@@ -167,7 +200,8 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
                            tp_dtype in_dt, tp_dtype out_dt, void* stream);
 
 /*
- * Bytes of workspace tp_mlp_swiglu_shard_fwd needs: H_i [tokens, f] in in_dt
+ * Bytes of workspace tp_mlp_swiglu_shard_fwd needs (the library does not
+ * allocate): H_i [tokens, f] in in_dt
  * (fp32 inputs: also the two gated projections), rounded up to 256 bytes;
  * 0 if invalid.
  */
@@ -197,7 +231,8 @@ tp_status tp_mlp_swiglu_shard_fwd(const void* x, const void* wg_i, const void* w
                                   tp_dtype in_dt, tp_dtype out_dt, void* stream);
 
 /*
- * Bytes of workspace tp_mlp_shard_bwd needs: dY_i and H_i [tokens, f] in
+ * Bytes of workspace tp_mlp_shard_bwd needs (the library does not
+ * allocate): dY_i and H_i [tokens, f] in
  * in_dt plus the column-sum partials of the bias gradients, each part
  * rounded up to 256 bytes.  Returns 0 for invalid arguments.
  */
@@ -205,7 +240,12 @@ size_t tp_mlp_shard_bwd_workspace_bytes(int64_t tokens, int64_t hidden, int64_t 
                                         tp_dtype in_dt);
 
 /*
- * Backward of one rank's MLP shard (the adjoint of tp_mlp_shard_fwd).  dz is
+ * Backward of one rank's MLP shard (the adjoint of tp_mlp_shard_fwd).
+ * Passages: Megatron Level 2, M025 (column layer: dW_i = X^T dY_i local, the
+ * input-gradient contributions SUM-reduced over the ranks) and M026 (row
+ * layer: dX_i = dY W_i^T is already the input block's gradient, dW_i local);
+ * the GeLU derivative is the product rule on z Phi(z) (列并行 tutorial,
+ * MLP 应用, for the definition).  dz is
  * dL/dZ of the summed output Z = sum over ranks of Z_r (the same tensor on
  * every rank); y_i is the rank's saved pre-activation Y_i = X A_i + a_i.
  *   dY_i      = (dz B_i^T) * GeLU'(Y_i), GeLU'(y) = Phi(y) + y phi(y)
@@ -235,14 +275,19 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const vo
                            int t, int rank, tp_dtype in_dt, tp_dtype grad_dt, void* stream);
 
 /*
- * Bytes of workspace tp_attn_shard_fwd needs (Q, K, V of the local heads and
+ * Bytes of workspace tp_attn_shard_fwd needs (the library does not allocate) (Q, K, V of the local heads and
  * the local attention output), rounded up to 256 bytes; 0 if invalid.
  */
 size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int64_t heads,
                                      int64_t head_dim, int t, tp_dtype in_dt);
 
 /*
- * One rank's head-local attention shard.
+ * One rank's head-local attention shard.  Passages: Tencent write-up,
+ * attention paragraph (QKV column-split by heads with each head's q, k, v
+ * kept together in an interleaved packed weight, local softmax(Q K^T / sqrt
+ * d) V, row-parallel output projection, one All-Reduce); Megatron Level 2,
+ * M028 (heads / t heads per rank; the softmax reduces over keys, not heads,
+ * so no exchange is needed inside attention).
  *   x       [batch, seq, hidden] contiguous                     (in_dt)
  *   wqkv_i  [hidden, 3 * hl * head_dim] contiguous, hl = heads / t: the
  *           rank's column block of the packed QKV weight, laid out per local
@@ -267,7 +312,10 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
 
 /*
  * Sequence-parallel boundary on one device: the SUM Reduce-Scatter half of
- * the exchange, fused with the shard's bias and residual.  Rank `rank`
+ * the exchange, fused with the shard's bias and residual.  Passages: Megatron
+ * Level 2, M026 and M034 (with sequence parallelism the partials' All-Reduce
+ * becomes a Reduce-Scatter that leaves each rank [s/t, b, h]; the per-token
+ * work then runs on that shard).  Rank `rank`
  * receives its sequence shard of the summed output,
  *   out_r[m, :] = sum_{j < t} Z_j[rank*M/t + m, :] + bias + residual_r[m, :],
  * m < M/t, M = tokens (rows ordered sequence-major, so the shard is the

@@ -325,7 +325,10 @@ def tp_attn_shard_fwd(x: torch.Tensor, wqkv_i: torch.Tensor, wo_i: torch.Tensor,
     dl = None if hl is None else hl * head_dim
     _expect(wqkv_i, "wqkv_i", (hidden, None if dl is None else 3 * dl), dt, w)
     _expect(wo_i, "wo_i", (dl, hidden), dt, w)
-    _expect(out_i, "out_i", (batch, seq, hidden), None, w)
+    # out_i: [batch, seq, hidden] or the same memory viewed as [batch*seq, hidden]
+    if out_i.shape[-1:] != (hidden,) or out_i.numel() != batch * seq * hidden:
+        raise ValueError(f"{w}: out_i has shape {tuple(out_i.shape)}, expected "
+                         f"[{batch}x{seq}x{hidden}] (or [{batch * seq}x{hidden}])")
     _contiguous(w, x=x, wqkv_i=wqkv_i, wo_i=wo_i, out_i=out_i)
     _workspace(workspace, w)
     _on_one_gpu(w, x=x, wqkv_i=wqkv_i, wo_i=wo_i, out_i=out_i, workspace=workspace)

@@ -12,6 +12,7 @@
 #include <climits>
 
 #include "../../include/tp_shard.h"
+#include "abi_internal.h"
 #include "kernels.h"
 
 namespace {
@@ -97,6 +98,50 @@ tp_status run_gemm_t(tp_dtype in_dt, const void* a, int64_t lda, bool a_kmajor, 
 size_t round256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
+
+namespace tpabi {
+
+tp_status mlp_fwd_validate(const void* x, const void* a_i, int64_t lda, const void* b_i,
+                           const void* bias_a_i, const void* bias_b, const void* residual,
+                           const void* z_i, const void* y_save, int64_t tokens, int64_t hidden,
+                           int64_t ffn, int t, int rank, tp_dtype in_dt, tp_dtype out_dt,
+                           int64_t* f_out) {
+  if (!dtype_known(in_dt) || !dtype_known(out_dt) || !gemm_pair_ok(in_dt, out_dt))
+    return TP_ERR_DTYPE;
+  if (tokens < 0 || hidden < 1) return TP_ERR_INVALID_ARG;
+  int64_t f = 0;
+  TP_TRY(check_split(ffn, t, rank, &f));
+  if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(f)) return TP_ERR_UNSUPPORTED;
+  *f_out = f;
+  if (tokens == 0) return TP_OK;
+  TP_TRY(check_matrix(x, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(a_i, lda, f, in_dt));
+  TP_TRY(check_matrix(b_i, hidden, hidden, in_dt));
+  TP_TRY(check_matrix(z_i, hidden, hidden, out_dt));
+  if (y_save != nullptr) TP_TRY(check_matrix(y_save, f, f, in_dt));
+  TP_TRY(check_optional_vec(bias_a_i));
+  const bool owner = rank == 0;
+  TP_TRY(check_optional_vec(owner ? bias_b : nullptr));
+  TP_TRY(check_optional_vec(owner ? residual : nullptr));
+  return TP_OK;
+}
+
+tp_status mlp_fwd_enqueue(const void* x, const void* a_i, int64_t lda, const void* b_i,
+                          const void* bias_a_i, const void* bias_use, const void* res_use,
+                          void* z_i, void* y_save, void* h, int64_t tokens, int64_t hidden,
+                          int64_t f, tp_dtype in_dt, tp_dtype out_dt, hipStream_t s) {
+  // Column-parallel GEMM with GeLU fused into its epilogue: H_i = GeLU(X A_i + a_i)
+  // stored once in h (bf16 for bf16 inputs, fp32 for fp32); the
+  // pre-activation also goes to y_save when asked for.
+  tpk::Epilogue ep1{bias_a_i, nullptr, 0, h, f, in_dt == TP_F32, tpk::EPI_GELU};
+  ep1.pre = y_save;
+  TP_TRY(run_gemm(in_dt, x, hidden, a_i, lda, tokens, f, hidden, ep1, s));
+  // Row-parallel GEMM: Z_i = H_i B_i (+ b + R on rank 0).
+  tpk::Epilogue ep2{bias_use, res_use, hidden, z_i, hidden, out_dt == TP_F32, tpk::EPI_LINEAR};
+  return run_gemm(in_dt, h, f, b_i, hidden, tokens, hidden, f, ep2, s);
+}
+
+}  // namespace tpabi
 
 extern "C" {
 
@@ -193,38 +238,16 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
                            int64_t tokens,
                            int64_t hidden, int64_t ffn, int t, int rank, tp_dtype in_dt,
                            tp_dtype out_dt, void* stream) {
-  if (!dtype_known(in_dt) || !dtype_known(out_dt) || !gemm_pair_ok(in_dt, out_dt))
-    return TP_ERR_DTYPE;
-  if (tokens < 0 || hidden < 1) return TP_ERR_INVALID_ARG;
   int64_t f = 0;
-  TP_TRY(check_split(ffn, t, rank, &f));
-  if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(f)) return TP_ERR_UNSUPPORTED;
+  TP_TRY(tpabi::mlp_fwd_validate(x, a_i, lda, b_i, bias_a_i, bias_b, residual, z_i, y_save, tokens,
+                                 hidden, ffn, t, rank, in_dt, out_dt, &f));
   if (tokens == 0) return TP_OK;
-  TP_TRY(check_matrix(x, hidden, hidden, in_dt));
-  TP_TRY(check_matrix(a_i, lda, f, in_dt));
-  TP_TRY(check_matrix(b_i, hidden, hidden, in_dt));
-  TP_TRY(check_matrix(z_i, hidden, hidden, out_dt));
-  if (y_save != nullptr) TP_TRY(check_matrix(y_save, f, f, in_dt));
-  TP_TRY(check_optional_vec(bias_a_i));
-  const bool owner = rank == 0;
-  const void* bias_use = owner ? bias_b : nullptr;
-  const void* res_use = owner ? residual : nullptr;
-  TP_TRY(check_optional_vec(bias_use));
-  TP_TRY(check_optional_vec(res_use));
   const size_t need = tp_mlp_shard_workspace_bytes(tokens, hidden, ffn, t, in_dt);
   if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // Column-parallel GEMM with GeLU fused into its epilogue: H_i = GeLU(X A_i + a_i)
-  // stored once in the workspace (bf16 for bf16 inputs, fp32 for fp32); the
-  // pre-activation also goes to y_save when asked for.
-  tpk::Epilogue ep1{bias_a_i, nullptr, 0, workspace, f, in_dt == TP_F32, tpk::EPI_GELU};
-  ep1.pre = y_save;
-  TP_TRY(run_gemm(in_dt, x, hidden, a_i, lda, tokens, f, hidden, ep1, s));
-  // Row-parallel GEMM: Z_i = H_i B_i (+ b + R on rank 0).
-  tpk::Epilogue ep2{bias_use, res_use, hidden, z_i, hidden, out_dt == TP_F32, tpk::EPI_LINEAR};
-  return run_gemm(in_dt, workspace, f, b_i, hidden, tokens, hidden, f, ep2, s);
+  return tpabi::mlp_fwd_enqueue(x, a_i, lda, b_i, bias_a_i, rank == 0 ? bias_b : nullptr,
+                                rank == 0 ? residual : nullptr, z_i, y_save, workspace, tokens,
+                                hidden, f, in_dt, out_dt, static_cast<hipStream_t>(stream));
 }
 
 
