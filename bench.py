@@ -331,7 +331,12 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str, mfma_csv:
         wb = med(write, key, lambda us, c: c["WRITE_SIZE"]) * 1024 * w_scale
         util = med(mfma, key, lambda us, c: c["SQ_VALU_MFMA_BUSY_CYCLES"] /
                    (c["GRBM_GUI_ACTIVE"] / N_XCD * N_SIMD))
+        # the counters' window is a few microseconds wider than the dispatch's
+        # timestamps (short launches come out above the 2.4 GHz maximum), so
+        # the clock is quoted for launches of 150 us and more only
         sclk = med(mfma, key, lambda us, c: c["GRBM_GUI_ACTIVE"] / N_XCD / (us * 1e3))
+        if sclk is not None and med(mfma, key, lambda us, c: us) < 150.0:
+            sclk = None
         mflops = med(mfma, key, lambda us, c: c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0)
         us = [d for d, _ in durs[key]]
         avg_us = statistics.mean(us)
@@ -371,12 +376,16 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str, mfma_csv:
                    f"{live['avg_us']:.1f} us -> frac {flops / (live['avg_us'] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f} |"]
         if util is not None:
             md += [f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs), median) | "
-                   f"{100 * util:.1f}% |",
-                   f"| shader clock (GRBM_GUI_ACTIVE / 8 / duration, median) | {sclk:.3f} GHz |"]
+                   f"{100 * util:.1f}% |"]
+            md += [f"| shader clock (GRBM_GUI_ACTIVE / 8 / duration, median) | {sclk:.3f} GHz |"
+                   if sclk is not None else
+                   "| shader clock | not quoted: the counter window exceeds a launch this short |"]
             if flops:
                 md += [f"| MFMA FLOP per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {mflops / 1e9:.1f} G "
-                       f"({mflops / flops:.3f} x algorithmic) |",
-                       f"| peak at that clock (2516.6 x clock / 2.4 GHz) | {PEAK_BF16_TFLOPS * sclk / 2.4:.1f} TFLOP/s |"]
+                       f"({mflops / flops:.3f} x algorithmic) |"]
+                if sclk is not None:
+                    md += [f"| peak at that clock (2516.6 x clock / 2.4 GHz) | "
+                           f"{PEAK_BF16_TFLOPS * sclk / 2.4:.1f} TFLOP/s |"]
         md += [f"| FETCH_SIZE per dispatch (median) | {fb / 1024 / f_scale:.0f} KiB (x{f_scale:.3f} from the 1 GiB copy) |",
                f"| WRITE_SIZE per dispatch (median) | {wb / 1024 / w_scale:.0f} KiB (x{w_scale:.3f}) |",
                f"| HBM bytes per launch (scaled) | {(fb + wb) / 1e6:.1f} MB (fetch {fb / 1e6:.1f}, write {wb / 1e6:.1f}) |",
@@ -934,6 +943,7 @@ def main() -> int:
     line = json.dumps(result)
     print(line, flush=True)
     if args.json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
         with open(args.json_out, "w") as fh:
             fh.write(line + "\n")
     return 0
