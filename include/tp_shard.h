@@ -200,6 +200,35 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
                            tp_dtype in_dt, tp_dtype out_dt, void* stream);
 
 /*
+ * Size of the library's fixed device array used by tp_mlp_shard_fwd_noalloc
+ * (one copy per GPU the library runs on, held until the process ends).
+ */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * tp_mlp_shard_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and errors without the workspace; the GeLU
+ * intermediate H_i lives in the library's own TP_NOALLOC_SCRATCH_BYTES device
+ * array.  Nothing is allocated, freed or synchronised.
+ *   Tokens are processed in row chunks whose H_i fits the array, so any
+ *   tokens works; the shard width is limited instead: if fewer than
+ *   min(tokens, 256) rows of H_i fit (f * element size > 256 KiB, i.e.
+ *   f > 131072 in bf16 or 65536 in fp32) the call returns TP_ERR_WORKSPACE.
+ *   The array's address on the current device is looked up on the first
+ *   call on that device (the stream must belong to the current device); a
+ *   failed lookup returns TP_ERR_HIP.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (on other streams or threads) race and must be serialised by the
+ *   caller.  Nothing in the array needs to start zeroed.
+ */
+tp_status tp_mlp_shard_fwd_noalloc(const void* x, const void* a_i, int64_t lda, const void* b_i,
+                                   const void* bias_a_i, const void* bias_b, const void* residual,
+                                   void* z_i, void* y_save, int64_t tokens, int64_t hidden,
+                                   int64_t ffn, int t, int rank, tp_dtype in_dt, tp_dtype out_dt,
+                                   void* stream);
+
+/*
  * Bytes of workspace tp_mlp_swiglu_shard_fwd needs (the library does not
  * allocate): H_i [tokens, f] in in_dt
  * (fp32 inputs: also the two gated projections), rounded up to 256 bytes;

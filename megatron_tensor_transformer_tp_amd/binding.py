@@ -38,6 +38,8 @@ SIGNATURES = {
     "tp_mlp_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "tp_mlp_shard_fwd": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I64,
                                 _I64, _I64, _INT, _INT, _INT, _INT, _VP]),
+    "tp_mlp_shard_fwd_noalloc": (_INT, [_VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64,
+                                        _I64, _INT, _INT, _INT, _INT, _VP]),
     "tp_mlp_swiglu_shard_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "tp_mlp_swiglu_shard_fwd": (_INT, [_VP, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _SZ, _I64,
                                        _I64, _I64, _INT, _INT, _INT, _INT, _VP]),
@@ -263,6 +265,23 @@ def tp_mlp_shard_fwd(x: torch.Tensor, a_i: torch.Tensor, b_i: torch.Tensor, z_i:
                                   _ptr(bias_b), _ptr(residual), _ptr(z_i), _ptr(y_save),
                                   _ptr(workspace), _nbytes(workspace), tokens, hidden, ffn,
                                   t, rank, _dt(x), _dt(z_i), _stream(stream)), w)
+    return z_i
+
+
+def tp_mlp_shard_fwd_noalloc(x: torch.Tensor, a_i: torch.Tensor, b_i: torch.Tensor, z_i: torch.Tensor,
+                             *, ffn: int, t: int, rank: int, bias_a_i: Optional[torch.Tensor] = None,
+                             bias_b: Optional[torch.Tensor] = None,
+                             residual: Optional[torch.Tensor] = None,
+                             y_save: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """As tp_mlp_shard_fwd, with H_i in the library's fixed device array instead of a
+    workspace (allocates nothing; calls overlapping on one GPU race)."""
+    w = "tp_mlp_shard_fwd_noalloc"
+    tokens, hidden = _mlp_fwd_checks(w, x, a_i, b_i, z_i, None, ffn, t, bias_a_i, bias_b,
+                                     residual, y_save)
+    _check(lib().tp_mlp_shard_fwd_noalloc(_ptr(x), _ptr(a_i), _rows(a_i, "a_i"), _ptr(b_i),
+                                          _ptr(bias_a_i), _ptr(bias_b), _ptr(residual), _ptr(z_i),
+                                          _ptr(y_save), tokens, hidden, ffn, t, rank, _dt(x), _dt(z_i),
+                                          _stream(stream)), w)
     return z_i
 
 

@@ -37,6 +37,7 @@ SOURCES = [
     "sp_reduce.hip",
     "gelu.hip",
     "attention.hip",
+    "noalloc.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
