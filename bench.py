@@ -144,8 +144,9 @@ PROFILE_CMDS = {
               "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
     "write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d rocprof_out/pmc_write -o pmc -- "
               "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2 --calibrate-copy"),
-    "mfma": ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE "
-             "GRBM_COUNT --output-format csv -d rocprof_out/pmc_mfma -o pmc -- "
+    "mfma": ("rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+             "SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE GRBM_COUNT --output-format csv "
+             "-d rocprof_out/pmc_mfma -o pmc -- "
              "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --kernel-reps 2"),
 }
 # The device's SIMD count and XCD count (MI355X: 256 CUs x 4 SIMDs, 8 XCDs):
@@ -337,7 +338,8 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str, mfma_csv:
         sclk = med(mfma, key, lambda us, c: c["GRBM_GUI_ACTIVE"] / N_XCD / (us * 1e3))
         if sclk is not None and med(mfma, key, lambda us, c: us) < 150.0:
             sclk = None
-        mflops = med(mfma, key, lambda us, c: c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0)
+        mflops = med(mfma, key, lambda us, c: (c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] +
+                                               c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)) * 512.0)
         us = [d for d, _ in durs[key]]
         avg_us = statistics.mean(us)
         ent = {"hbm_bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb), "write_bytes": int(wb),
@@ -381,7 +383,7 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str, mfma_csv:
                    if sclk is not None else
                    "| shader clock | not quoted: the counter window exceeds a launch this short |"]
             if flops:
-                md += [f"| MFMA FLOP per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {mflops / 1e9:.1f} G "
+                md += [f"| MFMA FLOP per launch ((SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F16) x 512) | {mflops / 1e9:.1f} G "
                        f"({mflops / flops:.3f} x algorithmic) |"]
                 if sclk is not None:
                     md += [f"| peak at that clock (2516.6 x clock / 2.4 GHz) | "
@@ -828,15 +830,19 @@ def main() -> int:
     }
     step()
     torch.cuda.synchronize()
+    # one event between consecutive launches (chained), so that each launch's
+    # interval carries one event record rather than two
     events = {name: [] for name in kernels}
+    prev = torch.cuda.Event(enable_timing=True)
+    prev.record(stream)
     for _ in range(args.kernel_reps):
         for r in range(wl.t):
             for name, (fn, _f, _b) in kernels.items():
-                k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                k0.record(stream)
                 fn(r)
-                k1.record(stream)
-                events[name].append((k0, k1))
+                nxt = torch.cuda.Event(enable_timing=True)
+                nxt.record(stream)
+                events[name].append((prev, nxt))
+                prev = nxt
     torch.cuda.synchronize()
     per_kernel = {}
     for name, (fn, flops, nbytes) in kernels.items():

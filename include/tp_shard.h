@@ -330,8 +330,10 @@ size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden,
  * dtype pairs: bf16 -> f32, bf16 -> bf16.  head_dim must be 128 and seq a
  * multiple of 128 (TP_ERR_UNSUPPORTED otherwise).  Q and K enter Q K^T as
  * fp16 (11 significant bits) scaled by 2^-8, so |q|, |k| must stay below
- * 2^24 (larger values overflow); V, the softmax weights and O are bf16
- * operands; every product accumulates in fp32.
+ * 2^24: a larger value overflows to infinity, and the rows of every query
+ * whose scores it reaches come out non-finite (Inf / NaN), never finite and
+ * wrong; V, the softmax weights and O are bf16 operands; every product
+ * accumulates in fp32.
  */
 tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i, void* out_i,
                             void* workspace, size_t workspace_bytes,

@@ -82,12 +82,10 @@ static_assert(kWaves / 2 * 64 * 66 * 4 <= kStages * kStage, "merge area");
 static_assert(kQkvPart == kD, "q / k / v parts of head_dim columns");
 
 // One global->LDS copy with a uniform base (SGPR pair) and a per-lane 32-bit
-// byte offset: lane t's 16 bytes land at LDS byte address lds_addr + 16 t.
+// byte offset: lane t's 16 bytes land at LDS byte address lds_addr + 16 t
+// (lds_addr bound to M0 as an input, written by the compiler).
 __device__ __forceinline__ void copy_to_lds_off(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(lds_addr)
-               : "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds_addr));
 }
 
 // The values of lanes l % 32 and l % 32 + 32 (lane l and its partner l ^ 32),

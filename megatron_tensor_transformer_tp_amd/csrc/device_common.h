@@ -96,20 +96,16 @@ __device__ __forceinline__ float silu_f32(float z) {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // One 1 KiB global->LDS copy: lane t's 16 bytes from `src` land at LDS byte
-// address lds_addr + 16 t (lds_addr uniform, loaded into M0).  Issued as
-// inline assembly so that the compiler does not treat it as an LDS store:
-// left to itself it would make later LDS reads of *other* stages wait for
-// every copy in flight (s_waitcnt vmcnt(0)), which defeats the pipeline.
-// Ordering against LDS reads is explicit instead: wait_vmcnt + lds_barrier.
-// The compiler warns that M0 is a reserved register in the clobber list: it
-// keeps no value of its own in M0 in these kernels (gfx950 LDS instructions
-// do not use it; in the generated code of every kernel that copies, each M0
-// reference is this sequence's write), so nothing live is overwritten.
+// address lds_addr + 16 t (lds_addr uniform, in M0).  Issued as inline
+// assembly so that the compiler does not treat it as an LDS store: left to
+// itself it would make later LDS reads of *other* stages wait for every copy
+// in flight (s_waitcnt vmcnt(0)), which defeats the pipeline.  Ordering
+// against LDS reads is explicit instead: wait_vmcnt + lds_barrier.  The LDS
+// address is an input bound to M0 ("{m0}"), so the compiler writes M0 itself
+// and knows the instruction reads it; the s_nop separates that write from
+// the copy.
 __device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_addr)
-               : "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr));
 }
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {

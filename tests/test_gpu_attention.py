@@ -112,6 +112,29 @@ def test_errors_and_empty():
     torch.cuda.synchronize()
 
 
+def test_projection_overflow_is_never_finite_and_wrong():
+    """X scaled by 2^24: Q and K exceed the scaled fp16 range (|q|, |k| >=
+    2^24).  Every output row is then either non-finite or still within the
+    bound of the oracle's (fp64, no overflow) result: an overflow is never a
+    finite wrong answer."""
+    wl = inputs.ATTN_WORKLOADS["attn_t2_h1024_b3_s128"]
+    x = x_all(wl)
+    xs = inputs.f32_to_bf16_bits(inputs.bf16_bits_to_f32(x) * np.float32(2.0 ** 24))
+    wqkv, wo = inputs.attn_wqkv_block(wl, 0), inputs.attn_wo_block(wl, 0)
+    say("attn_t2_h1024_b3_s128 rank 0 with X scaled by 2^24 (fp16 Q/K overflow)")
+    out = to_np(run(wl, 0, dev(xs, "bf16"), dev(wqkv, "bf16"), dev(wo, "bf16"), False))
+    ref = oracle.attn_shard(host64(xs, "bf16"), host64(wqkv, "bf16"), host64(wo, "bf16"), wl.heads,
+                            wl.head_dim, wl.t, 0, False)
+    rows_out, rows_ref = out.reshape(-1, wl.hidden), ref.reshape(-1, wl.hidden)
+    bad = ~np.isfinite(rows_out).all(axis=1)
+    assert bad.any(), "an overflow this large must reach some row"
+    ok = rows_out[~bad]
+    if ok.size:
+        d = np.abs(ok - rows_ref[~bad]) / (1.0 + np.abs(rows_ref[~bad]))
+        assert d.max() <= 2e-2, "a finite row differs from the oracle"
+    say(f"overflow: {bad.sum()} of {len(bad)} rows non-finite, the rest within the bound")
+
+
 def _attn_shapes(seed, n):
     """n seeded shard shapes: batch 1-3, seq a multiple of 128 up to 1152
     (1-36 key blocks of 32, so the loop unrolled by 4 ends at every phase),
