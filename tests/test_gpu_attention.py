@@ -79,19 +79,19 @@ def test_small_bf16_output():
 
 
 @pytest.mark.parametrize("rank,causal", [(0, False), (7, True)])
-def test_large_sampled_rows(rank, causal):
-    """hidden 8192, 64 heads, t=8, seq 4096: the whole shard runs on the GPU;
-    the oracle computes sampled query rows (each depends on all keys)."""
+def test_large_full(rank, causal):
+    """hidden 8192, 64 heads, t=8, seq 4096 (the attention workload the
+    benchmark times): every element of the rank's fp32 partial against the
+    fp64 oracle (~5 s of host time per shard)."""
     wl = inputs.ATTN_WORKLOADS["attn_t8_h8192_s4096"]
     x = x_all(wl)
     wqkv, wo = inputs.attn_wqkv_block(wl, rank), inputs.attn_wo_block(wl, rank)
-    say(f"attn_t8_h8192_s4096 rank {rank} causal={causal}")
+    say(f"attn_t8_h8192_s4096 rank {rank} causal={causal}: all 4096 x 8192 outputs")
     out = to_np(run(wl, rank, dev(x, "bf16"), dev(wqkv, "bf16"), dev(wo, "bf16"), causal))
     assert np.isfinite(out).all()
-    rows = np.r_[0:64, 1000:1064, 4032:4096]
     ref = oracle.attn_shard(host64(x, "bf16"), host64(wqkv, "bf16"), host64(wo, "bf16"), wl.heads,
-                            wl.head_dim, wl.t, rank, causal, rows=rows)
-    assert_close(out[:, rows, :], ref, "bf16", f"large rank {rank} causal={causal} sampled rows")
+                            wl.head_dim, wl.t, rank, causal)
+    assert_close(out, ref, "bf16", f"large rank {rank} causal={causal} full shard")
 
 
 def test_errors_and_empty():
