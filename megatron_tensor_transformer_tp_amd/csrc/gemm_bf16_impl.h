@@ -12,10 +12,11 @@
 // bias/residual epilogue (列并行 tutorial, 数学基础 and MLP 应用; Megatron
 // expert interview Level 2, M025/M026).
 //
-//   * Operand roles inside the MFMA (v_mfma_f32_32x32x16_bf16) are swapped
-//     (the B fragment is the MFMA's first operand, the A fragment the second),
-//     so each lane ends up owning 4 CONSECUTIVE output columns of one row: the
-//     epilogue stores 16-byte fp32 or 8-byte bf16 vectors.
+//   * Operand roles inside the MFMA (v_mfma_f32_16x16x32_bf16, or
+//     v_mfma_f32_32x32x16_bf16) are swapped (the B fragment is the MFMA's
+//     first operand, the A fragment the second), so each lane ends up owning
+//     4 CONSECUTIVE output columns of one row: the epilogue stores 16-byte
+//     fp32 or 8-byte bf16 vectors.
 //   * Workgroup -> tile mapping is XCD-aware: consecutive workgroup ids are
 //     dealt round-robin to the 8 XCDs, so ids are first regrouped so that
 //     each XCD owns a contiguous range of logical tiles, then tiles are
@@ -93,9 +94,13 @@ __device__ __forceinline__ void sched_group() {
 }
 
 // Epilogue shared by the GEMM kernels.  acc[j][i][4g + r] is C[m][n] with
-//   m = m_lane + i*32,  n = n_lane + j*32 + 8g + r,
+//   m = m_lane + i*32 + row_of(g),  n = n_lane + j*32 + col_of(g) + r,
 // i.e. each lane owns 4 consecutive columns per (i, j, g): one 16-byte fp32
-// or 8-byte bf16 store.  EPI selects the epilogue kind at compile time; the
+// or 8-byte bf16 store.  32 x 32 x 16 MFMA blocks: row_of(g) = 0,
+// col_of(g) = 8g (lanes l and l + 32 hold columns 4 apart), m_lane = .. + l % 32.
+// 16 x 16 x 32 MFMA blocks (MF16, four per 32 x 32 block, sub-block g at
+// rows 16 (g / 2), columns 16 (g % 2)): m_lane = .. + l % 16 and
+// n_lane = .. + 4 (l / 16).  EPI selects the epilogue kind at compile time; the
 // optional inputs (bias, residual) are uniform, so each combination's body is
 // instantiated once and selected with one branch (the GeLU kinds never take
 // a residual).
@@ -118,7 +123,12 @@ __device__ __forceinline__ void store_x4(void* base, int64_t off, const float (&
   }
 }
 
-template <int TM, int TN, bool MASKED, int EPI, bool OUT_F32>
+template <bool MF16>
+__device__ __forceinline__ constexpr int row_of(int g) { return MF16 ? 16 * (g >> 1) : 0; }
+template <bool MF16>
+__device__ __forceinline__ constexpr int col_of(int g) { return MF16 ? 16 * (g & 1) : 8 * g; }
+
+template <int TM, int TN, bool MASKED, int EPI, bool OUT_F32, bool MF16 = false>
 __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_lane, int n_lane,
                                            int M, int N, const Epilogue& ep) {
   const uint16_t* __restrict__ bias = static_cast<const uint16_t*>(ep.bias);
@@ -129,15 +139,16 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
     constexpr bool kRes = decltype(has_res)::value;
     constexpr bool kExtra = decltype(has_extra)::value;   // pre (GeLU)
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      const int m = m_lane + I * 32;
-      if (MASKED && m >= M) return;
-      const int64_t row_out = static_cast<int64_t>(m) * ep.ldo + n_lane;
-      const int64_t row_res = kRes ? static_cast<int64_t>(m) * ep.ldr + n_lane : 0;
-      const int64_t row_aux = EPI == EPI_GELU_BWD ? static_cast<int64_t>(m) * ep.ldaux + n_lane : 0;
+      const int m_i = m_lane + I * 32;
+      if (!MF16 && MASKED && m_i >= M) return;
       static_for<TN>([&](auto J) __attribute__((always_inline)) {
         static_for<4>([&](auto G) __attribute__((always_inline)) {
-          constexpr int col = J * 32 + G * 8;
-          if (MASKED && n_lane + col >= N) return;
+          constexpr int col = J * 32 + col_of<MF16>(G);
+          const int m = m_i + row_of<MF16>(G);
+          if (MASKED && ((MF16 && m >= M) || n_lane + col >= N)) return;
+          const int64_t row_out = static_cast<int64_t>(m) * ep.ldo + n_lane;
+          const int64_t row_res = kRes ? static_cast<int64_t>(m) * ep.ldr + n_lane : 0;
+          const int64_t row_aux = EPI == EPI_GELU_BWD ? static_cast<int64_t>(m) * ep.ldaux + n_lane : 0;
           float v[4];
           static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] = acc[J][I][4 * G + R]; });
           if constexpr (EPI == EPI_QKV_F16) {
@@ -192,17 +203,19 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
     // forms acc * GeLU'(y) and GeLU(y).
     u32x2_t yv[TM][TN][4];
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      const int64_t row_aux = static_cast<int64_t>(m_lane + I * 32) * ep.ldaux + n_lane;
       static_for<TN>([&](auto J) __attribute__((always_inline)) {
         static_for<4>([&](auto G) __attribute__((always_inline)) {
-          yv[I][J][G] = *reinterpret_cast<const u32x2_t*>(aux + row_aux + J * 32 + G * 8);
+          const int64_t row_aux =
+              static_cast<int64_t>(m_lane + I * 32 + row_of<MF16>(G)) * ep.ldaux + n_lane;
+          yv[I][J][G] = *reinterpret_cast<const u32x2_t*>(aux + row_aux + J * 32 + col_of<MF16>(G));
         });
       });
     });
     static_for<TM>([&](auto I) __attribute__((always_inline)) {
-      const int64_t row_out = static_cast<int64_t>(m_lane + I * 32) * ep.ldo + n_lane;
       static_for<TN>([&](auto J) __attribute__((always_inline)) {
         static_for<4>([&](auto G) __attribute__((always_inline)) {
+          const int64_t row_out =
+              static_cast<int64_t>(m_lane + I * 32 + row_of<MF16>(G)) * ep.ldo + n_lane;
           const float y[4] = {__uint_as_float(yv[I][J][G][0] << 16),
                               __uint_as_float(yv[I][J][G][0] & 0xFFFF0000u),
                               __uint_as_float(yv[I][J][G][1] << 16),
@@ -212,8 +225,8 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
             v[R] = acc[J][I][4 * G + R] * gelu_grad_f32(y[R]);
             h[R] = gelu_f32(y[R]);
           });
-          store_x4<OUT_F32>(ep.out, row_out + J * 32 + G * 8, v);
-          store_x4<OUT_F32>(ep.out2, row_out + J * 32 + G * 8, h);
+          store_x4<OUT_F32>(ep.out, row_out + J * 32 + col_of<MF16>(G), v);
+          store_x4<OUT_F32>(ep.out2, row_out + J * 32 + col_of<MF16>(G), h);
         });
         sched_fence();
       });
