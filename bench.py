@@ -163,7 +163,7 @@ N_SIMD, N_XCD = 1024, 8
 # workload, and the summary's file stem.  GEMM template arguments: tile BM,
 # BN, wave grid, LDS stages, A k-major, B k-major, epilogue kind, fp32 output,
 # K tail (false: K % 32 == 0), paired stages (0: none, 1: B, 2: A; a
-# k-contiguous operand with K % 64 == 0).
+# k-contiguous operand with K % 64 == 0), MFMA (true: 16 x 16 x 32).
 _M, _H, _F = 16384, 8192, 4096          # MLP shard: tokens, hidden, f = ffn / t
 _M3 = 4096                              # the 4096-token rank shard
 _M2, _H2, _F2 = 2048, 1024, 4096        # the t = 1 MLP: tokens, hidden, ffn
@@ -172,28 +172,28 @@ _GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "   # then A k-major, B k-major
 _GEMM128 = "gemm_bf16_dma_kernel<128, 128, 2, 2, 4, "
 _INF = 1e9
 PROFILED = {
-    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0>", (500.0, _INF),
+    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0, true>", (500.0, _INF),
                          2.0 * _M * _H * _F, 2 * (_M * _H + _H * _F + _M * _F),
                          "MLP rank shard, M=16384, h=8192, f=4096: X, A_i read, H_i written (bf16)",
                          "column_gemm_gelu_t8_h8192_m16384"),
-    "row_gemm": (_GEMM + "false, true, 0, true, false, 0>", (500.0, _INF),
+    "row_gemm": (_GEMM + "false, true, 0, true, false, 0, true>", (500.0, _INF),
                  2.0 * _M * _F * _H, 2 * (_M * _F + _F * _H) + 4 * _M * _H,
                  "MLP rank shard, M=16384, h=8192, f=4096: H_i, B_i read (bf16), Z_i written (fp32)",
                  "row_gemm_t8_h8192_m16384"),
-    "t8_h8192_m4096:column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0>", (100.0, 500.0),
+    "t8_h8192_m4096:column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0, true>", (100.0, 500.0),
                                         2.0 * _M3 * _H * _F, 2 * (_M3 * _H + _H * _F + _M3 * _F),
                                         "rank 0 of t=8, M=4096, h=8192, f=4096: X, A_0 read, H_0 written (bf16)",
                                         "column_gemm_gelu_t8_h8192_m4096"),
-    "t8_h8192_m4096:row_gemm": (_GEMM + "false, true, 0, true, false, 0>", (140.0, 500.0),
+    "t8_h8192_m4096:row_gemm": (_GEMM + "false, true, 0, true, false, 0, true>", (140.0, 500.0),
                                 2.0 * _M3 * _F * _H, 2 * (_M3 * _F + _F * _H) + 4 * _M3 * _H,
                                 "rank 0 of t=8, M=4096, h=8192, f=4096: H_0, B_0 read (bf16), Z_0 written (fp32)",
                                 "row_gemm_t8_h8192_m4096"),
-    "t1_h1024_m2048:column_gemm_gelu": (_GEMM128 + "false, true, 1, false, false, 2>", (0.0, _INF),
+    "t1_h1024_m2048:column_gemm_gelu": (_GEMM128 + "false, true, 1, false, false, 2, true>", (0.0, _INF),
                                         2.0 * _M2 * _H2 * _F2, 2 * (_M2 * _H2 + _H2 * _F2 + _M2 * _F2),
                                         "t=1 MLP, M=2048, h=1024, ffn=4096 (128 x 128 tiles): X, A read, "
                                         "H written (bf16)",
                                         "column_gemm_gelu_t1_h1024_m2048"),
-    "t1_h1024_m2048:row_gemm": (_GEMM128 + "false, true, 0, false, false, 2>", (0.0, _INF),
+    "t1_h1024_m2048:row_gemm": (_GEMM128 + "false, true, 0, false, false, 2, true>", (0.0, _INF),
                                 2.0 * _M2 * _F2 * _H2, 2 * (_M2 * _F2 + _F2 * _H2) + 2 * _M2 * _H2,
                                 "t=1 MLP, M=2048, ffn=4096, h=1024 (128 x 128 tiles): H, B read, "
                                 "Z written (bf16 final output)",
@@ -203,12 +203,12 @@ PROFILED = {
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K "
                        "(fp16) and V (bf16) read once, O written (bf16)",
                        "attention_core_t8_h8192_s4096"),
-    "attn_qkv_gemm": ("gemm_bf16_dma_kernel<128, 384, 2, 4, 4, false, true, 4, false, false, 2>", (0.0, _INF),
+    "attn_qkv_gemm": ("gemm_bf16_dma_kernel<128, 384, 2, 4, 4, false, true, 4, false, false, 2, true>", (0.0, _INF),
                       2.0 * _S * _H * 3 * _DL, 2 * (_S * _H + _H * 3 * _DL + _S * 3 * _DL),
                       "attention rank shard packed QKV projection, M=4096, K=8192, N=3072 "
                       "(one round of 256 128 x 384 tiles), q/k written as scaled fp16, v as bf16",
                       "attn_qkv_gemm_t8_h8192_s4096"),
-    "attn_out_gemm": (_GEMM + "false, true, 0, true, false, 0>", (0.0, 140.0),
+    "attn_out_gemm": (_GEMM + "false, true, 0, true, false, 0, true>", (0.0, 140.0),
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
                       "attention rank shard output projection, M=4096, K=1024, N=8192 (fp32 out)",
                       "attn_out_gemm_t8_h8192_s4096"),
@@ -218,23 +218,23 @@ PROFILED = {
                           "rank's [2048, 8192] shard with bf16 bias and residual rows, bf16 out "
                           "(HBM-bound: partial rows, residual and bias read, shard written)",
                           "sp_reduce_scatter_t8_h8192_m16384"),
-    "swiglu_gemm": (_GEMM + "false, true, 3, false, false, 0>", (0.0, _INF),
+    "swiglu_gemm": (_GEMM + "false, true, 3, false, false, 0, true>", (0.0, _INF),
                     2.0 * _M * _H * 2 * _F, 2 * (_M * _H + 2 * _H * _F + _M * _F),
                     "SwiGLU column layer, both projections in one product with SiLU(gate) * value "
                     "in the epilogue: X, Wg_i, Wu_i read, H_i written (bf16)",
                     "swiglu_gemm_t8_h8192_m16384"),
-    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false, false, 1>", (0.0, _INF),
+    "bwd_dgelu_gemm": (_GEMM + "false, false, 2, false, false, 1, true>", (0.0, _INF),
                        2.0 * _M * _H * _F, 2 * (_M * _H + _F * _H + _M * _F) + 2 * 2 * _M * _F,
                        "MLP shard backward dH = dZ B_i^T with dY_i = dH * GeLU'(Y_i) and H_i = "
                        "GeLU(Y_i) in the epilogue: dZ, B_i, Y_i read, dY_i and H_i written (bf16)",
                        "bwd_dgelu_gemm_t8_h8192_m16384"),
-    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true, false, 0>", (0.0, _INF),
+    "bwd_weight_grad_gemm": (_GEMM + "true, true, 0, true, false, 0, true>", (0.0, _INF),
                              2.0 * _M * _H * _F, 2 * (_M * _F + _M * _H) + 4 * _F * _H,
                              "MLP shard backward weight gradients H_i^T dZ and X^T dY_i (one "
                              "kernel, K = 16384 tokens): two bf16 operands read, fp32 [4096 x 8192] "
                              "written; both launches averaged",
                              "bwd_weight_grad_gemm_t8_h8192_m16384"),
-    "bwd_dx_gemm": (_GEMM + "false, false, 0, true, false, 1>", (0.0, _INF),
+    "bwd_dx_gemm": (_GEMM + "false, false, 0, true, false, 1, true>", (0.0, _INF),
                     2.0 * _M * _F * _H, 2 * (_M * _F + _H * _F) + 4 * _M * _H,
                     "MLP shard backward dX_i = dY_i A_i^T: dY_i, A_i read (bf16), dX_i written (fp32)",
                     "bwd_dx_gemm_t8_h8192_m16384"),
