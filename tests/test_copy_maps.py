@@ -10,8 +10,13 @@ Python and check, over all waves, lanes and k-tiles:
   * the tile orders are bijections onto the tile grid;
   * every copy source lies inside its operand, ragged shapes included;
   * every fragment read returns exactly the (row, k) elements the MFMA
-    operand layout asks for (lane l: row row0 + l % 32, k 16 s + 8 (l / 32)
-    .. +7), and the 16 lanes of a read group hit distinct 16-byte bank groups;
+    operand layout asks for (v_mfma_f32_32x32x16: lane l, row row0 + l % 32,
+    k 16 s + 8 (l / 32) .. +7; v_mfma_f32_16x16x32, the kernels' MF16 mode:
+    lane l, row row0 + l % 16, k 8 (l / 16) .. +7), and the lanes one read
+    cycle serves hit distinct banks;
+  * MF16: the MFMA result (lane l holds rows 4 (l / 16) .. +3 of column
+    l % 16 of operand 0 x operand 1, the weight fragment first) lands where
+    the epilogues and the fp32 LDS restaging expect it;
   * the paired stages' issue schedule never overwrites a stage that is
     still to be read, and the constant vmcnt waits cover every published
     k-tile under in-order completion.
@@ -67,7 +72,12 @@ def test_tile_orders_are_bijections(tiles_m, tiles_n):
 
 # ---- single k-tile stages (OperandTile) ----------------------------------------
 
-def single_copies(R, NW, kmajor, r0, rows, K, kc):
+def kswz(krow, mf16=False):
+    """Chunk swizzle of a k-major tile (OperandTile::kswz)."""
+    return ((krow & 3) << 2) ^ ((((krow >> 3) & 1) << 1) if mf16 else 0)
+
+
+def single_copies(R, NW, kmajor, r0, rows, K, kc, mf16=False):
     """{LDS 16-byte chunk index: (row or k-row, first k or first column)} of
     k-tile kc's copies (KTAIL clamping for a partial last k-tile)."""
     nk = -(-K // KBK)
@@ -85,7 +95,7 @@ def single_copies(R, NW, kmajor, r0, rows, K, kc):
             lds[slot] = (min(r0 + row, rows - 1), k)
         else:
             krow = slot // cb
-            c = (slot % cb) ^ ((krow & 3) << 2)
+            c = (slot % cb) ^ kswz(krow, mf16)
             kr = klast + min(krow, krem - 1) if tail else kc * KBK + krow
             lds[slot] = (kr, min(r0 + 8 * c, rows - 8))
     assert len(lds) == R * KBK * 2 // 16
@@ -237,3 +247,105 @@ def test_random_ragged_sources():
         for kc in (0, nk - 1):
             for a, b in single_copies(R, NW, kmajor, r0, rows, K, kc).values():
                 assert (0 <= a < K and 0 <= b and b + 8 <= rows) if kmajor else (0 <= a < rows and 0 <= b and b + 8 <= K)
+
+
+# ---- the 16 x 16 x 32 MFMA (MF16) -----------------------------------------------
+
+def test_kcontig_fragments16():
+    """OperandTile::frag16, k-contiguous: one ds_read_b128, lane l gets row
+    row0 + l % 16, k 8 (l / 16) .. +7; each 16-lane group (one k-chunk) hits
+    16 distinct 16-byte bank groups."""
+    R, NW = 256, 8
+    lds = single_copies(R, NW, False, 0, 10**6, 1024, 3, mf16=True)
+    for row0 in range(0, R, 16):
+        banks = {}
+        for lane in range(64):
+            chunk = (lane >> 4) ^ ((lane >> 2) & 3)
+            off = (row0 + (lane & 15)) * 64 + chunk * 16
+            assert lds[off // 16] == (row0 + (lane & 15), 3 * KBK + 8 * (lane >> 4))
+            banks.setdefault(lane // 16, set()).add((off // 16) % 16)
+        assert all(len(b) == 16 for b in banks.values())
+
+
+@pytest.mark.parametrize("R,NW", [(256, 8), (128, 4), (384, 8)])
+def test_kmajor_fragments16_through_the_transposing_read(R, NW):
+    """OperandTile::frag16, k-major: two transposing reads; lane l receives
+    column row0 + l % 16, k 8 (l / 16) + 4 H .. +3.  One read serves 32 lanes
+    (256 bytes) per cycle; with the MF16 swizzle their 64 banks are
+    distinct, without the extra bit groups 0 and 1 would collide."""
+    lds = single_copies(R, NW, True, 0, 10**6, 1024, 5, mf16=True)
+
+    def element(krow, byte):
+        kr, col0 = lds[(krow * R * 2 + byte) // 16]
+        return kr, col0 + (byte % 16) // 2
+
+    def addresses(row0, H, mf16):
+        addr = {}
+        for lane in range(64):
+            gi = lane & 15
+            krow = 8 * (lane >> 4) + 4 * H + (gi >> 2)
+            chunk = ((row0 >> 3) + ((gi & 3) >> 1)) ^ kswz(krow, mf16)
+            addr[lane] = (krow, chunk * 16 + (gi & 1) * 8)
+        return addr
+
+    def banks_distinct(addr, half):
+        banks = []
+        for lane in range(32 * half, 32 * half + 32):
+            krow, byte = addr[lane]
+            b = (krow * R * 2 + byte) // 4 % 64
+            banks += [b, (b + 1) % 64]
+        return len(set(banks)) == 64
+
+    for row0, H in itertools.product(range(0, R, 16), range(2)):
+        addr = addresses(row0, H, True)
+        for lane in range(64):
+            g0, gi = lane & ~15, lane & 15
+            for r in range(4):
+                krow, byte = addr[g0 + 4 * r + (gi >> 2)]
+                assert element(krow, byte + 2 * (gi & 3)) == (5 * KBK + 8 * (lane >> 4) + 4 * H + r, row0 + gi)
+        assert banks_distinct(addr, 0) and banks_distinct(addr, 1)
+    # the extra swizzle bit is what separates groups 0 and 1
+    assert not banks_distinct(addresses(0, 0, False), 0)
+
+
+@pytest.mark.parametrize("R,NW", [(256, 8), (128, 8), (128, 4)])
+@pytest.mark.parametrize("rows,K,r0,j", [(8192, 4096, 0, 0), (300, 128, 256, 1)])
+def test_pair_fragments16(R, NW, rows, K, r0, j):
+    """OperandPairTile::frag16: half h of pair j, lane l gets row row0 + l % 16,
+    k 64 j + 32 h + 8 (l / 16) .. +7."""
+    lds = pair_copies(R, NW, r0, rows, K, j)
+    for row0, h in itertools.product(range(0, R, 16), range(2)):
+        banks = {}
+        for lane in range(64):
+            r = lane & 15
+            chunk = (4 * h + (lane >> 4)) ^ ((r >> 1) & 7)
+            off = (row0 + r) * 128 + chunk * 16
+            assert lds[off // 16] == (min(r0 + row0 + r, rows - 1), j * 64 + 32 * h + 8 * (lane >> 4))
+            banks.setdefault(lane // 16, set()).add((off // 16) % 16)
+        assert all(len(b) == 16 for b in banks.values())
+
+
+@pytest.mark.parametrize("WM,WN", [(128, 64), (64, 64), (64, 96)])
+def test_mf16_result_lands_where_the_epilogues_expect(WM, WN):
+    """mfmas16_col: half h multiplies A fragment i (rows h WM/2 + 16 i) with
+    B fragment j (columns 16 j) into acc[j / 2][h TM/2 + i / 2], sub-block
+    q = 2 (i % 2) + j % 2.  The MFMA puts D[4 (l / 16) + r][l % 16] (rows of
+    operand 0 = columns n, columns of operand 1 = rows m) in lane l, register
+    r.  store_tile reads acc[J][I][4 q + r] as m = 32 I + row_of(q) + l % 16,
+    n = 32 J + col_of(q) + 4 (l / 16) + r; the restaging slab puts it at
+    row row_of(q) + l % 16 of block I, 16-byte chunk 8 J + col_of(q) / 4 +
+    l / 16, and every (m, n) of the wave tile is written exactly once."""
+    TM, TN = WM // 32, WN // 32
+    row_of = lambda q: 16 * (q >> 1)
+    col_of = lambda q: 16 * (q & 1)
+    seen = {}
+    for h, i, j, lane, r in itertools.product(range(2), range(TM), range(2 * TN), range(64), range(4)):
+        m = h * (WM // 2) + 16 * i + (lane & 15)           # MFMA result position
+        n = 16 * j + 4 * (lane >> 4) + r
+        J, I, q = j // 2, h * (TM // 2) + i // 2, 2 * (i % 2) + j % 2
+        assert (32 * I + row_of(q) + (lane & 15), 32 * J + col_of(q) + 4 * (lane >> 4) + r) == (m, n)
+        slab_row, chunk = row_of(q) + (lane & 15), 8 * J + col_of(q) // 4 + (lane >> 4)
+        assert (32 * I + slab_row, 4 * chunk + r) == (m, n)
+        assert (m, n) not in seen
+        seen[(m, n)] = (J, I, 4 * q + r)
+    assert len(seen) == WM * WN
