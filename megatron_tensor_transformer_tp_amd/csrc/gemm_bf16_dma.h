@@ -44,11 +44,17 @@
 //     clamped into the operand instead.  Rows (k-contiguous) or 8-column
 //     chunks (k-major) past M or N re-read the last valid one; their products
 //     reach only outputs that the masked epilogue of an edge tile does not
-//     store.  A K that is not a multiple of 32 (KTAIL) leaves krem valid k in
-//     the last k-tile: its copies past krem re-read valid k, and its fragments
-//     are zeroed there before the last MFMAs.  Requirements: 16-byte aligned
-//     bases and leading dimensions, a k-contiguous operand's K and a k-major
-//     operand's row length multiples of 8.
+//     store.  A K that is not a multiple of 32 (KTAIL) leaves fewer than 32
+//     valid k, [klast, K), in the last k-tile (klast = 32 (nk - 1)): that
+//     tile is copied from the window of the last 32 k,
+//     [K - 32, K) (one uniform offset on every lane's source, so the tail
+//     holds no per-lane registers), and its fragments are zeroed outside the
+//     k not yet accumulated, [klast, K), before the last MFMAs.  With
+//     K < 32 the window is [0, 32) and each lane's k (k-contiguous: its
+//     8-k chunk; k-major: its k-row) is clamped to the last valid one.
+//     Requirements: 16-byte aligned bases and leading dimensions, a
+//     k-contiguous operand's K and a k-major operand's row length multiples
+//     of 8.
 #pragma once
 
 #include "gemm_bf16_impl.h"
@@ -80,31 +86,36 @@ struct OperandTile {
     return ((r & 3) << 2) ^ (MF16 ? ((r >> 3) & 1) << 1 : 0);
   }
 
-  const uint16_t* src[Q];               // sources of k-tile 0
-  const uint16_t* last[KTAIL ? Q : 1];  // sources of the partial last k-tile
-  int64_t step;                         // elements per k-tile
+  const uint16_t* src[Q];   // sources of k-tile 0
+  int64_t step;             // elements per k-tile
+  int64_t unit;             // elements per k
+  int kbase;                // KTAIL: first k of the last k-tile's window
+
+  __device__ __forceinline__ void set_steps(int64_t ld, int K) {
+    unit = KMAJOR ? ld : 1;
+    step = kBKd * unit;
+    kbase = max(K - kBKd, 0);
+  }
 
   // Per-lane copy sources for the rows [r0, r0 + R) of an operand with `rows`
   // rows (k-contiguous: rows of [rows, K]; k-major: columns of [K, rows],
-  // rows % 8 == 0), clamped to the last row / chunk.  With KTAIL the last
-  // k-tile starts at k = klast and holds krem valid k.
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int r0, int rows,
-                                       int klast, int krem, int wave, int lane) {
+  // rows % 8 == 0), clamped to the last row / chunk, and with KTAIL to the
+  // last valid k (which changes nothing unless K < 32).
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int r0, int rows, int K,
+                                       int wave, int lane) {
     static_for<Q>([&](auto I) __attribute__((always_inline)) {
       const int slot = (wave * Q + I) * 64 + lane;
       if constexpr (!KMAJOR) {
         const int row = slot >> 2, kin = 8 * ((slot & 3) ^ ((row >> 2) & 3));
-        const uint16_t* p = base + static_cast<int64_t>(min(r0 + row, rows - 1)) * ld;
-        src[I] = p + kin;
-        if constexpr (KTAIL) last[I] = p + klast + min(kin, krem - 8);
+        src[I] = base + static_cast<int64_t>(min(r0 + row, rows - 1)) * ld +
+                 (KTAIL ? min(kin, K - 8) : kin);
       } else {
         const int krow = slot / CB, c = (slot % CB) ^ kswz(krow);
-        const uint16_t* p = base + min(r0 + 8 * c, rows - 8);
-        src[I] = p + static_cast<int64_t>(krow) * ld;
-        if constexpr (KTAIL) last[I] = p + static_cast<int64_t>(klast + min(krow, krem - 1)) * ld;
+        src[I] = base + min(r0 + 8 * c, rows - 8) +
+                 static_cast<int64_t>(KTAIL ? min(krow, K - 1) : krow) * ld;
       }
     });
-    step = KMAJOR ? static_cast<int64_t>(kBKd) * ld : kBKd;
+    set_steps(ld, K);
   }
 
   // SwiGLU form of a k-major weight tile: LDS columns in 32-column blocks
@@ -114,8 +125,7 @@ struct OperandTile {
   // Features [f0, f0 + R/2) of both projections (same ld) of `feats`
   // features, clamped to the last 8-feature chunk.
   __device__ __forceinline__ void init_dual(const uint16_t* gate, const uint16_t* value, int64_t ld,
-                                            int f0, int feats, int klast, int krem, int wave,
-                                            int lane) {
+                                            int f0, int feats, int K, int wave, int lane) {
     static_assert(KMAJOR, "the paired tile is a weight ([K, N]) tile");
     static_for<Q>([&](auto I) __attribute__((always_inline)) {
       const int slot = (wave * Q + I) * 64 + lane;
@@ -123,19 +133,19 @@ struct OperandTile {
       const int blk = c >> 2;
       const uint16_t* p = ((blk & 1) ? value : gate) +
                           min(f0 + (blk >> 1) * 32 + (c & 3) * 8, feats - 8);
-      src[I] = p + static_cast<int64_t>(krow) * ld;
-      if constexpr (KTAIL) last[I] = p + static_cast<int64_t>(klast + min(krow, krem - 1)) * ld;
+      src[I] = p + static_cast<int64_t>(KTAIL ? min(krow, K - 1) : krow) * ld;
     });
-    step = static_cast<int64_t>(kBKd) * ld;
+    set_steps(ld, K);
   }
 
-  // Copies of k-tile kc (the partial last one if `tail`) into the LDS region
-  // at byte address `lds`.
-  __device__ __forceinline__ void issue(int kc, bool tail, uint32_t lds, int wave) const {
+  // Copies of k-tile kc into the LDS region at byte address `lds`.  KTAIL:
+  // k-tile kc < nk - 1 starts at 32 kc < kbase, and the last one (kc =
+  // nk - 1, 32 kc >= kbase) is the window at kbase, so a uniform min picks
+  // the place without a branch.
+  __device__ __forceinline__ void issue(int kc, uint32_t lds, int wave) const {
+    const int64_t off = KTAIL ? min(kc * kBKd, kbase) * unit : kc * step;   // uniform
     static_for<Q>([&](auto I) __attribute__((always_inline)) {
-      const uint16_t* p = src[I] + kc * step;
-      if constexpr (KTAIL) p = tail ? last[I] : p;
-      copy_to_lds(p, lds + (wave * Q + I) * 1024);
+      copy_to_lds(src[I] + off, lds + (wave * Q + I) * 1024);
     });
   }
 
@@ -337,23 +347,29 @@ __device__ __forceinline__ void store_linear_f32_staged(const f32x16_t (&acc)[TN
   }
 }
 
-// Zeroes the bf16 elements of a fragment whose k (counted from the start of
-// the fragment's 8) is >= nvalid.
-__device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int nvalid) {
+// Keeps the bf16 elements e of a fragment (e counted from the fragment's
+// first k, 0 .. 7) with lo <= e < hi and zeroes the others.
+__device__ __forceinline__ bf16x8_t keep_range(bf16x8_t v, int lo, int hi) {
   u32x4_t w = __builtin_bit_cast(u32x4_t, v);
   static_for<4>([&](auto D) __attribute__((always_inline)) {
-    constexpr int d = D;
-    const uint32_t m = nvalid >= 2 * d + 2 ? 0xFFFFFFFFu : (nvalid == 2 * d + 1 ? 0x0000FFFFu : 0u);
-    w[d] &= m;
+    constexpr int e = 2 * D;
+    const uint32_t m = (lo <= e && e < hi ? 0x0000FFFFu : 0u) |
+                       (lo <= e + 1 && e + 1 < hi ? 0xFFFF0000u : 0u);
+    w[int(D)] &= m;
   });
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
-// LDS of one workgroup.  Single k-tile stages: STAGES stages of
-// (BM + BN) x 64 bytes; with the fp32 restaging (linear fp32 epilogue, wave
-// widths whose rows split evenly over the 64 lanes) the slabs sit in the
-// last stage and the bytes past the stages, so that the next tile's first
-// STAGES-1 k-tiles can be in flight during the epilogue.  PAIR 1 (B
+// LDS of one workgroup.  Single k-tile stages: A's STAGES stages of
+// BM x 64 bytes, then B's of BN x 64 bytes, so that each operand's stages lie
+// in one 64 KiB window and a fragment's LDS address is one register plus an
+// immediate offset (the LDS read's 16-bit field) for every stage (stages of
+// A and B interleaved put the last ones past 64 KiB, and a k-major operand,
+// whose fragments each need an address register of their own, then needs a
+// set per stage).  With the fp32 restaging (linear fp32 epilogue, wave widths
+// whose rows split evenly over the 64 lanes) the slabs sit in A's last stage,
+// B's last stage and the bytes past the stages, so that the next tile's
+// first STAGES-1 k-tiles can be in flight during the epilogue.  PAIR 1 (B
 // k-contiguous) or 2 (A k-contiguous), K % 64 == 0: STAGES single stages of
 // the other operand (rows x 64 bytes), then kPairs stages of the paired
 // operand holding two k-tiles each (rows x 128 bytes); the slabs reuse the
@@ -368,13 +384,25 @@ struct DmaLayout {
   static constexpr int kPairs = 3;
   static constexpr int kPairBytes = (PAIR == 2 ? BM : BN) * 2 * kBKd * 2;
   static constexpr int kPairAt = STAGES * (PAIR == 2 ? kBBytes : kABytes);
+  static constexpr int kBAt = STAGES * kABytes;   // PAIR 0: B's first stage
   static constexpr bool kStaged = EPI == EPI_LINEAR && OUT_F32 && 64 % (BN / WGN / 4) == 0;
   static constexpr bool kPrefetch = PAIR == 0 || !kStaged;   // next tile's copies during the epilogue
-  static constexpr int kStagingAt = PAIR ? 0 : (STAGES - 1) * kStage;
-  static constexpr int kStagingEnd = kStagingAt + kWaves * kStagedSlabBytes<kTN>;
+  static constexpr int kSlab = kStagedSlabBytes<kTN>;
+  static constexpr int kSlabsInA = PAIR ? 0 : kABytes / kSlab;   // in A's last stage
+  static constexpr int kSlabsInB = PAIR ? 0 : kBBytes / kSlab;   // in B's last stage
   static constexpr int kStageBytes = PAIR ? kPairAt + kPairs * kPairBytes : STAGES * kStage;
+  static constexpr int kSlabsPast = kWaves - kSlabsInA - kSlabsInB;
+  static constexpr int kStagingEnd =
+      PAIR ? kWaves * kSlab : kStageBytes + (kSlabsPast > 0 ? kSlabsPast : 0) * kSlab;
   static constexpr int kLdsBytes =
       kStaged && kStagingEnd > kStageBytes ? kStagingEnd : kStageBytes;
+  // LDS byte offset of wave w's staging slab
+  static __device__ __forceinline__ int slab_at(int w) {
+    if (PAIR) return w * kSlab;
+    if (w < kSlabsInA) return (STAGES - 1) * kABytes + w * kSlab;
+    if (w < kSlabsInA + kSlabsInB) return kBAt + (STAGES - 1) * kBBytes + (w - kSlabsInA) * kSlab;
+    return kStageBytes + (w - kSlabsInA - kSlabsInB) * kSlab;
+  }
   static constexpr int kPerCu = 160 * 1024 / kLdsBytes;   // resident workgroups per CU
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
@@ -418,7 +446,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
                 Layout::kPairBytes == TileP::kBytes, "stage sizes");
   constexpr bool kStaged = Layout::kStaged;
   constexpr bool kPrefetch = Layout::kPrefetch;
-  constexpr int kStagingAt = Layout::kStagingAt;
   constexpr int kPairs = Layout::kPairs;
   constexpr int kPairAt = Layout::kPairAt;
   constexpr int kPairBytes = Layout::kPairBytes;
@@ -432,8 +459,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
   const int nk = (K + kBKd - 1) / kBKd;
-  const int klast = (nk - 1) * kBKd, krem = K - klast;   // krem == kBKd unless KTAIL
-  const int npairs = nk / 2;                             // PAIR: nk is even
+  const int npairs = nk / 2;   // PAIR: nk is even
 
   // Workgroup b computes tiles b, b + gridDim.x, ...; tile t takes the place
   // workgroup t of a one-tile-per-workgroup grid would (XCD t % 8, round
@@ -451,33 +477,31 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
     if constexpr (PAIR == 2)
       tp.init(A, lda, m0, M, wave, lane);
     else
-      ta.init(A, lda, m0, M, klast, krem, wave, lane);
+      ta.init(A, lda, m0, M, K, wave, lane);
     if constexpr (PAIR == 1)
       tp.init(B, ldb, n0, N, wave, lane);
     else if constexpr (EPI == EPI_SWIGLU)
-      tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, N / 2, klast, krem, wave,
-                   lane);
+      tb.init_dual(B, static_cast<const uint16_t*>(ep.b2), ldb, n0 / 2, N / 2, K, wave, lane);
     else
-      tb.init(B, ldb, n0, N, klast, krem, wave, lane);
+      tb.init(B, ldb, n0, N, K, wave, lane);
   };
 
-  // LDS places of k-tile kt: a single-stage operand in stage kt % STAGES
-  // (both operands share that stage when nothing is paired), the paired one
-  // in pair stage (kt / 2) % kPairs, half kt % 2.
+  // LDS places of k-tile kt: a single-stage operand in its stage
+  // kt % STAGES, the paired one in pair stage (kt / 2) % kPairs, half kt % 2.
   const uint32_t smem_base = lds_address(smem);
   auto a_at = [](int ss, int sp) {
-    return PAIR == 2 ? kPairAt + sp * kPairBytes : PAIR == 1 ? ss * A_BYTES : ss * STAGE;
+    return PAIR == 2 ? kPairAt + sp * kPairBytes : ss * A_BYTES;
   };
   auto b_at = [](int ss, int sp) {
-    return PAIR == 1 ? kPairAt + sp * kPairBytes : PAIR == 2 ? ss * B_BYTES : ss * STAGE + A_BYTES;
+    return PAIR == 1 ? kPairAt + sp * kPairBytes : PAIR == 2 ? ss * B_BYTES : Layout::kBAt + ss * B_BYTES;
   };
   // Copies of k-tile kt of a single-stage operand (clamped to the last
   // tile), and of pair j of the paired one (clamped to the last pair).
   auto issue_a = [&](int kt) __attribute__((always_inline)) {
-    ta.issue(min(kt, nk - 1), kt >= nk - 1, smem_base + a_at(kt % STAGES, 0), wave);
+    ta.issue(min(kt, nk - 1), smem_base + a_at(kt % STAGES, 0), wave);
   };
   auto issue_b = [&](int kt) __attribute__((always_inline)) {
-    tb.issue(min(kt, nk - 1), kt >= nk - 1, smem_base + b_at(kt % STAGES, 0), wave);
+    tb.issue(min(kt, nk - 1), smem_base + b_at(kt % STAGES, 0), wave);
   };
   auto issue_single = [&](int kt) __attribute__((always_inline)) {
     if constexpr (PAIR == 2) issue_b(kt); else issue_a(kt);
@@ -619,20 +643,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
     constexpr bool kEvenKnown = decltype(sel(0))::kParityKnown;
     const int kn = kt + STAGES - 1;
     if constexpr (PAIR != 2)
-      ta.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + a_at(sel(STAGES - 1).a, 0), wave);
+      ta.issue(min(kn, nk - 1), smem_base + a_at(sel(STAGES - 1).a, 0), wave);
     if constexpr (PAIR != 0) {
       // the pair of k-tiles kt+4, kt+5 goes where kt-2, kt-1 were
       const int sp = sel(4).p;
       const uint32_t pair_lds = smem_base + (PAIR == 2 ? a_at(0, sp) : b_at(0, sp));
       if constexpr (PAIR == 2)
-        tb.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + b_at(sel(STAGES - 1).a, 0), wave);
+        tb.issue(min(kn, nk - 1), smem_base + b_at(sel(STAGES - 1).a, 0), wave);
       if constexpr (kEvenKnown) {
         if constexpr (decltype(sel(0))::kEven) tp.issue(min(kt / 2 + 2, npairs - 1), pair_lds, wave);
       } else {
         if ((kt & 1) == 0) tp.issue(min(kt / 2 + 2, npairs - 1), pair_lds, wave);
       }
     } else {
-      tb.issue(min(kn, nk - 1), kn >= nk - 1, smem_base + b_at(sel(STAGES - 1).a, 0), wave);
+      tb.issue(min(kn, nk - 1), smem_base + b_at(sel(STAGES - 1).a, 0), wave);
     }
   };
   auto ktile = [&](int kt, auto sel) __attribute__((always_inline)) {
@@ -716,14 +740,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
       // the last k-tile: its A half 0 is in af0 and its B in bq
       read_a16(nk - 1, 1, af1);
       if constexpr (KTAIL) {
-        // lane l's fragments hold k 8 (l / 16) .. +7 of the tile
+        // the window holds k kbase .. kbase + 31, of which [klast, K) are
+        // still to be added; lane l's fragments hold window places
+        // 8 (l / 16) .. +7
+        const int kbase = max(K - kBKd, 0), klast = (nk - 1) * kBKd;
         const int k_lane = 8 * (flane >> 4);
+        const int lo = klast - kbase - k_lane, hi = K - kbase - k_lane;
         static_for<TM>([&](auto I) __attribute__((always_inline)) {
-          af0[I] = keep_first(af0[I], krem - k_lane);
-          af1[I] = keep_first(af1[I], krem - k_lane);
+          af0[I] = keep_range(af0[I], lo, hi);
+          af1[I] = keep_range(af1[I], lo, hi);
         });
         static_for<2 * TN>([&](auto J) __attribute__((always_inline)) {
-          bq[J] = keep_first(bq[J], krem - k_lane);
+          bq[J] = keep_range(bq[J], lo, hi);
         });
       }
       mfmas16(af0, std::integral_constant<int, 0>{});
@@ -732,15 +760,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
       // the last k-tile (its substep-0 fragments are in af0 / bf0)
       read_frags(nk - 1, 1, af1, bf1);
       if constexpr (KTAIL) {
-        // lane l's fragments hold k 16 s + 8 (l / 32) .. +7 of the tile
+        // window places as above; lane l's fragments of substep s hold
+        // places 16 s + 8 (l / 32) .. +7
+        const int kbase = max(K - kBKd, 0), klast = (nk - 1) * kBKd;
         const int k_lane = 8 * (flane >> 5);
+        const int lo = klast - kbase - k_lane, hi = K - kbase - k_lane;
         static_for<TM>([&](auto I) __attribute__((always_inline)) {
-          af0[I] = keep_first(af0[I], krem - k_lane);
-          af1[I] = keep_first(af1[I], krem - 16 - k_lane);
+          af0[I] = keep_range(af0[I], lo, hi);
+          af1[I] = keep_range(af1[I], lo - 16, hi - 16);
         });
         static_for<TN>([&](auto J) __attribute__((always_inline)) {
-          bf0[J] = keep_first(bf0[J], krem - k_lane);
-          bf1[J] = keep_first(bf1[J], krem - 16 - k_lane);
+          bf0[J] = keep_range(bf0[J], lo, hi);
+          bf1[J] = keep_range(bf1[J], lo - 16, hi - 16);
         });
       }
       mfmas(af0, bf0);
@@ -788,7 +819,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
       bool stored = false;
       if constexpr (kStaged) {
         if (!edge) {
-          store_linear_f32_staged<TM, TN, MF16>(acc, smem + kStagingAt + wave * kStagedSlabBytes<TN>,
+          store_linear_f32_staged<TM, TN, MF16>(acc, smem + Layout::slab_at(wave),
                                                 elane, cm0 + wm * WM, cn0 + wn * WN, ep);
           stored = true;
         }

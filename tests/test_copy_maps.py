@@ -79,10 +79,12 @@ def kswz(krow, mf16=False):
 
 def single_copies(R, NW, kmajor, r0, rows, K, kc, mf16=False):
     """{LDS 16-byte chunk index: (row or k-row, first k or first column)} of
-    k-tile kc's copies (KTAIL clamping for a partial last k-tile)."""
-    nk = -(-K // KBK)
-    klast, krem = (nk - 1) * KBK, K - (nk - 1) * KBK
-    tail = K % KBK != 0 and kc == nk - 1
+    k-tile kc's copies.  K not a multiple of 32 (KTAIL): the last k-tile is
+    the window of the last 32 k, starting at kbase = max(K - 32, 0) (the
+    uniform min(32 kc, kbase)), and each lane's k is clamped to the last
+    valid one (a no-op unless K < 32)."""
+    ktail = K % KBK != 0
+    kstart = min(kc * KBK, max(K - KBK, 0)) if ktail else kc * KBK
     Q = R * KBK * 2 // 1024 // NW
     cb = R // 8
     lds = {}
@@ -91,15 +93,24 @@ def single_copies(R, NW, kmajor, r0, rows, K, kc, mf16=False):
         if not kmajor:
             row = slot >> 2
             kin = 8 * ((slot & 3) ^ ((row >> 2) & 3))
-            k = klast + min(kin, krem - 8) if tail else kc * KBK + kin
-            lds[slot] = (min(r0 + row, rows - 1), k)
+            lds[slot] = (min(r0 + row, rows - 1), kstart + (min(kin, K - 8) if ktail else kin))
         else:
             krow = slot // cb
             c = (slot % cb) ^ kswz(krow, mf16)
-            kr = klast + min(krow, krem - 1) if tail else kc * KBK + krow
-            lds[slot] = (kr, min(r0 + 8 * c, rows - 8))
+            lds[slot] = (kstart + (min(krow, K - 1) if ktail else krow), min(r0 + 8 * c, rows - 8))
     assert len(lds) == R * KBK * 2 // 16
     return lds
+
+
+def tail_mask(K, kc, place):
+    """Whether the kernel keeps window place `place` (0 .. 31) of k-tile kc:
+    for the last k-tile of a K with a tail, lo <= place < hi with
+    lo = klast - kbase, hi = K - kbase; every place of the other k-tiles."""
+    nk = -(-K // KBK)
+    if K % KBK == 0 or kc != nk - 1:
+        return True
+    kbase, klast = max(K - KBK, 0), (nk - 1) * KBK
+    return klast - kbase <= place < K - kbase
 
 
 @pytest.mark.parametrize("R,NW,kmajor,rows,K", [
@@ -115,6 +126,42 @@ def test_single_stage_sources_in_bounds(R, NW, kmajor, rows, K):
                     assert 0 <= a < rows and 0 <= b and b + 8 <= K
                 else:
                     assert 0 <= a < K and 0 <= b and b + 8 <= rows
+
+
+@pytest.mark.parametrize("kmajor", [False, True])
+@pytest.mark.parametrize("K", [8, 16, 24, 40, 56, 64, 72, 200, 1000, 1024, 16376])
+def test_ktail_window_adds_every_k_once(kmajor, K):
+    """Over all k-tiles of a row (k-contiguous) or column (k-major), the k
+    that survive the last k-tile's mask are exactly 0 .. K-1, each once; the
+    lane's data at window place p of k-tile kc is k = kstart + p (clamped
+    copies only at masked places).  k-major operands also take K % 8 != 0."""
+    Ks = [K] + ([K - 3, K + 5] if kmajor and K > 8 else [])
+    for K in Ks:
+        nk = -(-K // KBK)
+        R, NW = 256, 8
+        seen = []
+        for kc in range(nk):
+            lds = single_copies(R, NW, kmajor, 0, 10**6, K, kc)
+            cb = R // 8
+            for slot, (a, b) in lds.items():
+                if not kmajor:
+                    row = slot >> 2
+                    logical = 8 * ((slot & 3) ^ ((row >> 2) & 3))
+                    if row != 5:
+                        continue
+                    for e in range(8):
+                        if tail_mask(K, kc, logical + e):
+                            assert 0 <= b + e < K
+                            seen.append(b + e)
+                else:
+                    krow = slot // cb
+                    c = (slot % cb) ^ kswz(krow)
+                    if c != 3:
+                        continue
+                    if tail_mask(K, kc, krow):
+                        assert 0 <= a < K
+                        seen.append(a)
+        assert sorted(seen) == list(range(K))
 
 
 def test_kcontig_fragments():
@@ -158,6 +205,54 @@ def test_kmajor_fragments_through_the_transposing_read():
             for g in range(4):
                 wins = {((addr[g * 16 + 4 * r][0] * R * 2 + addr[g * 16 + 4 * r][1]) // 64) % 4 for r in range(4)}
                 assert len(wins) == 4
+
+
+# ---- LDS layout of the single-stage kernels (DmaLayout) --------------------------
+
+@pytest.mark.parametrize("BM,BN,WGM,WGN", [(256, 256, 2, 4), (128, 128, 2, 2), (128, 384, 2, 4)])
+def test_stage_windows_and_staging_slabs(BM, BN, WGM, WGN):
+    """A's stages, then B's: on the 256 x 256 and 128 x 128 tiles each
+    operand's four stages lie within 64 KiB of its first stage, so one
+    register plus the LDS read's 16-bit immediate reaches every stage (the
+    128 x 384 tile's B stages span 96 KiB; that kernel has registers to
+    spare for a second base).  The fp32 staging slab of each wave lies in A's
+    last stage, B's last stage or past the stages: never in a stage that the
+    next tile's first STAGES-1 k-tiles fill during the epilogue, never in
+    another wave's slab, and inside the 160 KiB of LDS."""
+    S = 4
+    a_bytes, b_bytes = BM * KBK * 2, BN * KBK * 2
+    b_at = S * a_bytes
+    stage_bytes = S * (a_bytes + b_bytes)
+    if BN <= 256:
+        assert S * a_bytes <= 65536 and S * b_bytes <= 65536
+    waves = WGM * WGN
+    tn = BN // WGN // 32
+    staged = 64 % (BN // WGN // 4) == 0
+    if not staged:
+        assert stage_bytes <= 160 * 1024
+        return
+    slab = 32 * tn * 32 * 4
+    in_a, in_b = a_bytes // slab, b_bytes // slab
+
+    def slab_at(w):
+        if w < in_a:
+            return (S - 1) * a_bytes + w * slab
+        if w < in_a + in_b:
+            return b_at + (S - 1) * b_bytes + (w - in_a) * slab
+        return stage_bytes + (w - in_a - in_b) * slab
+
+    lds_bytes = max(stage_bytes, stage_bytes + max(0, waves - in_a - in_b) * slab)
+    assert lds_bytes <= 160 * 1024
+    busy = [(s * a_bytes, (s + 1) * a_bytes) for s in range(S - 1)]
+    busy += [(b_at + s * b_bytes, b_at + (s + 1) * b_bytes) for s in range(S - 1)]
+    spans = []
+    for w in range(waves):
+        lo = slab_at(w)
+        hi = lo + slab
+        assert 0 <= lo and hi <= lds_bytes
+        assert all(hi <= b0 or lo >= b1 for b0, b1 in busy)
+        assert all(hi <= s0 or lo >= s1 for s0, s1 in spans)
+        spans.append((lo, hi))
 
 
 # ---- paired stages (OperandPairTile) --------------------------------------------

@@ -196,6 +196,61 @@ def test_large_rank_shards(name, rank):
     check_grads(got, ref, "bf16", f"{name} rank {rank}")
 
 
+def test_ragged_tokens_near_headline():
+    """16376 tokens (not a multiple of the 32-deep k-tile) at the headline
+    widths: the weight-gradient products take the K-tail path over 512
+    k-tiles.  Their gradients for a seeded block of 64 of the shard's f
+    columns are checked against the oracle run on that block (each column of
+    A with its row of B is an independent GeLU unit, so the block's weight
+    gradients do not depend on the other columns), and the launch must run
+    at close to the rate of the aligned 16384-token backward (a register
+    spill in the K-tail kernel once made it 2.5 times slower)."""
+    wl = inputs.MlpWorkload("bwd_ragged_16376", 16376, 8192, 32768, 8, "bf16", 1.0, 0.02, 0.02, "f32")
+    x, dz = inputs.mlp_x_rows(wl), inputs.mlp_dz_rows(wl)
+    a, b = inputs.mlp_a_block(wl, 2), inputs.mlp_b_block(wl, 2)
+    xd, ad, bd, dzd = dev(x, "bf16"), dev(a, "bf16"), dev(b, "bf16"), dev(dz, "bf16")
+    say("backward 16376 tokens, h 8192, f 4096: K-tail weight gradients")
+    _z, y = run_fwd_save(wl, 2, xd, ad, bd)
+    got = run_bwd(wl, 2, xd, ad, bd, y, dzd, "f32", with_bias=False)
+    cols = np.sort(np.random.default_rng(16376).choice(wl.f, 64, replace=False))
+    ref = shard_ref(host64(x, "bf16"), host64(a, "bf16")[:, cols], host64(b, "bf16")[cols, :],
+                    host64(dz, "bf16"))
+    check_grads({"da": got["da"][:, torch.from_numpy(cols).cuda()],
+                 "db": got["db"][torch.from_numpy(cols).cuda(), :]}, ref, "bf16",
+                "16376-token column block", keys=("da", "db"))
+
+    # rate: the same launch against an aligned 16384-token one, interleaved
+    tok2 = 16384
+    x2 = torch.randn(tok2, wl.hidden, device="cuda").to(torch.bfloat16)
+    y2 = torch.randn(tok2, wl.f, device="cuda").to(torch.bfloat16)
+    dz2 = torch.randn(tok2, wl.hidden, device="cuda").to(torch.bfloat16)
+    outs = {n: (torch.empty(n, wl.hidden, device="cuda"), torch.empty(wl.hidden, wl.f, device="cuda"),
+                torch.empty(wl.f, wl.hidden, device="cuda")) for n in (wl.tokens, tok2)}
+    args = {wl.tokens: (xd, y, dzd), tok2: (x2, y2, dz2)}
+    ws = torch.empty(binding.tp_mlp_shard_bwd_workspace_bytes(tok2, wl.hidden, wl.ffn, wl.t, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def launch(n):
+        xx, yy, zz = args[n]
+        binding.tp_mlp_shard_bwd(xx, ad, bd, yy, zz, *outs[n], ws, ffn=wl.ffn, t=wl.t, rank=2)
+
+    best = {n: float("inf") for n in args}
+    for n in args:
+        launch(n)
+    for _ in range(3):
+        for n in args:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                launch(n)
+            e1.record()
+            torch.cuda.synchronize()
+            best[n] = min(best[n], e0.elapsed_time(e1) / 3)
+    ratio = best[wl.tokens] / best[tok2]
+    say(f"backward 16376 tokens {best[wl.tokens]:.3f} ms, 16384 tokens {best[tok2]:.3f} ms, ratio {ratio:.3f}")
+    assert ratio < 1.25, f"ragged-token backward {ratio:.2f} times the aligned one"
+
+
 def test_zero_tokens_and_errors():
     wl = inputs.MLP_WORKLOADS["t4_h1024_m1024"]
     ad = dev(inputs.mlp_a_block(wl, 0), "bf16")
