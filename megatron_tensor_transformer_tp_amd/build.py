@@ -31,6 +31,8 @@ SOURCES = [
     "gemm_bf16_384_plain.hip",
     "gemm_bf16_256_nt.hip",
     "gemm_bf16_256_tn.hip",
+    "gemm_bf16_128_nt.hip",
+    "gemm_bf16_128_tn.hip",
     "gemm_bf16_256_swiglu.hip",
     "gemm_f32.hip",
     "colsum.hip",

@@ -43,12 +43,16 @@ int64_t device_cus() {
 // the 4096 x 8192 x {3072, 1536} products (128 x 384: 0.84, 128 x 128: 0.82
 // of the 256 x 256 rate; a last 128 x 128 round with one workgroup per CU
 // costs 0.73 of a full one).
-static int gemm_tile_choice(int64_t M, int64_t N) {
+// Without the 128 x 384 shape (with_384 false) the choice is between the
+// other two.
+static int gemm_tile_choice(int64_t M, int64_t N, bool with_384 = true) {
   const int64_t kCUs = device_cus();
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   const int64_t t256 = tiles(256, 256), t384 = tiles(128, 384), t128 = tiles(128, 128);
   const double c256 = static_cast<double>((t256 + kCUs - 1) / kCUs);
-  const double c384 = static_cast<double>((t384 + kCUs - 1) / kCUs) * (128.0 * 384.0) / (256.0 * 256.0) / 0.84;
+  const double c384 = with_384 ? static_cast<double>((t384 + kCUs - 1) / kCUs) * (128.0 * 384.0) /
+                                     (256.0 * 256.0) / 0.84
+                               : 1e300;
   const int64_t rem = t128 % (2 * kCUs);
   const double c128 = (static_cast<double>(t128 / (2 * kCUs)) + (rem == 0 ? 0.0 : rem <= kCUs ? 0.73 : 1.0)) *
                       2.0 * (128.0 * 128.0) / (256.0 * 256.0) / 0.82;
@@ -68,6 +72,32 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, i
   }
 }
 
+namespace {
+template <int BM, int BN>
+hipError_t launch_t_tile(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B,
+                         int64_t ldb, bool b_kmajor, int m, int n, int k, const Epilogue& ep,
+                         hipStream_t stream) {
+  if (!a_kmajor && !b_kmajor) {
+    if (ep.kind == EPI_GELU_BWD && !ep.out_f32)
+      return launch_gemm_bf16_t_cfg<BM, BN, false, false, EPI_GELU_BWD, false>(A, lda, B, ldb, m, n, k, ep, stream);
+    if (ep.kind == EPI_LINEAR)
+      return ep.out_f32
+                 ? launch_gemm_bf16_t_cfg<BM, BN, false, false, EPI_LINEAR, true>(A, lda, B, ldb, m, n, k, ep, stream)
+                 : launch_gemm_bf16_t_cfg<BM, BN, false, false, EPI_LINEAR, false>(A, lda, B, ldb, m, n, k, ep, stream);
+    return hipErrorInvalidValue;
+  }
+  if (a_kmajor && b_kmajor && ep.kind == EPI_LINEAR)
+    return ep.out_f32
+               ? launch_gemm_bf16_t_cfg<BM, BN, true, true, EPI_LINEAR, true>(A, lda, B, ldb, m, n, k, ep, stream)
+               : launch_gemm_bf16_t_cfg<BM, BN, true, true, EPI_LINEAR, false>(A, lda, B, ldb, m, n, k, ep, stream);
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+// The backward's layouts (both operands k-contiguous or both k-major) on
+// 256 x 256 or 128 x 128 tiles by the same estimate as the forward (small
+// weight gradients, e.g. 4096 x 1376, fill a fraction of the CUs with
+// 256 x 256 tiles).
 hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, const uint16_t* B,
                               int64_t ldb, bool b_kmajor, int64_t M, int64_t N, int64_t K,
                               const Epilogue& ep, hipStream_t stream) {
@@ -78,18 +108,10 @@ hipError_t launch_gemm_bf16_t(const uint16_t* A, int64_t lda, bool a_kmajor, con
     if (ep.kind == EPI_GELU_BWD) return hipErrorInvalidValue;
     return launch_gemm_bf16(A, lda, B, ldb, M, N, K, ep, stream);
   }
-  if (!a_kmajor && !b_kmajor) {
-    if (ep.kind == EPI_GELU_BWD && !ep.out_f32)
-      return launch_gemm_bf16_t_cfg<false, false, EPI_GELU_BWD, false>(A, lda, B, ldb, m, n, k, ep, stream);
-    if (ep.kind == EPI_LINEAR)
-      return ep.out_f32 ? launch_gemm_bf16_t_cfg<false, false, EPI_LINEAR, true>(A, lda, B, ldb, m, n, k, ep, stream)
-                        : launch_gemm_bf16_t_cfg<false, false, EPI_LINEAR, false>(A, lda, B, ldb, m, n, k, ep, stream);
-    return hipErrorInvalidValue;
-  }
-  if (a_kmajor && b_kmajor && ep.kind == EPI_LINEAR)
-    return ep.out_f32 ? launch_gemm_bf16_t_cfg<true, true, EPI_LINEAR, true>(A, lda, B, ldb, m, n, k, ep, stream)
-                      : launch_gemm_bf16_t_cfg<true, true, EPI_LINEAR, false>(A, lda, B, ldb, m, n, k, ep, stream);
-  return hipErrorInvalidValue;
+  if (a_kmajor != b_kmajor) return hipErrorInvalidValue;
+  if (gemm_tile_choice(M, N, false) == 256)
+    return launch_t_tile<256, 256>(A, lda, a_kmajor, B, ldb, b_kmajor, m, n, k, ep, stream);
+  return launch_t_tile<128, 128>(A, lda, a_kmajor, B, ldb, b_kmajor, m, n, k, ep, stream);
 }
 
 hipError_t launch_gemm_bf16_swiglu(const uint16_t* A, int64_t lda, const uint16_t* Bg,
@@ -100,7 +122,7 @@ hipError_t launch_gemm_bf16_swiglu(const uint16_t* A, int64_t lda, const uint16_
   Epilogue ep{nullptr, nullptr, 0, out, ldo, false, EPI_SWIGLU};
   ep.b2 = Bu;
   // the product runs over the 2F interleaved gate / value columns
-  return launch_gemm_bf16_t_cfg<false, true, EPI_SWIGLU, false>(
+  return launch_gemm_bf16_t_cfg<256, 256, false, true, EPI_SWIGLU, false>(
       A, lda, Bg, ldb, static_cast<int>(M), static_cast<int>(2 * F), static_cast<int>(K), ep, stream);
 }
 

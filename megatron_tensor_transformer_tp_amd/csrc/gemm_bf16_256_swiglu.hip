@@ -5,7 +5,7 @@
 
 namespace tpk {
 
-template hipError_t launch_gemm_bf16_t_cfg<false, true, EPI_SWIGLU, false>(
+template hipError_t launch_gemm_bf16_t_cfg<256, 256, false, true, EPI_SWIGLU, false>(
     const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);
 
 }  // namespace tpk

@@ -4,8 +4,8 @@
 
 namespace tpk {
 
-template hipError_t launch_gemm_bf16_t_cfg<true, true, EPI_LINEAR, true>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);
+template hipError_t launch_gemm_bf16_t_cfg<256, 256, true, true, EPI_LINEAR, true>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);
 
-template hipError_t launch_gemm_bf16_t_cfg<true, true, EPI_LINEAR, false>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);
+template hipError_t launch_gemm_bf16_t_cfg<256, 256, true, true, EPI_LINEAR, false>(const uint16_t*, int64_t, const uint16_t*, int64_t, int, int, int, const Epilogue&, hipStream_t);
 
 }  // namespace tpk

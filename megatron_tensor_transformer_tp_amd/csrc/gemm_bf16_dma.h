@@ -932,10 +932,12 @@ hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* 
       A, lda, B, ldb, M, N, K, ep, stream);
 }
 
-template <bool A_KMAJOR, bool B_KMAJOR, int EPI, bool OUT_F32>
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_t_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                   int M, int N, int K, const Epilogue& ep, hipStream_t stream) {
-  return gemm_detail::launch_tile_dma<256, 256, 2, 4, 4, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, kMf16>(
+  static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128), "tile shapes");
+  constexpr int kWgn = BM == 128 ? 2 : 4;
+  return gemm_detail::launch_tile_dma<BM, BN, 2, kWgn, 4, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, kMf16>(
       A, lda, B, ldb, M, N, K, ep, stream);
 }
 
