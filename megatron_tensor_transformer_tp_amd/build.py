@@ -34,6 +34,7 @@ SOURCES = [
     "gemm_bf16_128_nt.hip",
     "gemm_bf16_128_tn.hip",
     "gemm_bf16_256_swiglu.hip",
+    "gemm_bf16_128_swiglu.hip",
     "gemm_f32.hip",
     "colsum.hip",
     "sp_reduce.hip",
