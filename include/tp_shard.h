@@ -327,8 +327,10 @@ size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden,
  *   causal  0: every query sees every key; 1: key j <= query i only.
  * Per local head j: O_j = softmax(Q_j K_j^T / sqrt(head_dim)) V_j;
  * out_i = [O_0 | ... | O_{hl-1}] wo_i.  hidden == heads * head_dim.
- * dtype pairs: bf16 -> f32, bf16 -> bf16.  head_dim must be 128 and seq a
- * multiple of 128 (TP_ERR_UNSUPPORTED otherwise).  Q and K enter Q K^T as
+ * dtype pairs: bf16 -> f32, bf16 -> bf16.  head_dim must be 128 and, unless
+ * batch or seq is 0 (nothing to do), seq at least 32 (TP_ERR_UNSUPPORTED
+ * otherwise); any such seq, not only multiples of the kernel's blocks.
+ * Q and K enter Q K^T as
  * fp16 (11 significant bits) scaled by 2^-8, so |q|, |k| must stay below
  * 2^24: a larger value overflows to infinity, and the rows of every query
  * whose scores it reaches come out non-finite (Inf / NaN), never finite and

@@ -46,7 +46,12 @@
 //     large finite negative value, so fully masked (causal) entries give
 //     exp = 0 and never NaN; it is raised lazily (only when a block's max
 //     exceeds it by more than 8 in log2 units, decided per wave), so the
-//     64-register output rescale is rare.
+//     64-register output rescale is rare;
+//   * any sequence of at least 32 tokens: a partial last key block is read
+//     as the window of the last 32 keys (a uniform offset) with its keys
+//     before the block masked, an odd block count is padded by a fully
+//     masked block, and queries past the end load the last query's row and
+//     store nothing.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -100,7 +105,9 @@ __device__ __forceinline__ LanePair lane_pair(float v) {
   return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
-template <bool CAUSAL>
+// RAGGED: seq is not a multiple of 128 (partial query and key blocks); the
+// other instantiation carries none of the code for them.
+template <bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
                                                        int64_t ld_qkv, uint16_t* __restrict__ o,
                                                        int64_t ld_o, int seq, int heads,
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = wave >> 2;             // which half of the key blocks
-  const int nqb = seq / kBQ;
+  const int nqb = RAGGED ? (seq + kBQ - 1) / kBQ : seq / kBQ;
   const int id = blockIdx.x;
   const int head = id % heads;
   const int qb = (id / heads) % nqb;
@@ -121,10 +128,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int h = lane >> 5;                 // which half of the keys / dims this lane holds
   const int query = qb * kBQ + (wave & 3) * 32 + (lane & 31);
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds Q[query][16t + 8h .. +7].
+  // Q fragments (B operand of S^T = K Q^T): lane holds Q[query][16t + 8h .. +7]
+  // (a query past the end of the sequence, in the last block, reads the last
+  // one's and is never stored).
   f16x8_t qf[8];
   {
-    const int64_t qoff = (row0 + query) * ld_qkv + col_q + 8 * h;
+    const int64_t qoff = (row0 + (RAGGED ? min(query, seq - 1) : query)) * ld_qkv + col_q + 8 * h;
     static_for<8>([&](auto T) __attribute__((always_inline)) {
       qf[T] = *reinterpret_cast<const f16x8_t*>(qkv + qoff + 16 * T);
     });
@@ -145,8 +154,16 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   });
   const int64_t block_step = static_cast<int64_t>(kBKV) * ld_qkv;
   const uint32_t smem_base = lds_address(smem);
-  const int nblk = CAUSAL ? min(seq / kBKV, (qb + 1) * (kBQ / kBKV)) : seq / kBKV;  // even
-  const int nit = nblk / 2;
+  // Key blocks: a sequence that is not a multiple of 32 ends in a partial
+  // block, which is copied from the window of the last 32 keys, [seq - 32,
+  // seq), its keys before 32 kb (the previous block's) masked; an odd block
+  // count gets a phantom last block (a copy of the last real one, every key
+  // masked) so that both groups run the same iterations.
+  const int nblk_all = RAGGED ? (seq + kBKV - 1) / kBKV : seq / kBKV;
+  const int nblk = CAUSAL ? min(nblk_all, (qb + 1) * (kBQ / kBKV)) : nblk_all;
+  const int nit = RAGGED ? (nblk + 1) / 2 : nblk / 2;
+  // first key of block kb's window
+  auto key_base = [seq](int kb) { return RAGGED ? min(kb * kBKV, seq - kBKV) : kb * kBKV; };
 
   // LDS placement: block j sits in its group's half of the stages (j % 2)
   // at its iteration's place in a kCycle-iteration cycle ((j / 2) % kCycle),
@@ -163,7 +180,8 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
       const int j = 2 * it + q / kCopiesPerBlock;
       const int kc = min(j, nblk - 1);
       const int rem = q % kCopiesPerBlock;
-      const uint16_t* base = qkv + row0 * ld_qkv + kc * block_step;
+      const uint16_t* base = RAGGED ? qkv + (row0 + key_base(kc)) * ld_qkv
+                                    : qkv + row0 * ld_qkv + kc * block_step;
       copy_to_lds_off(base, coff[Q], smem_base + stage_off(j) + (rem / 8) * kArr + (rem % 8) * 1024);
     });
   };
@@ -203,17 +221,35 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     return sv;
   };
 
-  // Causal mask and the block's max (log2 units; this lane: its query and
-  // 16 of the 32 keys, S^T rows 8 (R / 4) + 4 h + R % 4).  The max is taken
-  // on the raw scores: it commutes with the positive scale, which enters the
-  // exponent through one fma.
+  // Masks and the block's max (log2 units; this lane: its query and 16 of
+  // the 32 keys, S^T rows 8 (R / 4) + 4 h + R % 4 of the block's window).
+  // A key is masked when it is later than the query (causal) or, in a
+  // partial or phantom block (a workgroup-uniform branch), when it precedes
+  // the block (already counted).  The max is taken on the raw scores: it
+  // commutes with the positive scale, which enters the exponent through one
+  // fma.
   auto block_max = [&](f32x16_t& sv, int kb) __attribute__((always_inline)) {
-    static_for<16>([&](auto R) __attribute__((always_inline)) {
-      if constexpr (CAUSAL) {
-        const int key = kb * kBKV + 8 * (R / 4) + 4 * h + (R % 4);
+    // window place of element R: 4 h + c(R), c(R) = 8 (R / 4) + R % 4
+    const int kbase = key_base(kb);
+    const int lo = kb * kBKV - kbase;   // places before lo: already counted (uniform)
+    if constexpr (CAUSAL && RAGGED) {
+      // the same comparison as a threshold on c(R) (fewer registers here)
+      const int hi = query - kbase - 4 * h;
+      static_for<16>([&](auto R) __attribute__((always_inline)) {
+        if (8 * (R / 4) + (R % 4) > hi) sv[int(R)] = -__builtin_inff();
+      });
+    } else if constexpr (CAUSAL) {
+      static_for<16>([&](auto R) __attribute__((always_inline)) {
+        const int key = kbase + 8 * (R / 4) + 4 * h + (R % 4);
         if (key > query) sv[int(R)] = -__builtin_inff();
-      }
-    });
+      });
+    }
+    if (RAGGED && lo > 0) {
+      const int lo_h = lo - 4 * h;
+      static_for<16>([&](auto R) __attribute__((always_inline)) {
+        if (8 * (R / 4) + (R % 4) < lo_h) sv[int(R)] = -__builtin_inff();
+      });
+    }
     float mraw = kNegBig;
     static_for<16>([&](auto R) __attribute__((always_inline)) { mraw = fmaxf(mraw, sv[int(R)]); });
     const LanePair mp = lane_pair(mraw);
@@ -349,7 +385,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     const float l_tot = lp.lo + lp.hi;
     const float inv = 1.0f / l_tot;
     uint16_t* orow = o + (row0 + query) * ld_o + head * kD + 4 * h;
-    static_for<4>([&](auto DT) __attribute__((always_inline)) {
+    if (!RAGGED || query < seq) static_for<4>([&](auto DT) __attribute__((always_inline)) {
       float v[16];
       static_for<16>([&](auto R) __attribute__((always_inline)) {
         v[R] = (acc_o[DT][int(R)] * a0 + mrg[2 + 16 * DT + R] * a1) * inv;
@@ -371,17 +407,20 @@ hipError_t launch_attention(const uint16_t* qkv, int64_t ld_qkv, uint16_t* o, in
   if (batch == 0 || seq == 0) return hipSuccess;
   // per-lane copy offsets are 32-bit byte offsets within one key block
   if (static_cast<int64_t>(kBKV) * ld_qkv * 2 >= (int64_t{1} << 31)) return hipErrorInvalidValue;
-  if (head_dim != kD || seq % kBQ != 0) return hipErrorInvalidValue;
+  if (head_dim != kD || seq < kBKV) return hipErrorInvalidValue;
   // log2(e) / sqrt(d), times 1 / kQkScale^2 for the scaled fp16 Q and K
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(static_cast<float>(head_dim)) /
                            (kQkScale * kQkScale);
-  const dim3 grid(static_cast<unsigned>(batch * heads * (seq / kBQ)));
+  const dim3 grid(static_cast<unsigned>(batch * heads * ((seq + kBQ - 1) / kBQ)));
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * kWaves), 0, stream, qkv, ld_qkv, o, ld_o, seq, heads,
+                       scale_log2);
+  };
+  const bool ragged = seq % kBQ != 0;
   if (causal)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, grid, dim3(64 * kWaves), 0, stream, qkv, ld_qkv, o,
-                       ld_o, seq, heads, scale_log2);
+    ragged ? go(attn_fwd_kernel<true, true>) : go(attn_fwd_kernel<true, false>);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, grid, dim3(64 * kWaves), 0, stream, qkv, ld_qkv, o,
-                       ld_o, seq, heads, scale_log2);
+    ragged ? go(attn_fwd_kernel<false, true>) : go(attn_fwd_kernel<false, false>);
   return hipGetLastError();
 }
 

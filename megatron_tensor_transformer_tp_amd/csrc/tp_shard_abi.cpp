@@ -438,8 +438,8 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
   TP_TRY(check_split(heads, t, rank, &hl));
   if (hidden != heads * head_dim) return TP_ERR_INVALID_ARG;
   if (hidden % 8 != 0) return TP_ERR_MISALIGNED;
-  if (head_dim != 128 || seq % 128 != 0) return TP_ERR_UNSUPPORTED;
   const int64_t tokens = batch * seq;
+  if (head_dim != 128 || (tokens > 0 && seq < 32)) return TP_ERR_UNSUPPORTED;
   if (!fits_int32(tokens) || !fits_int32(hidden) || !fits_int32(3 * hl * head_dim))
     return TP_ERR_UNSUPPORTED;
   if (tokens == 0) return TP_OK;

@@ -197,7 +197,9 @@ def test_attn_shard_validation(lib):
     assert attn(lib, rank=2) == BAD_RANK
     assert attn(lib, hidden=1000) == INVALID               # hidden != heads * head_dim
     assert attn(lib, head_dim=64, hidden=512) == UNSUPPORTED
-    assert attn(lib, seq=200) == UNSUPPORTED               # seq not a multiple of 128
+    assert attn(lib, seq=31) == UNSUPPORTED                # shorter than one key block
+    assert attn(lib, seq=200, ws_bytes=1) == WORKSPACE     # any seq >= 32 passes the shape checks
+    assert attn(lib, batch=0, seq=16, ws=None) == OK        # nothing to do
     assert attn(lib, in_dt=F32) == DTYPE
     assert attn(lib, causal=2) == INVALID
     assert attn(lib, x=None) == INVALID

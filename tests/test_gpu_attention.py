@@ -137,17 +137,19 @@ def test_projection_overflow_is_never_finite_and_wrong():
 
 def _attn_shapes(seed, n):
     """n seeded shard shapes: batch 1-3, seq a multiple of 128 up to 1152
-    (1-36 key blocks of 32, so the loop unrolled by 4 ends at every phase),
-    1-6 local heads, t in 1-4, hidden = heads x 128, causal or not."""
+    (1-36 key blocks of 32, so the loop unrolled by 4 ends at every phase)
+    for even draws and any length from 32 to 1152 for odd ones (partial key
+    and query blocks, odd block counts), 1-6 local heads, t in 1-4,
+    hidden = heads x 128, causal or not."""
     rng = np.random.default_rng(seed)
     out = []
-    for _ in range(n):
+    for i in range(n):
         t = int(rng.integers(1, 5))
         hl = int(rng.integers(1, 7))
         while hl * t > 16:
             hl -= 1
-        out.append((int(rng.integers(1, 4)), 128 * int(rng.integers(1, 10)), hl, t,
-                    int(rng.integers(0, t)), bool(rng.random() < 0.5)))
+        seq = 128 * int(rng.integers(1, 10)) if i % 2 == 0 else int(rng.integers(32, 1153))
+        out.append((int(rng.integers(1, 4)), seq, hl, t, int(rng.integers(0, t)), bool(rng.random() < 0.5)))
     return out
 
 
@@ -165,3 +167,41 @@ def test_random_shapes(batch, seq, hl, t, rank, causal):
     ref = oracle.attn_shard(host64(x, "bf16"), host64(wqkv, "bf16"), host64(wo, "bf16"), heads, 128, t,
                             rank, causal)
     assert_close(out, ref, "bf16", f"random attention {wl.name} rank {rank} causal={causal}")
+
+
+@pytest.mark.parametrize("batch,seq,hl,t,rank,causal", [
+    (2, 32, 2, 2, 1, False),    # one key block, its partner a phantom block
+    (2, 33, 2, 2, 0, True),     # a one-key partial block
+    (1, 100, 4, 2, 1, True),    # partial query and key blocks, odd block count
+    (3, 200, 2, 4, 3, False),
+    (1, 1000, 8, 1, 0, True),   # the headline's local heads, 1000 tokens
+    (1, 4095, 1, 8, 5, False),  # one short of the headline length
+])
+def test_ragged_seq(batch, seq, hl, t, rank, causal):
+    """Sequence lengths that are not multiples of the 128-query or 32-key
+    blocks, every output element against the oracle."""
+    heads = hl * t
+    hidden = heads * 128
+    wl = inputs.AttnWorkload(f"attn_ragged_{batch}_{seq}_{hl}_{t}", batch, seq, hidden, heads, 128, t,
+                             "bf16", 1.0, 1.8 / np.sqrt(hidden), "f32", 0.02)
+    x = x_all(wl)
+    wqkv, wo = inputs.attn_wqkv_block(wl, rank), inputs.attn_wo_block(wl, rank)
+    say(f"ragged attention: batch={batch} seq={seq} local heads={hl} t={t} rank={rank} causal={causal}")
+    out = to_np(run(wl, rank, dev(x, "bf16"), dev(wqkv, "bf16"), dev(wo, "bf16"), causal))
+    ref = oracle.attn_shard(host64(x, "bf16"), host64(wqkv, "bf16"), host64(wo, "bf16"), heads, 128, t,
+                            rank, causal)
+    assert_close(out, ref, "bf16", f"ragged attention {wl.name} rank {rank} causal={causal}")
+
+
+def test_short_seq_refused():
+    """A sequence shorter than one 32-key block is refused before any launch."""
+    wl = inputs.AttnWorkload("attn_short", 1, 31, 1024, 8, 128, 2, "bf16", 1.0, 0.02, "f32", 0.02)
+    x = torch.zeros((1, 31, 1024), dtype=torch.bfloat16, device="cuda")
+    wqkv = torch.zeros((1024, 3 * 4 * 128), dtype=torch.bfloat16, device="cuda")
+    wo = torch.zeros((4 * 128, 1024), dtype=torch.bfloat16, device="cuda")
+    out = nan_tensor((1, 31, 1024), torch.float32)
+    ws = torch.empty(binding.tp_attn_shard_workspace_bytes(1, 31, 1024, 8, 128, 2, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    with pytest.raises(binding.TpError, match="UNSUPPORTED"):
+        binding.tp_attn_shard_fwd(x, wqkv, wo, out, ws, heads=8, head_dim=128, t=2, rank=0)
+    assert torch.isnan(out).all()
