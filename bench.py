@@ -198,7 +198,7 @@ PROFILED = {
                                 "t=1 MLP, M=2048, ffn=4096, h=1024 (128 x 128 tiles): H, B read, "
                                 "Z written (bf16 final output)",
                                 "row_gemm_t1_h1024_m2048"),
-    "attention_core": ("attn_fwd_kernel<false>", (0.0, _INF),
+    "attention_core": ("attn_fwd_kernel<false, false>", (0.0, _INF),
                        4.0 * _S * _S * _DL, 2 * (3 * _S * _DL + _S * _DL),
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K "
                        "(fp16) and V (bf16) read once, O written (bf16)",
@@ -325,9 +325,12 @@ def summarize_profiles(trace_csv: str, fetch_csv: str, write_csv: str, mfma_csv:
     out = {"source_sha": kernel_source_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
            "n_simd": N_SIMD, "n_xcd": N_XCD, "commands": PROFILE_CMDS, "kernels": {},
            "traced_bench_line": {k: line[k] for k in ("value", "ms_per_step", "roofline", "kernels")}}
+    missing = [key for key in PROFILED if key not in durs]
+    if missing:
+        # a kernel renamed or no longer launched would otherwise leave its
+        # old summary in profiles/ looking current
+        raise SystemExit(f"no dispatch in the trace matches {missing}: update PROFILED")
     for key, (_pat, _band, flops, alg_bytes, what, stem) in PROFILED.items():
-        if key not in durs:
-            continue
         fb = med(fetch, key, lambda us, c: c["FETCH_SIZE"]) * 1024 * f_scale
         wb = med(write, key, lambda us, c: c["WRITE_SIZE"]) * 1024 * w_scale
         util = med(mfma, key, lambda us, c: c["SQ_VALU_MFMA_BUSY_CYCLES"] /

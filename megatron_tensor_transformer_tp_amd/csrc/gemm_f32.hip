@@ -6,12 +6,16 @@
 // rounded below fp32 anywhere.
 //
 // A is [M, K] row-major, or [K, M] if a_kmajor; B is [K, N] row-major if
-// b_kmajor, else [N, K].  64 x 64 output tile per 256-thread workgroup,
-// BK = 16, each thread a 4 x 4 block; both operand tiles staged in LDS
-// k-major (sA[k][m], sB[k][n]) so the inner product reads are
+// b_kmajor, else [N, K].  T x T output tile per 256-thread workgroup
+// (T = 64: each thread a 4 x 4 block; T = 32 for products with fewer than
+// four 64 x 64 tiles per CU, each thread a 2 x 2 block, so that a CU holds
+// enough waves to hide the load latency), BK = 16; both operand tiles
+// staged in LDS k-major (sA[k][m], sB[k][n]) so the inner product reads are
 // broadcast-friendly.  Edges are masked (zero-filled loads, predicated
 // stores), so any M, N, K >= 1 works.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -19,33 +23,34 @@
 namespace tpk {
 namespace {
 
-constexpr int kBM = 64, kBN = 64, kBKf = 16;
+constexpr int kBKf = 16;
 
-template <int EPI>
+template <int EPI, int T>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
                                                        bool a_kmajor, const float* __restrict__ B,
                                                        int64_t ldb, bool b_kmajor, int M, int N,
                                                        int K, const Epilogue ep) {
-  __shared__ float sA[kBKf][kBM + 4];
-  __shared__ float sB[kBKf][kBN + 4];
+  constexpr int R = T / 16;                 // rows (and columns) per thread
+  __shared__ float sA[kBKf][T + 4];
+  __shared__ float sB[kBKf][T + 4];
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * kBN;   // M tiles on x: no 65535 limit
+  const int m0 = blockIdx.x * T, n0 = blockIdx.y * T;   // M tiles on x: no 65535 limit
 
-  float acc[4][4];
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  float acc[R][R];
+  for (int i = 0; i < R; ++i)
+    for (int j = 0; j < R; ++j) acc[i][j] = 0.0f;
 
   for (int k0 = 0; k0 < K; k0 += kBKf) {
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < R; ++r) {
       const int idx = tid + 256 * r;
-      const int row = idx >> 4, kk = idx & 15;  // A: 64 rows x 16 k
+      const int row = idx >> 4, kk = idx & 15;  // A: T rows x 16 k
       const int gm = m0 + row, gk = k0 + kk;
       sA[kk][row] = (gm < M && gk < K)
                         ? A[a_kmajor ? static_cast<int64_t>(gk) * lda + gm
                                      : static_cast<int64_t>(gm) * lda + gk]
                         : 0.0f;
-      const int kb = idx >> 6, col = idx & 63;  // B: 16 k x 64 cols
+      const int kb = idx / T, col = idx % T;    // B: 16 k x T cols
       const int gkb = k0 + kb, gn = n0 + col;
       sB[kb][col] = (gkb < K && gn < N)
                         ? B[b_kmajor ? static_cast<int64_t>(gkb) * ldb + gn
@@ -55,11 +60,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kBKf; ++kk) {
-      float a[4], b[4];
-      for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty * 4 + i];
-      for (int j = 0; j < 4; ++j) b[j] = sB[kk][tx * 4 + j];
-      for (int i = 0; i < 4; ++i)
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      float a[R], b[R];
+      for (int i = 0; i < R; ++i) a[i] = sA[kk][ty * R + i];
+      for (int j = 0; j < R; ++j) b[j] = sB[kk][tx * R + j];
+      for (int i = 0; i < R; ++i)
+        for (int j = 0; j < R; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
     __syncthreads();
   }
@@ -70,11 +75,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   float* out = static_cast<float*>(ep.out);
   float* pre = static_cast<float*>(ep.pre);
   float* out2 = static_cast<float*>(ep.out2);
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
+  for (int i = 0; i < R; ++i) {
+    const int m = m0 + ty * R + i;
     if (m >= M) continue;
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
+    for (int j = 0; j < R; ++j) {
+      const int n = n0 + tx * R + j;
       if (n >= N) continue;
       const int64_t o = static_cast<int64_t>(m) * ep.ldo + n;
       float v = acc[i][j];
@@ -101,27 +106,33 @@ hipError_t launch_gemm_f32(const float* A, int64_t lda, bool a_kmajor, const flo
                            bool b_kmajor, int64_t M, int64_t N, int64_t K, const Epilogue& ep,
                            hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int64_t tiles_n = (N + kBN - 1) / kBN;
-  if (tiles_n > 65535) return hipErrorInvalidValue;     // grid y limit
-  const dim3 grid(static_cast<unsigned>((M + kBM - 1) / kBM), static_cast<unsigned>(tiles_n));
-  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  switch (ep.kind) {
-    case EPI_LINEAR:
-      hipLaunchKernelGGL(gemm_f32_kernel<EPI_LINEAR>, grid, dim3(256), 0, stream, A, lda, a_kmajor,
-                         B, ldb, b_kmajor, m, n, k, ep);
-      break;
-    case EPI_GELU:
-      hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU>, grid, dim3(256), 0, stream, A, lda, a_kmajor,
-                         B, ldb, b_kmajor, m, n, k, ep);
-      break;
-    case EPI_GELU_BWD:
-      hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU_BWD>, grid, dim3(256), 0, stream, A, lda,
-                         a_kmajor, B, ldb, b_kmajor, m, n, k, ep);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  auto launch = [&](auto tile) {
+    constexpr int T = decltype(tile)::value;
+    const int64_t tiles_n = (N + T - 1) / T;
+    if (tiles_n > 65535) return hipErrorInvalidValue;     // grid y limit
+    const dim3 grid(static_cast<unsigned>((M + T - 1) / T), static_cast<unsigned>(tiles_n));
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    switch (ep.kind) {
+      case EPI_LINEAR:
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI_LINEAR, T>), grid, dim3(256), 0, stream, A, lda,
+                           a_kmajor, B, ldb, b_kmajor, m, n, k, ep);
+        break;
+      case EPI_GELU:
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI_GELU, T>), grid, dim3(256), 0, stream, A, lda,
+                           a_kmajor, B, ldb, b_kmajor, m, n, k, ep);
+        break;
+      case EPI_GELU_BWD:
+        hipLaunchKernelGGL((gemm_f32_kernel<EPI_GELU_BWD, T>), grid, dim3(256), 0, stream, A, lda,
+                           a_kmajor, B, ldb, b_kmajor, m, n, k, ep);
+        break;
+      default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  };
+  const int64_t tiles64 = ((M + 63) / 64) * ((N + 63) / 64);
+  if (tiles64 < 4 * device_cus()) return launch(std::integral_constant<int, 32>{});
+  return launch(std::integral_constant<int, 64>{});
 }
 
 }  // namespace tpk

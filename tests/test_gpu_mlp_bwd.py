@@ -53,14 +53,19 @@ def run_bwd(wl, r, xd, ad, bd, yd, dzd, grad_dt, with_bias=True, da=None):
 
 
 def check_grads(got, ref, dtype, what, keys=("dx", "da", "db", "dbias_a", "dbias_b")):
-    """fp32: every gradient to the stated bound.  bf16: dX (near unit scale)
-    to the stated bound in its own units (floor max(1, rms)); the weight and
-    bias gradients, sums over all the tokens (RMS in the tens to hundreds),
-    with the RMS as the floor."""
+    """dX (near unit scale) to the stated bound: fp32 with the floor 1, bf16
+    in its own units (floor max(1, rms)); the weight and bias gradients,
+    sums over all the tokens (RMS in the tens to hundreds, whose rounding
+    error grows with the summands in either precision), with the RMS as the
+    floor (fp32: max(1, rms), the stated bound at or below unit scale).  The
+    figure with the floor 1 is always printed."""
     for k in keys:
         if got.get(k) is None:
             continue
-        floor = "one" if dtype == "f32" else ("scale" if k == "dx" else "rms")
+        if dtype == "f32":
+            floor = "one" if k == "dx" else "scale"
+        else:
+            floor = "scale" if k == "dx" else "rms"
         assert_close(to_np(got[k]), ref[k], dtype, f"{what} {k}", floor=floor)
 
 
@@ -194,6 +199,25 @@ def test_large_rank_shards(name, rank):
     del xd, ad, bd
     ref = shard_ref(host64(x, "bf16"), host64(a, "bf16"), host64(b, "bf16"), host64(dz, "bf16"))
     check_grads(got, ref, "bf16", f"{name} rank {rank}")
+
+
+def test_f32_shard_on_64x64_tiles():
+    """fp32 forward (saved pre-activation) and backward at 2048 tokens,
+    hidden 2048, f 2048: every product has at least 1024 tiles of 64 x 64,
+    the fp32 GEMM's larger tile (the small fp32 cases run on 32 x 32 tiles)."""
+    wl = inputs.MlpWorkload("f32_2048", 2048, 2048, 4096, 2, "f32", 1.0, 1.0 / np.sqrt(2048),
+                            1.0 / np.sqrt(4096), "f32")
+    x, dz = inputs.mlp_x_rows(wl), inputs.mlp_dz_rows(wl)
+    a, b = inputs.mlp_a_block(wl, 1), inputs.mlp_b_block(wl, 1)
+    ba = inputs.mlp_bias_a_block(wl, 1)
+    xd, ad, bd = dev(x, "f32"), dev(a, "f32"), dev(b, "f32")
+    say("fp32 forward and backward, 2048 tokens, hidden 2048, f 2048")
+    _z, y = run_fwd_save(wl, 1, xd, ad, bd, dev(ba, "f32"))
+    ref = shard_ref(host64(x, "f32"), host64(a, "f32"), host64(b, "f32"), host64(dz, "f32"),
+                    host64(ba, "f32"))
+    assert_close(to_np(y), ref["y"], "f32", "fp32 2048 saved pre-activation")
+    got = run_bwd(wl, 1, xd, ad, bd, y, dev(dz, "f32"), "f32")
+    check_grads(got, ref, "f32", "fp32 2048")
 
 
 def test_ragged_tokens_near_headline():
