@@ -172,19 +172,19 @@ _GEMM = "gemm_bf16_dma_kernel<256, 256, 2, 4, 4, "   # then A k-major, B k-major
 _GEMM128 = "gemm_bf16_dma_kernel<128, 128, 2, 2, 4, "
 _INF = 1e9
 PROFILED = {
-    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0, true>", (500.0, _INF),
+    "column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 2, true>", (500.0, _INF),
                          2.0 * _M * _H * _F, 2 * (_M * _H + _H * _F + _M * _F),
                          "MLP rank shard, M=16384, h=8192, f=4096: X, A_i read, H_i written (bf16)",
                          "column_gemm_gelu_t8_h8192_m16384"),
-    "row_gemm": (_GEMM + "false, true, 0, true, false, 0, true>", (500.0, _INF),
+    "row_gemm": (_GEMM + "false, true, 0, true, false, 2, true>", (500.0, _INF),
                  2.0 * _M * _F * _H, 2 * (_M * _F + _F * _H) + 4 * _M * _H,
                  "MLP rank shard, M=16384, h=8192, f=4096: H_i, B_i read (bf16), Z_i written (fp32)",
                  "row_gemm_t8_h8192_m16384"),
-    "t8_h8192_m4096:column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 0, true>", (100.0, 500.0),
+    "t8_h8192_m4096:column_gemm_gelu": (_GEMM + "false, true, 1, false, false, 2, true>", (100.0, 500.0),
                                         2.0 * _M3 * _H * _F, 2 * (_M3 * _H + _H * _F + _M3 * _F),
                                         "rank 0 of t=8, M=4096, h=8192, f=4096: X, A_0 read, H_0 written (bf16)",
                                         "column_gemm_gelu_t8_h8192_m4096"),
-    "t8_h8192_m4096:row_gemm": (_GEMM + "false, true, 0, true, false, 0, true>", (140.0, 500.0),
+    "t8_h8192_m4096:row_gemm": (_GEMM + "false, true, 0, true, false, 2, true>", (140.0, 500.0),
                                 2.0 * _M3 * _F * _H, 2 * (_M3 * _F + _F * _H) + 4 * _M3 * _H,
                                 "rank 0 of t=8, M=4096, h=8192, f=4096: H_0, B_0 read (bf16), Z_0 written (fp32)",
                                 "row_gemm_t8_h8192_m4096"),
@@ -208,7 +208,7 @@ PROFILED = {
                       "attention rank shard packed QKV projection, M=4096, K=8192, N=3072 "
                       "(one round of 256 128 x 384 tiles), q/k written as scaled fp16, v as bf16",
                       "attn_qkv_gemm_t8_h8192_s4096"),
-    "attn_out_gemm": (_GEMM + "false, true, 0, true, false, 0, true>", (0.0, 140.0),
+    "attn_out_gemm": (_GEMM + "false, true, 0, true, false, 2, true>", (0.0, 140.0),
                       2.0 * _S * _DL * _H, 2 * (_S * _DL + _DL * _H) + 4 * _S * _H,
                       "attention rank shard output projection, M=4096, K=1024, N=8192 (fp32 out)",
                       "attn_out_gemm_t8_h8192_s4096"),
