@@ -427,9 +427,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave sub-tiles of whole 32 x 32 MFMA blocks");
-  static_assert(PAIR == 0 || (!KTAIL && EPI != EPI_SWIGLU && STAGES == 4 &&
+  static_assert(PAIR == 0 || (!KTAIL && (EPI != EPI_SWIGLU || PAIR == 2) && STAGES == 4 &&
                               (PAIR == 1 ? !B_KMAJOR : PAIR == 2 && !A_KMAJOR)),
-                "paired stages: a k-contiguous operand, whole 64-k pairs, 4 single stages");
+                "paired stages: a k-contiguous operand (SwiGLU: A), whole 64-k pairs, 4 single stages");
   static_assert(!MF16 || TM % 2 == 0, "MF16: the k-tile's MFMAs in two halves of whole 32-row blocks");
   using TileA = OperandTile<BM, NW, A_KMAJOR, KTAIL, MF16>;
   using TileB = OperandTile<BN, NW, B_KMAJOR, KTAIL, MF16>;
@@ -894,8 +894,8 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
     // paired stages, else a k-contiguous A does (each copy instruction then
     // reads whole 128-byte lines, which the copy path turns into fewer
     // addresser cycles per byte: 256 x 256 headline products 1.7-3.8% faster)
-    constexpr int kPair = EPI == EPI_SWIGLU || STAGES != 4 ? 0
-                          : !B_KMAJOR                       ? 1
+    constexpr int kPair = STAGES != 4                      ? 0
+                          : !B_KMAJOR && EPI != EPI_SWIGLU  ? 1
                           : !A_KMAJOR                       ? 2
                                                             : 0;
     if constexpr (kPair != 0) {
