@@ -218,7 +218,7 @@ PROFILED = {
                           "rank's [2048, 8192] shard with bf16 bias and residual rows, bf16 out "
                           "(HBM-bound: partial rows, residual and bias read, shard written)",
                           "sp_reduce_scatter_t8_h8192_m16384"),
-    "swiglu_gemm": (_GEMM + "false, true, 3, false, false, 0, true>", (0.0, _INF),
+    "swiglu_gemm": (_GEMM + "false, true, 3, false, false, 2, true>", (0.0, _INF),
                     2.0 * _M * _H * 2 * _F, 2 * (_M * _H + 2 * _H * _F + _M * _F),
                     "SwiGLU column layer, both projections in one product with SiLU(gate) * value "
                     "in the epilogue: X, Wg_i, Wu_i read, H_i written (bf16)",
