@@ -155,6 +155,31 @@ def test_headline_reconstruction_full(headline):
                  floor=float(np.sqrt(wl.t)))
 
 
+def test_large_token_count_sampled():
+    """65536 tokens at the headline widths (t = 8, rank 5): 16 rounds of
+    256 x 256 column tiles and 32 of row tiles, a 2 GiB fp32 partial.  X
+    goes up in row chunks; every output must be written (finite), and four
+    64-row blocks spread over the rounds, the last rows included, are
+    checked against the oracle (the shard is row-independent)."""
+    wl = inputs.MlpWorkload("t8_h8192_m65536", 65536, 8192, 32768, 8, "bf16", 1.0, 0.02, 0.02, "f32")
+    r = 5
+    xd = torch.empty((wl.tokens, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    step = 8192
+    for r0 in range(0, wl.tokens, step):
+        xd[r0:r0 + step] = dev(inputs.mlp_x_rows(wl, r0, step), "bf16")
+    a, b = inputs.mlp_a_block(wl, r), inputs.mlp_b_block(wl, r)
+    say(f"65536 tokens, rank {r}")
+    z = run_shard(wl, r, xd, dev(a, "bf16"), dev(b, "bf16"), "f32")
+    del xd
+    assert bool(torch.isfinite(z).all()), "unwritten or non-finite outputs"
+    a64, b64 = host64(a, "bf16"), host64(b, "bf16")
+    for r0 in (0, 21824, 43712, wl.tokens - 64):
+        x64 = host64(inputs.mlp_x_rows(wl, r0, 64), "bf16")
+        ref = oracle.mlp_shard(x64, a64, b64, 1, 0)
+        got = z[r0:r0 + 64].cpu().numpy().astype(np.float64)
+        assert_close(got, ref, "bf16", f"65536 tokens rank {r} rows {r0}..{r0 + 63}")
+
+
 @pytest.mark.parametrize("tokens,hidden,f,gelu,out", [
     (5, 8, 64, True, "f32"),            # K = 8: the only k-tile is a partial one
     (33, 24, 72, False, "bf16"),        # K = 24
