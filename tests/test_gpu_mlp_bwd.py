@@ -275,6 +275,46 @@ def test_ragged_tokens_near_headline():
     assert ratio < 1.25, f"ragged-token backward {ratio:.2f} times the aligned one"
 
 
+def test_large_token_count_sampled():
+    """65536 tokens at the headline widths (rank 4): the weight-gradient
+    products accumulate over 2048 k-tiles.  dA and dB are checked on a
+    seeded block of 32 of the shard's f columns against the oracle run on
+    that block (the columns are independent GeLU units), dX on three 64-row
+    blocks against the oracle run on those rows (each token's dX depends on
+    that token only); every output must be written (finite)."""
+    wl = inputs.MlpWorkload("bwd_t8_h8192_m65536", 65536, 8192, 32768, 8, "bf16", 1.0, 0.02, 0.02, "f32")
+    r, step = 4, 8192
+    xd = torch.empty((wl.tokens, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    dzd = torch.empty((wl.tokens, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    x_parts, dz_parts = [], []
+    for r0 in range(0, wl.tokens, step):
+        xp, dp = inputs.mlp_x_rows(wl, r0, step), inputs.mlp_dz_rows(wl, r0, step)
+        xd[r0:r0 + step], dzd[r0:r0 + step] = dev(xp, "bf16"), dev(dp, "bf16")
+        x_parts.append(xp)
+        dz_parts.append(dp)
+    a, b = inputs.mlp_a_block(wl, r), inputs.mlp_b_block(wl, r)
+    ad, bd = dev(a, "bf16"), dev(b, "bf16")
+    say(f"backward 65536 tokens, rank {r}")
+    _z, y = run_fwd_save(wl, r, xd, ad, bd)
+    got = run_bwd(wl, r, xd, ad, bd, y, dzd, "f32", with_bias=False)
+    del xd, dzd, y, _z
+    for k in ("dx", "da", "db"):
+        assert bool(torch.isfinite(got[k]).all()), f"{k}: unwritten or non-finite outputs"
+    a64, b64 = host64(a, "bf16"), host64(b, "bf16")
+    cols = np.sort(np.random.default_rng(65536).choice(wl.f, 32, replace=False))
+    x64 = np.concatenate([host64(p, "bf16") for p in x_parts])
+    dz64 = np.concatenate([host64(p, "bf16") for p in dz_parts])
+    del x_parts, dz_parts
+    ref = shard_ref(x64, a64[:, cols], b64[cols, :], dz64)
+    tc = torch.from_numpy(cols).cuda()
+    check_grads({"da": got["da"][:, tc], "db": got["db"][tc, :]}, ref, "bf16",
+                "65536-token column block", keys=("da", "db"))
+    for r0 in (0, 32768, wl.tokens - 64):
+        ref_rows = shard_ref(x64[r0:r0 + 64], a64, b64, dz64[r0:r0 + 64])
+        check_grads({"dx": got["dx"][r0:r0 + 64]}, ref_rows, "bf16", f"65536 tokens dX rows {r0}..",
+                    keys=("dx",))
+
+
 def test_zero_tokens_and_errors():
     wl = inputs.MLP_WORKLOADS["t4_h1024_m1024"]
     ad = dev(inputs.mlp_a_block(wl, 0), "bf16")
