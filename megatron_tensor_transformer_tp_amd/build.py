@@ -27,6 +27,8 @@ SOURCES = [
     "gemm_bf16_256_plain.hip",
     "gemm_bf16_128_gelu.hip",
     "gemm_bf16_128_plain.hip",
+    "gemm_bf16_64_gelu.hip",
+    "gemm_bf16_64_plain.hip",
     "gemm_bf16_384_gelu.hip",
     "gemm_bf16_384_plain.hip",
     "gemm_bf16_256_nt.hip",

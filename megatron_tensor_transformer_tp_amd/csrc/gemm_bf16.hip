@@ -43,22 +43,33 @@ int64_t device_cus() {
 // the 4096 x 8192 x {3072, 1536} products (128 x 384: 0.84, 128 x 128: 0.82
 // of the 256 x 256 rate; a last 128 x 128 round with one workgroup per CU
 // costs 0.73 of a full one).
-// Without the 128 x 384 shape (with_384 false) the choice is between the
-// other two; r128 is the 128 x 128 tile's per-CU rate relative to the
+// The forward's linears also have 64 x 128 tiles (two workgroups per CU,
+// 0.456 of the 256 x 256 rate per CU: fitted to the 2048 x 1024 x 4096 row
+// product, 128 x 128 tiles on half the CUs 31.5 us, 64 x 128 on all 28.4),
+// which win only where 128 x 128 tiles leave CUs idle.  Without the
+// forward-only shapes (forward false) the choice is between 256 x 256 and
+// 128 x 128; r128 is the 128 x 128 tile's per-CU rate relative to the
 // 256 x 256 tile's.
-static int gemm_tile_choice(int64_t M, int64_t N, bool with_384 = true, double r128 = 0.82) {
+static int gemm_tile_choice(int64_t M, int64_t N, bool forward = true, double r128 = 0.82) {
   const int64_t kCUs = device_cus();
   auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  const int64_t t256 = tiles(256, 256), t384 = tiles(128, 384), t128 = tiles(128, 128);
+  // rounds of two workgroups per CU, a last round with at most one per CU
+  // costing 0.73 of a full one, in units of one 256 x 256 tile's time
+  auto cost2 = [&](int64_t t, double area, double rate) {
+    const int64_t rem = t % (2 * kCUs);
+    return (static_cast<double>(t / (2 * kCUs)) + (rem == 0 ? 0.0 : rem <= kCUs ? 0.73 : 1.0)) * 2.0 *
+           area / (256.0 * 256.0) / rate;
+  };
+  const int64_t t256 = tiles(256, 256), t384 = tiles(128, 384);
   const double c256 = static_cast<double>((t256 + kCUs - 1) / kCUs);
-  const double c384 = with_384 ? static_cast<double>((t384 + kCUs - 1) / kCUs) * (128.0 * 384.0) /
-                                     (256.0 * 256.0) / 0.84
-                               : 1e300;
-  const int64_t rem = t128 % (2 * kCUs);
-  const double c128 = (static_cast<double>(t128 / (2 * kCUs)) + (rem == 0 ? 0.0 : rem <= kCUs ? 0.73 : 1.0)) *
-                      2.0 * (128.0 * 128.0) / (256.0 * 256.0) / r128;
-  if (c256 <= c384 && c256 <= c128) return 256;
-  return c384 < c128 ? 384 : 128;
+  const double c384 = forward ? static_cast<double>((t384 + kCUs - 1) / kCUs) * (128.0 * 384.0) /
+                                    (256.0 * 256.0) / 0.84
+                              : 1e300;
+  const double c128 = cost2(tiles(128, 128), 128.0 * 128.0, r128);
+  const double c64 = forward ? cost2(tiles(64, 128), 64.0 * 128.0, 0.456) : 1e300;
+  if (c256 <= c384 && c256 <= c128 && c256 <= c64) return 256;
+  if (c384 <= c128 && c384 <= c64) return 384;
+  return c128 <= c64 ? 128 : 64;
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
@@ -69,7 +80,8 @@ hipError_t launch_gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, i
   switch (gemm_tile_choice(M, N)) {
     case 256: return launch_epi<256, 256>(A, lda, B, ldb, m, n, k, ep, stream);
     case 384: return launch_epi<128, 384>(A, lda, B, ldb, m, n, k, ep, stream);
-    default: return launch_epi<128, 128>(A, lda, B, ldb, m, n, k, ep, stream);
+    case 128: return launch_epi<128, 128>(A, lda, B, ldb, m, n, k, ep, stream);
+    default: return launch_epi<64, 128>(A, lda, B, ldb, m, n, k, ep, stream);
   }
 }
 

@@ -917,7 +917,8 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
 // gemm_bf16_*.hip unit only instantiates its share of them.  256 x 256 and
 // 128 x 384 tiles run 8 waves (2 per SIMD: 256 x 256 as 2 x 4 waves of
 // 128 x 64, 128 x 384 as 2 x 4 of 64 x 96), 128 x 128 tiles 4 waves of
-// 64 x 64 (two workgroups per CU); 4 LDS stages throughout.
+// 64 x 64 and 64 x 128 tiles 1 x 4 waves of 64 x 32 (two workgroups per
+// CU); 4 LDS stages throughout.
 // Every tile multiplies with v_mfma_f32_16x16x32_bf16 (MF16): on this
 // power-capped part it sustains 12-19% more FLOP/s than v_mfma_f32_32x32x16
 // with random operands (fewer accumulator register bytes per FLOP), and the
@@ -928,8 +929,9 @@ constexpr bool kMf16 = true;
 template <int BM, int BN, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                 int M, int N, int K, const Epilogue& ep, hipStream_t stream) {
+  constexpr int kWgm = BM == 64 ? 1 : 2;
   constexpr int kWgn = BM == 128 && BN == 128 ? 2 : 4;
-  return gemm_detail::launch_tile_dma<BM, BN, 2, kWgn, 4, false, true, EPI, OUT_F32, kMf16>(
+  return gemm_detail::launch_tile_dma<BM, BN, kWgm, kWgn, 4, false, true, EPI, OUT_F32, kMf16>(
       A, lda, B, ldb, M, N, K, ep, stream);
 }
 

@@ -153,8 +153,9 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[TN][TM], int m_
           static_for<4>([&](auto R) __attribute__((always_inline)) { v[R] = acc[J][I][4 * G + R]; });
           if constexpr (EPI == EPI_QKV_F16) {
             static_assert(!OUT_F32, "the packed projection is 16-bit");
-            // every wave's columns lie in one 128-column part (wave widths 64
-            // or 128 at 64-aligned offsets), so the part is wave-uniform
+            // this store's columns (MF16: 16 at a 16-aligned offset; 8 at an
+            // 8-aligned one otherwise) lie in one 128-column part, so the
+            // part is wave-uniform
             if (__builtin_amdgcn_readfirstlane(((n_lane + col) / kQkvPart) % 3) < 2) {
               typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
               const f16x2_t a = {static_cast<_Float16>(v[0] * kQkScale), static_cast<_Float16>(v[1] * kQkScale)};

@@ -116,6 +116,7 @@ def tail_mask(K, kc, place):
 @pytest.mark.parametrize("R,NW,kmajor,rows,K", [
     (256, 8, False, 300, 200), (256, 8, False, 16, 8), (256, 8, True, 264, 300), (256, 8, True, 8, 1),
     (128, 4, False, 300, 136), (128, 4, True, 1000, 40), (256, 8, False, 257, 40), (384, 8, True, 3072, 8192),
+    (64, 4, False, 100, 72), (64, 4, False, 2048, 4096),
 ])
 def test_single_stage_sources_in_bounds(R, NW, kmajor, rows, K):
     nk = -(-K // KBK)
@@ -271,11 +272,11 @@ def pair_copies(R, NW, r0, rows, K, j):
     return lds
 
 
-@pytest.mark.parametrize("R,NW", [(256, 8), (128, 8), (128, 4)])
+@pytest.mark.parametrize("R,NW", [(256, 8), (128, 8), (128, 4), (64, 4)])
 @pytest.mark.parametrize("rows,K,r0,j", [(8192, 4096, 0, 0), (8192, 4096, 7936, 63), (300, 128, 256, 1), (260, 64, 256, 0)])
 def test_pair_fragments(R, NW, rows, K, r0, j):
-    """B pairs of the 256 x 256 tile (8 waves), A pairs of the 128 x 384 (8
-    waves) and 128 x 128 (4 waves) tiles."""
+    """B pairs of the 256 x 256 tile (8 waves), A pairs of the 256 x 256 and
+    128 x 384 (8 waves), 128 x 128 and 64 x 128 (4 waves) tiles."""
     lds = pair_copies(R, NW, r0, rows, K, j)
     for row0, h, s in itertools.product(range(0, R, 32), range(2), range(2)):
         banks = {}
@@ -403,7 +404,7 @@ def test_kmajor_fragments16_through_the_transposing_read(R, NW):
     assert not banks_distinct(addresses(0, 0, False), 0)
 
 
-@pytest.mark.parametrize("R,NW", [(256, 8), (128, 8), (128, 4)])
+@pytest.mark.parametrize("R,NW", [(256, 8), (128, 8), (128, 4), (64, 4)])
 @pytest.mark.parametrize("rows,K,r0,j", [(8192, 4096, 0, 0), (300, 128, 256, 1)])
 def test_pair_fragments16(R, NW, rows, K, r0, j):
     """OperandPairTile::frag16: half h of pair j, lane l gets row row0 + l % 16,

@@ -189,6 +189,8 @@ def test_large_token_count_sampled():
     (513, 1024, 520, True, "bf16"),
     (4000, 1000, 4096, True, "bf16"),   # 256x256 tile path, ragged M and K
     (4000, 1000, 3000, True, "bf16"),   # 128x384 tile path, ragged M, N and K
+    (2048, 1024, 1024, True, "bf16"),   # 64x128 tile path (128 tiles of 128x128 fill half the CUs)
+    (1900, 1000, 1000, True, "f32"),    # 64x128 tiles, ragged M, N and K
 ])
 def test_column_linear_ragged(tokens, hidden, f, gelu, out):
     t = 2
@@ -211,6 +213,9 @@ def test_column_linear_ragged(tokens, hidden, f, gelu, out):
     (1000, 520, 1024, 0, "f32"),
     (4000, 1000, 4096, 0, "f32"),       # 256x256 tile path, ragged M and K, residual
     (4000, 1000, 3000, 0, "f32"),       # 128x384 tile path, ragged M, N and K, residual
+    (2048, 4096, 1024, 0, "f32"),       # 64x128 tiles, paired A stages, fp32 restaging, residual
+    (2000, 4000, 1000, 0, "f32"),       # 64x128 tiles, single stages (K % 64 != 0), ragged M and N
+    (2048, 4096, 1024, 1, "bf16"),      # 64x128 tiles, bf16 out
 ])
 def test_row_linear_ragged(tokens, f, hidden, rank, out):
     t = 2
