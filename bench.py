@@ -193,9 +193,9 @@ PROFILED = {
                                         "t=1 MLP, M=2048, h=1024, ffn=4096 (128 x 128 tiles): X, A read, "
                                         "H written (bf16)",
                                         "column_gemm_gelu_t1_h1024_m2048"),
-    "t1_h1024_m2048:row_gemm": (_GEMM128 + "false, true, 0, false, false, 2, true>", (0.0, _INF),
+    "t1_h1024_m2048:row_gemm": ("gemm_bf16_dma_kernel<64, 128, 1, 4, 4, false, true, 0, false, false, 2, true>", (0.0, _INF),
                                 2.0 * _M2 * _F2 * _H2, 2 * (_M2 * _F2 + _F2 * _H2) + 2 * _M2 * _H2,
-                                "t=1 MLP, M=2048, ffn=4096, h=1024 (128 x 128 tiles): H, B read, "
+                                "t=1 MLP, M=2048, ffn=4096, h=1024 (64 x 128 tiles): H, B read, "
                                 "Z written (bf16 final output)",
                                 "row_gemm_t1_h1024_m2048"),
     "attention_core": ("attn_fwd_kernel<false, false>", (0.0, _INF),
