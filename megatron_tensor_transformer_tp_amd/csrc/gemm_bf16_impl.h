@@ -271,8 +271,7 @@ hipError_t launch_gemm_bf16_cfg(const uint16_t* A, int64_t lda, const uint16_t* 
                                 int M, int N, int K, const Epilogue& ep, hipStream_t stream);
 
 // Products with k-major flags (256 x 256 or 128 x 128 tiles, copy kernel);
-// instantiated in the gemm_bf16_{256,128}_{nt,tn}.hip and
-// gemm_bf16_256_swiglu.hip units.
+// instantiated in the gemm_bf16_{256,128}_{nt,tn,swiglu}.hip units.
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int EPI, bool OUT_F32>
 hipError_t launch_gemm_bf16_t_cfg(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                   int M, int N, int K, const Epilogue& ep, hipStream_t stream);
