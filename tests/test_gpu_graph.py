@@ -88,3 +88,55 @@ def test_attention_and_sp_replay():
         binding.tp_sp_reduce_scatter([out, other], sp_out, t=2, rank=1)
 
     _replay_matches(run, [out, sp_out])
+
+
+def test_swiglu_linears_ragged_attention_and_empty_backward_replay():
+    """One graph with the entry points the other captures leave out: the
+    SwiGLU shard, the column linear with GeLU, the standalone GeLU, the row
+    linear with bias and residual, attention at a length that is not a
+    multiple of its blocks (the ragged kernel, causal), and a backward over
+    zero tokens (its gradients zeroed by a fill kernel, not a memset)."""
+    wl = inputs.MLP_WORKLOADS["t4_h1024_m1024"]
+    r = 2
+    say("graph: SwiGLU shard, column / row linears, GeLU, ragged causal attention, empty backward")
+    xd = dev(inputs.mlp_x_rows(wl), "bf16")
+    ad, bd = dev(inputs.mlp_a_block(wl, r), "bf16"), dev(inputs.mlp_b_block(wl, r), "bf16")
+    wg, wu = dev(inputs.mlp_wg_block(wl, r), "bf16"), dev(inputs.mlp_wu_block(wl, r), "bf16")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    zs = torch.empty((wl.tokens, wl.hidden), **f32)
+    wss = torch.empty(binding.tp_mlp_swiglu_shard_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t,
+                                                                  torch.bfloat16), dtype=torch.uint8, device="cuda")
+    y = torch.empty((wl.tokens, wl.f), **f32)
+    h = torch.empty((wl.tokens, wl.f), dtype=torch.bfloat16, device="cuda")
+    bias = torch.randn((wl.hidden,), device="cuda").to(torch.bfloat16)
+    res = torch.randn((wl.tokens, wl.hidden), device="cuda").to(torch.bfloat16)
+    zr = torch.empty((wl.tokens, wl.hidden), **f32)
+
+    aw = inputs.AttnWorkload("attn_graph_ragged", 2, 200, 1024, 8, 128, 2, "bf16", 1.0, 1.8 / np.sqrt(1024),
+                             "f32", 0.02)
+    xa = dev(np.stack([inputs.attn_x(aw, b) for b in range(aw.batch)]), "bf16")
+    wqkv, wo = dev(inputs.attn_wqkv_block(aw, 1), "bf16"), dev(inputs.attn_wo_block(aw, 1), "bf16")
+    wsa = torch.empty(binding.tp_attn_shard_workspace_bytes(aw.batch, aw.seq, aw.hidden, aw.heads, aw.head_dim,
+                                                            aw.t, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    oa = torch.empty((aw.batch * aw.seq, aw.hidden), **f32)
+
+    x0 = torch.empty((0, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    y0 = torch.empty((0, wl.f), dtype=torch.bfloat16, device="cuda")
+    dx0 = torch.empty((0, wl.hidden), **f32)
+    da0, db0 = torch.empty((wl.hidden, wl.f), **f32), torch.empty((wl.f, wl.hidden), **f32)
+    dba0, dbb0 = torch.empty((wl.f,), **f32), torch.empty((wl.hidden,), **f32)
+    wsb = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+    def run():
+        binding.tp_mlp_swiglu_shard_fwd(xd, wg, wu, bd, zs, wss, ffn=wl.ffn, t=wl.t, rank=r)
+        binding.tp_column_linear(xd, ad, y, ffn=wl.ffn, t=wl.t, rank=r)
+        binding.tp_gelu(y, h)
+        binding.tp_row_linear(h, bd, zr, ffn=wl.ffn, t=wl.t, rank=0, bias=bias, residual=res)
+        binding.tp_attn_shard_fwd(xa, wqkv, wo, oa, wsa, heads=aw.heads, head_dim=aw.head_dim, t=aw.t,
+                                  rank=1, causal=True)
+        binding.tp_mlp_shard_bwd(x0, ad, bd, y0, x0, dx0, da0, db0, wsb, ffn=wl.ffn, t=wl.t, rank=r,
+                                 dbias_a_i=dba0, dbias_b=dbb0)
+
+    _replay_matches(run, [zs, y, h, zr, oa, da0, db0, dba0, dbb0])
+    for g in (da0, db0, dba0, dbb0):
+        assert bool((g == 0).all()), "gradients over zero tokens must be zero"
