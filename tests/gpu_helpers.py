@@ -1,5 +1,7 @@
 """Shared helpers for the GPU parity tests (host <-> device marshalling and
 the error metrics the tolerances are stated in)."""
+import os
+
 import numpy as np
 import torch
 
@@ -9,6 +11,10 @@ from megatron_tensor_transformer_tp_amd import inputs
 BF16_MAX, BF16_FRO = 2e-2, 5e-3
 # fp32 path: relative 1e-5, read as both bounds.
 F32_MAX, F32_FRO = 1e-5, 1e-5
+
+# Opt-in wider sweeps: TP_SHAPE_SWEEP=k makes the seeded random-shape tests
+# draw k times as many shapes (the default draws come first, unchanged).
+SHAPE_SWEEP = max(1, int(os.environ.get("TP_SHAPE_SWEEP", "1")))
 
 
 def say(msg: str) -> None:

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from megatron_tensor_transformer_tp_amd import binding, inputs
-from tests.gpu_helpers import assert_close, dev, host64, nan_tensor, say, to_np
+from tests.gpu_helpers import SHAPE_SWEEP, assert_close, dev, host64, nan_tensor, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -153,7 +153,7 @@ def _attn_shapes(seed, n):
     return out
 
 
-@pytest.mark.parametrize("batch,seq,hl,t,rank,causal", _attn_shapes(11, 10))
+@pytest.mark.parametrize("batch,seq,hl,t,rank,causal", _attn_shapes(11, 10 * SHAPE_SWEEP))
 def test_random_shapes(batch, seq, hl, t, rank, causal):
     heads = hl * t
     hidden = heads * 128

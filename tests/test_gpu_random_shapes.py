@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from megatron_tensor_transformer_tp_amd import binding, inputs
-from tests.gpu_helpers import assert_close, dev, host64, nan_tensor, say, to_np
+from tests.gpu_helpers import SHAPE_SWEEP, assert_close, dev, host64, nan_tensor, say, to_np
 from tests.test_gpu_mlp_bwd import check_grads, run_bwd, run_fwd_save, shard_ref
 
 pytestmark = pytest.mark.gpu
@@ -44,7 +44,7 @@ def _shapes(seed, n, large_every=0):
     return out
 
 
-@pytest.mark.parametrize("tokens,hidden,f", _shapes(2024, 16, large_every=2))
+@pytest.mark.parametrize("tokens,hidden,f", _shapes(2024, 16 * SHAPE_SWEEP, large_every=2))
 def test_column_and_row_linear(tokens, hidden, f):
     t = 2
     wl = inputs.MlpWorkload(f"rand_{tokens}_{hidden}_{f}", tokens, hidden, f * t, t, "bf16", 1.0, 0.05, 0.05,
@@ -70,7 +70,7 @@ def test_column_and_row_linear(tokens, hidden, f):
     assert_close(zz, ref_z, "bf16", "random row_linear")
 
 
-@pytest.mark.parametrize("tokens,hidden,f", _shapes(7, 8))
+@pytest.mark.parametrize("tokens,hidden,f", _shapes(7, 8 * SHAPE_SWEEP))
 def test_backward(tokens, hidden, f):
     wl = inputs.MlpWorkload(f"rand_bwd_{tokens}_{hidden}_{f}", tokens, hidden, 2 * f, 2, "bf16", 1.0,
                             0.05, 0.05, "f32")
@@ -93,7 +93,7 @@ def _f32_shapes(seed, n):
             for _ in range(n)]
 
 
-@pytest.mark.parametrize("tokens,hidden,f", _f32_shapes(5, 6))
+@pytest.mark.parametrize("tokens,hidden,f", _f32_shapes(5, 6 * SHAPE_SWEEP))
 def test_f32_column_and_row_linear(tokens, hidden, f):
     t = 2
     wl = inputs.MlpWorkload(f"rand_f32_{tokens}_{hidden}_{f}", tokens, hidden, f * t, t, "f32", 1.0,

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from megatron_tensor_transformer_tp_amd import binding, inputs
-from tests.gpu_helpers import assert_close, dev, host64, nan_tensor, rms, say, to_np
+from tests.gpu_helpers import SHAPE_SWEEP, assert_close, dev, host64, nan_tensor, rms, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -164,7 +164,7 @@ def _swiglu_shapes(seed, n):
     return out
 
 
-@pytest.mark.parametrize("tokens,hidden,f,rank", _swiglu_shapes(31, 9))
+@pytest.mark.parametrize("tokens,hidden,f,rank", _swiglu_shapes(31, 9 * SHAPE_SWEEP))
 def test_bf16_random_shapes(tokens, hidden, f, rank):
     wl = inputs.MlpWorkload(f"swiglu_rand_{tokens}_{hidden}_{f}", tokens, hidden, 2 * f, 2, "bf16", 1.0,
                             0.05, 0.05, "f32")
