@@ -47,6 +47,9 @@
 //     exp = 0 and never NaN; it is raised lazily (only when a block's max
 //     exceeds it by more than 8 in log2 units, decided per wave), so the
 //     64-register output rescale is rare;
+//   * causal: only the key blocks that cross the diagonal of a wave's 32
+//     queries run the mask comparisons (a wave-uniform test of the block's
+//     last key against the wave's first query);
 //   * any sequence of at least 32 tokens: a partial last key block is read
 //     as the window of the last 32 keys (a uniform offset) with its keys
 //     before the block masked, an odd block count is padded by a fully
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int col_q = head * 3 * kD, col_k = col_q + kD, col_v = col_q + 2 * kD;
   const int h = lane >> 5;                 // which half of the keys / dims this lane holds
   const int query = qb * kBQ + (wave & 3) * 32 + (lane & 31);
+  const int wave_q0 = qb * kBQ + (wave & 3) * 32;   // the wave's first query (uniform)
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[query][16t + 8h .. +7]
   // (a query past the end of the sequence, in the last block, reads the last
@@ -223,26 +227,32 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
 
   // Masks and the block's max (log2 units; this lane: its query and 16 of
   // the 32 keys, S^T rows 8 (R / 4) + 4 h + R % 4 of the block's window).
-  // A key is masked when it is later than the query (causal) or, in a
-  // partial or phantom block (a workgroup-uniform branch), when it precedes
-  // the block (already counted).  The max is taken on the raw scores: it
-  // commutes with the positive scale, which enters the exponent through one
-  // fma.
+  // A key is masked when it is later than the query (causal; only a block
+  // whose last key is later than the wave's first query can hold such a
+  // key, so the others skip the comparisons in a wave-uniform branch) or,
+  // in a partial or phantom block (a workgroup-uniform branch), when it
+  // precedes the block (already counted).  The max is taken on the raw
+  // scores: it commutes with the positive scale, which enters the exponent
+  // through one fma.
   auto block_max = [&](f32x16_t& sv, int kb) __attribute__((always_inline)) {
     // window place of element R: 4 h + c(R), c(R) = 8 (R / 4) + R % 4
     const int kbase = key_base(kb);
     const int lo = kb * kBKV - kbase;   // places before lo: already counted (uniform)
     if constexpr (CAUSAL && RAGGED) {
       // the same comparison as a threshold on c(R) (fewer registers here)
-      const int hi = query - kbase - 4 * h;
-      static_for<16>([&](auto R) __attribute__((always_inline)) {
-        if (8 * (R / 4) + (R % 4) > hi) sv[int(R)] = -__builtin_inff();
-      });
+      if (kbase + kBKV - 1 > wave_q0) {
+        const int hi = query - kbase - 4 * h;
+        static_for<16>([&](auto R) __attribute__((always_inline)) {
+          if (8 * (R / 4) + (R % 4) > hi) sv[int(R)] = -__builtin_inff();
+        });
+      }
     } else if constexpr (CAUSAL) {
-      static_for<16>([&](auto R) __attribute__((always_inline)) {
-        const int key = kbase + 8 * (R / 4) + 4 * h + (R % 4);
-        if (key > query) sv[int(R)] = -__builtin_inff();
-      });
+      if (kbase + kBKV - 1 > wave_q0) {
+        static_for<16>([&](auto R) __attribute__((always_inline)) {
+          const int key = kbase + 8 * (R / 4) + 4 * h + (R % 4);
+          if (key > query) sv[int(R)] = -__builtin_inff();
+        });
+      }
     }
     if (RAGGED && lo > 0) {
       const int lo_h = lo - 4 * h;
