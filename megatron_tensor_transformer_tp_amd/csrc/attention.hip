@@ -25,7 +25,8 @@
 //     block (MFMA) while it takes the max of the next block; the wave raises
 //     its issue priority (s_setprio) for the first of the two phases;
 //   * grid ids are ordered head-fastest, so with 8 local heads each XCD
-//     serves one head and its K/V stay in that XCD's L2;
+//     serves one head and its K/V stay in that XCD's L2; causal grids run
+//     the query blocks from the last (longest row) to the first;
 //   * K and V of a 32-key block (16 KiB) arrive by global->LDS copies (saddr
 //     form: uniform base + 32-bit lane offset); 8 LDS stages, 4 per group:
 //     the current block, the next block, one in flight and one being issued;
@@ -123,8 +124,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int nqb = RAGGED ? (seq + kBQ - 1) / kBQ : seq / kBQ;
   const int id = blockIdx.x;
   const int head = id % heads;
-  const int qb = (id / heads) % nqb;
-  const int b = id / (heads * nqb);
+  // causal rows grow with the query block: the longest are dispatched
+  // first (query block slowest, descending), so that when the grid takes
+  // several rounds the shorter ones fill in behind them
+  const int batch = static_cast<int>(gridDim.x) / (heads * nqb);
+  const int qb = CAUSAL ? nqb - 1 - id / (heads * batch) : (id / heads) % nqb;
+  const int b = CAUSAL ? (id / heads) % batch : id / (heads * nqb);
 
   const int64_t row0 = static_cast<int64_t>(b) * seq;   // first token row of this batch
   const int col_q = head * 3 * kD, col_k = col_q + kD, col_v = col_q + 2 * kD;

@@ -76,3 +76,25 @@ def test_the_mask_threshold_forms_agree(seq):
                     key = kbase + place
                     assert (c < lo - 4 * h) == (key < kb * KBKV)
                     assert (c > query - kbase - 4 * h) == (key > query)
+
+
+def grid_map(i, batch, heads, nqb, causal):
+    """Workgroup id -> (batch, head, query block), as the kernel derives it."""
+    head = i % heads
+    if causal:
+        return (i // heads) % batch, head, nqb - 1 - i // (heads * batch)
+    return i // (heads * nqb), head, (i // heads) % nqb
+
+
+@pytest.mark.parametrize("batch,heads,nqb", [(1, 8, 32), (3, 5, 7), (2, 16, 1), (4, 1, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grid_map_covers_every_block_once(batch, heads, nqb, causal):
+    """Every (batch, head, query block) gets exactly one workgroup; heads
+    vary fastest (one head per XCD with 8 local heads); causal grids run the
+    query blocks, whose rows grow with the index, from the last to the first."""
+    n = batch * heads * nqb
+    got = [grid_map(i, batch, heads, nqb, causal) for i in range(n)]
+    assert sorted(got) == [(b, h, q) for b in range(batch) for h in range(heads) for q in range(nqb)]
+    assert all(got[i][1] == i % heads for i in range(n))
+    if causal:
+        assert all(got[i][2] >= got[i + 1][2] for i in range(n - 1))
