@@ -89,6 +89,15 @@ constexpr float kRescaleSlack = 8.0f;
 static_assert(kStages * kStage <= 160 * 1024, "LDS");
 static_assert(kWaves / 2 * 64 * 66 * 4 <= kStages * kStage, "merge area");
 static_assert(kQkvPart == kD, "q / k / v parts of head_dim columns");
+// Split causal rows: values per (token, head) partial state (the
+// unnormalised output, then the running max and the weight sum), stored
+// value-major, part[half][head][value][token], so that a store or load of
+// one value by a wave covers consecutive tokens.
+constexpr int kPartValues = kD + 2;
+static_assert(kPartValues == 130, "attn_part_floats");
+// shortest sequence whose rows are split (each half then has at least one
+// iteration, and the split pays for its extra launch)
+constexpr int kSplitMinSeq = 2048;
 
 // One global->LDS copy with a uniform base (SGPR pair) and a per-lane 32-bit
 // byte offset: lane t's 16 bytes land at LDS byte address lds_addr + 16 t
@@ -110,12 +119,17 @@ __device__ __forceinline__ LanePair lane_pair(float v) {
 }
 
 // RAGGED: seq is not a multiple of 128 (partial query and key blocks); the
-// other instantiation carries none of the code for them.
-template <bool CAUSAL, bool RAGGED>
+// other instantiation carries none of the code for them.  SPLIT: two
+// workgroups per query block, each taking one half of the row's key
+// iterations; each publishes its partial state (unnormalised output, max,
+// weight sum) in `part`, counts itself in `arrivals` (zeroed before the
+// launch), and the second to arrive merges the two and stores O.
+template <bool CAUSAL, bool RAGGED, bool SPLIT>
 __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restrict__ qkv,
                                                        int64_t ld_qkv, uint16_t* __restrict__ o,
                                                        int64_t ld_o, int seq, int heads,
-                                                       float scale_log2) {
+                                                       float scale_log2, float* __restrict__ part,
+                                                       int* __restrict__ arrivals) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
   const int lane = threadIdx.x & 63;
@@ -126,10 +140,14 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   const int head = id % heads;
   // causal rows grow with the query block: the longest are dispatched
   // first (query block slowest, descending), so that when the grid takes
-  // several rounds the shorter ones fill in behind them
-  const int batch = static_cast<int>(gridDim.x) / (heads * nqb);
-  const int qb = CAUSAL ? nqb - 1 - id / (heads * batch) : (id / heads) % nqb;
-  const int b = CAUSAL ? (id / heads) % batch : id / (heads * nqb);
+  // several rounds the shorter ones fill in behind them; the two halves of
+  // a split row are neighbours (same head, so the same XCD with 8 heads)
+  const int nsplit = SPLIT ? 2 : 1;
+  const int batch = static_cast<int>(gridDim.x) / (heads * nqb * nsplit);
+  const int rest = SPLIT ? id / heads / 2 : id / heads;
+  const int half_id = SPLIT ? (id / heads) % 2 : 0;
+  const int qb = CAUSAL ? nqb - 1 - rest / batch : rest % nqb;
+  const int b = CAUSAL ? rest % batch : rest / nqb;
 
   const int64_t row0 = static_cast<int64_t>(b) * seq;   // first token row of this batch
   const int col_q = head * 3 * kD, col_k = col_q + kD, col_v = col_q + 2 * kD;
@@ -170,7 +188,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   // masked) so that both groups run the same iterations.
   const int nblk_all = RAGGED ? (seq + kBKV - 1) / kBKV : seq / kBKV;
   const int nblk = CAUSAL ? min(nblk_all, (qb + 1) * (kBQ / kBKV)) : nblk_all;
-  const int nit = RAGGED ? (nblk + 1) / 2 : nblk / 2;
+  const int nit_row = RAGGED ? (nblk + 1) / 2 : nblk / 2;
+  // this workgroup's iterations: all of the row's, or one half of them
+  // (the first half rounded up); blk0 is its first key block
+  const int nit_first = (nit_row + 1) / 2;
+  const int nit = SPLIT ? (half_id == 0 ? nit_first : nit_row - nit_first) : nit_row;
+  const int blk0 = SPLIT && half_id == 1 ? 2 * nit_first : 0;
   // first key of block kb's window
   auto key_base = [seq](int kb) { return RAGGED ? min(kb * kBKV, seq - kBKV) : kb * kBKV; };
 
@@ -182,12 +205,13 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   // LDS instruction's immediate field carries.
   auto stage_off = [](int j) { return (j % 2) * kCycle * kStage + ((j / 2) % kCycle) * kStage; };
 
-  // Copies of blocks 2 it and 2 it + 1 (clamped to the last block).
+  // Copies of blocks blk0 + 2 it and blk0 + 2 it + 1 (clamped to the last
+  // block) into the stages of local blocks 2 it, 2 it + 1.
   auto issue = [&](int it) __attribute__((always_inline)) {
     static_for<kCopies>([&](auto Q) __attribute__((always_inline)) {
       const int q = wave * kCopies + Q;
       const int j = 2 * it + q / kCopiesPerBlock;
-      const int kc = min(j, nblk - 1);
+      const int kc = min(blk0 + j, nblk - 1);
       const int rem = q % kCopiesPerBlock;
       const uint16_t* base = RAGGED ? qkv + (row0 + key_base(kc)) * ld_qkv
                                     : qkv + row0 * ld_qkv + kc * block_step;
@@ -345,7 +369,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
   // parity (the unroll factor is even), so no copy passes them on
   f32x16_t s_buf[2];
   s_buf[0] = qk(0);                             // block group: stage offset 0 in the group's half
-  raise_max(block_max(s_buf[0], group));
+  raise_max(block_max(s_buf[0], blk0 + group));
 
   auto step = [&](int it, auto U) __attribute__((always_inline)) {
     constexpr int ust = U * kStage;                        // block 2 it + group
@@ -364,7 +388,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     pv(pf, ust);
-    const float mx = block_max(s_buf[N], 2 * it + 2 + group);
+    const float mx = block_max(s_buf[N], blk0 + 2 * it + 2 + group);
     if (it + 1 < nit) raise_max(mx);
   };
   static_assert(kCycle % 2 == 0, "score buffers alternate within one unrolled group");
@@ -391,34 +415,113 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     });
   }
   lds_barrier();
-  if (group == 0) {
-    const float m1 = mrg[0], l1 = mrg[1];
-    const float m = fmaxf(m_run, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-    const float l_lane = l_run * a0 + l1 * a1;
-    const LanePair lp = lane_pair(l_lane);
-    const float l_tot = lp.lo + lp.hi;
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = o + (row0 + query) * ld_o + head * kD + 4 * h;
-    if (!RAGGED || query < seq) static_for<4>([&](auto DT) __attribute__((always_inline)) {
-      float v[16];
-      static_for<16>([&](auto R) __attribute__((always_inline)) {
-        v[R] = (acc_o[DT][int(R)] * a0 + mrg[2 + 16 * DT + R] * a1) * inv;
+  if constexpr (!SPLIT) {
+    if (group == 0) {
+      const float m1 = mrg[0], l1 = mrg[1];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+      const float l_lane = l_run * a0 + l1 * a1;
+      const LanePair lp = lane_pair(l_lane);
+      const float l_tot = lp.lo + lp.hi;
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = o + (row0 + query) * ld_o + head * kD + 4 * h;
+      if (!RAGGED || query < seq) static_for<4>([&](auto DT) __attribute__((always_inline)) {
+        float v[16];
+        static_for<16>([&](auto R) __attribute__((always_inline)) {
+          v[R] = (acc_o[DT][int(R)] * a0 + mrg[2 + 16 * DT + R] * a1) * inv;
+        });
+        // O[query][dt*32 + 8g + 4h + r]: 4 consecutive dims per store
+        static_for<4>([&](auto G) __attribute__((always_inline)) {
+          const u32x2_t w = {pack_bf16x2(v[4 * G], v[4 * G + 1]), pack_bf16x2(v[4 * G + 2], v[4 * G + 3])};
+          *reinterpret_cast<u32x2_t*>(orow + DT * 32 + 8 * G) = w;
+        });
       });
-      // O[query][dt*32 + 8g + 4h + r]: 4 consecutive dims per store
-      static_for<4>([&](auto G) __attribute__((always_inline)) {
-        const u32x2_t w = {pack_bf16x2(v[4 * G], v[4 * G + 1]), pack_bf16x2(v[4 * G + 2], v[4 * G + 3])};
-        *reinterpret_cast<u32x2_t*>(orow + DT * 32 + 8 * G) = w;
+    }
+  } else {
+    // This half's state (group 0 merges its two groups without
+    // normalising) goes to `part` (value-major), by device-scope
+    // atomic stores (written where every XCD sees them, so no cache
+    // write-back or invalidation is needed); once they have completed, one
+    // thread counts the workgroup in; the second of the row's two
+    // workgroups to arrive reads the other half's state by device-scope
+    // atomic loads and stores O = (O_a w_a + O_b w_b) / (l_a w_a + l_b w_b),
+    // w = 2^(m - max), symmetric in the halves, so the result does not
+    // depend on which of the two arrives last.
+    const int64_t tokens = static_cast<int64_t>(batch) * seq;
+    const int64_t token = row0 + query;
+    float m = 0.0f, l_tot = 0.0f;
+    const bool live = !RAGGED || query < seq;
+    if (group == 0) {
+      const float m1 = mrg[0], l1 = mrg[1];
+      m = fmaxf(m_run, m1);
+      const float a0 = __builtin_amdgcn_exp2f(m_run - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+      const LanePair lp = lane_pair(l_run * a0 + l1 * a1);
+      l_tot = lp.lo + lp.hi;
+      static_for<4>([&](auto DT) __attribute__((always_inline)) {
+        static_for<16>([&](auto R) __attribute__((always_inline)) {
+          acc_o[DT][int(R)] = acc_o[DT][int(R)] * a0 + mrg[2 + 16 * DT + R] * a1;
+        });
       });
-    });
+      if (live) {
+        float* pr = part + (static_cast<int64_t>(half_id) * heads + head) * kPartValues * tokens + token;
+        static_for<4>([&](auto DT) __attribute__((always_inline)) {
+          static_for<16>([&](auto R) __attribute__((always_inline)) {
+            __hip_atomic_store(pr + (DT * 32 + 8 * (R / 4) + 4 * h + R % 4) * tokens, acc_o[DT][int(R)],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          });
+        });
+        if (h == 0) {
+          __hip_atomic_store(pr + kD * tokens, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(pr + (kD + 1) * tokens, l_tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      wait_vmcnt<0>();
+    }
+    int* flag = reinterpret_cast<int*>(smem + kStages * kStage - 16);   // past the merge area
+    lds_barrier();
+    if (threadIdx.x == 0) *flag = atomicAdd(arrivals + (static_cast<int64_t>(b) * nqb + qb) * heads + head, 1);
+    lds_barrier();
+    if (*flag == 1 && group == 0) {
+      if (live) {
+        // products rounded apart (no fused multiply-add): each sum is then
+        // the same whichever half merges
+#pragma clang fp contract(off)
+        const float* po = part + (static_cast<int64_t>(1 - half_id) * heads + head) * kPartValues * tokens + token;
+        const float mo = __hip_atomic_load(po + kD * tokens, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float lo = __hip_atomic_load(po + (kD + 1) * tokens, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float mm = fmaxf(m, mo);
+        const float w0 = __builtin_amdgcn_exp2f(m - mm), w1 = __builtin_amdgcn_exp2f(mo - mm);
+        const float inv = 1.0f / (l_tot * w0 + lo * w1);
+        uint16_t* orow = o + (row0 + query) * ld_o + head * kD + 4 * h;
+        static_for<4>([&](auto DT) __attribute__((always_inline)) {
+          static_for<4>([&](auto G) __attribute__((always_inline)) {
+            float v[4];
+            static_for<4>([&](auto R) __attribute__((always_inline)) {
+              const float x = __hip_atomic_load(po + (DT * 32 + 8 * G + 4 * h + R) * tokens,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              v[R] = (acc_o[DT][4 * G + R] * w0 + x * w1) * inv;
+            });
+            const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2_t*>(orow + DT * 32 + 8 * G) = w;
+          });
+        });
+      }
+    }
   }
+}
+
+// Zeroes the arrival counters of a split launch (a kernel, so that the
+// launch sequence can be captured in a graph).
+__global__ __launch_bounds__(256) void attn_clear_kernel(int* __restrict__ p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 }  // namespace
 
 hipError_t launch_attention(const uint16_t* qkv, int64_t ld_qkv, uint16_t* o, int64_t ld_o,
-                            int batch, int seq, int heads, int head_dim, bool causal,
-                            hipStream_t stream) {
+                            int batch, int seq, int heads, int head_dim, bool causal, float* part,
+                            int* arrivals, hipStream_t stream) {
   if (batch == 0 || seq == 0) return hipSuccess;
   // per-lane copy offsets are 32-bit byte offsets within one key block
   if (static_cast<int64_t>(kBKV) * ld_qkv * 2 >= (int64_t{1} << 31)) return hipErrorInvalidValue;
@@ -426,16 +529,34 @@ hipError_t launch_attention(const uint16_t* qkv, int64_t ld_qkv, uint16_t* o, in
   // log2(e) / sqrt(d), times 1 / kQkScale^2 for the scaled fp16 Q and K
   const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf(static_cast<float>(head_dim)) /
                            (kQkScale * kQkScale);
-  const dim3 grid(static_cast<unsigned>(batch * heads * ((seq + kBQ - 1) / kBQ)));
+  const int64_t rows = static_cast<int64_t>(batch) * heads * ((seq + kBQ - 1) / kBQ);
+  // A grid of at most half as many query blocks as CUs leaves CUs idle:
+  // long rows are split over two workgroups each.  Measured (kernel alone,
+  // 128 query blocks): seq 4096 13% / 25% faster (non-causal / causal),
+  // seq 8192 22% / 35%, seq 2048 0% / 12%, but seq 1024 8-11% slower (the
+  // counter-clearing launch and the per-workgroup start take what the
+  // split saves); fuller grids gain nothing under the power cap (one query
+  // block per CU, causal: 6%; two rounds: 24% slower).
+  const bool split = part != nullptr && arrivals != nullptr && seq >= kSplitMinSeq &&
+                     2 * rows <= device_cus();
+  if (split) {
+    hipLaunchKernelGGL(attn_clear_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0,
+                       stream, arrivals, rows);
+  }
+  const dim3 grid(static_cast<unsigned>(rows * (split ? 2 : 1)));
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(64 * kWaves), 0, stream, qkv, ld_qkv, o, ld_o, seq, heads,
-                       scale_log2);
+                       scale_log2, part, arrivals);
   };
   const bool ragged = seq % kBQ != 0;
-  if (causal)
-    ragged ? go(attn_fwd_kernel<true, true>) : go(attn_fwd_kernel<true, false>);
+  if (causal && split)
+    ragged ? go(attn_fwd_kernel<true, true, true>) : go(attn_fwd_kernel<true, false, true>);
+  else if (causal)
+    ragged ? go(attn_fwd_kernel<true, true, false>) : go(attn_fwd_kernel<true, false, false>);
+  else if (split)
+    ragged ? go(attn_fwd_kernel<false, true, true>) : go(attn_fwd_kernel<false, false, true>);
   else
-    ragged ? go(attn_fwd_kernel<false, true>) : go(attn_fwd_kernel<false, false>);
+    ragged ? go(attn_fwd_kernel<false, true, false>) : go(attn_fwd_kernel<false, false, false>);
   return hipGetLastError();
 }
 

@@ -105,10 +105,16 @@ hipError_t launch_zero_2d(void* p, int64_t rows, int64_t cols, int64_t ld, int e
 // Head-local attention: qkv [batch*seq, ld_qkv] holding the rank's packed
 // projection as written by EPI_QKV_F16 (per head [q | k | v], head_dim
 // columns each; q and k fp16 scaled by kQkScale, v bf16); o [batch*seq,
-// ld_o] bf16, head j at columns j*head_dim.  head_dim == 128, seq % 128 == 0.
+// ld_o] bf16, head j at columns j*head_dim.  head_dim == 128, seq >= 32.
+// part (attn_part_floats floats) and arrivals (attn_arrival_ints ints), or
+// null: scratch for causal grids whose rows are split over two workgroups.
 hipError_t launch_attention(const uint16_t* qkv, int64_t ld_qkv, uint16_t* o, int64_t ld_o,
-                            int batch, int seq, int heads, int head_dim, bool causal,
-                            hipStream_t stream);
+                            int batch, int seq, int heads, int head_dim, bool causal, float* part,
+                            int* arrivals, hipStream_t stream);
+inline int64_t attn_part_floats(int64_t tokens, int64_t heads) { return 2 * tokens * heads * 130; }
+inline int64_t attn_arrival_ints(int64_t batch, int64_t seq, int64_t heads) {
+  return batch * heads * ((seq + 127) / 128);
+}
 
 // Sequence-parallel reduce-scatter on one device: out[m, :] = sum_{j < t}
 // parts.p[j][row0 + m, :] (+ bias) (+ residual[m, :]) for m < rows; partials

@@ -407,15 +407,19 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const vo
 
 namespace {
 // Workspace of tp_attn_shard_fwd: the rank's packed QKV projection [tokens,
-// 3*hl*d] (q, k columns fp16 scaled, v columns bf16), then the attention
-// output [tokens, hl*d] bf16.
+// 3*hl*d] (q, k columns fp16 scaled, v columns bf16), the attention output
+// [tokens, hl*d] bf16, then the scratch of causal launches that split their
+// rows over two workgroups (partial states, arrival counters).
 struct AttnWorkspace {
-  size_t qkv_bytes, o_bytes, total;
+  size_t qkv_bytes, o_bytes, part_bytes, arrival_bytes, total;
 };
-AttnWorkspace attn_workspace(int64_t tokens, int64_t hl, int64_t head_dim) {
+AttnWorkspace attn_workspace(int64_t batch, int64_t seq, int64_t hl, int64_t head_dim) {
+  const int64_t tokens = batch * seq;
   const size_t qkv = round256(static_cast<size_t>(tokens) * 3 * hl * head_dim * 2);
   const size_t o = round256(static_cast<size_t>(tokens) * hl * head_dim * 2);
-  return {qkv, o, qkv + o};
+  const size_t part = round256(static_cast<size_t>(tpk::attn_part_floats(tokens, hl)) * 4);
+  const size_t arr = round256(static_cast<size_t>(tpk::attn_arrival_ints(batch, seq, hl)) * 4);
+  return {qkv, o, part, arr, qkv + o + part + arr};
 }
 }  // namespace
 
@@ -424,7 +428,7 @@ size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden,
   if (in_dt != TP_BF16 || batch < 0 || seq < 0 || hidden < 1 || head_dim < 1) return 0;
   int64_t hl = 0;
   if (check_split(heads, t, 0, &hl) != TP_OK || hidden != heads * head_dim) return 0;
-  return attn_workspace(batch * seq, hl, head_dim).total;
+  return attn_workspace(batch, seq, hl, head_dim).total;
 }
 
 tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i, void* out_i,
@@ -448,7 +452,7 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
   TP_TRY(check_matrix(wqkv_i, 3 * dl, 3 * dl, in_dt));
   TP_TRY(check_matrix(wo_i, hidden, hidden, in_dt));
   TP_TRY(check_matrix(out_i, hidden, hidden, out_dt));
-  const AttnWorkspace ws = attn_workspace(tokens, hl, head_dim);
+  const AttnWorkspace ws = attn_workspace(batch, seq, hl, head_dim);
   if (workspace == nullptr || workspace_bytes < ws.total) return TP_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;
 
@@ -456,6 +460,8 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
   uint8_t* w = static_cast<uint8_t*>(workspace);
   uint16_t* qkv = reinterpret_cast<uint16_t*>(w);
   uint16_t* o = reinterpret_cast<uint16_t*>(w + ws.qkv_bytes);
+  float* part = reinterpret_cast<float*>(w + ws.qkv_bytes + ws.o_bytes);
+  int* arrivals = reinterpret_cast<int*>(w + ws.qkv_bytes + ws.o_bytes + ws.part_bytes);
   // 1. Column-parallel packed QKV projection of the rank's heads; Q and K
   //    leave the fp32 accumulator as scaled fp16 (11 significant bits for
   //    Q K^T), V as bf16.
@@ -464,7 +470,8 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
   // 2. softmax(Q K^T / sqrt(d)) V per local head.
   TP_TRY(from_hip(tpk::launch_attention(qkv, 3 * dl, o, dl, static_cast<int>(batch),
                                         static_cast<int>(seq), static_cast<int>(hl),
-                                        static_cast<int>(head_dim), causal == 1, s)));
+                                        static_cast<int>(head_dim), causal == 1, part, arrivals,
+                                        s)));
   // 3. Row-parallel output projection: the rank's full-hidden partial.
   tpk::Epilogue ep3{nullptr, nullptr, 0, out_i, hidden, out_dt == TP_F32, tpk::EPI_LINEAR};
   return run_gemm(in_dt, o, dl, wo_i, hidden, tokens, hidden, dl, ep3, s);

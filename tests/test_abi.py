@@ -206,7 +206,10 @@ def test_attn_shard_validation(lib):
     assert attn(lib, out=P + 8) == MISALIGNED
     need = lib.tp_attn_shard_workspace_bytes(1, 256, 1024, 8, 128, 2, BF16)
     # packed projection [256, 3*4*128] (16-bit) + output [256, 4*128] bf16
-    assert need == 256 * 1536 * 2 + 256 * 512 * 2
+    # + split-row partial states (2 halves x 256 tokens x 4 heads x 130
+    # floats) + arrival counters (1 x 4 heads x 2 query blocks, one 256-byte
+    # unit)
+    assert need == 256 * 1536 * 2 + 256 * 512 * 2 + 2 * 256 * 4 * 130 * 4 + 256
     assert attn(lib, ws_bytes=need - 1) == WORKSPACE
     assert attn(lib, ws=P + 16) == MISALIGNED
     assert attn(lib, batch=0, ws=None) == OK

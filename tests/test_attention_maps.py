@@ -98,3 +98,29 @@ def test_grid_map_covers_every_block_once(batch, heads, nqb, causal):
     assert all(got[i][1] == i % heads for i in range(n))
     if causal:
         assert all(got[i][2] >= got[i + 1][2] for i in range(n - 1))
+
+
+@pytest.mark.parametrize("seq", [128, 129, 200, 256, 333, 1000, 4095, 4096])
+def test_split_rows_count_every_key_once(seq):
+    """Causal launches that fit one round split each query block's key
+    iterations into two halves (the first rounded up; blk0 = twice the first
+    half's count for the second workgroup): both halves are non-empty from
+    128 keys on, and together they count every key a query may attend once."""
+    nqb = -(-seq // KBQ)
+    for qb in range(nqb):
+        nblk, nit_row = blocks(seq, qb, True)
+        first = (nit_row + 1) // 2
+        halves = [(0, first), (2 * first, nit_row - first)]
+        assert all(n >= 1 for _, n in halves)
+        for query in range(qb * KBQ, min(qb * KBQ + KBQ, seq)):
+            seen = []
+            for blk0, nit in halves:
+                for g in range(2):
+                    for it in range(nit):
+                        kb = blk0 + 2 * it + g
+                        kc = min(kb, nblk - 1)              # the block copied
+                        assert 0 <= key_base(kc, seq) <= seq - KBKV
+                        kbase = key_base(kb, seq)
+                        lo = kb * KBKV - kbase
+                        seen += [kbase + p for p in range(KBKV) if p >= lo and kbase + p <= query]
+            assert sorted(seen) == list(range(query + 1)), (seq, qb, query)

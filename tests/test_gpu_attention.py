@@ -176,10 +176,22 @@ def test_random_shapes(batch, seq, hl, t, rank, causal):
     (3, 200, 2, 4, 3, False),
     (1, 1000, 8, 1, 0, True),   # the headline's local heads, 1000 tokens
     (1, 4095, 1, 8, 5, False),  # one short of the headline length
+    # causal grids of more query blocks than the 256 CUs: rows not split
+    (3, 1408, 8, 1, 0, True),
+    (3, 1400, 8, 1, 0, True),
+    # few long rows (at most 128 query blocks, 2048 keys or more): each
+    # row's keys on two workgroups, merged by the second to finish
+    (1, 2048, 2, 1, 0, False),
+    (1, 2048, 2, 1, 0, True),
+    (2, 2100, 2, 2, 1, True),
+    (1, 4096, 4, 2, 1, False),
+    (1, 4000, 4, 2, 0, True),
 ])
 def test_ragged_seq(batch, seq, hl, t, rank, causal):
     """Sequence lengths that are not multiples of the 128-query or 32-key
-    blocks, every output element against the oracle."""
+    blocks, causal grids of more than one round, and small grids of long
+    rows split over two workgroups, every output element against the
+    oracle."""
     heads = hl * t
     hidden = heads * 128
     wl = inputs.AttnWorkload(f"attn_ragged_{batch}_{seq}_{hl}_{t}", batch, seq, hidden, heads, 128, t,

@@ -140,3 +140,31 @@ def test_swiglu_linears_ragged_attention_and_empty_backward_replay():
     _replay_matches(run, [zs, y, h, zr, oa, da0, db0, dba0, dbb0])
     for g in (da0, db0, dba0, dbb0):
         assert bool((g == 0).all()), "gradients over zero tokens must be zero"
+
+
+def test_split_attention_replay():
+    """Attention over few long rows (at most half as many query blocks as
+    CUs, 2048 keys or more), where each row's keys run on two workgroups and
+    the second of the two to finish merges both halves: the merge is
+    symmetric in the halves, so every call and replay gives the same bits
+    whichever finishes last (non-causal, and causal at a ragged length)."""
+    say("graph: split attention rows, non-causal seq 2048 and causal seq 2100")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    calls, outs = [], []
+    for seq, causal in ((2048, False), (2100, True)):
+        aw = inputs.AttnWorkload(f"attn_graph_split_{seq}", 1, seq, 512, 4, 128, 2, "bf16", 1.0,
+                                 1.8 / np.sqrt(512), "f32", 0.02)
+        xa = dev(np.stack([inputs.attn_x(aw, 0)]), "bf16")
+        wqkv, wo = dev(inputs.attn_wqkv_block(aw, 1), "bf16"), dev(inputs.attn_wo_block(aw, 1), "bf16")
+        wsa = torch.empty(binding.tp_attn_shard_workspace_bytes(1, seq, aw.hidden, aw.heads, aw.head_dim, aw.t,
+                                                                torch.bfloat16), dtype=torch.uint8, device="cuda")
+        oa = torch.empty((seq, aw.hidden), **f32)
+        calls.append((xa, wqkv, wo, oa, wsa, aw, causal))
+        outs.append(oa)
+
+    def run():
+        for xa, wqkv, wo, oa, wsa, aw, causal in calls:
+            binding.tp_attn_shard_fwd(xa, wqkv, wo, oa, wsa, heads=aw.heads, head_dim=aw.head_dim, t=aw.t,
+                                      rank=1, causal=causal)
+
+    _replay_matches(run, outs, reps=4)
