@@ -51,6 +51,11 @@
 //   * causal: only the key blocks that cross the diagonal of a wave's 32
 //     queries run the mask comparisons (a wave-uniform test of the block's
 //     last key against the wave's first query);
+//   * grids of at most half as many query blocks as CUs with 2048 keys or
+//     more split each row's key iterations over two workgroups; each
+//     publishes its unnormalised partial state with device-scope stores and
+//     counts itself in; the second to arrive merges the two (symmetric in
+//     the halves, so the bits do not depend on the order of arrival);
 //   * any sequence of at least 32 tokens: a partial last key block is read
 //     as the window of the last 32 keys (a uniform offset) with its keys
 //     before the block masked, an odd block count is padded by a fully
