@@ -198,7 +198,7 @@ PROFILED = {
                                 "t=1 MLP, M=2048, ffn=4096, h=1024 (64 x 128 tiles): H, B read, "
                                 "Z written (bf16 final output)",
                                 "row_gemm_t1_h1024_m2048"),
-    "attention_core": ("attn_fwd_kernel<false, false>", (0.0, _INF),
+    "attention_core": ("attn_fwd_kernel<false, false, false>", (0.0, _INF),
                        4.0 * _S * _S * _DL, 2 * (3 * _S * _DL + _S * _DL),
                        "attention rank shard, 8 local heads of 128, seq 4096, non-causal: Q, K "
                        "(fp16) and V (bf16) read once, O written (bf16)",
