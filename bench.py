@@ -636,8 +636,9 @@ def bench_backward(wl, x, a0, b0, stream, reps: int):
 
 
 def bench_attention(stream, reps: int, name: str = "attn_t8_h8192_s4096"):
-    """Time one head-local attention shard (rank 0, non-causal) and its two
-    projection GEMMs; the attention kernel's time is the difference."""
+    """Time one head-local attention shard (rank 0, non-causal; the causal
+    form beside it) and its two projection GEMMs; the attention kernel's
+    time is the difference."""
     import torch
     from megatron_tensor_transformer_tp_amd import binding, inputs
 
@@ -664,6 +665,9 @@ def bench_attention(stream, reps: int, name: str = "attn_t8_h8192_s4096"):
         "shard": lambda: binding.tp_attn_shard_fwd(x, wqkv, wo, out, ws, heads=wl.heads,
                                                    head_dim=wl.head_dim, t=wl.t, rank=0,
                                                    stream=stream),
+        "shard_causal": lambda: binding.tp_attn_shard_fwd(x, wqkv, wo, out, ws, heads=wl.heads,
+                                                          head_dim=wl.head_dim, t=wl.t, rank=0,
+                                                          causal=True, stream=stream),
         "qkv_gemm": lambda: binding.tp_column_linear(x2, wqkv, qkv, ffn=3 * wl.hidden, t=wl.t,
                                                      rank=0, stream=stream),
         "out_gemm": lambda: binding.tp_row_linear(o, wo, out2, ffn=wl.hidden, t=wl.t, rank=0,
@@ -695,6 +699,9 @@ def bench_attention(stream, reps: int, name: str = "attn_t8_h8192_s4096"):
     f_att = 4.0 * wl.batch * wl.seq * wl.seq * wl.head_dim * nl   # Q K^T and P V, non-causal
     f_out = 2.0 * tokens * dl * wl.hidden
     core_us = us["shard"] - us["qkv_gemm"] - us["out_gemm"]
+    core_causal_us = us["shard_causal"] - us["qkv_gemm"] - us["out_gemm"]
+    # causal: each query's keys up to itself, seq (seq + 1) / 2 pairs per head
+    f_att_causal = 2.0 * wl.batch * wl.seq * (wl.seq + 1) * wl.head_dim * nl
 
     def tf(flops, t_us):
         return round(flops / (t_us * 1e-6) / 1e12, 2)
@@ -713,9 +720,15 @@ def bench_attention(stream, reps: int, name: str = "attn_t8_h8192_s4096"):
                                    "interleaved with the shard in the sustained clock state "
                                    "(medians over rounds)"},
         "out_gemm": {"avg_us": round(us["out_gemm"], 2), "tflops": tf(f_out, us["out_gemm"])},
+        "causal": {"shard_us": round(us["shard_causal"], 2),
+                   "attention_core": {"avg_us": round(core_causal_us, 2),
+                                      "tflops": tf(f_att_causal, core_causal_us),
+                                      "flops": int(f_att_causal)}},
     }
     log(f"attention shard {us['shard']:.1f} us ({res['shard_tflops']} TFLOP/s): qkv {us['qkv_gemm']:.1f}, "
-        f"core ~{core_us:.1f} ({res['attention_core']['tflops']} TFLOP/s), out {us['out_gemm']:.1f}")
+        f"core ~{core_us:.1f} ({res['attention_core']['tflops']} TFLOP/s), out {us['out_gemm']:.1f}; "
+        f"causal shard {us['shard_causal']:.1f} us, core ~{core_causal_us:.1f} "
+        f"({res['causal']['attention_core']['tflops']} TFLOP/s)")
     return res
 
 
