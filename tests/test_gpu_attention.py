@@ -169,6 +169,36 @@ def test_random_shapes(batch, seq, hl, t, rank, causal):
     assert_close(out, ref, "bf16", f"random attention {wl.name} rank {rank} causal={causal}")
 
 
+def _attn_long_shapes(seed, n):
+    """n seeded shard shapes of long sequences on small grids: batch 1-2,
+    seq 2048-4600 (a multiple of 128 for even draws, any length for odd
+    ones), 1-3 local heads, t in 1-2, causal or not; the grids of at most
+    128 query blocks run each row on two workgroups."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        t = int(rng.integers(1, 3))
+        hl = int(rng.integers(1, 4))
+        seq = 128 * int(rng.integers(16, 36)) if i % 2 == 0 else int(rng.integers(2048, 4601))
+        out.append((int(rng.integers(1, 3)), seq, hl, t, int(rng.integers(0, t)), bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("batch,seq,hl,t,rank,causal", _attn_long_shapes(13, 6 * SHAPE_SWEEP))
+def test_random_long_shapes(batch, seq, hl, t, rank, causal):
+    heads = hl * t
+    hidden = heads * 128
+    wl = inputs.AttnWorkload(f"attn_long_{batch}_{seq}_{hl}_{t}", batch, seq, hidden, heads, 128, t,
+                             "bf16", 1.0, 1.8 / np.sqrt(hidden), "f32", 0.02)
+    x = x_all(wl)
+    wqkv, wo = inputs.attn_wqkv_block(wl, rank), inputs.attn_wo_block(wl, rank)
+    say(f"random long attention: batch={batch} seq={seq} local heads={hl} t={t} rank={rank} causal={causal}")
+    out = to_np(run(wl, rank, dev(x, "bf16"), dev(wqkv, "bf16"), dev(wo, "bf16"), causal))
+    ref = oracle.attn_shard(host64(x, "bf16"), host64(wqkv, "bf16"), host64(wo, "bf16"), heads, 128, t,
+                            rank, causal)
+    assert_close(out, ref, "bf16", f"random long attention {wl.name} rank {rank} causal={causal}")
+
+
 @pytest.mark.parametrize("batch,seq,hl,t,rank,causal", [
     (2, 32, 2, 2, 1, False),    # one key block, its partner a phantom block
     (2, 33, 2, 2, 0, True),     # a one-key partial block
