@@ -52,7 +52,8 @@
 //     queries run the mask comparisons (a wave-uniform test of the block's
 //     last key against the wave's first query);
 //   * grids of at most half as many query blocks as CUs with 2048 keys or
-//     more split each row's key iterations over two workgroups; each
+//     more (causal: one per CU with 4096 keys or more) split each row's key
+//     iterations over two workgroups; each
 //     publishes its unnormalised partial state with device-scope stores and
 //     counts itself in; the second to arrive merges the two (symmetric in
 //     the halves, so the bits do not depend on the order of arrival);
@@ -540,10 +541,13 @@ hipError_t launch_attention(const uint16_t* qkv, int64_t ld_qkv, uint16_t* o, in
   // 128 query blocks): seq 4096 13% / 25% faster (non-causal / causal),
   // seq 8192 22% / 35%, seq 2048 0% / 12%, but seq 1024 8-11% slower (the
   // counter-clearing launch and the per-workgroup start take what the
-  // split saves); fuller grids gain nothing under the power cap (one query
-  // block per CU, causal: 6%; two rounds: 24% slower).
-  const bool split = part != nullptr && arrivals != nullptr && seq >= kSplitMinSeq &&
-                     2 * rows <= device_cus();
+  // split saves).  Fuller grids mostly gain nothing under the power cap:
+  // one query block per CU, seq 4096: non-causal 0%, causal 6% (its rows
+  // are unequal; split); seq 2048, causal: 24% slower; two rounds: none.
+  const int64_t cus = device_cus();
+  const bool split = part != nullptr && arrivals != nullptr &&
+                     ((seq >= kSplitMinSeq && 2 * rows <= cus) ||
+                      (causal && seq >= 2 * kSplitMinSeq && rows <= cus));
   if (split) {
     hipLaunchKernelGGL(attn_clear_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0,
                        stream, arrivals, rows);
