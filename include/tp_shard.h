@@ -305,11 +305,11 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const vo
 
 /*
  * Bytes of workspace tp_attn_shard_fwd needs (the library does not
- * allocate): Q, K, V of the local heads, the local attention output, and
- * the partial softmax states and counters of causal launches that split
+ * allocate): Q, K, V of the local heads, the local attention output, and,
+ * for grids of at most 512 query blocks of 128 (batch * hl * ceil(seq /
+ * 128)), the partial softmax states and counters of launches that split
  * each query block's keys over two workgroups (2 * batch * seq * hl * 130
- * floats: 8.1 bytes per element of the local attention output); rounded up to
- * 256 bytes; 0 if invalid.
+ * floats, at most ~68 MB); rounded up to 256 bytes; 0 if invalid.
  */
 size_t tp_attn_shard_workspace_bytes(int64_t batch, int64_t seq, int64_t hidden, int64_t heads,
                                      int64_t head_dim, int t, tp_dtype in_dt);

@@ -408,8 +408,11 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* a_i, int64_t lda, const vo
 namespace {
 // Workspace of tp_attn_shard_fwd: the rank's packed QKV projection [tokens,
 // 3*hl*d] (q, k columns fp16 scaled, v columns bf16), the attention output
-// [tokens, hl*d] bf16, then the scratch of causal launches that split their
-// rows over two workgroups (partial states, arrival counters).
+// [tokens, hl*d] bf16, then, for grids small enough that their rows may be
+// split over two workgroups (at most kAttnSplitMaxRows query blocks: twice
+// the CUs of a whole MI355X), the split's partial states and arrival
+// counters; larger grids never split and get none (at most ~68 MB).
+constexpr int64_t kAttnSplitMaxRows = 512;
 struct AttnWorkspace {
   size_t qkv_bytes, o_bytes, part_bytes, arrival_bytes, total;
 };
@@ -417,8 +420,10 @@ AttnWorkspace attn_workspace(int64_t batch, int64_t seq, int64_t hl, int64_t hea
   const int64_t tokens = batch * seq;
   const size_t qkv = round256(static_cast<size_t>(tokens) * 3 * hl * head_dim * 2);
   const size_t o = round256(static_cast<size_t>(tokens) * hl * head_dim * 2);
-  const size_t part = round256(static_cast<size_t>(tpk::attn_part_floats(tokens, hl)) * 4);
-  const size_t arr = round256(static_cast<size_t>(tpk::attn_arrival_ints(batch, seq, hl)) * 4);
+  const int64_t rows = tpk::attn_arrival_ints(batch, seq, hl);   // query blocks
+  const bool may_split = rows <= kAttnSplitMaxRows;
+  const size_t part = may_split ? round256(static_cast<size_t>(tpk::attn_part_floats(tokens, hl)) * 4) : 0;
+  const size_t arr = may_split ? round256(static_cast<size_t>(rows) * 4) : 0;
   return {qkv, o, part, arr, qkv + o + part + arr};
 }
 }  // namespace
@@ -460,8 +465,9 @@ tp_status tp_attn_shard_fwd(const void* x, const void* wqkv_i, const void* wo_i,
   uint8_t* w = static_cast<uint8_t*>(workspace);
   uint16_t* qkv = reinterpret_cast<uint16_t*>(w);
   uint16_t* o = reinterpret_cast<uint16_t*>(w + ws.qkv_bytes);
-  float* part = reinterpret_cast<float*>(w + ws.qkv_bytes + ws.o_bytes);
-  int* arrivals = reinterpret_cast<int*>(w + ws.qkv_bytes + ws.o_bytes + ws.part_bytes);
+  float* part = ws.part_bytes ? reinterpret_cast<float*>(w + ws.qkv_bytes + ws.o_bytes) : nullptr;
+  int* arrivals =
+      ws.arrival_bytes ? reinterpret_cast<int*>(w + ws.qkv_bytes + ws.o_bytes + ws.part_bytes) : nullptr;
   // 1. Column-parallel packed QKV projection of the rank's heads; Q and K
   //    leave the fp32 accumulator as scaled fp16 (11 significant bits for
   //    Q K^T), V as bf16.

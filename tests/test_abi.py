@@ -214,6 +214,13 @@ def test_attn_shard_validation(lib):
     assert attn(lib, ws=P + 16) == MISALIGNED
     assert attn(lib, batch=0, ws=None) == OK
     assert lib.tp_attn_shard_workspace_bytes(1, 256, 1024, 8, 128, 3, BF16) == 0
+    # a grid of more than 512 query blocks never splits its rows: no split
+    # scratch (batch 4 x 8 local heads x 64 blocks of 128 = 2048 blocks)
+    big = lib.tp_attn_shard_workspace_bytes(4, 8192, 8192, 64, 128, 8, BF16)
+    assert big == 32768 * 3 * 1024 * 2 + 32768 * 1024 * 2
+    # 512 query blocks still carry it (batch 1 x 8 heads x 64 blocks)
+    edge = lib.tp_attn_shard_workspace_bytes(1, 8192, 8192, 64, 128, 8, BF16)
+    assert edge == 8192 * 3 * 1024 * 2 + 8192 * 1024 * 2 + 2 * 8192 * 8 * 130 * 4 + 2048
 
 
 def test_product_never_imports_the_oracle():
