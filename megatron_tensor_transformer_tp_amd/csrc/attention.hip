@@ -51,7 +51,7 @@
 //   * causal: only the key blocks that cross the diagonal of a wave's 32
 //     queries run the mask comparisons (a wave-uniform test of the block's
 //     last key against the wave's first query);
-//   * grids of at most half as many query blocks as CUs with 2048 keys or
+//   * grids of at most half as many query blocks as CUs with 1024 keys or
 //     more (causal: one per CU with 4096 keys or more) split each row's key
 //     iterations over two workgroups; each
 //     publishes its unnormalised partial state with device-scope stores and
@@ -103,7 +103,10 @@ constexpr int kPartValues = kD + 2;
 static_assert(kPartValues == 130, "attn_part_floats");
 // shortest sequence whose rows are split (each half then has at least one
 // iteration, and the split pays for its extra launch)
-constexpr int kSplitMinSeq = 2048;
+constexpr int kSplitMinSeq = 1024;
+// shortest sequence whose causal rows are split in a grid of one query
+// block per CU
+constexpr int kSplitCausalFullSeq = 4096;
 
 // One global->LDS copy with a uniform base (SGPR pair) and a per-lane 32-bit
 // byte offset: lane t's 16 bytes land at LDS byte address lds_addr + 16 t
@@ -493,8 +496,18 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
         // the same whichever half merges
 #pragma clang fp contract(off)
         const float* po = part + (static_cast<int64_t>(1 - half_id) * heads + head) * kPartValues * tokens + token;
+        // every load issued before the first use: one round trip to where
+        // the device-scope stores landed, not one per group of four
+        float xo[4][16];
         const float mo = __hip_atomic_load(po + kD * tokens, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float lo = __hip_atomic_load(po + (kD + 1) * tokens, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        static_for<4>([&](auto DT) __attribute__((always_inline)) {
+          static_for<16>([&](auto R) __attribute__((always_inline)) {
+            xo[DT][R] = __hip_atomic_load(po + (DT * 32 + 8 * (R / 4) + 4 * h + R % 4) * tokens,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          });
+        });
+        __builtin_amdgcn_sched_barrier(0);
         const float mm = fmaxf(m, mo);
         const float w0 = __builtin_amdgcn_exp2f(m - mm), w1 = __builtin_amdgcn_exp2f(mo - mm);
         const float inv = 1.0f / (l_tot * w0 + lo * w1);
@@ -503,9 +516,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
           static_for<4>([&](auto G) __attribute__((always_inline)) {
             float v[4];
             static_for<4>([&](auto R) __attribute__((always_inline)) {
-              const float x = __hip_atomic_load(po + (DT * 32 + 8 * G + 4 * h + R) * tokens,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              v[R] = (acc_o[DT][4 * G + R] * w0 + x * w1) * inv;
+              v[R] = (acc_o[DT][4 * G + R] * w0 + xo[DT][4 * G + R] * w1) * inv;
             });
             const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             *reinterpret_cast<u32x2_t*>(orow + DT * 32 + 8 * G) = w;
@@ -537,17 +548,19 @@ hipError_t launch_attention(const uint16_t* qkv, int64_t ld_qkv, uint16_t* o, in
                            (kQkScale * kQkScale);
   const int64_t rows = static_cast<int64_t>(batch) * heads * ((seq + kBQ - 1) / kBQ);
   // A grid of at most half as many query blocks as CUs leaves CUs idle:
-  // long rows are split over two workgroups each.  Measured (kernel alone,
-  // 128 query blocks): seq 4096 13% / 25% faster (non-causal / causal),
-  // seq 8192 22% / 35%, seq 2048 0% / 12%, but seq 1024 8-11% slower (the
-  // counter-clearing launch and the per-workgroup start take what the
-  // split saves).  Fuller grids mostly gain nothing under the power cap:
-  // one query block per CU, seq 4096: non-causal 0%, causal 6% (its rows
-  // are unequal; split); seq 2048, causal: 24% slower; two rounds: none.
+  // its rows are split over two workgroups each.  Measured (kernel alone,
+  // non-causal / causal): 128 query blocks at seq 2048 9% / 20% faster, at
+  // seq 4096 16% / 30%, 64 at seq 8192 25% / 37%, 64 at seq 1024 2-4% /
+  // 5-7%, but 64 at seq 512 11-14% slower (the counter-clearing launch and
+  // the workgroups' start take what the split saves).  Fuller grids lose
+  // under the power cap (one query block per CU: non-causal 19-33% slower,
+  // causal at seq 2048 10% slower), except causal ones at seq 4096 and
+  // more, whose unequal rows make the split pay (8 heads x seq 4096: 11%,
+  // 4 heads x seq 8192: 22% faster); grids of two rounds or more lose.
   const int64_t cus = device_cus();
   const bool split = part != nullptr && arrivals != nullptr &&
                      ((seq >= kSplitMinSeq && 2 * rows <= cus) ||
-                      (causal && seq >= 2 * kSplitMinSeq && rows <= cus));
+                      (causal && seq >= kSplitCausalFullSeq && rows <= cus));
   if (split) {
     hipLaunchKernelGGL(attn_clear_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0,
                        stream, arrivals, rows);
