@@ -423,6 +423,10 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
       static_for<16>([&](auto R) __attribute__((always_inline)) { mrg[2 + 16 * DT + R] = acc_o[DT][int(R)]; });
     });
   }
+  // the barrier does not wait for LDS writes: each wave waits for its own
+  // first, so the other groups' reads after it see them (whatever SIMD
+  // the writing wave runs on)
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   lds_barrier();
   if constexpr (!SPLIT) {
     if (group == 0) {
@@ -489,6 +493,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(const uint16_t* __restric
     int* flag = reinterpret_cast<int*>(smem + kStages * kStage - 16);   // past the merge area
     lds_barrier();
     if (threadIdx.x == 0) *flag = atomicAdd(arrivals + (static_cast<int64_t>(b) * nqb + qb) * heads + head, 1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // the flag's LDS write, before the barrier
     lds_barrier();
     if (*flag == 1 && group == 0) {
       if (live) {
