@@ -43,6 +43,7 @@ SOURCES = [
     "gelu.hip",
     "attention.hip",
     "noalloc.hip",
+    "splitk.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

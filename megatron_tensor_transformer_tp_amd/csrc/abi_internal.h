@@ -21,10 +21,12 @@ tp_status mlp_fwd_validate(const void* x, const void* a_i, int64_t lda, const vo
 
 // The two GEMMs of the shard over `tokens` rows, H_i in h ([tokens, f], row
 // stride f, in_dt); bias_use / res_use already resolved for the rank
-// (NULL unless rank 0).  Arguments validated.
+// (NULL unless rank 0).  part: room for splitk_part_floats(tokens,
+// max(f, hidden)) floats, or NULL: with it, products of few tiles (bf16, at
+// most kSplitKMaxRows tokens) run split-K.  Arguments validated.
 tp_status mlp_fwd_enqueue(const void* x, const void* a_i, int64_t lda, const void* b_i,
                           const void* bias_a_i, const void* bias_use, const void* res_use,
-                          void* z_i, void* y_save, void* h, int64_t tokens, int64_t hidden,
-                          int64_t f, tp_dtype in_dt, tp_dtype out_dt, hipStream_t s);
+                          void* z_i, void* y_save, void* h, float* part, int64_t tokens,
+                          int64_t hidden, int64_t f, tp_dtype in_dt, tp_dtype out_dt, hipStream_t s);
 
 }  // namespace tpabi

@@ -421,8 +421,18 @@ template <int BM, int BN, int WGM, int WGN, int STAGES, bool A_KMAJOR, bool B_KM
 // at least two waves per SIMD (256 x 256: 8 waves of one workgroup; 128 x
 // 128: 4 waves each of two workgroups), so at most 256 registers per wave
 __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_dma_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    int M, int N, int K, const Epilogue ep) {
+    const uint16_t* __restrict__ A_in, int64_t lda, const uint16_t* __restrict__ B_in, int64_t ldb,
+    int M, int N, int K_in, const Epilogue ep_in) {
+  // split-K: workgroup set blockIdx.y takes k-slice blockIdx.y of K /
+  // gridDim.y and writes its partial product to its own output slab (one
+  // set, the whole product, when gridDim.y is 1)
+  const int ks = blockIdx.y;
+  const int K = K_in / static_cast<int>(gridDim.y);
+  const int64_t k0 = static_cast<int64_t>(ks) * K;
+  const uint16_t* __restrict__ A = A_in + (A_KMAJOR ? k0 * lda : k0);
+  const uint16_t* __restrict__ B = B_in + (B_KMAJOR ? k0 * ldb : k0);
+  Epilogue ep = ep_in;
+  ep.out = static_cast<float*>(ep_in.out) + ks * ep_in.slab;
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -870,6 +880,12 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
     return hipErrorInvalidValue;
   const int64_t tiles = ((static_cast<int64_t>(M) + BM - 1) / BM) * ((static_cast<int64_t>(N) + BN - 1) / BN);
   if (tiles > INT32_MAX) return hipErrorInvalidValue;     // tile indices are ints
+  // split-K: whole 64-k pairs per slice, partial products only
+  const int ks = ep.ksplit > 1 ? ep.ksplit : 1;
+  if (ks > 1 && (EPI != EPI_LINEAR || !OUT_F32 || ep.bias != nullptr || ep.residual != nullptr ||
+                 K % (2 * kBKd * ks) != 0 || ks > 65535))
+    return hipErrorInvalidValue;
+  const int kslice = K / ks;
   // one round of resident workgroups (whole XCD rounds: a multiple of 8),
   // each looping over its tiles
   auto launch = [&](auto ktail, auto pair) {
@@ -882,12 +898,12 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
     hipLaunchKernelGGL(
         (gemm_bf16_dma_kernel<BM, BN, WGM, WGN, STAGES, A_KMAJOR, B_KMAJOR, EPI, OUT_F32, kTail, kPair,
                               MF16>),
-        dim3(grid), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
+        dim3(grid, ks), dim3(64 * WGM * WGN), 0, stream, A, lda, B, ldb, M, N, K, ep);
   };
   using T = std::true_type;
   using F = std::false_type;
   using P0 = std::integral_constant<int, 0>;
-  if (K % kBKd != 0) {
+  if (kslice % kBKd != 0) {
     launch(T{}, P0{});
   } else {
     // Whole 64-k pairs of a k-contiguous operand: a k-contiguous B takes the
@@ -899,7 +915,7 @@ hipError_t launch_tile_dma(const uint16_t* A, int64_t lda, const uint16_t* B, in
                           : !A_KMAJOR                       ? 2
                                                             : 0;
     if constexpr (kPair != 0) {
-      if (K % (2 * kBKd) == 0) {
+      if (kslice % (2 * kBKd) == 0) {
         launch(F{}, std::integral_constant<int, kPair>{});
         return hipGetLastError();
       }

@@ -40,11 +40,35 @@ struct Epilogue {
   int64_t ldaux = 0;
   void* out2 = nullptr;
   const void* b2 = nullptr;   // EPI_SWIGLU: the value projection (B is the gate)
+  // split-K (EPI_LINEAR, fp32 out, no bias or residual): ksplit workgroup
+  // sets each take K / ksplit of the k range (K % (64 ksplit) == 0) and
+  // write their partial product to out + s * slab (elements)
+  int ksplit = 1;
+  int64_t slab = 0;
 };
 
 // Compute units of the current device (cached per device; 256 on a whole
 // MI355X).  The GEMM kernels size their grids by it.
 int64_t device_cus();
+
+// Split-K for products of few tiles (splitk.hip): at most kSplitKMaxRows
+// rows, at most kSplitKMax k-slices.  splitk_factor: the slices for an
+// M x N x K product on this device (1: do not split; a power of two whose
+// 64 x 128 tiles times slices fill at most the CUs, with K % (64 ks) == 0).
+// launch_gemm_bf16_splitk: part[s][M][N] fp32 = A[:, kslice s] B[kslice s, :]
+// (A [M, K] k-contiguous, B [K, N] k-major, as launch_gemm_bf16);
+// launch_splitk_reduce: out = epilogue(sum over s of part[s]) in slice order,
+// ep as for the unsplit product (EPI_GELU or EPI_LINEAR, bf16 bias and
+// residual).
+constexpr int64_t kSplitKMaxRows = 128;
+constexpr int kSplitKMax = 8;
+inline int64_t splitk_part_floats(int64_t rows, int64_t width) { return kSplitKMax * rows * width; }
+int splitk_factor(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                   int64_t M, int64_t N, int64_t K, int ksplit, float* part,
+                                   hipStream_t stream);
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int64_t M, int64_t N,
+                                const Epilogue& ep, hipStream_t stream);
 
 // bf16 x bf16 -> fp32 accumulate, MFMA.  A [M, K] row-major (lda), B [K, N]
 // row-major (ldb).  Any M, N and K >= 1 with N % 8 == 0, K % 8 == 0,

@@ -86,7 +86,7 @@ tp_status tp_mlp_shard_fwd_noalloc(const void* x, const void* a_i, int64_t lda, 
     const tp_status e = tpabi::mlp_fwd_enqueue(
         xb + m0 * hidden * ie, a_i, lda, b_i, bias_a_i, owner ? bias_b : nullptr,
         rb == nullptr ? nullptr : rb + m0 * hidden * ie, zb + m0 * hidden * oe,
-        yb == nullptr ? nullptr : yb + m0 * f * ie, h, rows, hidden, f, in_dt, out_dt, s);
+        yb == nullptr ? nullptr : yb + m0 * f * ie, h, nullptr, rows, hidden, f, in_dt, out_dt, s);
     if (e != TP_OK) return e;
   }
   return TP_OK;

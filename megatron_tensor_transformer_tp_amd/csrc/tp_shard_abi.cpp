@@ -128,16 +128,35 @@ tp_status mlp_fwd_validate(const void* x, const void* a_i, int64_t lda, const vo
 
 tp_status mlp_fwd_enqueue(const void* x, const void* a_i, int64_t lda, const void* b_i,
                           const void* bias_a_i, const void* bias_use, const void* res_use,
-                          void* z_i, void* y_save, void* h, int64_t tokens, int64_t hidden,
-                          int64_t f, tp_dtype in_dt, tp_dtype out_dt, hipStream_t s) {
+                          void* z_i, void* y_save, void* h, float* part, int64_t tokens,
+                          int64_t hidden, int64_t f, tp_dtype in_dt, tp_dtype out_dt, hipStream_t s) {
+  // Few tokens: each product has few tiles and most CUs would sit idle
+  // while it streams its weights, so its k range is split (fp32 partial
+  // products in `part`, summed in slice order by a kernel that applies the
+  // epilogue; the part buffer serves the two products one after the other).
+  const int ks1 = in_dt == TP_BF16 && part != nullptr ? tpk::splitk_factor(tokens, f, hidden) : 1;
+  const int ks2 = in_dt == TP_BF16 && part != nullptr ? tpk::splitk_factor(tokens, hidden, f) : 1;
   // Column-parallel GEMM with GeLU fused into its epilogue: H_i = GeLU(X A_i + a_i)
   // stored once in h (bf16 for bf16 inputs, fp32 for fp32); the
   // pre-activation also goes to y_save when asked for.
   tpk::Epilogue ep1{bias_a_i, nullptr, 0, h, f, in_dt == TP_F32, tpk::EPI_GELU};
   ep1.pre = y_save;
-  TP_TRY(run_gemm(in_dt, x, hidden, a_i, lda, tokens, f, hidden, ep1, s));
+  if (ks1 > 1) {
+    TP_TRY(from_hip(tpk::launch_gemm_bf16_splitk(static_cast<const uint16_t*>(x), hidden,
+                                                 static_cast<const uint16_t*>(a_i), lda, tokens, f,
+                                                 hidden, ks1, part, s)));
+    TP_TRY(from_hip(tpk::launch_splitk_reduce(part, ks1, tokens, f, ep1, s)));
+  } else {
+    TP_TRY(run_gemm(in_dt, x, hidden, a_i, lda, tokens, f, hidden, ep1, s));
+  }
   // Row-parallel GEMM: Z_i = H_i B_i (+ b + R on rank 0).
   tpk::Epilogue ep2{bias_use, res_use, hidden, z_i, hidden, out_dt == TP_F32, tpk::EPI_LINEAR};
+  if (ks2 > 1) {
+    TP_TRY(from_hip(tpk::launch_gemm_bf16_splitk(static_cast<const uint16_t*>(h), f,
+                                                 static_cast<const uint16_t*>(b_i), hidden, tokens,
+                                                 hidden, f, ks2, part, s)));
+    return from_hip(tpk::launch_splitk_reduce(part, ks2, tokens, hidden, ep2, s));
+  }
   return run_gemm(in_dt, h, f, b_i, hidden, tokens, hidden, f, ep2, s);
 }
 
@@ -223,13 +242,29 @@ tp_status tp_row_linear(const void* h_i, int64_t ldh, const void* b_i, int64_t l
                   static_cast<hipStream_t>(stream));
 }
 
+namespace {
+// Workspace of tp_mlp_shard_fwd: H_i [tokens, f] (in_dt), then, for bf16
+// calls of at most kSplitKMaxRows tokens, the split-K partial products.
+struct MlpFwdWorkspace {
+  size_t h_bytes, part_bytes, total;
+};
+MlpFwdWorkspace mlp_fwd_workspace(int64_t tokens, int64_t hidden, int64_t f, tp_dtype in_dt) {
+  const size_t hb = round256(static_cast<size_t>(tokens) * static_cast<size_t>(f) *
+                             static_cast<size_t>(elem_bytes(in_dt)));
+  const bool split = in_dt == TP_BF16 && tokens > 0 && tokens <= tpk::kSplitKMaxRows;
+  const size_t pb = split ? round256(static_cast<size_t>(tpk::splitk_part_floats(
+                                         tokens, f > hidden ? f : hidden)) * 4)
+                          : 0;
+  return {hb, pb, hb + pb};
+}
+}  // namespace
+
 size_t tp_mlp_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn, int t,
                                     tp_dtype in_dt) {
   if (!dtype_known(in_dt) || tokens < 0 || hidden < 1) return 0;
   int64_t f = 0;
   if (check_split(ffn, t, 0, &f) != TP_OK) return 0;
-  return round256(static_cast<size_t>(tokens) * static_cast<size_t>(f) *
-                  static_cast<size_t>(elem_bytes(in_dt)));
+  return mlp_fwd_workspace(tokens, hidden, f, in_dt).total;
 }
 
 tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const void* b_i,
@@ -242,12 +277,15 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
   TP_TRY(tpabi::mlp_fwd_validate(x, a_i, lda, b_i, bias_a_i, bias_b, residual, z_i, y_save, tokens,
                                  hidden, ffn, t, rank, in_dt, out_dt, &f));
   if (tokens == 0) return TP_OK;
-  const size_t need = tp_mlp_shard_workspace_bytes(tokens, hidden, ffn, t, in_dt);
-  if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  const MlpFwdWorkspace ws = mlp_fwd_workspace(tokens, hidden, f, in_dt);
+  if (workspace == nullptr || workspace_bytes < ws.total) return TP_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return TP_ERR_MISALIGNED;
+  float* part = ws.part_bytes
+                    ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws.h_bytes)
+                    : nullptr;
   return tpabi::mlp_fwd_enqueue(x, a_i, lda, b_i, bias_a_i, rank == 0 ? bias_b : nullptr,
-                                rank == 0 ? residual : nullptr, z_i, y_save, workspace, tokens,
-                                hidden, f, in_dt, out_dt, static_cast<hipStream_t>(stream));
+                                rank == 0 ? residual : nullptr, z_i, y_save, workspace, part,
+                                tokens, hidden, f, in_dt, out_dt, static_cast<hipStream_t>(stream));
 }
 
 

@@ -76,6 +76,37 @@ def test_t1_h1024_bf16_final_output(with_extras):
     assert_close(z, ref, "bf16", "t=1 h=1024 M=2048 bf16 out")
 
 
+@pytest.mark.parametrize("tokens,hidden,f,rank,out", [
+    (1, 1024, 512, 0, "f32"),
+    (7, 1024, 512, 1, "f32"),
+    (16, 8192, 4096, 0, "f32"),     # the headline shard's widths at 16 tokens
+    (64, 2048, 1024, 0, "bf16"),
+    (100, 1024, 1376, 0, "f32"),    # f = 1376: the row product's k range does not split, it stays tiled
+    (128, 4096, 1024, 0, "f32"),
+    (129, 1024, 512, 0, "f32"),     # past the split-K limit: the tiled products
+])
+def test_small_token_counts(tokens, hidden, f, rank, out):
+    """Few tokens: the two products have few tiles and run split-K (k-slices
+    written as fp32 partial products, summed in slice order by the kernel
+    that applies the epilogue) up to 128 tokens; bias, residual and the
+    saved pre-activation included, every element against the oracle."""
+    t = 4
+    wl = inputs.MlpWorkload(f"small_{tokens}_{hidden}_{f}", tokens, hidden, f * t, t, "bf16", 1.0, 0.02,
+                            0.02, out)
+    x, a, b = inputs.mlp_x_rows(wl), inputs.mlp_a_block(wl, rank), inputs.mlp_b_block(wl, rank)
+    ba, bb, res = inputs.mlp_bias_a_block(wl, rank), inputs.mlp_bias_b(wl), inputs.mlp_residual_rows(wl)
+    say(f"small token count: tokens={tokens} hidden={hidden} f={f} rank={rank} out={out}")
+    y = nan_tensor((tokens, f), torch.bfloat16)
+    ed = dict(bias_a_i=dev(ba, "bf16"), bias_b=dev(bb, "bf16"), residual=dev(res, "bf16"), y_save=y)
+    z = to_np(run_shard(wl, rank, dev(x, "bf16"), dev(a, "bf16"), dev(b, "bf16"), out, ed))
+    ref_y = oracle.column_linear(host64(x, "bf16"), host64(a, "bf16"), host64(ba, "bf16"))
+    assert_close(to_np(y), ref_y, "bf16", f"small {tokens} tokens: saved pre-activation")
+    ref = oracle.row_linear(oracle.column_linear(host64(x, "bf16"), host64(a, "bf16"), host64(ba, "bf16"),
+                                                 apply_gelu=True),
+                            host64(b, "bf16"), host64(bb, "bf16"), host64(res, "bf16"), rank=rank)
+    assert_close(z, ref, out if out == "bf16" else "bf16", f"small {tokens} tokens: partial")
+
+
 def test_t8_h8192_m4096_rank0_full():
     wl = inputs.MLP_WORKLOADS["t8_h8192_m4096"]
     x = inputs.mlp_x_rows(wl)
