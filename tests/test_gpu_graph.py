@@ -168,3 +168,27 @@ def test_split_attention_replay():
                                       rank=1, causal=causal)
 
     _replay_matches(run, outs, reps=4)
+
+
+def test_few_token_split_k_replay():
+    """The MLP shard at few tokens, where both products run split-K (fp32
+    partial products of k-slices, summed in a fixed order by the epilogue
+    kernel): captured and replayed, bit for bit (16 tokens, h 2048, f 1024,
+    bias, residual and the saved pre-activation)."""
+    say("graph: 16-token MLP shard (split-K products)")
+    t, rank = 4, 0
+    wl = inputs.MlpWorkload("graph_few_tokens", 16, 2048, 1024 * t, t, "bf16", 1.0, 0.02, 0.02, "f32")
+    xd = dev(inputs.mlp_x_rows(wl), "bf16")
+    ad, bd = dev(inputs.mlp_a_block(wl, rank), "bf16"), dev(inputs.mlp_b_block(wl, rank), "bf16")
+    ba, bb = dev(inputs.mlp_bias_a_block(wl, rank), "bf16"), dev(inputs.mlp_bias_b(wl), "bf16")
+    res = dev(inputs.mlp_residual_rows(wl), "bf16")
+    ws = torch.empty(binding.tp_mlp_shard_workspace_bytes(wl.tokens, wl.hidden, wl.ffn, wl.t, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    z = torch.empty((wl.tokens, wl.hidden), dtype=torch.float32, device="cuda")
+    y = torch.empty((wl.tokens, wl.f), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        binding.tp_mlp_shard_fwd(xd, ad, bd, z, ws, ffn=wl.ffn, t=wl.t, rank=rank, bias_a_i=ba, bias_b=bb,
+                                 residual=res, y_save=y)
+
+    _replay_matches(run, [z, y], reps=4)
