@@ -166,7 +166,7 @@ tp_status tp_row_linear(const void* h_i, int64_t ldh, const void* b_i, int64_t l
  * Bytes of workspace tp_mlp_shard_fwd needs (this interface's addition: the
  * library does not allocate): the GeLU intermediate
  * H_i [tokens, f] in in_dt (bf16 for bf16 inputs, f32 for f32), rounded up to
- * 256 bytes, and for bf16 calls of at most 128 tokens the split-K partial
+ * 256 bytes, and for bf16 calls of at most 512 tokens the split-K partial
  * products that follow it (8 * tokens * max(f, hidden) floats).  Returns 0
  * for invalid arguments (and for tokens == 0).
  */
@@ -194,7 +194,7 @@ size_t tp_mlp_shard_workspace_bytes(int64_t tokens, int64_t hidden, int64_t ffn,
  *             holds H_i between the two GEMMs (one HBM round trip) and is
  *             scratch: its contents after the call are unspecified.
  * dtype pairs: bf16 -> f32, bf16 -> bf16, f32 -> f32.
- * With bf16 inputs and at most 128 tokens, a product of few tiles splits
+ * With bf16 inputs and at most 512 tokens, a product of few tiles splits
  * its k range over several workgroup sets (fp32 partial products summed in
  * a fixed order), so the result is reproducible but not bitwise the tiled
  * product's.
@@ -227,7 +227,7 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* a_i, int64_t lda, const vo
  *   Every call on one GPU shares that GPU's array: calls that overlap on one
  *   GPU (on other streams or threads) race and must be serialised by the
  *   caller.  Nothing in the array needs to start zeroed.
- *   The products always run tiled (no split-K), so below 129 tokens the
+ *   The products always run tiled (no split-K), so below 513 tokens the
  *   results agree with tp_mlp_shard_fwd's to the rounding of the sums, not
  *   bit for bit.
  */

@@ -54,13 +54,14 @@ int64_t device_cus();
 // Split-K for products of few tiles (splitk.hip): at most kSplitKMaxRows
 // rows, at most kSplitKMax k-slices.  splitk_factor: the slices for an
 // M x N x K product on this device (1: do not split; a power of two whose
-// 64 x 128 tiles times slices fill at most the CUs, with K % (64 ks) == 0).
+// tiles (64 x 128 up to 128 rows, 128 x 128 above) times slices fill at most
+// the CUs, with K % (64 ks) == 0).
 // launch_gemm_bf16_splitk: part[s][M][N] fp32 = A[:, kslice s] B[kslice s, :]
 // (A [M, K] k-contiguous, B [K, N] k-major, as launch_gemm_bf16);
 // launch_splitk_reduce: out = epilogue(sum over s of part[s]) in slice order,
 // ep as for the unsplit product (EPI_GELU or EPI_LINEAR, bf16 bias and
 // residual).
-constexpr int64_t kSplitKMaxRows = 128;
+constexpr int64_t kSplitKMaxRows = 512;
 constexpr int kSplitKMax = 8;
 inline int64_t splitk_part_floats(int64_t rows, int64_t width) { return kSplitKMax * rows * width; }
 int splitk_factor(int64_t M, int64_t N, int64_t K);

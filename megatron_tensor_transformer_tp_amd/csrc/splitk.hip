@@ -68,9 +68,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 }  // namespace
 
+namespace {
+// Rows of the split products' tiles: 64 x 128 up to 128 rows, 128 x 128 above.
+int splitk_tile_rows(int64_t M) { return M <= 128 ? 64 : 128; }
+}  // namespace
+
 int splitk_factor(int64_t M, int64_t N, int64_t K) {
   if (M > kSplitKMaxRows) return 1;
-  const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);   // 64 x 128 tiles
+  const int64_t bm = splitk_tile_rows(M);
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + 127) / 128);
   const int64_t cus = device_cus();
   int ks = 1;
   while (ks < kSplitKMax && tiles * ks * 2 <= cus && K % (64 * ks * 2) == 0) ks *= 2;
@@ -83,6 +89,10 @@ hipError_t launch_gemm_bf16_splitk(const uint16_t* A, int64_t lda, const uint16_
   Epilogue ep{nullptr, nullptr, 0, part, N, true, EPI_LINEAR};
   ep.ksplit = ksplit;
   ep.slab = M * N;
+  if (splitk_tile_rows(M) == 128)
+    return launch_gemm_bf16_cfg<128, 128, EPI_LINEAR, true>(A, lda, B, ldb, static_cast<int>(M),
+                                                            static_cast<int>(N), static_cast<int>(K),
+                                                            ep, stream);
   return launch_gemm_bf16_cfg<64, 128, EPI_LINEAR, true>(A, lda, B, ldb, static_cast<int>(M),
                                                          static_cast<int>(N), static_cast<int>(K), ep,
                                                          stream);

@@ -125,10 +125,11 @@ def mlp(lib, **kw):
 
 def test_mlp_shard_validation(lib):
     need = lib.tp_mlp_shard_workspace_bytes(16, 1024, 4096, 8, BF16)
-    # H_i [16, 512] bf16, then (bf16, at most 128 tokens) the split-K partial
+    # H_i [16, 512] bf16, then (bf16, at most 512 tokens) the split-K partial
     # products: 8 slices x 16 tokens x max(f, hidden) = 1024 floats
     assert need == 16 * 512 * 2 + 8 * 16 * 1024 * 4
-    assert lib.tp_mlp_shard_workspace_bytes(129, 1024, 4096, 8, BF16) == 129 * 512 * 2   # no split part
+    assert lib.tp_mlp_shard_workspace_bytes(512, 1024, 4096, 8, BF16) == 512 * 512 * 2 + 8 * 512 * 1024 * 4
+    assert lib.tp_mlp_shard_workspace_bytes(513, 1024, 4096, 8, BF16) == 513 * 512 * 2   # no split part
     assert lib.tp_mlp_shard_workspace_bytes(3, 1024, 4096, 8, F32) == 3 * 512 * 4
     assert lib.tp_mlp_shard_workspace_bytes(3, 1024, 40, 8, F32) == 256  # 60 B rounded up
     assert lib.tp_mlp_shard_workspace_bytes(16, 1024, 4100, 8, BF16) == 0

@@ -83,12 +83,17 @@ def test_t1_h1024_bf16_final_output(with_extras):
     (64, 2048, 1024, 0, "bf16"),
     (100, 1024, 1376, 0, "f32"),    # f = 1376: the row product's k range does not split, it stays tiled
     (128, 4096, 1024, 0, "f32"),
-    (129, 1024, 512, 0, "f32"),     # past the split-K limit: the tiled products
+    (129, 1024, 512, 0, "f32"),     # 128 x 128 tiles for the split products from here on
+    (200, 2048, 1024, 1, "bf16"),
+    (256, 8192, 4096, 0, "f32"),    # headline widths: 4 and 2 k-slices
+    (384, 2048, 1536, 0, "bf16"),
+    (512, 1024, 512, 1, "f32"),
+    (513, 1024, 512, 0, "f32"),     # past the split-K limit: the tiled products
 ])
 def test_small_token_counts(tokens, hidden, f, rank, out):
     """Few tokens: the two products have few tiles and run split-K (k-slices
     written as fp32 partial products, summed in slice order by the kernel
-    that applies the epilogue) up to 128 tokens; bias, residual and the
+    that applies the epilogue) up to 512 tokens; bias, residual and the
     saved pre-activation included, every element against the oracle."""
     t = 4
     wl = inputs.MlpWorkload(f"small_{tokens}_{hidden}_{f}", tokens, hidden, f * t, t, "bf16", 1.0, 0.02,
