@@ -34,9 +34,9 @@ __device__ __forceinline__ void store4(void* out, bool f32, int64_t off, const f
   }
 }
 
-// One thread per 4 consecutive columns of one row.
-template <int EPI>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int ks,
+// One thread per 4 consecutive columns of one row; KS slabs.
+template <int EPI, int KS>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                              int64_t slab, int64_t M, int64_t N,
                                                              const Epilogue ep) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -44,8 +44,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   if (i >= M * qn) return;
   const int64_t m = i / qn, n = (i - m * qn) * 4;
   const float* p = part + m * N + n;
-  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(p);
-  for (int s = 1; s < ks; ++s) acc += *reinterpret_cast<const f32x4_t*>(p + s * slab);
+  // Every slab's load is issued before the first add (one memory round
+  // trip instead of one per slab); the sum runs in slice order.
+  f32x4_t x[KS];
+  static_for<KS>([&](auto S) { x[S] = *reinterpret_cast<const f32x4_t*>(p + S * slab); });
+  f32x4_t acc = x[0];
+  static_for<KS - 1>([&](auto S) { acc += x[S + 1]; });
   float v[4] = {acc[0], acc[1], acc[2], acc[3]};
   if (ep.bias != nullptr) {
     float b[4];
@@ -104,11 +108,17 @@ hipError_t launch_splitk_reduce(const float* part, int ksplit, int64_t M, int64_
   if (N % 4 != 0 || (ep.kind != EPI_GELU && ep.kind != EPI_LINEAR)) return hipErrorInvalidValue;
   const int64_t threads = M * (N / 4);
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
-  if (ep.kind == EPI_GELU)
-    hipLaunchKernelGGL(splitk_reduce_kernel<EPI_GELU>, grid, dim3(256), 0, stream, part, ksplit, M * N, M, N, ep);
-  else
-    hipLaunchKernelGGL(splitk_reduce_kernel<EPI_LINEAR>, grid, dim3(256), 0, stream, part, ksplit, M * N, M, N, ep);
-  return hipGetLastError();
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, part, M * N, M, N, ep);
+    return hipGetLastError();
+  };
+  const bool gelu = ep.kind == EPI_GELU;
+  switch (ksplit) {
+    case 2: return gelu ? launch(splitk_reduce_kernel<EPI_GELU, 2>) : launch(splitk_reduce_kernel<EPI_LINEAR, 2>);
+    case 4: return gelu ? launch(splitk_reduce_kernel<EPI_GELU, 4>) : launch(splitk_reduce_kernel<EPI_LINEAR, 4>);
+    case 8: return gelu ? launch(splitk_reduce_kernel<EPI_GELU, 8>) : launch(splitk_reduce_kernel<EPI_LINEAR, 8>);
+    default: return hipErrorInvalidValue;   // splitk_factor gives 2, 4 or 8 when it splits
+  }
 }
 
 }  // namespace tpk
