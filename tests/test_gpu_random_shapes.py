@@ -6,8 +6,8 @@ launcher select: 128 x 128, 128 x 384 and 256 x 256 tiles, one or several
 rounds of resident workgroups, ragged M and N, a partial last k-tile, and
 (when a k extent is a multiple of 64) the paired stages of a k-contiguous
 operand: A for the 128-row tiles of the forward products, B for the
-backward's dX and dH products; and small fp32 shapes through the fp32
-GEMM.  Tolerances as in the other GPU parity tests.
+backward's dX and dH products; the MLP shard at 1-512 tokens, whose
+products run split-K; and small fp32 shapes through the fp32 GEMM.  Tolerances as in the other GPU parity tests.
 """
 import numpy as np
 import pytest
@@ -82,6 +82,54 @@ def test_backward(tokens, hidden, f):
     ref = shard_ref(host64(x, "bf16"), host64(a, "bf16"), host64(b, "bf16"), host64(dz, "bf16"))
     got = run_bwd(wl, 1, xd, ad, bd, y, dev(dz, "bf16"), "f32")
     check_grads(got, ref, "bf16", f"random {tokens}x{hidden}x{f}")
+
+
+def _few_token_shapes(seed, n):
+    """Token counts of 1-512 (the MLP shard's products run split-K there:
+    64-row tiles up to 128 tokens, 128-row tiles above), widths a multiple
+    of 8, often of 64 so that the k range splits into 2, 4 or 8 slices."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        tokens = int(rng.integers(1, 513))
+        hidden, f = 8 * int(rng.integers(1, 260)), 8 * int(rng.integers(1, 260))
+        if rng.random() < 0.6:
+            hidden = 64 * max(1, hidden // 64)
+        if rng.random() < 0.6:
+            f = 64 * max(1, f // 64)
+        out.append((tokens, hidden, f))
+    return out
+
+
+@pytest.mark.parametrize("tokens,hidden,f", _few_token_shapes(31, 10 * SHAPE_SWEEP))
+def test_shard_few_tokens(tokens, hidden, f):
+    """The MLP shard entry point at few tokens (split-K products, their
+    ordered sums applying bias, saved pre-activation, GeLU and residual):
+    every element against the oracle, the pre-activation included.  Weights
+    at the workload's scale (0.02): the partial is checked end to end, so
+    its error includes the bf16 rounding of H_i, which grows with the
+    pre-activation's scale (at 0.05 and h ~1700 it reaches the bound on
+    the tiled path alone)."""
+    t = 2
+    wl = inputs.MlpWorkload(f"rand_few_{tokens}_{hidden}_{f}", tokens, hidden, f * t, t, "bf16", 1.0, 0.02,
+                            0.02, "f32")
+    x, a, bias_a = inputs.mlp_x_rows(wl), inputs.mlp_a_block(wl, 0), inputs.mlp_bias_a_block(wl, 0)
+    b, bias_b, res = inputs.mlp_b_block(wl, 0), inputs.mlp_bias_b(wl), inputs.mlp_residual_rows(wl)
+    say(f"random shapes: MLP shard at few tokens tokens={tokens} hidden={hidden} f={f}")
+    ws = torch.empty(binding.tp_mlp_shard_workspace_bytes(tokens, hidden, f * t, t, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    y = nan_tensor((tokens, f), torch.bfloat16)
+    z = nan_tensor((tokens, hidden), torch.float32)
+    binding.tp_mlp_shard_fwd(dev(x, "bf16"), dev(a, "bf16"), dev(b, "bf16"), z, ws, ffn=f * t, t=t, rank=0,
+                             bias_a_i=dev(bias_a, "bf16"), bias_b=dev(bias_b, "bf16"),
+                             residual=dev(res, "bf16"), y_save=y)
+    torch.cuda.synchronize()
+    pre = oracle.column_linear(host64(x, "bf16"), host64(a, "bf16"), host64(bias_a, "bf16"))
+    assert_close(to_np(y), pre, "bf16", "few-token shard: saved pre-activation")
+    ref = oracle.row_linear(oracle.column_linear(host64(x, "bf16"), host64(a, "bf16"), host64(bias_a, "bf16"),
+                                                 apply_gelu=True),
+                            host64(b, "bf16"), host64(bias_b, "bf16"), host64(res, "bf16"), rank=0)
+    assert_close(to_np(z), ref, "bf16", "few-token shard: partial")
 
 
 def _f32_shapes(seed, n):
